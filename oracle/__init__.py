@@ -1,0 +1,174 @@
+"""fp64 CPU oracle for the selective scan (S6) and its one-token decode step.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the benchmark's
+CPU-baseline leg are the only callers.  The HIP library never imports, links or runs
+anything here, and this package imports nothing from the HIP library.
+
+The arithmetic lives in ``oracle.c`` (plain C, IEEE fp64, sequential in time, OpenMP
+over independent rows); this module builds it with gcc, converts inputs to exact
+float64 copies and calls it through ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+_lock = threading.Lock()
+
+_d = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (fp64, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                build(force=False)
+            lib = ctypes.CDLL(_LIB_PATH)
+            lib.oracle_selective_scan.restype = ctypes.c_int
+            lib.oracle_selective_scan.argtypes = [
+                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i64p,
+                _d, _d, _d, _d, _d, _d, _d, _d, ctypes.c_int, _d, _d, ctypes.c_int]
+            lib.oracle_state_update.restype = ctypes.c_int
+            lib.oracle_state_update.argtypes = [
+                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i64p,
+                _d, _d, _d, _d, _d, _d, _d, _d, _d, _d, ctypes.c_int]
+            lib.oracle_softplus.restype = None
+            lib.oracle_softplus.argtypes = [_d, _d, ctypes.c_int64]
+            lib.oracle_silu.restype = None
+            lib.oracle_silu.argtypes = [_d, _d, ctypes.c_int64]
+            lib.oracle_max_threads.restype = ctypes.c_int
+            lib.oracle_max_threads.argtypes = []
+            _lib = lib
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return ctypes.cast(None, _d)
+    return a.ctypes.data_as(_d)
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def softplus(x) -> np.ndarray:
+    x = _f64(x)
+    y = np.empty_like(x)
+    _load().oracle_softplus(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def silu(x) -> np.ndarray:
+    x = _f64(x)
+    y = np.empty_like(x)
+    _load().oracle_silu(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus_flag=True,
+                   rows=None, nthreads: int = 0):
+    """Run the fp64 scan.
+
+    u, delta, z: (batch, d_inner, L); A: (d_inner, d_state); B, C: (batch, d_state, L);
+    D, delta_bias: (d_inner,).  Any float dtype; values are taken exactly as float64.
+    rows: optional flat row indices r = b * d_inner + d to compute (default: all rows).
+    Returns (out, last_state): (batch, d_inner, L) and (batch, d_inner, d_state) when rows
+    is None, else (len(rows), L) and (len(rows), d_state).
+    """
+    u = np.asarray(u)
+    Bt, Dn, L = u.shape
+    N = np.asarray(A).shape[1]
+    if rows is None:
+        sel = np.arange(Bt * Dn, dtype=np.int64)
+    else:
+        sel = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    ch = sel % Dn
+    rb = np.ascontiguousarray(sel // Dn)
+
+    def rows_of(a):
+        return None if a is None else _f64(np.asarray(a).reshape(Bt * Dn, L)[sel])
+
+    u_r, dl_r, z_r = rows_of(u), rows_of(delta), rows_of(z)
+    A_r = _f64(np.asarray(A)[ch])
+    D_r = None if D is None else _f64(np.asarray(D)[ch])
+    b_r = None if delta_bias is None else _f64(np.asarray(delta_bias)[ch])
+    Bm, Cm = _f64(B), _f64(C)
+    R = sel.size
+    out = np.empty((R, L), np.float64)
+    last = np.empty((R, N), np.float64)
+    rc = _load().oracle_selective_scan(
+        R, N, L, Bt, rb.ctypes.data_as(_i64p), _ptr(u_r), _ptr(dl_r), _ptr(z_r), _ptr(A_r),
+        _ptr(Bm), _ptr(Cm), _ptr(D_r), _ptr(b_r), int(bool(softplus_flag)), _ptr(out),
+        _ptr(last), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_selective_scan rejected its arguments")
+    if rows is None:
+        return out.reshape(Bt, Dn, L), last.reshape(Bt, Dn, N)
+    return out, last
+
+
+def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
+                           rows=None, nthreads: int = 0):
+    """One fp64 decode step.
+
+    state: (batch, d_inner, d_state) float64, updated in place (rows=None) -- or, with
+    rows given, a (len(rows), d_state) float64 array of those rows' states, updated in place.
+    x, dt, z: (batch, d_inner); B, C: (batch, d_state); A: (d_inner, d_state).
+    Returns out: (batch, d_inner), or (len(rows),) with rows.
+    """
+    x = np.asarray(x)
+    Bt, Dn = x.shape
+    N = np.asarray(A).shape[1]
+    if rows is None:
+        sel = np.arange(Bt * Dn, dtype=np.int64)
+        if not (isinstance(state, np.ndarray) and state.dtype == np.float64
+                and state.flags.c_contiguous and state.shape == (Bt, Dn, N)):
+            raise ValueError("state must be a C-contiguous float64 (batch, d_inner, d_state) array")
+    else:
+        sel = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        if not (isinstance(state, np.ndarray) and state.dtype == np.float64
+                and state.flags.c_contiguous and state.shape == (sel.size, N)):
+            raise ValueError("state must be a C-contiguous float64 (len(rows), d_state) array")
+    ch = sel % Dn
+    rb = np.ascontiguousarray(sel // Dn)
+
+    def rows_of(a):
+        return None if a is None else _f64(np.asarray(a).reshape(Bt * Dn)[sel])
+
+    R = sel.size
+    out = np.empty(R, np.float64)
+    rc = _load().oracle_state_update(
+        R, N, Bt, rb.ctypes.data_as(_i64p), _ptr(state), _ptr(rows_of(x)), _ptr(rows_of(dt)),
+        _ptr(rows_of(z)), _ptr(_f64(np.asarray(A)[ch])), _ptr(_f64(B)), _ptr(_f64(C)),
+        _ptr(None if D is None else _f64(np.asarray(D)[ch])),
+        _ptr(None if dt_bias is None else _f64(np.asarray(dt_bias)[ch])), _ptr(out), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_state_update rejected its arguments")
+    return out.reshape(Bt, Dn) if rows is None else out

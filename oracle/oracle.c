@@ -1,0 +1,155 @@
+/*
+ * oracle.c -- plain fp64 CPU definition of Mamba's selective SSM scan (S6) and of its
+ * one-token recurrent step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path links, loads or calls this
+ * file: only the tests, the smoke check and the benchmark's CPU-baseline leg use it.
+ * It shares no code, header or constant with the HIP library.
+ *
+ * What it computes, and where the pages define it:
+ *   - Keras/TensorFlow tutorial page ("Mamba SSM concept and implementation in Keras and
+ *     TensorFlow"), function `selective_scan`: A_bar = exp(delta * A) per (t, d, n), the
+ *     input term delta * u * B (Euler form for B; the zero-order-hold formulas on that page
+ *     did not survive extraction), the inclusive recurrence h_t = A_bar_t h_{t-1} + B_bar_t
+ *     u_t from h_0 = 0 (the page's unrolled sum assumes h0 = 0), y_t = sum_n C_t h_t, then
+ *     the D skip y + u * D.
+ *   - Same page, `MambaBlock.ssm`: delta = softplus(delta_projection(...)) where the
+ *     projection carries a bias, so delta = softplus(delta_raw + bias).
+ *   - Same page, `MambaBlock.call`: the SSM output is multiplied by swish(res) = silu(z)
+ *     after the D skip, so out = (C.h + D u) * silu(z).
+ *   - mamba-jax README and the upstream README (generation): the recurrent mode carries the
+ *     state token by token; one token of it is the loop body below with L = 1.
+ * Arithmetic is IEEE fp64 throughout, sequential in t; rows (batch, channel) are
+ * independent and are the only thing run in parallel.
+ *
+ * Parity pins (all in tests/test_oracle_pins.py, each independent of this loop): the L = 1
+ * closed form; the LTI case against a brute-force convolution with kernel
+ * K_k = sum_n C_n exp(k delta A_n) delta B_n; the unrolled time-varying sum with exponents
+ * summed directly; the tutorial's own suffix-sum / ratio formulation; linearity in u; A = 0
+ * against numpy.cumsum; the memoryless limit; causality; gate / skip / bias placement;
+ * the decode step chained L times against the scan; softplus and silu against numpy/scipy.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* softplus(x) = log(1 + e^x), written as max(x, 0) + log1p(e^-|x|) so it neither
+ * overflows nor loses digits for very negative x.  (tutorial page, tf.nn.softplus) */
+static double sp(double x) { return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x))); }
+
+/* silu(v) = v * sigmoid(v) = v / (1 + e^-v)  (tutorial page, tf.nn.swish) */
+static double silu(double v) { return v / (1.0 + exp(-v)); }
+
+void oracle_softplus(const double* x, double* y, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) y[i] = sp(x[i]);
+}
+
+void oracle_silu(const double* x, double* y, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) y[i] = silu(x[i]);
+}
+
+static void set_threads(int nthreads) {
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Forward selective scan over R independent rows.
+ *   row_batch[r]      batch index b of row r (selects B[b], C[b])
+ *   u, delta, z       R x L (z may be NULL: no gate); delta is the raw value before bias
+ *   A                 R x N (A of the row's channel)
+ *   Bm, Cm            Bt x N x L
+ *   D, bias           R (either may be NULL: treated as 0)
+ *   softplus_flag     nonzero: delta = softplus(delta_raw + bias); zero: delta_raw + bias
+ *   out               R x L
+ *   last_state        R x N, h_L (may be NULL)
+ * Returns 0, or -1 for a bad size.
+ */
+int oracle_selective_scan(int64_t R, int64_t N, int64_t L, int64_t Bt,
+                          const int64_t* row_batch,
+                          const double* u, const double* delta, const double* z,
+                          const double* A, const double* Bm, const double* Cm,
+                          const double* D, const double* bias, int softplus_flag,
+                          double* out, double* last_state, int nthreads) {
+    if (R < 0 || N <= 0 || L < 0 || Bt <= 0) return -1;
+    set_threads(nthreads);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t r = 0; r < R; ++r) {
+        const int64_t b = row_batch[r];
+        if (b < 0 || b >= Bt) { bad = 1; continue; }
+        double* h = (double*)calloc((size_t)N, sizeof(double)); /* h_0 = 0 */
+        if (!h) { bad = 1; continue; }
+        const double* Ar = A + r * N;
+        const double* Bb = Bm + b * N * L;
+        const double* Cb = Cm + b * N * L;
+        const double Dr = D ? D[r] : 0.0;
+        const double br = bias ? bias[r] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            const double ut = u[r * L + t];
+            const double pre = delta[r * L + t] + br;
+            const double dt = softplus_flag ? sp(pre) : pre;
+            double y = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                const double abar = exp(dt * Ar[n]);          /* A_bar = exp(delta A) */
+                h[n] = abar * h[n] + dt * Bb[n * L + t] * ut;  /* + delta B u        */
+                y += Cb[n * L + t] * h[n];                     /* C . h_t            */
+            }
+            y += Dr * ut;                                      /* D skip             */
+            out[r * L + t] = z ? y * silu(z[r * L + t]) : y;   /* gate after skip    */
+        }
+        if (last_state)
+            for (int64_t n = 0; n < N; ++n) last_state[r * N + n] = h[n];
+        free(h);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * One recurrent (decode) step over R rows, state updated in place.
+ *   state      R x N (in/out)
+ *   x, dt, z   R (z may be NULL); dt is raw, softplus(dt + dt_bias) is always applied
+ *   A          R x N
+ *   Bm, Cm     Bt x N (this token's B and C)
+ *   D, dt_bias R (may be NULL: 0)
+ *   out        R
+ */
+int oracle_state_update(int64_t R, int64_t N, int64_t Bt, const int64_t* row_batch,
+                        double* state, const double* x, const double* dt, const double* z,
+                        const double* A, const double* Bm, const double* Cm,
+                        const double* D, const double* dt_bias, double* out, int nthreads) {
+    if (R < 0 || N <= 0 || Bt <= 0) return -1;
+    set_threads(nthreads);
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t r = 0; r < R; ++r) {
+        const int64_t b = row_batch[r];
+        if (b < 0 || b >= Bt) { bad = 1; continue; }
+        double* h = state + r * N;
+        const double d = sp(dt[r] + (dt_bias ? dt_bias[r] : 0.0));
+        double y = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            h[n] = exp(d * A[r * N + n]) * h[n] + d * Bm[b * N + n] * x[r];
+            y += Cm[b * N + n] * h[n];
+        }
+        y += (D ? D[r] : 0.0) * x[r];
+        out[r] = z ? y * silu(z[r]) : y;
+    }
+    return bad ? -1 : 0;
+}

@@ -1,0 +1,305 @@
+"""Pins of the fp64 oracle to facts the pages and the mathematics fix.
+
+Every check here is computed by an independent route (a closed form, a brute-force sum,
+the tutorial page's own suffix-sum formulation, a numpy/scipy routine, an invariant) and
+never by re-running the oracle's own loop.  Sources: the Keras/TensorFlow Mamba tutorial
+page (sections on the discrete SSM, the convolution kernel K, the parallel associative
+scan, and its `selective_scan` / `MambaBlock` code), the mamba-jax README (recurrent
+`--scan` generation) and the upstream mamba README (delta bias initialisation).
+"""
+import numpy as np
+import pytest
+from scipy.special import expit
+
+from synth import scan_inputs, round_to_bf16
+
+RTOL = 1e-12
+
+
+def _close(a, b, rtol=RTOL, atol=1e-14):
+    np.testing.assert_allclose(a, b, rtol=rtol, atol=atol)
+
+
+def _np_softplus(x):
+    return np.logaddexp(0.0, x)
+
+
+def _np_silu(x):
+    return x * expit(x)
+
+
+def _small(seed=3, Bt=2, Dn=3, N=5, L=24, with_z=True, a_kind="random"):
+    s = scan_inputs(Bt, Dn, N, L, dtype="f32", with_z=with_z, seed=seed, a_kind=a_kind)
+    return s
+
+
+# ---------------------------------------------------------------- component functions
+
+def test_softplus_matches_logaddexp(oracle_mod):
+    x = np.concatenate([np.linspace(-60, 60, 2001), [-745.0, -30.5, 0.0, 1e-9, 700.0]])
+    _close(oracle_mod.softplus(x), _np_softplus(x), rtol=2e-15, atol=0)
+
+
+def test_silu_matches_expit(oracle_mod):
+    x = np.concatenate([np.linspace(-60, 60, 2001), [-700.0, 0.0, 1e-12, 700.0]])
+    _close(oracle_mod.silu(x), _np_silu(x), rtol=4e-15, atol=1e-300)
+
+
+# ---------------------------------------------------------------- closed forms
+
+def test_single_step_closed_form(oracle_mod):
+    """L = 1 from h_0 = 0: h_1 = delta B u (inclusive), out = (delta u C.B + D u) silu(z)."""
+    s = _small(L=1, Dn=7, N=6)
+    out, last = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias)
+    dl = _np_softplus(s.delta.astype(np.float64) + s.delta_bias[None, :, None])  # (Bt,Dn,1)
+    u = s.u.astype(np.float64)
+    CB = np.einsum("bnl,bnl->bl", s.C.astype(np.float64), s.B.astype(np.float64))  # (Bt,1)
+    y = dl * u * CB[:, None, :] + s.D[None, :, None] * u
+    _close(out, y * _np_silu(s.z.astype(np.float64)))
+    expect_last = dl[..., 0][:, :, None] * s.B[:, None, :, 0] * u[..., 0][:, :, None]
+    _close(last, expect_last)
+
+
+def test_lti_equals_convolution(oracle_mod):
+    """Delta, B, C constant in time: y = K * u + D u with K_k = sum_n C_n e^{k delta A_n} delta B_n."""
+    rng = np.random.default_rng(11)
+    Bt, Dn, N, L = 1, 4, 6, 48
+    u = rng.standard_normal((Bt, Dn, L))
+    raw = np.repeat(rng.standard_normal((Bt, Dn, 1)), L, axis=2)
+    A = -np.exp(rng.uniform(np.log(0.2), np.log(4.0), (Dn, N)))
+    B = np.repeat(rng.standard_normal((Bt, N, 1)), L, axis=2)
+    C = np.repeat(rng.standard_normal((Bt, N, 1)), L, axis=2)
+    D = rng.standard_normal(Dn)
+    bias = rng.uniform(-3, 0, Dn)
+    out, last = oracle_mod.selective_scan(u, raw, A, B, C, D, None, bias)
+    for d in range(Dn):
+        dl = _np_softplus(raw[0, d, 0] + bias[d])
+        k = np.arange(L)
+        K = (C[0, :, 0][None, :] * np.exp(k[:, None] * dl * A[d][None, :]) * dl * B[0, :, 0][None, :]).sum(1)
+        y = np.array([np.dot(K[: t + 1], u[0, d, t::-1]) for t in range(L)]) + D[d] * u[0, d]
+        _close(out[0, d], y, rtol=1e-11, atol=1e-13)
+
+
+def test_unrolled_time_varying_sum(oracle_mod):
+    """h_t[n] = sum_{s<=t} exp(A_n sum_{r=s+1..t} delta_r) delta_s B_s u_s, exponent summed directly."""
+    s = _small(seed=5, Bt=2, Dn=3, N=5, L=30)
+    out, last = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias)
+    Bt, Dn, L = s.u.shape
+    N = s.A.shape[1]
+    for b in range(Bt):
+        for d in range(Dn):
+            dl = _np_softplus(s.delta[b, d].astype(np.float64) + s.delta_bias[d])
+            u = s.u[b, d].astype(np.float64)
+            for t in range(L):
+                h = np.zeros(N)
+                for s_ in range(t + 1):
+                    expo = s.A[d].astype(np.float64) * np.sum(dl[s_ + 1: t + 1])
+                    h += np.exp(expo) * dl[s_] * s.B[b, :, s_] * u[s_]
+                y = np.dot(s.C[b, :, t], h) + s.D[d] * u[t]
+                y *= _np_silu(float(s.z[b, d, t]))
+                np.testing.assert_allclose(out[b, d, t], y, rtol=1e-11, atol=1e-13)
+            np.testing.assert_allclose(last[b, d], h, rtol=1e-11, atol=1e-13)
+
+
+def test_tutorial_suffix_sum_formulation(oracle_mod):
+    """The tutorial's own route: exponent suffix sums, exp, cumsum of dBu * P, divide by (P + 1e-12).
+
+    Only valid while the exponents stay small (the 1e-12 term then perturbs < 1e-10);
+    it ties the oracle to the one piece of executable math on the pages.
+    """
+    rng = np.random.default_rng(7)
+    Bt, Dn, N, L = 2, 3, 4, 20
+    u = rng.standard_normal((Bt, Dn, L))
+    dl = rng.uniform(0.001, 0.1, (Bt, Dn, L))          # delta given directly (softplus off)
+    A = -rng.uniform(0.5, 1.5, (Dn, N))
+    B = rng.standard_normal((Bt, N, L))
+    C = rng.standard_normal((Bt, N, L))
+    D = rng.standard_normal(Dn)
+    out, _ = oracle_mod.selective_scan(u, dl, A, B, C, D, None, None, softplus_flag=False)
+    # (b, l, d, n) tensors as on the tutorial page
+    dA = np.einsum("bdl,dn->bldn", dl, A)
+    dBu = np.einsum("bdl,bdl,bnl->bldn", dl, u, B)
+    suffix = np.zeros_like(dA)                           # suffix[t] = sum_{r > t} dA[r]
+    suffix[:, :-1] = np.flip(np.cumsum(np.flip(dA[:, 1:], axis=1), axis=1), axis=1)
+    P = np.exp(suffix)
+    h = np.cumsum(dBu * P, axis=1) / (P + 1e-12)
+    y = np.einsum("bldn,bnl->bdl", h, C) + u * D[None, :, None]
+    _close(out, y, rtol=1e-9, atol=1e-12)
+
+
+def test_zero_A_is_cumsum(oracle_mod):
+    """A = 0: A_bar = 1, so h_t = numpy.cumsum(delta B u) over t."""
+    s = _small(seed=8, L=40)
+    A0 = np.zeros_like(s.A)
+    out, last = oracle_mod.selective_scan(s.u, s.delta, A0, s.B, s.C, s.D, None, s.delta_bias)
+    dl = _np_softplus(s.delta.astype(np.float64) + s.delta_bias[None, :, None])
+    bu = dl[:, :, None, :] * s.B[:, None, :, :] * s.u[:, :, None, :]     # (Bt,Dn,N,L)
+    h = np.cumsum(bu, axis=-1)
+    y = np.einsum("bdnl,bnl->bdl", h, s.C) + s.D[None, :, None] * s.u
+    _close(out, y, rtol=1e-11, atol=1e-12)
+    _close(last, h[..., -1], rtol=1e-11, atol=1e-12)
+
+
+def test_memoryless_limit(oracle_mod):
+    """delta |A| >> 1: exp underflows to exactly 0, so h_t = delta_t B_t u_t."""
+    s = _small(seed=9, L=16)
+    A = np.full_like(s.A, -1e7)
+    out, last = oracle_mod.selective_scan(s.u, s.delta, A, s.B, s.C, s.D, s.z, s.delta_bias)
+    dl = _np_softplus(s.delta.astype(np.float64) + s.delta_bias[None, :, None])
+    assert dl.min() * 1e7 > 800  # exp(-800) == 0.0 in fp64
+    h = dl[:, :, None, :] * s.B[:, None, :, :] * s.u[:, :, None, :]
+    y = np.einsum("bdnl,bnl->bdl", h, s.C) + s.D[None, :, None] * s.u
+    _close(out, y * _np_silu(s.z.astype(np.float64)))
+    _close(last, h[..., -1])
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_linear_in_u(oracle_mod):
+    """Gate off, delta/B/C fixed: the map u -> y is linear."""
+    s = _small(seed=12, L=32)
+    rng = np.random.default_rng(2)
+    u1, u2 = rng.standard_normal(s.u.shape), rng.standard_normal(s.u.shape)
+    al, be = 0.75, -2.5
+
+    def run(u):
+        return oracle_mod.selective_scan(u, s.delta, s.A, s.B, s.C, s.D, None, s.delta_bias)
+
+    o1, l1 = run(u1)
+    o2, l2 = run(u2)
+    o3, l3 = run(al * u1 + be * u2)
+    _close(o3, al * o1 + be * o2, rtol=1e-11, atol=1e-12)
+    _close(l3, al * l1 + be * l2, rtol=1e-11, atol=1e-12)
+
+
+def test_causality(oracle_mod):
+    """Changing any input at t >= t0 leaves out[..., :t0] bit-identical."""
+    s = _small(seed=13, L=40)
+    t0 = 17
+    base, _ = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias)
+    rng = np.random.default_rng(4)
+    u, dl, z, B, C = (a.copy() for a in (s.u, s.delta, s.z, s.B, s.C))
+    for a in (u, dl, z, B, C):
+        a[..., t0:] = rng.standard_normal(a[..., t0:].shape)
+    pert, _ = oracle_mod.selective_scan(u, dl, s.A, B, C, s.D, z, s.delta_bias)
+    assert np.array_equal(base[..., :t0], pert[..., :t0])
+    assert not np.array_equal(base[..., t0:], pert[..., t0:])
+
+
+def test_channel_permutation_and_batch_independence(oracle_mod):
+    s = _small(seed=14, Bt=3, Dn=5, L=20)
+    base, last = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias)
+    perm = np.array([3, 0, 4, 1, 2])
+    po, pl = oracle_mod.selective_scan(s.u[:, perm], s.delta[:, perm], s.A[perm], s.B, s.C,
+                                       s.D[perm], s.z[:, perm], s.delta_bias[perm])
+    assert np.array_equal(po, base[:, perm]) and np.array_equal(pl, last[:, perm])
+    one, _ = oracle_mod.selective_scan(s.u[1:2], s.delta[1:2], s.A, s.B[1:2], s.C[1:2], s.D,
+                                       s.z[1:2], s.delta_bias)
+    assert np.array_equal(one[0], base[1])
+    # a row subset gives the same values as the full run
+    rows = np.array([0, 7, 14])
+    so, sl = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias, rows=rows)
+    assert np.array_equal(so, base.reshape(-1, 20)[rows])
+    assert np.array_equal(sl, last.reshape(-1, s.A.shape[1])[rows])
+
+
+def test_gate_multiplies_skipped_output(oracle_mod):
+    """out(z) = out(no z) * silu(z): the gate wraps y + D u, it is not inside the skip."""
+    s = _small(seed=15, L=24)
+    og, _ = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias)
+    on, _ = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, None, s.delta_bias)
+    _close(og, on * _np_silu(s.z.astype(np.float64)), rtol=1e-14, atol=1e-300)
+
+
+def test_D_is_a_skip(oracle_mod):
+    """out(D) - out(D = 0) = D u exactly up to rounding; the state does not see D."""
+    s = _small(seed=16, L=24)
+    D = 1.7 * s.D.astype(np.float64)
+    o1, l1 = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, D, None, s.delta_bias)
+    o0, l0 = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, None, None, s.delta_bias)
+    _close(o1 - o0, D[None, :, None] * s.u, rtol=1e-12, atol=1e-13)
+    assert np.array_equal(l1, l0)
+
+
+def test_bias_added_before_softplus(oracle_mod):
+    s = _small(seed=17, L=24)
+    ob, lb = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias)
+    shifted = s.delta.astype(np.float64) + s.delta_bias[None, :, None].astype(np.float64)
+    on, ln = oracle_mod.selective_scan(s.u, shifted, s.A, s.B, s.C, s.D, s.z, None)
+    assert np.array_equal(ob, on) and np.array_equal(lb, ln)
+
+
+def test_softplus_off_uses_delta_directly(oracle_mod):
+    """softplus_flag = 0: delta = delta_raw + bias, checked against the unrolled sum."""
+    rng = np.random.default_rng(18)
+    Bt, Dn, N, L = 1, 2, 3, 12
+    u = rng.standard_normal((Bt, Dn, L))
+    dl = rng.uniform(0.01, 0.2, (Bt, Dn, L))
+    bias = rng.uniform(0, 0.05, Dn)
+    A = -rng.uniform(0.5, 3, (Dn, N))
+    B, C = rng.standard_normal((Bt, N, L)), rng.standard_normal((Bt, N, L))
+    out, _ = oracle_mod.selective_scan(u, dl, A, B, C, None, None, bias, softplus_flag=False)
+    for d in range(Dn):
+        D_ = dl[0, d] + bias[d]
+        for t in range(L):
+            h = sum(np.exp(A[d] * D_[s + 1: t + 1].sum()) * D_[s] * B[0, :, s] * u[0, d, s]
+                    for s in range(t + 1))
+            np.testing.assert_allclose(out[0, d, t], np.dot(C[0, :, t], h), rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------- recurrent mode
+
+def test_decode_chain_equals_scan(oracle_mod):
+    """The one-token step chained L times from h = 0 reproduces every output and h_L."""
+    s = _small(seed=19, Bt=2, Dn=4, N=5, L=33)
+    out, last = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias)
+    Bt, Dn, L = s.u.shape
+    state = np.zeros((Bt, Dn, s.A.shape[1]))
+    for t in range(L):
+        o = oracle_mod.selective_state_update(state, s.u[..., t], s.delta[..., t], s.A,
+                                              s.B[..., t], s.C[..., t], s.D, s.z[..., t],
+                                              s.delta_bias)
+        _close(o, out[..., t])
+    _close(state, last)
+
+
+def test_scan_then_decode_continues(oracle_mod):
+    """scan(L1) then decode of the remaining tokens from last_state = scan(L)."""
+    s = _small(seed=20, L=30)
+    out, last = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias)
+    L1 = 11
+    o1, state = oracle_mod.selective_scan(s.u[..., :L1], s.delta[..., :L1], s.A, s.B[..., :L1],
+                                          s.C[..., :L1], s.D, s.z[..., :L1], s.delta_bias)
+    _close(o1, out[..., :L1])
+    state = np.ascontiguousarray(state)
+    for t in range(L1, 30):
+        o = oracle_mod.selective_state_update(state, s.u[..., t], s.delta[..., t], s.A,
+                                              s.B[..., t], s.C[..., t], s.D, s.z[..., t],
+                                              s.delta_bias)
+        _close(o, out[..., t])
+    _close(state, last)
+
+
+# ---------------------------------------------------------------- input generator
+
+def test_inputs_are_deterministic_and_seeded():
+    a = scan_inputs(2, 8, 16, 64, dtype="bf16", seed=0)
+    b = scan_inputs(2, 8, 16, 64, dtype="bf16", seed=0)
+    c = scan_inputs(2, 8, 16, 64, dtype="bf16", seed=1)
+    for f in ("u", "delta", "z", "A", "B", "C", "D", "delta_bias"):
+        assert np.array_equal(getattr(a, f), getattr(b, f))
+    assert not np.array_equal(a.u, c.u)
+    assert np.all(a.A == -np.arange(1, 17, dtype=np.float32)[None, :])
+    dt = _np_softplus(a.delta_bias.astype(np.float64))
+    assert dt.min() >= 1e-3 * (1 - 1e-5) and dt.max() <= 1e-1 * (1 + 1e-5)
+
+
+def test_bf16_rounding_matches_torch():
+    import torch
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32),
+                        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 0.0, 3e-39],
+                                 dtype=np.float32)])
+    ours = round_to_bf16(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(ours.view(np.uint32), ref.view(np.uint32))
