@@ -1,0 +1,176 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective-scan hot path on one MI355X.
+
+One step = the whole hot path over one batch of the Mamba-2.8B-shaped layer
+(batch 4, d_inner 5120, d_state 16, L 2048; bf16 u / delta / z / out, fp32 A / B / C / D /
+state; softplus, delta bias, D skip and silu(z) gate on):
+  1. mss_selective_scan_fwd over the 2048-token sequence (prefill), writing out and h_L;
+  2. one mss_selective_state_update token continuing from h_L (decode).
+Inputs are seeded synthetic data (synth.scan_inputs, seed 0) resident in HBM before timing.
+Three copies of the inputs are rotated so that a step never finds its inputs in the 256 MB
+Infinity Cache from the previous step.
+
+Prints ONE JSON line.  `value` is algorithmic GB/s of the whole step (every input read once,
+every output written once) over the K timed steps; the scan alone is also timed with HIP
+events on the stream it runs on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
+WORKLOAD = "mamba2p8b_bf16"
+
+
+def scan_bytes(Bt, Dn, N, L, es_io=2, with_z=True, last_state=True):
+    """Algorithmic bytes of one forward scan: each input read once, each output written once."""
+    io = Bt * Dn * L * es_io
+    n = io * (3 if with_z else 2)          # u, delta (, z)
+    n += 2 * Bt * N * L * 4                # B, C
+    n += Dn * N * 4 + 2 * Dn * 4           # A, D, delta_bias
+    n += io                                # out
+    n += Bt * Dn * N * 4 if last_state else 0
+    return n
+
+
+def decode_bytes(Bt, Dn, N, es_io=2):
+    rows = Bt * Dn
+    return (2 * rows * N * 4                # state read + write
+            + 3 * rows * es_io + rows * es_io  # x, dt, z in; out
+            + 2 * Bt * N * 4 + Dn * N * 4 + 2 * Dn * 4)
+
+
+def cpu_baseline(s, Bt, Dn, N, L):
+    """The fp64 oracle (as it stands) on the host cores, over the same step."""
+    import numpy as np
+    import oracle
+    threads = oracle.max_threads()
+    t = time.perf_counter()
+    _, last = oracle.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias)
+    state = np.ascontiguousarray(last)
+    oracle.selective_state_update(state, s.u[..., -1], s.delta[..., -1], s.A, s.B[..., -1],
+                                  s.C[..., -1], D=s.D, z=s.z[..., -1], dt_bias=s.delta_bias)
+    dt = time.perf_counter() - t
+    nbytes = scan_bytes(Bt, Dn, N, L) + decode_bytes(Bt, Dn, N)
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one full step: all {Bt * Dn} rows x {L} steps of the scan + 1 decode token, "
+                      f"fp64, {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=3, help="input sets rotated across steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build runs the scan on a single MI355X "
+              "(no multi-GPU path); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import selective_state_space_06_amd as mss
+    from synth import CONFIGS, scan_inputs
+
+    c = CONFIGS[WORKLOAD]
+    Bt, Dn, N, L = c["batch"], c["d_inner"], c["d_state"], c["L"]
+    mss.load_library()
+    s = scan_inputs(Bt, Dn, N, L, dtype="bf16", with_z=True, seed=0)
+    devc = torch.device("cuda:0")
+    torch.cuda.set_device(devc)
+
+    def up(a, bf16=False):
+        t = torch.from_numpy(np.ascontiguousarray(a)).to(devc)
+        return t.to(torch.bfloat16) if bf16 else t
+
+    A, D, bias = up(s.A), up(s.D), up(s.delta_bias)
+    sets = []
+    for _ in range(max(1, args.copies)):
+        sets.append(dict(u=up(s.u, True), delta=up(s.delta, True), z=up(s.z, True),
+                         B=up(s.B), C=up(s.C),
+                         out=torch.empty((Bt, Dn, L), dtype=torch.bfloat16, device=devc),
+                         last=torch.empty((Bt, Dn, N), dtype=torch.float32, device=devc),
+                         x1=up(s.u[..., -1], True), dt1=up(s.delta[..., -1], True),
+                         z1=up(s.z[..., -1], True), B1=up(np.ascontiguousarray(s.B[..., -1])),
+                         C1=up(np.ascontiguousarray(s.C[..., -1])),
+                         out1=torch.empty((Bt, Dn), dtype=torch.bfloat16, device=devc)))
+    stream = torch.cuda.current_stream(devc)
+
+    def step(k, ev=None):
+        p = sets[k % len(sets)]
+        if ev is not None:
+            ev[0].record(stream)
+        mss.selective_scan_fwd(p["u"], p["delta"], A, p["B"], p["C"], D=D, z=p["z"],
+                               delta_bias=bias, out=p["out"], last_state=p["last"])
+        if ev is not None:
+            ev[1].record(stream)
+        mss.selective_state_update(p["last"], p["x1"], p["dt1"], A, p["B1"], p["C1"], D=D,
+                                   z=p["z1"], dt_bias=bias, out=p["out1"])
+        if ev is not None:
+            ev[2].record(stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k, evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    scan_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    sb, db = scan_bytes(Bt, Dn, N, L), decode_bytes(Bt, Dn, N)
+    value = (sb + db) * args.steps / wall / 1e9
+    scan_avg_ms = float(np.mean(scan_ms))
+    scan_gbps = sb / (scan_avg_ms * 1e-3) / 1e9
+    updates = Bt * Dn * L * N + Bt * Dn * N
+
+    res = {
+        "metric": "selective-scan fwd GB/s + state-updates/s (B*D*L*N/s), % of MI355X HBM peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "storage": "bf16 u/delta/z/out; f32 A/B/C/D/delta_bias/state",
+        "data": "synthetic (seeded: N(0,1) u/delta/z/B/C, S4D-real A=-(n+1), D=1, "
+                "dt bias = inv_softplus(logU[1e-3,1e-1]))",
+        "config": {"workload": f"{WORKLOAD}: selective scan fwd (prefill) + 1 decode token",
+                   "batch": Bt, "d_inner": Dn, "d_state": N, "seq_len": L,
+                   "input_copies_rotated": len(sets)},
+        "state_updates_per_s": round(updates * args.steps / wall, 1),
+        "scan_fwd": {"avg_ms": round(scan_avg_ms, 4), "min_ms": round(float(np.min(scan_ms)), 4),
+                     "gbps": round(scan_gbps, 2), "frac_hbm_peak": round(scan_gbps / HBM_PEAK_GBPS, 4),
+                     "state_updates_per_s": round(Bt * Dn * L * N / (scan_avg_ms * 1e-3), 1)},
+        "decode_token": {"avg_us": round(float(np.mean(dec_ms)) * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(scan_gbps, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(scan_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "mss_selective_scan_fwd (one call: aggregate, combine and main "
+                               "kernels), timed with HIP events on its stream"},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(s, Bt, Dn, N, L)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

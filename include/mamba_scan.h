@@ -1,0 +1,120 @@
+/*
+ * mamba_scan.h -- C ABI of libmamba_scan: Mamba's selective state-space scan (S6) and its
+ * one-token recurrent step on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (Mamba paper, Section 3 "Selective State Space Models" / Algorithm 2, as
+ * restated on the Keras/TensorFlow Mamba tutorial page in its `selective_scan` and
+ * `MambaBlock.ssm` code, and on the upstream mamba README under "Selective SSM"):
+ * for every batch b, channel d and state n,
+ *     delta_t   = softplus(delta_raw_t + delta_bias[d])        (or without softplus)
+ *     Abar_t    = exp(delta_t * A[d, n])
+ *     h_t[n]    = Abar_t * h_{t-1}[n] + delta_t * B[b, n, t] * u_t      (h_0 = 0)
+ *     y_t       = sum_n C[b, n, t] * h_t[n] + D[d] * u_t
+ *     out_t     = y_t * silu(z_t)                              (when z is given)
+ * The input term is the Euler form delta * B * u, the form the tutorial's code computes;
+ * silu(v) = v / (1 + e^-v).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are passed as mss_tensor_t descriptors of DEVICE memory on the current HIP
+ *     device.  The caller allocates and owns every buffer; the library never frees or
+ *     keeps user memory.  Layout must be dense row-major (last stride 1, every other
+ *     stride the product of the later extents), strides counted in elements, and data
+ *     aligned to its element size.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream) and return
+ *     as soon as the work is queued.  Kernel faults surface at the caller's next
+ *     synchronisation.  Every argument is validated before any HIP call is made, so an
+ *     invalid call never touches the device.
+ *   - Return value: MSS_OK (0) or a negative mss_status_t; mss_status_string() names it.
+ *     No C++ exception crosses the ABI.
+ *   - The forward scan may split long sequences across workgroups; it then uses a
+ *     library-owned device workspace per (device, stream), grown on demand with hipMalloc
+ *     and kept until the process ends.  Calls on one stream are ordered, so they never
+ *     share that workspace concurrently.
+ */
+#ifndef MAMBA_SCAN_H
+#define MAMBA_SCAN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSS_VERSION 10000 /* major * 10000 + minor * 100 + patch */
+
+typedef enum { MSS_F32 = 0, MSS_BF16 = 1 } mss_dtype_t;
+
+typedef enum {
+    MSS_OK = 0,
+    MSS_ERR_NULL_ARG = -1,    /* a required descriptor or its data pointer is NULL          */
+    MSS_ERR_SHAPE = -2,       /* ndim or extents inconsistent with the other arguments      */
+    MSS_ERR_DTYPE = -3,       /* dtype not allowed for that argument                         */
+    MSS_ERR_LAYOUT = -4,      /* not dense row-major, or misaligned data pointer             */
+    MSS_ERR_ALIAS = -5,       /* an output overlaps an input or another output               */
+    MSS_ERR_UNSUPPORTED = -6, /* valid but not implemented (d_state not 16, sizes too large) */
+    MSS_ERR_HIP = -7          /* the HIP runtime reported an error while queuing the work    */
+} mss_status_t;
+
+/* A dense tensor in device memory.  Only the first `ndim` entries of shape/stride are read. */
+typedef struct {
+    void* data;        /* device pointer                                   */
+    int32_t dtype;     /* mss_dtype_t                                      */
+    int32_t ndim;      /* 1, 2 or 3                                        */
+    int64_t shape[3];
+    int64_t stride[3]; /* in elements                                      */
+} mss_tensor_t;
+
+/*
+ * Forward selective scan (the equations above) over a whole sequence, h_0 = 0.
+ *   u, delta    (batch, d_inner, L)      f32 or bf16, same dtype; delta is the raw value
+ *   A           (d_inner, d_state)       f32, real (callers pass A, e.g. -exp(A_log))
+ *   B, C        (batch, d_state, L)      f32, one B and C per (batch, time) shared by all d
+ *   D           (d_inner,)               f32, nullable (no skip)
+ *   z           (batch, d_inner, L)      dtype of u, nullable (no gate)
+ *   delta_bias  (d_inner,)               f32, nullable (bias 0)
+ *   softplus_flag  nonzero: delta = softplus(delta_raw + bias); zero: delta_raw + bias
+ *   out         (batch, d_inner, L)      dtype of u, written
+ *   last_state  (batch, d_inner, d_state) f32, nullable; written with h_L (zeros if L = 0)
+ * d_state must be 16.  out must not overlap any input or last_state.
+ */
+int mss_selective_scan_fwd(const mss_tensor_t* u, const mss_tensor_t* delta,
+                           const mss_tensor_t* A, const mss_tensor_t* B, const mss_tensor_t* C,
+                           const mss_tensor_t* D, const mss_tensor_t* z,
+                           const mss_tensor_t* delta_bias, int softplus_flag,
+                           const mss_tensor_t* out, const mss_tensor_t* last_state,
+                           void* stream);
+
+/*
+ * One recurrent (decode) step: the same equations for a single token, continuing from
+ * `state`, which is updated in place (the recurrent mode the mamba-jax README's `--scan`
+ * generation loop and the upstream README's generation benchmark run token by token).
+ * softplus is always applied to dt + dt_bias.
+ *   state       (batch, d_inner, d_state) f32, read and written
+ *   x, dt       (batch, d_inner)         f32 or bf16, same dtype
+ *   A           (d_inner, d_state)       f32
+ *   B, C        (batch, d_state)         f32
+ *   D           (d_inner,)               f32, nullable
+ *   z           (batch, d_inner)         dtype of x, nullable
+ *   dt_bias     (d_inner,)               f32, nullable
+ *   out         (batch, d_inner)         dtype of x, written
+ * d_state must be 16.  out must not overlap any input or the state; the state must not
+ * overlap any input.
+ */
+int mss_selective_state_update(const mss_tensor_t* state, const mss_tensor_t* x,
+                               const mss_tensor_t* dt, const mss_tensor_t* A,
+                               const mss_tensor_t* B, const mss_tensor_t* C,
+                               const mss_tensor_t* D, const mss_tensor_t* z,
+                               const mss_tensor_t* dt_bias, const mss_tensor_t* out,
+                               void* stream);
+
+/* Static, NUL-terminated name of a status code ("MSS_OK", "MSS_ERR_SHAPE", ...). */
+const char* mss_status_string(int status);
+
+/* MSS_VERSION of the loaded library. */
+int mss_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_SCAN_H */

@@ -1,0 +1,20 @@
+"""libmamba_scan: Mamba's selective state-space scan (S6) and its one-token decode step,
+hand-written in HIP for AMD Instinct MI355X (gfx950), behind the C ABI of
+include/mamba_scan.h.  This package is the thin Python binding (ctypes + torch for device
+memory and streams); every step of the computation runs in the HIP kernels.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    MSS_BF16,
+    MSS_F32,
+    MssError,
+    Tensor,
+    load_library,
+    scan_fwd_raw,
+    selective_scan_fwd,
+    selective_state_update,
+    state_update_raw,
+    status_string,
+    version,
+)

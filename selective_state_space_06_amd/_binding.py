@@ -1,0 +1,156 @@
+"""ctypes binding of libmamba_scan (argument marshalling only; all compute runs in the HIP
+kernels behind the C ABI declared in include/mamba_scan.h).
+
+There is no fallback: if the shared library has not been built, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libmamba_scan.so")
+
+MSS_F32, MSS_BF16 = 0, 1
+STATUS = {0: "MSS_OK", -1: "MSS_ERR_NULL_ARG", -2: "MSS_ERR_SHAPE", -3: "MSS_ERR_DTYPE",
+          -4: "MSS_ERR_LAYOUT", -5: "MSS_ERR_ALIAS", -6: "MSS_ERR_UNSUPPORTED", -7: "MSS_ERR_HIP"}
+
+# every symbol include/mamba_scan.h declares
+EXPORTS = ("mss_selective_scan_fwd", "mss_selective_state_update", "mss_status_string",
+           "mss_version")
+
+
+class Tensor(ctypes.Structure):
+    """mss_tensor_t"""
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 3), ("stride", ctypes.c_int64 * 3)]
+
+    @classmethod
+    def make(cls, data: int, dtype: int, shape, stride=None) -> "Tensor":
+        t = cls()
+        t.data = data
+        t.dtype = dtype
+        t.ndim = len(shape)
+        if stride is None:
+            stride, acc = [], 1
+            for s in reversed(shape):
+                stride.insert(0, acc)
+                acc *= s
+        for i, (s, st) in enumerate(zip(shape, stride)):
+            t.shape[i] = s
+            t.stride[i] = st
+        return t
+
+
+_TP = ctypes.POINTER(Tensor)
+_lib = None
+_lock = threading.Lock()
+
+
+class MssError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where} failed: {STATUS.get(status, status)}")
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmamba_scan.so; raises if it is missing (build it first)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise RuntimeError(
+                    f"{path} is missing: build it with `python -m selective_state_space_06_amd.build` "
+                    "or __graft_entry__.build(); there is no fallback implementation")
+            lib = ctypes.CDLL(path)
+            lib.mss_selective_scan_fwd.restype = ctypes.c_int
+            lib.mss_selective_scan_fwd.argtypes = [_TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP,
+                                                   ctypes.c_int, _TP, _TP, ctypes.c_void_p]
+            lib.mss_selective_state_update.restype = ctypes.c_int
+            lib.mss_selective_state_update.argtypes = [_TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP,
+                                                       _TP, _TP, ctypes.c_void_p]
+            lib.mss_status_string.restype = ctypes.c_char_p
+            lib.mss_status_string.argtypes = [ctypes.c_int]
+            lib.mss_version.restype = ctypes.c_int
+            lib.mss_version.argtypes = []
+            _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load_library().mss_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(load_library().mss_version())
+
+
+def _ref(t):
+    return None if t is None else ctypes.byref(t)
+
+
+def scan_fwd_raw(u, delta, A, B, C, D, z, delta_bias, softplus_flag, out, last_state, stream) -> int:
+    """Direct call of mss_selective_scan_fwd with Tensor descriptors (or None)."""
+    return load_library().mss_selective_scan_fwd(
+        _ref(u), _ref(delta), _ref(A), _ref(B), _ref(C), _ref(D), _ref(z), _ref(delta_bias),
+        int(softplus_flag), _ref(out), _ref(last_state), stream)
+
+
+def state_update_raw(state, x, dt, A, B, C, D, z, dt_bias, out, stream) -> int:
+    """Direct call of mss_selective_state_update with Tensor descriptors (or None)."""
+    return load_library().mss_selective_state_update(
+        _ref(state), _ref(x), _ref(dt), _ref(A), _ref(B), _ref(C), _ref(D), _ref(z),
+        _ref(dt_bias), _ref(out), stream)
+
+
+# ----------------------------------------------------------------------- torch front end
+
+def _desc(t):
+    import torch
+    if t is None:
+        return None
+    if t.device.type != "cuda":
+        raise ValueError("libmamba_scan takes device tensors")
+    dt = {torch.float32: MSS_F32, torch.bfloat16: MSS_BF16}.get(t.dtype, -1)
+    return Tensor.make(t.data_ptr(), dt, list(t.shape), list(t.stride()))
+
+
+def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                       return_last_state=True, out=None, last_state=None):
+    """Forward selective scan on the current stream of u's device.
+
+    u, delta, z: (batch, d_inner, L) float32 or bfloat16; A: (d_inner, 16) float32;
+    B, C: (batch, 16, L) float32; D, delta_bias: (d_inner,) float32.
+    Returns out (dtype of u), or (out, last_state) with last_state (batch, d_inner, 16) float32.
+    """
+    import torch
+    if out is None:
+        out = torch.empty_like(u, memory_format=torch.contiguous_format)
+    if return_last_state and last_state is None:
+        last_state = torch.empty((u.shape[0], u.shape[1], A.shape[1]), dtype=torch.float32,
+                                 device=u.device)
+    with torch.cuda.device(u.device):
+        stream = torch.cuda.current_stream(u.device).cuda_stream
+        st = scan_fwd_raw(_desc(u), _desc(delta), _desc(A), _desc(B), _desc(C), _desc(D), _desc(z),
+                          _desc(delta_bias), 1 if delta_softplus else 0, _desc(out),
+                          _desc(last_state) if return_last_state else None, stream)
+    if st != 0:
+        raise MssError(st, "mss_selective_scan_fwd")
+    return (out, last_state) if return_last_state else out
+
+
+def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None):
+    """One decode step on the current stream; `state` (batch, d_inner, 16) float32 is updated
+    in place.  x, dt, z: (batch, d_inner) float32 or bfloat16; B, C: (batch, 16) float32.
+    Returns out (batch, d_inner) in x's dtype."""
+    import torch
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        st = state_update_raw(_desc(state), _desc(x), _desc(dt), _desc(A), _desc(B), _desc(C),
+                              _desc(D), _desc(z), _desc(dt_bias), _desc(out), stream)
+    if st != 0:
+        raise MssError(st, "mss_selective_state_update")
+    return out

@@ -1,0 +1,55 @@
+"""Build libmamba_scan.so (gfx950) in-tree with hipcc.
+
+    python -m selective_state_space_06_amd.build
+
+Every HIP source is compiled for gfx950 only, with packed-fp32 instruction selection
+turned off (-Xclang -target-feature -Xclang -packed-fp32-ops): plain fp32 VALU code.
+The host pass warns that it does not know that feature; the warning is harmless.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libmamba_scan.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+SOURCES = ["abi.hip", "scan_fwd.hip", "state_update.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC or install ROCm under /opt/rocm)")
+
+
+def compile_flags() -> list[str]:
+    return ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
+
+
+def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+    """Compile every source into LIB_PATH (atomically replaced). Returns the path."""
+    tmp = LIB_PATH + f".tmp{os.getpid()}"
+    cmd = [hipcc(), *compile_flags(), *(extra or []), "-shared",
+           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        sys.stderr.write(proc.stdout + proc.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,316 @@
+// abi.hip -- the extern "C" boundary of libmamba_scan: argument validation, the carry
+// workspace, and dispatch to the gfx950 kernels.  Every check runs before the first HIP call,
+// so invalid arguments never reach the device.
+#include <initializer_list>
+#include <mutex>
+#include <unordered_map>
+#include <utility>
+
+#include "mamba_scan.h"
+#include "mss_internal.hpp"
+
+namespace {
+
+using mss::kN;
+
+int64_t numel(const mss_tensor_t& t) {
+    int64_t n = 1;
+    for (int i = 0; i < t.ndim; ++i) n *= t.shape[i];
+    return n;
+}
+
+size_t elem_size(int32_t dtype) { return dtype == MSS_BF16 ? 2 : 4; }
+
+bool shape_is(const mss_tensor_t& t, int ndim, int64_t s0, int64_t s1 = 0, int64_t s2 = 0) {
+    if (t.ndim != ndim) return false;
+    const int64_t s[3] = {s0, s1, s2};
+    for (int i = 0; i < ndim; ++i)
+        if (t.shape[i] != s[i]) return false;
+    return true;
+}
+
+bool dense(const mss_tensor_t& t) {
+    if (numel(t) == 0) return true;
+    int64_t expect = 1;
+    for (int i = t.ndim - 1; i >= 0; --i) {
+        if (t.shape[i] != 1 && t.stride[i] != expect) return false;
+        expect *= t.shape[i];
+    }
+    return true;
+}
+
+bool aligned(const mss_tensor_t& t, size_t a) {
+    return (reinterpret_cast<uintptr_t>(t.data) % a) == 0;
+}
+
+struct Range {
+    uintptr_t lo, hi;
+};
+Range range_of(const mss_tensor_t* t) {
+    if (!t || !t->data) return {0, 0};
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(t->data);
+    return {lo, lo + static_cast<uintptr_t>(numel(*t)) * elem_size(t->dtype)};
+}
+bool overlap(const mss_tensor_t* a, const mss_tensor_t* b) {
+    const Range x = range_of(a), y = range_of(b);
+    if (x.lo == x.hi || y.lo == y.hi) return false;
+    return x.lo < y.hi && y.lo < x.hi;
+}
+
+// Status of one descriptor before its extents are compared: NULL descriptor or NULL data
+// (for a non-empty tensor) -> NULL_ARG; ndim outside 1..3 -> SHAPE.
+int check_desc(const mss_tensor_t* t, bool required) {
+    if (!t) return required ? MSS_ERR_NULL_ARG : MSS_OK;
+    if (t->ndim < 1 || t->ndim > 3) return MSS_ERR_SHAPE;
+    if (!t->data && numel(*t) != 0) return MSS_ERR_NULL_ARG;
+    return MSS_OK;
+}
+
+template <size_t K>
+int check_descs(const mss_tensor_t* const (&req)[K], std::initializer_list<const mss_tensor_t*> opt) {
+    for (const mss_tensor_t* t : req)
+        if (!t) return MSS_ERR_NULL_ARG;
+    for (const mss_tensor_t* t : req) {
+        const int s = check_desc(t, true);
+        if (s != MSS_OK) return s;
+    }
+    for (const mss_tensor_t* t : opt) {
+        const int s = check_desc(t, false);
+        if (s != MSS_OK) return s;
+    }
+    return MSS_OK;
+}
+
+// ---- per-device facts and the per-(device, stream) carry workspace
+struct WsKey {
+    int dev;
+    void* stream;
+    bool operator==(const WsKey& o) const { return dev == o.dev && stream == o.stream; }
+};
+struct WsHash {
+    size_t operator()(const WsKey& k) const {
+        return std::hash<void*>()(k.stream) * 31u + static_cast<size_t>(k.dev);
+    }
+};
+struct WsEntry {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_mu;
+std::unordered_map<WsKey, WsEntry, WsHash> g_ws;
+std::unordered_map<int, int> g_cus;
+
+hipError_t device_cus(int dev, int* cus) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_cus.find(dev);
+    if (it != g_cus.end()) {
+        *cus = it->second;
+        return hipSuccess;
+    }
+    int v = 0;
+    hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    g_cus[dev] = v;
+    *cus = v;
+    return hipSuccess;
+}
+
+hipError_t workspace(int dev, void* stream, size_t bytes, float** out) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    WsEntry& w = g_ws[WsKey{dev, stream}];
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            hipError_t e = hipFree(w.ptr);  // synchronises the device: no kernel still uses it
+            w.ptr = nullptr;
+            w.bytes = 0;
+            if (e != hipSuccess) return e;
+        }
+        const size_t grown = bytes + bytes / 4;
+        hipError_t e = hipMalloc(&w.ptr, grown);
+        if (e != hipSuccess) {
+            w.ptr = nullptr;
+            return e;
+        }
+        w.bytes = grown;
+    }
+    *out = static_cast<float*>(w.ptr);
+    return hipSuccess;
+}
+
+int validate_fwd(const mss_tensor_t* u, const mss_tensor_t* delta, const mss_tensor_t* A,
+                 const mss_tensor_t* B, const mss_tensor_t* C, const mss_tensor_t* D,
+                 const mss_tensor_t* z, const mss_tensor_t* bias, const mss_tensor_t* out,
+                 const mss_tensor_t* last) {
+    {
+        const mss_tensor_t* const req[] = {u, delta, A, B, C, out};
+        const int s = check_descs(req, {D, z, bias, last});
+        if (s != MSS_OK) return s;
+    }
+    if (u->ndim != 3 || A->ndim != 2) return MSS_ERR_SHAPE;
+    const int64_t Bt = u->shape[0], Dn = u->shape[1], L = u->shape[2], N = A->shape[1];
+    if (Bt < 0 || Dn < 0 || L < 0 || N < 0) return MSS_ERR_SHAPE;
+    if (!shape_is(*delta, 3, Bt, Dn, L) || !shape_is(*out, 3, Bt, Dn, L)) return MSS_ERR_SHAPE;
+    if (z && !shape_is(*z, 3, Bt, Dn, L)) return MSS_ERR_SHAPE;
+    if (!shape_is(*A, 2, Dn, N)) return MSS_ERR_SHAPE;
+    if (!shape_is(*B, 3, Bt, N, L) || !shape_is(*C, 3, Bt, N, L)) return MSS_ERR_SHAPE;
+    if (D && !shape_is(*D, 1, Dn)) return MSS_ERR_SHAPE;
+    if (bias && !shape_is(*bias, 1, Dn)) return MSS_ERR_SHAPE;
+    if (last && !shape_is(*last, 3, Bt, Dn, N)) return MSS_ERR_SHAPE;
+
+    if (u->dtype != MSS_F32 && u->dtype != MSS_BF16) return MSS_ERR_DTYPE;
+    if (delta->dtype != u->dtype || out->dtype != u->dtype || (z && z->dtype != u->dtype))
+        return MSS_ERR_DTYPE;
+    if (A->dtype != MSS_F32 || B->dtype != MSS_F32 || C->dtype != MSS_F32) return MSS_ERR_DTYPE;
+    if ((D && D->dtype != MSS_F32) || (bias && bias->dtype != MSS_F32) || (last && last->dtype != MSS_F32))
+        return MSS_ERR_DTYPE;
+
+    const mss_tensor_t* all[] = {u, delta, A, B, C, D, z, bias, out, last};
+    for (const mss_tensor_t* t : all) {
+        if (!t) continue;
+        if (!dense(*t) || !aligned(*t, elem_size(t->dtype))) return MSS_ERR_LAYOUT;
+    }
+    if (!aligned(*A, 16) || (last && !aligned(*last, 16))) return MSS_ERR_LAYOUT;
+
+    const mss_tensor_t* ins[] = {u, delta, A, B, C, D, z, bias};
+    for (const mss_tensor_t* t : ins) {
+        if (overlap(out, t)) return MSS_ERR_ALIAS;
+        if (last && overlap(last, t)) return MSS_ERR_ALIAS;
+    }
+    if (last && overlap(out, last)) return MSS_ERR_ALIAS;
+
+    if (N != kN) return MSS_ERR_UNSUPPORTED;
+    if (Bt > 65535) return MSS_ERR_UNSUPPORTED;
+    return MSS_OK;
+}
+
+int validate_decode(const mss_tensor_t* state, const mss_tensor_t* x, const mss_tensor_t* dt,
+                    const mss_tensor_t* A, const mss_tensor_t* B, const mss_tensor_t* C,
+                    const mss_tensor_t* D, const mss_tensor_t* z, const mss_tensor_t* bias,
+                    const mss_tensor_t* out) {
+    {
+        const mss_tensor_t* const req[] = {state, x, dt, A, B, C, out};
+        const int s = check_descs(req, {D, z, bias});
+        if (s != MSS_OK) return s;
+    }
+    if (state->ndim != 3) return MSS_ERR_SHAPE;
+    const int64_t Bt = state->shape[0], Dn = state->shape[1], N = state->shape[2];
+    if (Bt < 0 || Dn < 0 || N < 0) return MSS_ERR_SHAPE;
+    if (!shape_is(*x, 2, Bt, Dn) || !shape_is(*dt, 2, Bt, Dn) || !shape_is(*out, 2, Bt, Dn))
+        return MSS_ERR_SHAPE;
+    if (z && !shape_is(*z, 2, Bt, Dn)) return MSS_ERR_SHAPE;
+    if (!shape_is(*A, 2, Dn, N) || !shape_is(*B, 2, Bt, N) || !shape_is(*C, 2, Bt, N))
+        return MSS_ERR_SHAPE;
+    if (D && !shape_is(*D, 1, Dn)) return MSS_ERR_SHAPE;
+    if (bias && !shape_is(*bias, 1, Dn)) return MSS_ERR_SHAPE;
+
+    if (x->dtype != MSS_F32 && x->dtype != MSS_BF16) return MSS_ERR_DTYPE;
+    if (dt->dtype != x->dtype || out->dtype != x->dtype || (z && z->dtype != x->dtype))
+        return MSS_ERR_DTYPE;
+    if (state->dtype != MSS_F32 || A->dtype != MSS_F32 || B->dtype != MSS_F32 || C->dtype != MSS_F32)
+        return MSS_ERR_DTYPE;
+    if ((D && D->dtype != MSS_F32) || (bias && bias->dtype != MSS_F32)) return MSS_ERR_DTYPE;
+
+    const mss_tensor_t* all[] = {state, x, dt, A, B, C, D, z, bias, out};
+    for (const mss_tensor_t* t : all) {
+        if (!t) continue;
+        if (!dense(*t) || !aligned(*t, elem_size(t->dtype))) return MSS_ERR_LAYOUT;
+    }
+    if (!aligned(*state, 16) || !aligned(*A, 16) || !aligned(*B, 16) || !aligned(*C, 16))
+        return MSS_ERR_LAYOUT;
+
+    const mss_tensor_t* ins[] = {x, dt, A, B, C, D, z, bias};
+    for (const mss_tensor_t* t : ins) {
+        if (overlap(out, t) || overlap(state, t)) return MSS_ERR_ALIAS;
+    }
+    if (overlap(out, state)) return MSS_ERR_ALIAS;
+
+    if (N != kN) return MSS_ERR_UNSUPPORTED;
+    if (Bt * Dn * 4 > (int64_t)0x7fffffff * 256) return MSS_ERR_UNSUPPORTED;
+    return MSS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mss_version(void) { return MSS_VERSION; }
+
+const char* mss_status_string(int status) {
+    switch (status) {
+        case MSS_OK: return "MSS_OK";
+        case MSS_ERR_NULL_ARG: return "MSS_ERR_NULL_ARG";
+        case MSS_ERR_SHAPE: return "MSS_ERR_SHAPE";
+        case MSS_ERR_DTYPE: return "MSS_ERR_DTYPE";
+        case MSS_ERR_LAYOUT: return "MSS_ERR_LAYOUT";
+        case MSS_ERR_ALIAS: return "MSS_ERR_ALIAS";
+        case MSS_ERR_UNSUPPORTED: return "MSS_ERR_UNSUPPORTED";
+        case MSS_ERR_HIP: return "MSS_ERR_HIP";
+        default: return "MSS_ERR_UNKNOWN";
+    }
+}
+
+int mss_selective_scan_fwd(const mss_tensor_t* u, const mss_tensor_t* delta, const mss_tensor_t* A,
+                           const mss_tensor_t* B, const mss_tensor_t* C, const mss_tensor_t* D,
+                           const mss_tensor_t* z, const mss_tensor_t* delta_bias, int softplus_flag,
+                           const mss_tensor_t* out, const mss_tensor_t* last_state, void* stream) {
+    try {
+        const int st = validate_fwd(u, delta, A, B, C, D, z, delta_bias, out, last_state);
+        if (st != MSS_OK) return st;
+        mss::ScanLaunch a;
+        a.u = u->data; a.delta = delta->data; a.z = z ? z->data : nullptr;
+        a.A = static_cast<const float*>(A->data);
+        a.B = static_cast<const float*>(B->data);
+        a.C = static_cast<const float*>(C->data);
+        a.D = D ? static_cast<const float*>(D->data) : nullptr;
+        a.bias = delta_bias ? static_cast<const float*>(delta_bias->data) : nullptr;
+        a.out = out->data;
+        a.last_state = last_state ? static_cast<float*>(last_state->data) : nullptr;
+        a.Bt = u->shape[0]; a.Dn = u->shape[1]; a.L = u->shape[2];
+        a.softplus = softplus_flag ? 1 : 0;
+        a.bf16 = u->dtype == MSS_BF16;
+        const size_t es = elem_size(u->dtype);
+        a.vec_ok = (a.L * static_cast<int64_t>(es)) % 16 == 0 && aligned(*u, 16) &&
+                   aligned(*delta, 16) && aligned(*out, 16) && (!z || aligned(*z, 16));
+        if (a.Bt * a.Dn == 0) return MSS_OK;
+
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return MSS_ERR_HIP;
+        if (device_cus(dev, &cus) != hipSuccess) return MSS_ERR_HIP;
+        const mss::ScanPlan plan = mss::plan_scan(a, cus);
+        float* ws = nullptr;
+        if (plan.workspace_bytes > 0 && workspace(dev, stream, plan.workspace_bytes, &ws) != hipSuccess)
+            return MSS_ERR_HIP;
+        return mss::launch_scan_fwd(a, plan, ws, s) == hipSuccess ? MSS_OK : MSS_ERR_HIP;
+    } catch (...) {
+        return MSS_ERR_HIP;
+    }
+}
+
+int mss_selective_state_update(const mss_tensor_t* state, const mss_tensor_t* x, const mss_tensor_t* dt,
+                               const mss_tensor_t* A, const mss_tensor_t* B, const mss_tensor_t* C,
+                               const mss_tensor_t* D, const mss_tensor_t* z, const mss_tensor_t* dt_bias,
+                               const mss_tensor_t* out, void* stream) {
+    try {
+        const int st = validate_decode(state, x, dt, A, B, C, D, z, dt_bias, out);
+        if (st != MSS_OK) return st;
+        mss::DecodeLaunch a;
+        a.state = static_cast<float*>(state->data);
+        a.x = x->data; a.dt = dt->data; a.z = z ? z->data : nullptr;
+        a.A = static_cast<const float*>(A->data);
+        a.B = static_cast<const float*>(B->data);
+        a.C = static_cast<const float*>(C->data);
+        a.D = D ? static_cast<const float*>(D->data) : nullptr;
+        a.bias = dt_bias ? static_cast<const float*>(dt_bias->data) : nullptr;
+        a.out = out->data;
+        a.Bt = state->shape[0]; a.Dn = state->shape[1];
+        a.bf16 = x->dtype == MSS_BF16;
+        if (a.Bt * a.Dn == 0) return MSS_OK;
+        return mss::launch_state_update(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MSS_OK
+                                                                                        : MSS_ERR_HIP;
+    } catch (...) {
+        return MSS_ERR_HIP;
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// mss_internal.hpp -- host-side launch descriptions passed from the validated C ABI
+// (abi.hip) to the kernel launchers (scan_fwd.hip, state_update.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mss {
+
+constexpr int kN = 16;      // d_state handled by the kernels
+constexpr int kRows = 64;   // channels per wavefront (one lane per channel)
+
+struct ScanLaunch {
+    const void* u;
+    const void* delta;
+    const void* z;          // nullable
+    const float* A;         // (Dn, N)
+    const float* B;         // (Bt, N, L)
+    const float* C;         // (Bt, N, L)
+    const float* D;         // nullable
+    const float* bias;      // nullable
+    void* out;
+    float* last_state;      // nullable
+    int64_t Bt, Dn, L;
+    int softplus;
+    bool bf16;              // storage type of u / delta / z / out
+    bool vec_ok;            // rows of u / delta / z / out are 16-byte aligned
+};
+
+struct DecodeLaunch {
+    float* state;           // (Bt, Dn, N), in/out
+    const void* x;
+    const void* dt;
+    const void* z;          // nullable
+    const float* A;
+    const float* B;         // (Bt, N)
+    const float* C;         // (Bt, N)
+    const float* D;         // nullable
+    const float* bias;      // nullable
+    void* out;
+    int64_t Bt, Dn;
+    bool bf16;
+};
+
+// How the forward scan is decomposed along L: `segments` workgroup-rows per channel
+// group, each covering `seg_len` steps (a multiple of the time tile).
+struct ScanPlan {
+    int segments;
+    int64_t seg_len;
+    size_t workspace_bytes;  // carry workspace needed (0 when segments == 1)
+};
+
+ScanPlan plan_scan(const ScanLaunch& a, int num_cus);
+hipError_t launch_scan_fwd(const ScanLaunch& a, const ScanPlan& plan, float* workspace,
+                           hipStream_t stream);
+hipError_t launch_state_update(const DecodeLaunch& a, hipStream_t stream);
+
+}  // namespace mss

@@ -1,0 +1,237 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header declares, and
+rejects invalid arguments with the documented status before any HIP call.
+
+Every call below is invalid in a way the validation layer catches (or has an empty batch,
+which returns before touching HIP), so no kernel is ever launched and the fake device
+addresses are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_06_amd as mss
+from selective_state_space_06_amd import Tensor, MSS_F32, MSS_BF16
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mamba_scan.h")
+
+OK, NULL_ARG, SHAPE, DTYPE, LAYOUT, ALIAS, UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mss.LIB_PATH):
+        from selective_state_space_06_amd import build
+        build.build()
+    return mss.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(mss_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(mss.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    m = re.search(r"#define MSS_VERSION (\d+)", open(HEADER).read())
+    assert mss.version() == int(m.group(1))
+    for code, name in mss._binding.STATUS.items():
+        assert mss.status_string(code) == name
+    assert mss.status_string(12345) == "MSS_ERR_UNKNOWN"
+
+
+# --------------------------------------------------------------------- forward scan
+
+BT, DN, N, L = 2, 64, 16, 256
+_next = [0x100000]
+
+
+def addr(nbytes):
+    a = _next[0]
+    _next[0] += (nbytes + 0xFFFF) & ~0xFFFF
+    return a
+
+
+def fwd_args(dtype=MSS_F32, n=N, with_optional=True):
+    es = 2 if dtype == MSS_BF16 else 4
+    big = BT * DN * L
+    a = dict(
+        u=Tensor.make(addr(big * es), dtype, [BT, DN, L]),
+        delta=Tensor.make(addr(big * es), dtype, [BT, DN, L]),
+        A=Tensor.make(addr(DN * n * 4), MSS_F32, [DN, n]),
+        B=Tensor.make(addr(BT * n * L * 4), MSS_F32, [BT, n, L]),
+        C=Tensor.make(addr(BT * n * L * 4), MSS_F32, [BT, n, L]),
+        D=Tensor.make(addr(DN * 4), MSS_F32, [DN]) if with_optional else None,
+        z=Tensor.make(addr(big * es), dtype, [BT, DN, L]) if with_optional else None,
+        delta_bias=Tensor.make(addr(DN * 4), MSS_F32, [DN]) if with_optional else None,
+        softplus_flag=1,
+        out=Tensor.make(addr(big * es), dtype, [BT, DN, L]),
+        last_state=Tensor.make(addr(BT * DN * n * 4), MSS_F32, [BT, DN, n]) if with_optional else None,
+        stream=None,
+    )
+    return a
+
+
+def call_fwd(a):
+    return mss.scan_fwd_raw(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                            a["delta_bias"], a["softplus_flag"], a["out"], a["last_state"], a["stream"])
+
+
+@pytest.mark.parametrize("name", ["u", "delta", "A", "B", "C", "out"])
+def test_fwd_null_required(lib, name):
+    a = fwd_args()
+    a[name] = None
+    assert call_fwd(a) == NULL_ARG
+    a = fwd_args()
+    a[name].data = None
+    assert call_fwd(a) == NULL_ARG
+
+
+def test_fwd_bad_ndim(lib):
+    a = fwd_args()
+    a["u"].ndim = 4
+    assert call_fwd(a) == SHAPE
+    a = fwd_args()
+    a["A"] = Tensor.make(addr(DN * N * 4), MSS_F32, [DN * N])
+    assert call_fwd(a) == SHAPE
+
+
+@pytest.mark.parametrize("name,shape", [
+    ("delta", [BT, DN, L + 1]), ("z", [BT, DN - 1, L]), ("out", [BT + 1, DN, L]),
+    ("A", [DN + 1, N]), ("B", [BT, N, L - 1]), ("C", [BT, N + 1, L]), ("D", [DN + 2]),
+    ("delta_bias", [1]), ("last_state", [BT, DN, N - 1])])
+def test_fwd_shape_mismatch(lib, name, shape):
+    a = fwd_args()
+    t = a[name]
+    a[name] = Tensor.make(t.data, t.dtype, shape)
+    assert call_fwd(a) == SHAPE
+
+
+@pytest.mark.parametrize("name,dtype", [
+    ("delta", MSS_BF16), ("z", MSS_BF16), ("out", MSS_BF16), ("A", MSS_BF16), ("B", MSS_BF16),
+    ("C", MSS_BF16), ("D", MSS_BF16), ("delta_bias", MSS_BF16), ("last_state", MSS_BF16),
+    ("u", 7)])
+def test_fwd_dtype(lib, name, dtype):
+    a = fwd_args()
+    a[name].dtype = dtype
+    assert call_fwd(a) == DTYPE
+
+
+def test_fwd_layout(lib):
+    a = fwd_args()
+    a["u"].stride[2] = 2                       # not dense
+    assert call_fwd(a) == LAYOUT
+    a = fwd_args()
+    a["B"].stride[0], a["B"].stride[1] = L, BT * L  # transposed strides
+    assert call_fwd(a) == LAYOUT
+    a = fwd_args()
+    a["u"].data += 2                           # misaligned f32
+    assert call_fwd(a) == LAYOUT
+    a = fwd_args()
+    a["A"].data += 4                           # A must be 16-byte aligned
+    assert call_fwd(a) == LAYOUT
+    a = fwd_args()
+    a["last_state"].data += 8
+    assert call_fwd(a) == LAYOUT
+
+
+@pytest.mark.parametrize("victim", ["u", "delta", "z", "A", "B", "C", "D", "delta_bias", "last_state"])
+def test_fwd_out_alias(lib, victim):
+    a = fwd_args()
+    a["out"].data = a[victim].data
+    assert call_fwd(a) == ALIAS
+
+
+def test_fwd_last_state_alias(lib):
+    a = fwd_args()
+    a["last_state"].data = a["u"].data + 64
+    assert call_fwd(a) == ALIAS
+
+
+def test_fwd_unsupported_dstate(lib):
+    a = fwd_args(n=8)
+    assert call_fwd(a) == UNSUPPORTED
+
+
+def test_fwd_empty_batch_is_ok(lib):
+    a = fwd_args()
+    for k in ("u", "delta", "z", "out"):
+        a[k] = Tensor.make(a[k].data, MSS_F32, [0, DN, L])
+    for k in ("B", "C"):
+        a[k] = Tensor.make(a[k].data, MSS_F32, [0, N, L])
+    a["last_state"] = Tensor.make(a["last_state"].data, MSS_F32, [0, DN, N])
+    assert call_fwd(a) == OK
+
+
+# --------------------------------------------------------------------- decode step
+
+def dec_args(dtype=MSS_BF16, n=N):
+    es = 2 if dtype == MSS_BF16 else 4
+    rows = BT * DN
+    return dict(
+        state=Tensor.make(addr(rows * n * 4), MSS_F32, [BT, DN, n]),
+        x=Tensor.make(addr(rows * es), dtype, [BT, DN]),
+        dt=Tensor.make(addr(rows * es), dtype, [BT, DN]),
+        A=Tensor.make(addr(DN * n * 4), MSS_F32, [DN, n]),
+        B=Tensor.make(addr(BT * n * 4), MSS_F32, [BT, n]),
+        C=Tensor.make(addr(BT * n * 4), MSS_F32, [BT, n]),
+        D=Tensor.make(addr(DN * 4), MSS_F32, [DN]),
+        z=Tensor.make(addr(rows * es), dtype, [BT, DN]),
+        dt_bias=Tensor.make(addr(DN * 4), MSS_F32, [DN]),
+        out=Tensor.make(addr(rows * es), dtype, [BT, DN]),
+        stream=None)
+
+
+def call_dec(a):
+    return mss.state_update_raw(a["state"], a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"],
+                                a["z"], a["dt_bias"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("name", ["state", "x", "dt", "A", "B", "C", "out"])
+def test_dec_null_required(lib, name):
+    a = dec_args()
+    a[name] = None
+    assert call_dec(a) == NULL_ARG
+
+
+@pytest.mark.parametrize("name,shape", [("x", [BT, DN + 1]), ("dt", [BT + 1, DN]), ("z", [DN]),
+                                        ("A", [DN, N + 1]), ("B", [BT, N - 1]), ("C", [1, N]),
+                                        ("out", [BT, DN, 1]), ("D", [DN - 1])])
+def test_dec_shape(lib, name, shape):
+    a = dec_args()
+    t = a[name]
+    a[name] = Tensor.make(t.data, t.dtype, shape)
+    assert call_dec(a) == SHAPE
+
+
+@pytest.mark.parametrize("name,dtype", [("state", MSS_BF16), ("dt", MSS_F32), ("z", MSS_F32),
+                                        ("out", MSS_F32), ("B", MSS_BF16), ("dt_bias", MSS_BF16)])
+def test_dec_dtype(lib, name, dtype):
+    a = dec_args()
+    a[name].dtype = dtype
+    assert call_dec(a) == DTYPE
+
+
+def test_dec_layout_and_alias(lib):
+    a = dec_args()
+    a["state"].data += 4
+    assert call_dec(a) == LAYOUT
+    a = dec_args()
+    a["x"].stride[0] = DN + 1
+    assert call_dec(a) == LAYOUT
+    a = dec_args()
+    a["out"].data = a["z"].data
+    assert call_dec(a) == ALIAS
+    a = dec_args()
+    a["state"].data = a["A"].data
+    assert call_dec(a) == ALIAS
+    a = dec_args(n=4)
+    assert call_dec(a) == UNSUPPORTED
