@@ -1,6 +1,7 @@
 // abi.hip -- the extern "C" boundary of libmamba_scan: argument validation, the carry
 // workspace, and dispatch to the gfx950 kernels.  Every check runs before the first HIP call,
 // so invalid arguments never reach the device.
+#include <cstdlib>
 #include <initializer_list>
 #include <mutex>
 #include <unordered_map>
@@ -277,11 +278,16 @@ int mss_selective_scan_fwd(const mss_tensor_t* u, const mss_tensor_t* delta, con
         int dev = 0, cus = 0;
         if (hipGetDevice(&dev) != hipSuccess) return MSS_ERR_HIP;
         if (device_cus(dev, &cus) != hipSuccess) return MSS_ERR_HIP;
-        const mss::ScanPlan plan = mss::plan_scan(a, cus);
+        const bool fast = a.vec_ok && a.L > 0 && getenv("MSS_SCAN_GENERIC") == nullptr;
+        const int tile = fast ? mss::kFastTileBytes / static_cast<int>(es) : mss::generic_tile();
+        mss::ScanPlan plan = mss::plan_scan(a, cus, tile);
+        plan.workspace_bytes = fast ? mss::fast_workspace_bytes(a, plan.segments)
+                                    : mss::generic_workspace_bytes(a, plan.segments);
         float* ws = nullptr;
         if (plan.workspace_bytes > 0 && workspace(dev, stream, plan.workspace_bytes, &ws) != hipSuccess)
             return MSS_ERR_HIP;
-        return mss::launch_scan_fwd(a, plan, ws, s) == hipSuccess ? MSS_OK : MSS_ERR_HIP;
+        const hipError_t e = fast ? mss::launch_scan_fast(a, plan, ws, s) : mss::launch_scan_fwd(a, plan, ws, s);
+        return e == hipSuccess ? MSS_OK : MSS_ERR_HIP;
     } catch (...) {
         return MSS_ERR_HIP;
     }

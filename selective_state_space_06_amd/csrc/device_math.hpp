@@ -70,6 +70,11 @@ struct F32 {
         return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]),
                           __float_as_uint(v[2]), __float_as_uint(v[3]));
     }
+    // element e (compile-time after unrolling) of a 16-byte vector
+    __device__ static float elem(const uint4& w, int e) {
+        const uint32_t x = e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w;
+        return __uint_as_float(x);
+    }
 };
 
 struct BF16 {
@@ -88,6 +93,10 @@ struct BF16 {
     __device__ static uint4 pack(const float* v) {
         return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                           pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    }
+    __device__ static float elem(const uint4& w, int e) {
+        const uint32_t x = (e >> 1) == 0 ? w.x : (e >> 1) == 1 ? w.y : (e >> 1) == 2 ? w.z : w.w;
+        return (e & 1) ? bf16_hi(x) : bf16_lo(x);
     }
 };
 

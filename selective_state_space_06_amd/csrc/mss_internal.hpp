@@ -9,6 +9,7 @@ namespace mss {
 
 constexpr int kN = 16;      // d_state handled by the kernels
 constexpr int kRows = 64;   // channels per wavefront (one lane per channel)
+constexpr int kFastTileBytes = 64;  // bytes of each row (per array) a fast-path tile covers
 
 struct ScanLaunch {
     const void* u;
@@ -50,9 +51,17 @@ struct ScanPlan {
     size_t workspace_bytes;  // carry workspace needed (0 when segments == 1)
 };
 
-ScanPlan plan_scan(const ScanLaunch& a, int num_cus);
+// Segment plan for a time tile of `tile` steps (segments are whole tiles).
+ScanPlan plan_scan(const ScanLaunch& a, int num_cus, int tile);
+// Generic path (any alignment): scan_fwd.hip.
 hipError_t launch_scan_fwd(const ScanLaunch& a, const ScanPlan& plan, float* workspace,
                            hipStream_t stream);
+int generic_tile();
+size_t generic_workspace_bytes(const ScanLaunch& a, int segments);
+// Fast path (rows 16-byte aligned): scan_fast.hip.
+size_t fast_workspace_bytes(const ScanLaunch& a, int segments);
+hipError_t launch_scan_fast(const ScanLaunch& a, const ScanPlan& plan, float* workspace,
+                            hipStream_t stream);
 hipError_t launch_state_update(const DecodeLaunch& a, hipStream_t stream);
 
 }  // namespace mss

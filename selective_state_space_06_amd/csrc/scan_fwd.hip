@@ -365,12 +365,12 @@ hipError_t launch_typed(const KArgs& k, int64_t Bt, hipStream_t stream) {
 
 }  // namespace
 
-ScanPlan plan_scan(const ScanLaunch& a, int num_cus) {
+ScanPlan plan_scan(const ScanLaunch& a, int num_cus, int tile) {
     ScanPlan p;
     const int64_t groups = a.Bt * ((a.Dn + kRows - 1) / kRows);
-    const int64_t tiles = (a.L + kTile - 1) / kTile;
-    // aim for ~4 wavefronts per SIMD (4 SIMDs per CU) across the whole launch
-    const int64_t target = 16LL * (num_cus > 0 ? num_cus : 256);
+    const int64_t tiles = (a.L + tile - 1) / tile;
+    // aim for ~2 wavefronts per SIMD (4 SIMDs per CU) across the whole launch
+    const int64_t target = 8LL * (num_cus > 0 ? num_cus : 256);
     int64_t S = (target + groups - 1) / groups;
     const char* env = getenv("MSS_SCAN_SEGMENTS");
     if (env && atoi(env) > 0) S = atoi(env);
@@ -379,12 +379,18 @@ ScanPlan plan_scan(const ScanLaunch& a, int num_cus) {
     if (S > 65535) S = 65535;
     int64_t seg_tiles = (tiles + S - 1) / S;
     if (seg_tiles < 1) seg_tiles = 1;
-    p.seg_len = seg_tiles * kTile;
+    p.seg_len = seg_tiles * tile;
     p.segments = static_cast<int>(tiles > 0 ? (tiles + seg_tiles - 1) / seg_tiles : 1);
-    p.workspace_bytes = p.segments > 1
-        ? static_cast<size_t>(p.segments) * (kN + 1) * static_cast<size_t>(a.Bt * a.Dn) * sizeof(float)
-        : 0;
+    p.workspace_bytes = 0;
     return p;
+}
+
+int generic_tile() { return kTile; }
+
+size_t generic_workspace_bytes(const ScanLaunch& a, int segments) {
+    return segments > 1
+        ? static_cast<size_t>(segments) * (kN + 1) * static_cast<size_t>(a.Bt * a.Dn) * sizeof(float)
+        : 0;
 }
 
 hipError_t launch_scan_fwd(const ScanLaunch& a, const ScanPlan& plan, float* workspace,
