@@ -271,7 +271,8 @@ int mss_selective_scan_fwd(const mss_tensor_t* u, const mss_tensor_t* delta, con
         a.bf16 = u->dtype == MSS_BF16;
         const size_t es = elem_size(u->dtype);
         a.vec_ok = (a.L * static_cast<int64_t>(es)) % 16 == 0 && aligned(*u, 16) &&
-                   aligned(*delta, 16) && aligned(*out, 16) && (!z || aligned(*z, 16));
+                   aligned(*delta, 16) && aligned(*out, 16) && (!z || aligned(*z, 16)) &&
+                   aligned(*B, 16) && aligned(*C, 16);
         if (a.Bt * a.Dn == 0) return MSS_OK;
 
         hipStream_t s = static_cast<hipStream_t>(stream);
@@ -279,10 +280,13 @@ int mss_selective_scan_fwd(const mss_tensor_t* u, const mss_tensor_t* delta, con
         if (hipGetDevice(&dev) != hipSuccess) return MSS_ERR_HIP;
         if (device_cus(dev, &cus) != hipSuccess) return MSS_ERR_HIP;
         const bool fast = a.vec_ok && a.L > 0 && getenv("MSS_SCAN_GENERIC") == nullptr;
-        const int tile = fast ? mss::kFastTileBytes / static_cast<int>(es) : mss::generic_tile();
-        mss::ScanPlan plan = mss::plan_scan(a, cus, tile);
-        plan.workspace_bytes = fast ? mss::fast_workspace_bytes(a, plan.segments)
-                                    : mss::generic_workspace_bytes(a, plan.segments);
+        mss::ScanPlan plan;
+        if (fast) {
+            plan = mss::plan_fast(a, cus);
+        } else {
+            plan = mss::plan_scan(a, cus, mss::generic_tile());
+            plan.workspace_bytes = mss::generic_workspace_bytes(a, plan.segments);
+        }
         float* ws = nullptr;
         if (plan.workspace_bytes > 0 && workspace(dev, stream, plan.workspace_bytes, &ws) != hipSuccess)
             return MSS_ERR_HIP;

@@ -58,7 +58,9 @@ hipError_t launch_scan_fwd(const ScanLaunch& a, const ScanPlan& plan, float* wor
                            hipStream_t stream);
 int generic_tile();
 size_t generic_workspace_bytes(const ScanLaunch& a, int segments);
-// Fast path (rows 16-byte aligned): scan_fast.hip.
+// Fast path (rows 16-byte aligned): scan_fast.hip.  Its plan splits the tiles of L evenly
+// over the segments (seg_len is not used).
+ScanPlan plan_fast(const ScanLaunch& a, int num_cus);
 size_t fast_workspace_bytes(const ScanLaunch& a, int segments);
 hipError_t launch_scan_fast(const ScanLaunch& a, const ScanPlan& plan, float* workspace,
                             hipStream_t stream);

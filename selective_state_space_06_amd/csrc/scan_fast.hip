@@ -8,56 +8,48 @@
 //     states in VGPRs; the wave walks its time segment sequentially, two steps per iteration of
 //     a loop that is deliberately not unrolled further (so the compiler cannot interleave the
 //     independent per-step work of many steps and run out of registers);
-//   * u / delta / z stream in as 16-byte vectors of the lane's own row, a 64-byte tile (32 bf16 or
+//   * u / delta stream in as 16-byte vectors of the lane's own row, a 64-byte tile (32 bf16 or
 //     16 fp32 steps) at a time; the next tile is prefetched into VGPRs while the current one
-//     runs, and the current one sits in a lane-private LDS row that the step loop indexes;
-//     outputs overwrite the consumed u slots and leave as 16-byte stores per tile;
-//   * B_t and C_t are the same for all 64 lanes of a wave (one batch): a kernel first writes a
-//     time-major copy (Bt, L, 32) of B and C; each tile's block of it is prefetched with
-//     coalesced 16-byte loads together with the u / delta / z tile, written to LDS at the tile
-//     boundary, and read back per step as broadcast 16-byte LDS loads (all lanes one address);
-//   * long sequences are split into S segments per channel group.  A first kernel computes,
+//     runs from LDS, stored word-major ([word][lane]) so every per-step LDS access of the wave
+//     hits 64 distinct banks;
+//   * B_t and C_t are shared by the 64 lanes of a wave (one batch).  Per tile, the wave loads
+//     the (N, tile) blocks of B and C straight from their (Bt, N, L) layout (prefetched with the
+//     u / delta tile) and stores them time-major in LDS; each step reads its B_t | C_t as eight
+//     16-byte broadcast loads (all lanes one address) into plain VGPR operands.  (Feeding them
+//     through DPP row broadcasts instead saves those loads but stops the SIMD from dual-issuing
+//     VALU work of different waves, which costs more than it saves.)
+//   * the per-step result y + D u stays fp32 in the LDS words the step has consumed; an
+//     epilogue per tile applies the gate silu(z) (z of the tile is loaded into VGPRs when the
+//     tile starts), rounds to the storage type and writes 16-byte vectors;
+//   * long sequences are split into S segments of whole tiles per channel group (segment k
+//     takes tiles [k T / S, (k + 1) T / S) of the T tiles).  A first kernel computes,
 //     per segment, the pair (sum of delta, local end state from h = 0); the main kernel folds
 //     the pairs of the preceding segments with the associative operator
 //     (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2) into its starting state and runs the segment.
 //
 // exp is exp2 of a log2(e)-prescaled argument.  When every row of a wave satisfies
 // A[d, n] == (n + 1) A[d, 0] exactly (the S4D-real A = -(1..N) of the tutorial's init),
-// Abar_n = Abar_0^(n+1) is formed by repeated multiplication (one exp2 per (b, d, t)); the
-// aggregate pass then uses the backward form sum_s x_s B_s R_s^(n+1), R_s the product of the
-// later Abar_0, which costs two VALU operations per state update.
+// Abar_n = Abar_0^(n+1) is formed by multiplications (one exp2 per (b, d, t)); the aggregate
+// pass then uses the backward form sum_s x_s B_s R_s^(n+1), R_s the product of the later
+// Abar_0, which costs two VALU operations per state update.
+#include <cstdlib>
+
 #include "device_math.hpp"
 #include "mss_internal.hpp"
 
 namespace mss {
 namespace {
 
-constexpr int kBCW = 2 * kN;                   // B|C floats per time step in the time-major copy
-constexpr int kNV = kFastTileBytes / 16;       // 16-byte vectors per row and array in a tile
-constexpr int kRowWords = kFastTileBytes / 4 + 1;  // LDS words per lane row (+1: bank skew)
+constexpr int kNV = kFastTileBytes / 16;  // 16-byte vectors per row and array in a tile
 
-// (Bt, N, L) B and C -> (Bt, L, 2N): B in [0, N), C in [N, 2N).
-__global__ __launch_bounds__(256) void bc_transpose_kernel(const float* __restrict__ B,
-                                                           const float* __restrict__ C,
-                                                           float* __restrict__ bc, int64_t L,
-                                                           int64_t total) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t b = i / L, t = i - b * L;
-        const float* Bb = B + b * kN * L + t;
-        const float* Cb = C + b * kN * L + t;
-        float v[kBCW];
-#pragma unroll
-        for (int n = 0; n < kN; ++n) {
-            v[n] = Bb[n * L];
-            v[kN + n] = Cb[n * L];
-        }
-        float4* dst = reinterpret_cast<float4*>(bc + i * kBCW);
-#pragma unroll
-        for (int q = 0; q < kBCW / 4; ++q)
-            dst[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-    }
-}
+template <class E>
+struct Geo {
+    static constexpr int V = E::kPerVec;           // elements per 16 bytes
+    static constexpr int TT = kNV * V;             // steps per tile
+    static constexpr int W = kFastTileBytes / 4;   // words per row and array
+    static constexpr int kBCChunks = TT / 8;       // 16-byte B|C chunks per lane
+    static constexpr int kRowWords = 2 * W * 64;   // u and delta, [word][lane]
+};
 
 struct RowSetup {
     int64_t row;      // flat (b, d) row, clamped to a valid row for inactive lanes
@@ -92,44 +84,81 @@ __device__ __forceinline__ RowSetup row_setup(const float* __restrict__ A, const
     return r;
 }
 
-// One tile of this lane's row (u, delta and optionally z), as loaded from HBM.
-struct Raw {
-    uint4 u[kNV], d[kNV], z[kNV];
+// One tile of this lane's row of u and delta as loaded from HBM (plain words: an array of vector
+// structs here ends up in scratch memory).
+struct RawUD {
+    uint32_t u[4 * kNV], d[4 * kNV];
 };
 
-// Loads the tile starting at t0.  Vectors at or past t_end re-read the last valid vector (their
-// steps are never used), so every load is unconditional and in bounds.
-template <class E, bool HAS_Z>
-__device__ __forceinline__ void load_tile(Raw& r, const typename E::storage* __restrict__ up,
-                                          const typename E::storage* __restrict__ dp,
-                                          const typename E::storage* __restrict__ zp, int64_t t0,
-                                          int64_t t_end) {
+// Vectors at or past t_end re-read the last valid vector (their steps are never used), so every
+// load is unconditional and in bounds.
+template <class E>
+__device__ __forceinline__ void load_ud(RawUD& r, const typename E::storage* __restrict__ up,
+                                        const typename E::storage* __restrict__ dp, int64_t t0,
+                                        int64_t t_end) {
     constexpr int V = E::kPerVec;
 #pragma unroll
     for (int v = 0; v < kNV; ++v) {
         int64_t t = t0 + v * V;
         t = t < t_end ? t : t_end - V;
-        r.u[v] = *reinterpret_cast<const uint4*>(up + t);
-        r.d[v] = *reinterpret_cast<const uint4*>(dp + t);
-        if (HAS_Z) r.z[v] = *reinterpret_cast<const uint4*>(zp + t);
+        const uint4 a = *reinterpret_cast<const uint4*>(up + t);
+        const uint4 b = *reinterpret_cast<const uint4*>(dp + t);
+        r.u[4 * v] = a.x; r.u[4 * v + 1] = a.y; r.u[4 * v + 2] = a.z; r.u[4 * v + 3] = a.w;
+        r.d[4 * v] = b.x; r.d[4 * v + 1] = b.y; r.d[4 * v + 2] = b.z; r.d[4 * v + 3] = b.w;
     }
 }
 
-// Lane-private LDS rows (kRowWords words per lane and array).
-__device__ __forceinline__ void stage_vec(uint32_t* row, int v, const uint4& x) {
-    row[4 * v + 0] = x.x;
-    row[4 * v + 1] = x.y;
-    row[4 * v + 2] = x.z;
-    row[4 * v + 3] = x.w;
+// Word-major staging: word w of lane l at srow[w * 64 + l]; delta follows u after W words.
+template <class E>
+__device__ __forceinline__ void stage_ud(uint32_t* srow, const RawUD& r) {
+    constexpr int W = Geo<E>::W;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        srow[w * 64 + threadIdx.x] = r.u[w];
+        srow[(W + w) * 64 + threadIdx.x] = r.d[w];
+    }
 }
 
-template <bool HAS_Z>
-__device__ __forceinline__ void stage_tile(uint32_t* ru, uint32_t* rd, uint32_t* rz, const Raw& r) {
+// The tile's B and C blocks: chunk k of lane l is the 16-byte run of B (k < K/2) or C at
+// n = l % 16, steps t0 + 4 * (4 (k % (K/2)) + l / 16) .. + 3.  Runs at or past t_end are clamped
+// to the last four valid steps (t_end is a multiple of 4 here).
+template <class E>
+struct RawBC {
+    uint32_t w[4 * Geo<E>::kBCChunks];
+};
+
+template <class E, bool WITH_C>
+__device__ __forceinline__ void load_bc(RawBC<E>& r, const float* __restrict__ Bb,
+                                        const float* __restrict__ Cb, int64_t L, int64_t t0,
+                                        int64_t t_end) {
+    constexpr int K = Geo<E>::kBCChunks;
+    const int n = threadIdx.x & 15;
 #pragma unroll
-    for (int v = 0; v < kNV; ++v) {
-        stage_vec(ru, v, r.u[v]);
-        stage_vec(rd, v, r.d[v]);
-        if (HAS_Z) stage_vec(rz, v, r.z[v]);
+    for (int k = 0; k < (WITH_C ? K : K / 2); ++k) {
+        const float* src = k < K / 2 ? Bb : Cb;
+        const int kk = k % (K / 2);
+        int64_t t = t0 + 4 * (4 * kk + (threadIdx.x >> 4));
+        t = t < t_end ? t : t_end - 4;
+        const uint4 v = *reinterpret_cast<const uint4*>(src + n * L + t);
+        r.w[4 * k] = v.x; r.w[4 * k + 1] = v.y; r.w[4 * k + 2] = v.z; r.w[4 * k + 3] = v.w;
+    }
+}
+
+// Time-major LDS block: step t of the tile at sbc + t * SB, B_t in floats [0, 16), C_t in
+// [16, 32).  SB = 16 (B only) + 4 or 32 + 4: the 4 spare floats per step put the 16 lanes x 4
+// step groups of each scattered 4-byte store in 64 distinct banks.
+template <class E, bool WITH_C>
+__device__ __forceinline__ void stage_bc(float* sbc, const RawBC<E>& r) {
+    constexpr int K = Geo<E>::kBCChunks;
+    constexpr int SB = WITH_C ? 36 : 20;
+    const int n = threadIdx.x & 15;
+#pragma unroll
+    for (int k = 0; k < (WITH_C ? K : K / 2); ++k) {
+        const int kk = k % (K / 2);
+        const int t = 4 * (4 * kk + (threadIdx.x >> 4));
+        float* dst = sbc + t * SB + (k < K / 2 ? 0 : kN) + n;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i * SB] = __uint_as_float(r.w[4 * k + i]);
     }
 }
 
@@ -139,197 +168,249 @@ __device__ __forceinline__ float delta_of(float raw, float bias) {
     return SOFTPLUS ? softplus(pre) : pre;
 }
 
-struct BCStep {
-    float v[kBCW];
-};
-
-// The tile's B|C block from the time-major copy: TT steps x 128 bytes, contiguous; lane l holds
-// 16-byte chunks l, l + 64, ...  Steps at or past t_end are clamped to the last valid step.
-// (Plain words: an array of vector structs here ends up in scratch memory.)
-template <int TT>
-struct RawBC {
-    static constexpr int kChunks = TT * kBCW / 4 / 64;
-    uint32_t w[4 * kChunks];
-};
-
-template <int TT>
-__device__ __forceinline__ void load_bc_tile(RawBC<TT>& r, const float* __restrict__ bcb, int64_t t0,
-                                             int64_t t_end) {
-#pragma unroll
-    for (int k = 0; k < RawBC<TT>::kChunks; ++k) {
-        const int chunk = threadIdx.x + 64 * k;  // 8 chunks per step
-        int64_t t = t0 + chunk / 8;
-        t = t < t_end ? t : t_end - 1;
-        const uint4 v = *reinterpret_cast<const uint4*>(bcb + t * kBCW + (chunk % 8) * 4);
-        r.w[4 * k] = v.x; r.w[4 * k + 1] = v.y; r.w[4 * k + 2] = v.z; r.w[4 * k + 3] = v.w;
+// Elements j, j + 1 (j even) of the lane's staged row of one array.
+template <class E>
+__device__ __forceinline__ void staged2(const uint32_t* arr, int j, float& e0, float& e1) {
+    if (E::kPerVec == 8) {
+        const uint32_t w = arr[(j >> 1) * 64 + threadIdx.x];
+        e0 = bf16_lo(w);
+        e1 = bf16_hi(w);
+    } else {
+        e0 = __uint_as_float(arr[j * 64 + threadIdx.x]);
+        e1 = __uint_as_float(arr[(j + 1) * 64 + threadIdx.x]);
     }
 }
 
-template <int TT>
-__device__ __forceinline__ void stage_bc_tile(float* sbc, const RawBC<TT>& r) {
-#pragma unroll
-    for (int k = 0; k < RawBC<TT>::kChunks; ++k)
-        reinterpret_cast<uint4*>(sbc)[threadIdx.x + 64 * k] =
-            make_uint4(r.w[4 * k], r.w[4 * k + 1], r.w[4 * k + 2], r.w[4 * k + 3]);
-}
+// Per-step scalars of the step pair (j, j + 1): delta, x = delta u, Abar_0 = exp2(delta A2_0)
+// (power path) and D u (main kernel).  The loops compute the pair after next while the current
+// pair's state updates run, so the softplus / exp2 latency of one pair overlaps the other's work.
+struct Pair {
+    float d[2], x[2], a[2], du[2];
+};
 
-// Broadcast read of B_t | C_t from the LDS block: every lane reads the same 128 bytes.
-__device__ __forceinline__ BCStep read_bc(const float* sbc_t) {
-    BCStep r;
+template <class E, bool SOFTPLUS, bool POW, bool WITH_DU>
+__device__ __forceinline__ Pair pair_of(const uint32_t* su, const uint32_t* sd, int j, const RowSetup& rs) {
+    Pair p;
+    float u[2], r[2];
+    staged2<E>(su, j, u[0], u[1]);
+    staged2<E>(sd, j, r[0], r[1]);
 #pragma unroll
-    for (int q = 0; q < kBCW / 4; ++q) {
-        const float4 v = reinterpret_cast<const float4*>(sbc_t)[q];
-        r.v[4 * q] = v.x; r.v[4 * q + 1] = v.y; r.v[4 * q + 2] = v.z; r.v[4 * q + 3] = v.w;
+    for (int i = 0; i < 2; ++i) {
+        p.d[i] = delta_of<SOFTPLUS>(r[i], rs.bias);
+        p.x[i] = p.d[i] * u[i];
+        p.a[i] = POW ? fast_exp2(p.d[i] * rs.A2[0]) : 0.0f;
+        p.du[i] = WITH_DU ? rs.dskip * u[i] : 0.0f;
     }
-    return r;
+    return p;
 }
 
-// One time step for one lane: 16 state updates and y = C.h.
+// Step results j, j + 1 (fp32) written into words the step pair has consumed: bf16 puts them in
+// the u and delta words j / 2, fp32 in the u words j and j + 1.
+template <class E>
+__device__ __forceinline__ void put2(uint32_t* srow, int j, float o0, float o1) {
+    constexpr int W = Geo<E>::W;
+    if (E::kPerVec == 8) {
+        srow[(j >> 1) * 64 + threadIdx.x] = __float_as_uint(o0);
+        srow[(W + (j >> 1)) * 64 + threadIdx.x] = __float_as_uint(o1);
+    } else {
+        srow[j * 64 + threadIdx.x] = __float_as_uint(o0);
+        srow[(j + 1) * 64 + threadIdx.x] = __float_as_uint(o1);
+    }
+}
+
+// Step result e of the tile as written by put2.
+template <class E>
+__device__ __forceinline__ float result_of(const uint32_t* srow, int e) {
+    constexpr int W = Geo<E>::W;
+    if (E::kPerVec == 8)
+        return __uint_as_float(srow[((e & 1) ? W + (e >> 1) : (e >> 1)) * 64 + threadIdx.x]);
+    return __uint_as_float(srow[e * 64 + threadIdx.x]);
+}
+
+// Element e of the 16-byte vector held in words w[0..3].
+template <class E>
+__device__ __forceinline__ float vec_elem(const uint32_t* w, int e) {
+    if (E::kPerVec == 8) return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+    return __uint_as_float(w[e]);
+}
+
+// Powers a^1 .. a^16 with a multiplication tree of depth 4 (15 multiplications).
+__device__ __forceinline__ void powers16(float a, float (&p)[kN]) {
+    p[0] = a;
+    p[1] = a * a;
+    p[2] = p[1] * a;
+    p[3] = p[1] * p[1];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) p[4 + k] = p[3] * p[k];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p[8 + k] = p[7] * p[k];
+}
+
+// One time step for one lane: 16 state updates and y0 + C.h; bc = B_t | C_t in LDS; a = Abar_0
+// on the power path.
 template <bool POW>
 __device__ __forceinline__ float step_main(float (&h)[kN], const float (&A2)[kN], float dl, float x,
-                                           const BCStep& bc) {
-    float y0 = 0.0f, y1 = 0.0f;
+                                           float a, const float* bc, float y0) {
+    const float4* b4 = reinterpret_cast<const float4*>(bc);
+    float bv[kN], cv[kN];
+#pragma unroll
+    for (int q = 0; q < kN / 4; ++q) {
+        const float4 b = b4[q], c = b4[kN / 4 + q];
+        bv[4 * q] = b.x; bv[4 * q + 1] = b.y; bv[4 * q + 2] = b.z; bv[4 * q + 3] = b.w;
+        cv[4 * q] = c.x; cv[4 * q + 1] = c.y; cv[4 * q + 2] = c.z; cv[4 * q + 3] = c.w;
+    }
+    float y1 = 0.0f;
     if (POW) {
-        const float a = fast_exp2(dl * A2[0]);
-        float p = a;
+        float p[kN];
+        powers16(a, p);
 #pragma unroll
         for (int n = 0; n < kN; ++n) {
-            if (n) p *= a;
-            h[n] = fmaf(p, h[n], x * bc.v[n]);
-            if (n & 1) y1 = fmaf(bc.v[kN + n], h[n], y1);
-            else y0 = fmaf(bc.v[kN + n], h[n], y0);
+            h[n] = fmaf(p[n], h[n], x * bv[n]);
+            if (n & 1) y1 = fmaf(cv[n], h[n], y1);
+            else y0 = fmaf(cv[n], h[n], y0);
         }
     } else {
 #pragma unroll
         for (int n = 0; n < kN; ++n) {
-            h[n] = fmaf(fast_exp2(dl * A2[n]), h[n], x * bc.v[n]);
-            if (n & 1) y1 = fmaf(bc.v[kN + n], h[n], y1);
-            else y0 = fmaf(bc.v[kN + n], h[n], y0);
+            h[n] = fmaf(fast_exp2(dl * A2[n]), h[n], x * bv[n]);
+            if (n & 1) y1 = fmaf(cv[n], h[n], y1);
+            else y0 = fmaf(cv[n], h[n], y0);
         }
     }
     return y0 + y1;
-}
-
-// Element i of the staged row (bf16: two per word, fp32: one per word).
-template <class E>
-__device__ __forceinline__ float staged(const uint32_t* row, int i) {
-    if (E::kPerVec == 8) {
-        const uint32_t w = row[i >> 1];
-        return (i & 1) ? bf16_hi(w) : bf16_lo(w);
-    }
-    return __uint_as_float(row[i]);
-}
-
-// Outputs i and i + 1 (i even) written over the consumed u slots.
-template <class E>
-__device__ __forceinline__ void put_out2(uint32_t* row, int i, float o0, float o1) {
-    if (E::kPerVec == 8) {
-        row[i >> 1] = pack_bf16x2(o0, o1);
-    } else {
-        row[i] = __float_as_uint(o0);
-        row[i + 1] = __float_as_uint(o1);
-    }
 }
 
 template <class E, bool HAS_Z, bool SOFTPLUS, bool POW>
 __device__ __forceinline__ void main_body(
     const RowSetup& rs, float (&h)[kN], const typename E::storage* __restrict__ up,
     const typename E::storage* __restrict__ dp, const typename E::storage* __restrict__ zp,
-    typename E::storage* __restrict__ op, const float* __restrict__ bcb, uint32_t* ru, uint32_t* rd,
-    uint32_t* rz, float* sbc, int64_t t_begin, int64_t t_end) {
-    constexpr int V = E::kPerVec;
-    constexpr int TT = kNV * V;
-    Raw pre;
-    RawBC<TT> bpre;
-    load_tile<E, HAS_Z>(pre, up, dp, zp, t_begin, t_end);
-    load_bc_tile<TT>(bpre, bcb, t_begin, t_end);
+    typename E::storage* __restrict__ op, const float* __restrict__ Bb, const float* __restrict__ Cb,
+    int64_t L, uint32_t* srow, float* sbc, int64_t t_begin, int64_t t_end) {
+    using G = Geo<E>;
+    constexpr int V = G::V, TT = G::TT, W = G::W;
+    const uint32_t* su = srow;
+    const uint32_t* sd = srow + W * 64;
+    RawUD pre;
+    RawBC<E> bpre;
+    load_ud<E>(pre, up, dp, t_begin, t_end);
+    load_bc<E, true>(bpre, Bb, Cb, L, t_begin, t_end);
     for (int64_t t0 = t_begin; t0 < t_end; t0 += TT) {
-        stage_tile<HAS_Z>(ru, rd, rz, pre);
-        stage_bc_tile<TT>(sbc, bpre);
-        if (t0 + TT < t_end) {
-            load_tile<E, HAS_Z>(pre, up, dp, zp, t0 + TT, t_end);
-            load_bc_tile<TT>(bpre, bcb, t0 + TT, t_end);
+        __syncthreads();  // the previous tile's reads of the shared B|C block are done
+        stage_ud<E>(srow, pre);
+        stage_bc<E, true>(sbc, bpre);
+        __syncthreads();
+        uint32_t zw[4 * kNV];  // z of this tile, consumed by the epilogue
+        if (HAS_Z) {
+#pragma unroll
+            for (int v = 0; v < kNV; ++v) {
+                int64_t t = t0 + v * V;
+                t = t < t_end ? t : t_end - V;
+                const uint4 a = *reinterpret_cast<const uint4*>(zp + t);
+                zw[4 * v] = a.x; zw[4 * v + 1] = a.y; zw[4 * v + 2] = a.z; zw[4 * v + 3] = a.w;
+            }
         }
-        const int nsteps = static_cast<int>(t_end - t0 < TT ? t_end - t0 : TT);  // even
+        if (t0 + TT < t_end) {
+            load_ud<E>(pre, up, dp, t0 + TT, t_end);
+            load_bc<E, true>(bpre, Bb, Cb, L, t0 + TT, t_end);
+        }
+        const int nsteps = static_cast<int>(t_end - t0 < TT ? t_end - t0 : TT);  // multiple of 4
+        Pair cur = pair_of<E, SOFTPLUS, POW, true>(su, sd, 0, rs);
 #pragma unroll 1
         for (int j = 0; j < nsteps; j += 2) {
-            const float u0 = staged<E>(ru, j), u1 = staged<E>(ru, j + 1);
-            const float d0 = delta_of<SOFTPLUS>(staged<E>(rd, j), rs.bias);
-            const float y0 = step_main<POW>(h, rs.A2, d0, d0 * u0, read_bc(sbc + j * kBCW));
-            const float d1 = delta_of<SOFTPLUS>(staged<E>(rd, j + 1), rs.bias);
-            const float y1 = step_main<POW>(h, rs.A2, d1, d1 * u1, read_bc(sbc + (j + 1) * kBCW));
-            float o0 = fmaf(rs.dskip, u0, y0), o1 = fmaf(rs.dskip, u1, y1);
-            if (HAS_Z) {
-                o0 *= silu(staged<E>(rz, j));
-                o1 *= silu(staged<E>(rz, j + 1));
-            }
-            put_out2<E>(ru, j, o0, o1);
+            // the last iteration recomputes its own pair (read before put2 overwrites it)
+            const Pair nxt = pair_of<E, SOFTPLUS, POW, true>(su, sd, j + 2 < nsteps ? j + 2 : j, rs);
+            const float y0 = step_main<POW>(h, rs.A2, cur.d[0], cur.x[0], cur.a[0], sbc + j * 36, cur.du[0]);
+            const float y1 =
+                step_main<POW>(h, rs.A2, cur.d[1], cur.x[1], cur.a[1], sbc + (j + 1) * 36, cur.du[1]);
+            put2<E>(srow, j, y0, y1);
+            cur = nxt;
         }
-        if (rs.active) {
+        // Epilogue: gate, round to the storage type, 16-byte stores.
 #pragma unroll
-            for (int v = 0; v < kNV; ++v)
-                if (t0 + v * V < t_end)
-                    *reinterpret_cast<uint4*>(op + t0 + v * V) =
-                        make_uint4(ru[4 * v], ru[4 * v + 1], ru[4 * v + 2], ru[4 * v + 3]);
+        for (int v = 0; v < kNV; ++v) {
+            float o[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                o[e] = result_of<E>(srow, v * V + e);
+                if (HAS_Z) o[e] *= silu(vec_elem<E>(zw + 4 * v, e));
+            }
+            if (rs.active && t0 + v * V < t_end)
+                *reinterpret_cast<uint4*>(op + t0 + v * V) = E::pack(o);
         }
     }
 }
 
-// Folds the aggregates of segments [0, seg) into the starting state of segment seg.
+// Segment seg of S: tiles [seg T / S, (seg + 1) T / S) of the T = ceil(L / TT) tiles.
+__device__ __forceinline__ void seg_bounds(int seg, int S, int64_t L, int TT, int64_t& t_begin,
+                                           int64_t& t_end) {
+    const int64_t T = (L + TT - 1) / TT;
+    t_begin = (seg * T / S) * TT;
+    const int64_t e = ((seg + 1) * T / S) * TT;
+    t_end = e < L ? e : L;
+}
+
+// Folds the aggregates of segments [0, seg) into the starting state of segment seg.  The
+// 17 values of segment s + 1 are loaded before segment s is folded in, so the loads of
+// consecutive segments overlap instead of forming a chain of memory round trips.
 template <bool POW>
 __device__ __forceinline__ void fold_carry(float (&h)[kN], const float (&A2)[kN],
                                            const float* __restrict__ agg, int seg, int64_t R,
                                            int64_t row) {
 #pragma unroll
     for (int n = 0; n < kN; ++n) h[n] = 0.0f;
-    for (int s = 0; s < seg; ++s) {
-        const float* a = agg + (int64_t)s * (kN + 1) * R + row;
-        const float sd = a[(int64_t)kN * R];
-        if (POW) {
-            const float q = fast_exp2(sd * A2[0]);
-            float p = q;
+    if (seg == 0) return;
+    float nxt[kN + 1];
 #pragma unroll
-            for (int n = 0; n < kN; ++n) {
-                if (n) p *= q;
-                h[n] = fmaf(p, h[n], a[(int64_t)n * R]);
-            }
+    for (int n = 0; n <= kN; ++n) nxt[n] = agg[(int64_t)n * R + row];
+    for (int s = 0; s < seg; ++s) {
+        float cur[kN + 1];
+#pragma unroll
+        for (int n = 0; n <= kN; ++n) cur[n] = nxt[n];
+        if (s + 1 < seg) {
+            const float* a = agg + (int64_t)(s + 1) * (kN + 1) * R + row;
+#pragma unroll
+            for (int n = 0; n <= kN; ++n) nxt[n] = a[(int64_t)n * R];
+        }
+        if (POW) {
+            float p[kN];
+            powers16(fast_exp2(cur[kN] * A2[0]), p);
+#pragma unroll
+            for (int n = 0; n < kN; ++n) h[n] = fmaf(p[n], h[n], cur[n]);
         } else {
 #pragma unroll
-            for (int n = 0; n < kN; ++n) h[n] = fmaf(fast_exp2(sd * A2[n]), h[n], a[(int64_t)n * R]);
+            for (int n = 0; n < kN; ++n) h[n] = fmaf(fast_exp2(cur[kN] * A2[n]), h[n], cur[n]);
         }
     }
 }
 
 template <class E, bool HAS_Z, bool SOFTPLUS>
-__global__ __launch_bounds__(64) void scan_main_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void scan_main_kernel(
     const typename E::storage* __restrict__ u, const typename E::storage* __restrict__ delta,
     const typename E::storage* __restrict__ z, const float* __restrict__ A,
-    const float* __restrict__ bc, const float* __restrict__ D, const float* __restrict__ bias,
-    const float* __restrict__ agg, typename E::storage* __restrict__ out,
-    float* __restrict__ last_state, int64_t Dn, int64_t L, int64_t seg_len, int S) {
-    constexpr int TT = kNV * E::kPerVec;
-    __shared__ uint32_t rows[3 * 64 * kRowWords];
-    __shared__ __align__(16) float sbc[TT * kBCW];
-    uint32_t* ru = rows + threadIdx.x * kRowWords;
-    uint32_t* rd = ru + 64 * kRowWords;
-    uint32_t* rz = rd + 64 * kRowWords;
+    const float* __restrict__ B, const float* __restrict__ C, const float* __restrict__ D,
+    const float* __restrict__ bias, const float* __restrict__ agg, typename E::storage* __restrict__ out,
+    float* __restrict__ last_state, int64_t Dn, int64_t L, int S) {
+    using G = Geo<E>;
+    __shared__ uint32_t srow[G::kRowWords];
+    __shared__ __align__(16) float sbc[G::TT * 36];
     const RowSetup rs = row_setup(A, D, bias, Dn);
     const int seg = blockIdx.z;
     const int64_t R = (int64_t)gridDim.y * Dn;
-    const int64_t t_begin = (int64_t)seg * seg_len;
-    const int64_t t_end = (t_begin + seg_len < L) ? t_begin + seg_len : L;
+    int64_t t_begin, t_end;
+    seg_bounds(seg, S, L, G::TT, t_begin, t_end);
     const int64_t base = rs.row * L;
-    const float* bcb = bc + (int64_t)blockIdx.y * L * kBCW;
+    const float* Bb = B + (int64_t)blockIdx.y * kN * L;
+    const float* Cb = C + (int64_t)blockIdx.y * kN * L;
     const typename E::storage* zp = z ? z + base : nullptr;
     float h[kN];
     if (__all(rs.pow_ok)) {
         fold_carry<true>(h, rs.A2, agg, seg, R, rs.row);
-        main_body<E, HAS_Z, SOFTPLUS, true>(rs, h, u + base, delta + base, zp, out + base, bcb, ru, rd,
-                                            rz, sbc, t_begin, t_end);
+        main_body<E, HAS_Z, SOFTPLUS, true>(rs, h, u + base, delta + base, zp, out + base, Bb, Cb, L,
+                                            srow, sbc, t_begin, t_end);
     } else {
         fold_carry<false>(h, rs.A2, agg, seg, R, rs.row);
-        main_body<E, HAS_Z, SOFTPLUS, false>(rs, h, u + base, delta + base, zp, out + base, bcb, ru, rd,
-                                             rz, sbc, t_begin, t_end);
+        main_body<E, HAS_Z, SOFTPLUS, false>(rs, h, u + base, delta + base, zp, out + base, Bb, Cb, L,
+                                             srow, sbc, t_begin, t_end);
     }
     if (last_state && rs.active && seg == S - 1) {
         float4* dst = reinterpret_cast<float4*>(last_state + rs.row * kN);
@@ -345,65 +426,87 @@ __global__ __launch_bounds__(64) void scan_main_kernel(
 template <class E, bool SOFTPLUS, bool POW>
 __device__ __forceinline__ void agg_body(const RowSetup& rs, const typename E::storage* __restrict__ up,
                                          const typename E::storage* __restrict__ dp,
-                                         const float* __restrict__ bcb, uint32_t* ru, uint32_t* rd,
+                                         const float* __restrict__ Bb, int64_t L, uint32_t* srow,
                                          float* sbc, int64_t t_begin, int64_t t_end, float (&acc)[kN],
                                          float& dsum) {
-    constexpr int V = E::kPerVec;
-    constexpr int TT = kNV * V;
+    using G = Geo<E>;
+    constexpr int TT = G::TT, W = G::W;
+    const uint32_t* su = srow;
+    const uint32_t* sd = srow + W * 64;
 #pragma unroll
     for (int n = 0; n < kN; ++n) acc[n] = 0.0f;
     dsum = 0.0f;
     float Rp = 1.0f;
-    Raw pre;
-    RawBC<TT> bpre;
+    RawUD pre;
+    RawBC<E> bpre;
     const int64_t ntiles = (t_end - t_begin + TT - 1) / TT;
     // tiles in visiting order (POW: from the last tile of the segment back to the first)
     int64_t t0 = POW ? t_begin + (ntiles - 1) * TT : t_begin;
-    load_tile<E, false>(pre, up, dp, nullptr, t0, t_end);
-    load_bc_tile<TT>(bpre, bcb, t0, t_end);
+    load_ud<E>(pre, up, dp, t0, t_end);
+    load_bc<E, false>(bpre, Bb, nullptr, L, t0, t_end);
     for (int64_t k = 0; k < ntiles; ++k) {
-        stage_tile<false>(ru, rd, nullptr, pre);
-        stage_bc_tile<TT>(sbc, bpre);
+        __syncthreads();
+        stage_ud<E>(srow, pre);
+        stage_bc<E, false>(sbc, bpre);
+        __syncthreads();
         const int64_t tnext = POW ? t0 - TT : t0 + TT;
         if (k + 1 < ntiles) {
-            load_tile<E, false>(pre, up, dp, nullptr, tnext, t_end);
-            load_bc_tile<TT>(bpre, bcb, tnext, t_end);
+            load_ud<E>(pre, up, dp, tnext, t_end);
+            load_bc<E, false>(bpre, Bb, nullptr, L, tnext, t_end);
         }
         const int nsteps = static_cast<int>(t_end - t0 < TT ? t_end - t0 : TT);
         if (POW) {
+            Pair cur = pair_of<E, SOFTPLUS, true, false>(su, sd, nsteps - 2, rs);
 #pragma unroll 1
-            for (int j = nsteps - 1; j >= 0; --j) {
-                const float* bt = sbc + j * kBCW;
-                const float dl = delta_of<SOFTPLUS>(staged<E>(rd, j), rs.bias);
-                float w = dl * staged<E>(ru, j) * Rp;
+            for (int j = nsteps - 2; j >= 0; j -= 2) {
+                const Pair nxt = pair_of<E, SOFTPLUS, true, false>(su, sd, j >= 2 ? j - 2 : 0, rs);
+                const float4* b0 = reinterpret_cast<const float4*>(sbc + j * 20);
+                const float4* b1 = reinterpret_cast<const float4*>(sbc + (j + 1) * 20);
+                // step j + 1 first (backward), then step j
+                const float R1 = Rp;
+                const float R0 = Rp * cur.a[1];
+                Rp = R0 * cur.a[0];
+                float w1 = cur.x[1], w0 = cur.x[0];
 #pragma unroll
                 for (int q = 0; q < kN / 4; ++q) {
-                    const float4 b4 = reinterpret_cast<const float4*>(bt)[q];
-                    const float bq[4] = {b4.x, b4.y, b4.z, b4.w};
+                    const float4 x1 = b1[q], x0 = b0[q];
+                    const float c1[4] = {x1.x, x1.y, x1.z, x1.w};
+                    const float c0[4] = {x0.x, x0.y, x0.z, x0.w};
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        if (q | i) w *= Rp;
-                        acc[4 * q + i] = fmaf(bq[i], w, acc[4 * q + i]);
+                        w1 *= R1;
+                        w0 *= R0;
+                        acc[4 * q + i] = fmaf(c1[i], w1, acc[4 * q + i]);
+                        acc[4 * q + i] = fmaf(c0[i], w0, acc[4 * q + i]);
                     }
                 }
-                Rp *= fast_exp2(dl * rs.A2[0]);
-                dsum += dl;
+                dsum += cur.d[1] + cur.d[0];
+                cur = nxt;
             }
         } else {
 #pragma unroll 1
-            for (int j = 0; j < nsteps; ++j) {
-                const float* bt = sbc + j * kBCW;
-                const float dl = delta_of<SOFTPLUS>(staged<E>(rd, j), rs.bias);
-                const float x = dl * staged<E>(ru, j);
+            for (int j = 0; j < nsteps; j += 2) {
+                float u0, u1, r0, r1;
+                staged2<E>(su, j, u0, u1);
+                staged2<E>(sd, j, r0, r1);
+                const float4* b0 = reinterpret_cast<const float4*>(sbc + j * 20);
+                const float4* b1 = reinterpret_cast<const float4*>(sbc + (j + 1) * 20);
+                const float d0 = delta_of<SOFTPLUS>(r0, rs.bias);
+                const float d1 = delta_of<SOFTPLUS>(r1, rs.bias);
+                const float x0 = d0 * u0, x1 = d1 * u1;
 #pragma unroll
                 for (int q = 0; q < kN / 4; ++q) {
-                    const float4 b4 = reinterpret_cast<const float4*>(bt)[q];
-                    const float bq[4] = {b4.x, b4.y, b4.z, b4.w};
+                    const float4 y0 = b0[q], y1 = b1[q];
+                    const float c0[4] = {y0.x, y0.y, y0.z, y0.w};
+                    const float c1[4] = {y1.x, y1.y, y1.z, y1.w};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc[4 * q + i] = fmaf(fast_exp2(dl * rs.A2[4 * q + i]), acc[4 * q + i], x * bq[i]);
+                    for (int i = 0; i < 4; ++i) {
+                        const int n = 4 * q + i;
+                        acc[n] = fmaf(fast_exp2(d0 * rs.A2[n]), acc[n], x0 * c0[i]);
+                        acc[n] = fmaf(fast_exp2(d1 * rs.A2[n]), acc[n], x1 * c1[i]);
+                    }
                 }
-                dsum += dl;
+                dsum += d0 + d1;
             }
         }
         t0 = tnext;
@@ -413,25 +516,23 @@ __device__ __forceinline__ void agg_body(const RowSetup& rs, const typename E::s
 template <class E, bool SOFTPLUS>
 __global__ __launch_bounds__(64) void scan_agg_kernel(
     const typename E::storage* __restrict__ u, const typename E::storage* __restrict__ delta,
-    const float* __restrict__ A, const float* __restrict__ bc, const float* __restrict__ bias,
-    float* __restrict__ agg, int64_t Dn, int64_t L, int64_t seg_len) {
-    constexpr int TT = kNV * E::kPerVec;
-    __shared__ uint32_t rows[2 * 64 * kRowWords];
-    __shared__ __align__(16) float sbc[TT * kBCW];
-    uint32_t* ru = rows + threadIdx.x * kRowWords;
-    uint32_t* rd = ru + 64 * kRowWords;
+    const float* __restrict__ A, const float* __restrict__ B, const float* __restrict__ bias,
+    float* __restrict__ agg, int64_t Dn, int64_t L, int S) {
+    using G = Geo<E>;
+    __shared__ uint32_t srow[G::kRowWords];
+    __shared__ __align__(16) float sbc[G::TT * 20];
     const RowSetup rs = row_setup(A, nullptr, bias, Dn);
     const int seg = blockIdx.z;
     const int64_t R = (int64_t)gridDim.y * Dn;
-    const int64_t t_begin = (int64_t)seg * seg_len;
-    const int64_t t_end = (t_begin + seg_len < L) ? t_begin + seg_len : L;
+    int64_t t_begin, t_end;
+    seg_bounds(seg, S, L, G::TT, t_begin, t_end);
     const int64_t base = rs.row * L;
-    const float* bcb = bc + (int64_t)blockIdx.y * L * kBCW;
+    const float* Bb = B + (int64_t)blockIdx.y * kN * L;
     float acc[kN], dsum;
     if (__all(rs.pow_ok))
-        agg_body<E, SOFTPLUS, true>(rs, u + base, delta + base, bcb, ru, rd, sbc, t_begin, t_end, acc, dsum);
+        agg_body<E, SOFTPLUS, true>(rs, u + base, delta + base, Bb, L, srow, sbc, t_begin, t_end, acc, dsum);
     else
-        agg_body<E, SOFTPLUS, false>(rs, u + base, delta + base, bcb, ru, rd, sbc, t_begin, t_end, acc, dsum);
+        agg_body<E, SOFTPLUS, false>(rs, u + base, delta + base, Bb, L, srow, sbc, t_begin, t_end, acc, dsum);
     if (rs.active) {
         float* a = agg + (int64_t)seg * (kN + 1) * R + rs.row;
 #pragma unroll
@@ -443,23 +544,16 @@ __global__ __launch_bounds__(64) void scan_agg_kernel(
 template <class E, bool HAS_Z, bool SOFTPLUS>
 hipError_t launch_fast_t(const ScanLaunch& a, const ScanPlan& p, float* ws, hipStream_t stream) {
     using S_t = typename E::storage;
-    float* bc = ws;
-    float* agg = ws + a.Bt * a.L * kBCW;
-    {
-        const int64_t total = a.Bt * a.L;
-        int64_t blocks = (total + 255) / 256;
-        if (blocks > 65535) blocks = 65535;
-        bc_transpose_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(a.B, a.C, bc, a.L, total);
-    }
+    float* agg = ws;
     const dim3 block(64);
     const unsigned gx = static_cast<unsigned>((a.Dn + 63) / 64);
     if (p.segments > 1)
         scan_agg_kernel<E, SOFTPLUS><<<dim3(gx, (unsigned)a.Bt, (unsigned)(p.segments - 1)), block, 0, stream>>>(
-            static_cast<const S_t*>(a.u), static_cast<const S_t*>(a.delta), a.A, bc, a.bias, agg, a.Dn,
-            a.L, p.seg_len);
+            static_cast<const S_t*>(a.u), static_cast<const S_t*>(a.delta), a.A, a.B, a.bias, agg, a.Dn, a.L,
+            p.segments);
     scan_main_kernel<E, HAS_Z, SOFTPLUS><<<dim3(gx, (unsigned)a.Bt, (unsigned)p.segments), block, 0, stream>>>(
-        static_cast<const S_t*>(a.u), static_cast<const S_t*>(a.delta), static_cast<const S_t*>(a.z), a.A,
-        bc, a.D, a.bias, agg, static_cast<S_t*>(a.out), a.last_state, a.Dn, a.L, p.seg_len, p.segments);
+        static_cast<const S_t*>(a.u), static_cast<const S_t*>(a.delta), static_cast<const S_t*>(a.z), a.A, a.B,
+        a.C, a.D, a.bias, agg, static_cast<S_t*>(a.out), a.last_state, a.Dn, a.L, p.segments);
     return hipGetLastError();
 }
 
@@ -472,9 +566,28 @@ hipError_t launch_fast_e(const ScanLaunch& a, const ScanPlan& p, float* ws, hipS
 
 }  // namespace
 
+// Segments per channel group: enough wavefronts to give each SIMD about 2.5 (the main kernel
+// holds 3 per SIMD), at most one per tile.  MSS_SCAN_SEGMENTS overrides.
+ScanPlan plan_fast(const ScanLaunch& a, int num_cus) {
+    ScanPlan p;
+    const int TT = kFastTileBytes / (a.bf16 ? 2 : 4);
+    const int64_t groups = a.Bt * ((a.Dn + 63) / 64);
+    const int64_t tiles = (a.L + TT - 1) / TT;
+    const int64_t target = 10LL * (num_cus > 0 ? num_cus : 256);
+    int64_t S = (target + groups / 2) / groups;
+    const char* env = getenv("MSS_SCAN_SEGMENTS");
+    if (env && atoi(env) > 0) S = atoi(env);
+    if (S > tiles) S = tiles;
+    if (S > 65535) S = 65535;
+    if (S < 1) S = 1;
+    p.segments = static_cast<int>(S);
+    p.seg_len = 0;
+    p.workspace_bytes = fast_workspace_bytes(a, p.segments);
+    return p;
+}
+
 size_t fast_workspace_bytes(const ScanLaunch& a, int segments) {
-    return (static_cast<size_t>(a.Bt * a.L) * kBCW +
-            static_cast<size_t>(segments > 1 ? segments - 1 : 0) * (kN + 1) * static_cast<size_t>(a.Bt * a.Dn)) *
+    return static_cast<size_t>(segments > 1 ? segments - 1 : 0) * (kN + 1) * static_cast<size_t>(a.Bt * a.Dn) *
            sizeof(float);
 }
 
