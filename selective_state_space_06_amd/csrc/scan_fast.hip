@@ -325,7 +325,9 @@ __device__ __forceinline__ void main_body(
             put2<E>(srow, j, y0, y1);
             cur = nxt;
         }
-        // Epilogue: gate, round to the storage type, 16-byte stores.
+        // Epilogue: gate and round the whole tile first (one block of independent work the
+        // compiler can interleave), then the 16-byte stores of the valid vectors.
+        uint4 packed[kNV];
 #pragma unroll
         for (int v = 0; v < kNV; ++v) {
             float o[V];
@@ -334,8 +336,12 @@ __device__ __forceinline__ void main_body(
                 o[e] = result_of<E>(srow, v * V + e);
                 if (HAS_Z) o[e] *= silu(vec_elem<E>(zw + 4 * v, e));
             }
-            if (rs.active && t0 + v * V < t_end)
-                *reinterpret_cast<uint4*>(op + t0 + v * V) = E::pack(o);
+            packed[v] = E::pack(o);
+        }
+        if (rs.active) {
+#pragma unroll
+            for (int v = 0; v < kNV; ++v)
+                if (t0 + v * V < t_end) *reinterpret_cast<uint4*>(op + t0 + v * V) = packed[v];
         }
     }
 }
@@ -349,36 +355,38 @@ __device__ __forceinline__ void seg_bounds(int seg, int S, int64_t L, int TT, in
     t_end = e < L ? e : L;
 }
 
-// Folds the aggregates of segments [0, seg) into the starting state of segment seg.  The
-// 17 values of segment s + 1 are loaded before segment s is folded in, so the loads of
-// consecutive segments overlap instead of forming a chain of memory round trips.
+// Folds the aggregates of segments [0, seg) into the starting state of segment seg, four
+// segments per round: the 68 loads of a round are issued together, so a round costs one memory
+// round trip.
 template <bool POW>
 __device__ __forceinline__ void fold_carry(float (&h)[kN], const float (&A2)[kN],
                                            const float* __restrict__ agg, int seg, int64_t R,
                                            int64_t row) {
+    constexpr int kRound = 4;
 #pragma unroll
     for (int n = 0; n < kN; ++n) h[n] = 0.0f;
-    if (seg == 0) return;
-    float nxt[kN + 1];
+    for (int s0 = 0; s0 < seg; s0 += kRound) {
+        float v[kRound][kN + 1];
 #pragma unroll
-    for (int n = 0; n <= kN; ++n) nxt[n] = agg[(int64_t)n * R + row];
-    for (int s = 0; s < seg; ++s) {
-        float cur[kN + 1];
+        for (int i = 0; i < kRound; ++i) {
+            const int s = s0 + i < seg ? s0 + i : seg - 1;  // past the end: reload the last one
+            const float* a = agg + (int64_t)s * (kN + 1) * R + row;
 #pragma unroll
-        for (int n = 0; n <= kN; ++n) cur[n] = nxt[n];
-        if (s + 1 < seg) {
-            const float* a = agg + (int64_t)(s + 1) * (kN + 1) * R + row;
-#pragma unroll
-            for (int n = 0; n <= kN; ++n) nxt[n] = a[(int64_t)n * R];
+            for (int n = 0; n <= kN; ++n) v[i][n] = a[(int64_t)n * R];
         }
-        if (POW) {
-            float p[kN];
-            powers16(fast_exp2(cur[kN] * A2[0]), p);
 #pragma unroll
-            for (int n = 0; n < kN; ++n) h[n] = fmaf(p[n], h[n], cur[n]);
-        } else {
+        for (int i = 0; i < kRound; ++i) {
+            if (s0 + i < seg) {
+                if (POW) {
+                    float p[kN];
+                    powers16(fast_exp2(v[i][kN] * A2[0]), p);
 #pragma unroll
-            for (int n = 0; n < kN; ++n) h[n] = fmaf(fast_exp2(cur[kN] * A2[n]), h[n], cur[n]);
+                    for (int n = 0; n < kN; ++n) h[n] = fmaf(p[n], h[n], v[i][n]);
+                } else {
+#pragma unroll
+                    for (int n = 0; n < kN; ++n) h[n] = fmaf(fast_exp2(v[i][kN] * A2[n]), h[n], v[i][n]);
+                }
+            }
         }
     }
 }
