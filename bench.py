@@ -12,7 +12,16 @@ Infinity Cache from the previous step.
 
 Prints ONE JSON line.  `value` is algorithmic GB/s of the whole step (every input read once,
 every output written once) over the K timed steps; the scan alone is also timed with HIP
-events on the stream it runs on.
+events on the stream it runs on, and the library's launch-timing hook (mss_profile_enable /
+mss_profile_fwd) times its two kernels separately over the same timed steps.
+
+`roofline` describes the scan's dominant kernel, the main scan kernel: it is bound by VALU and
+transcendental issue, so it is priced in algorithmic fp32 work against the MI355X fp32 vector
+peak.  Algorithmic work of the recurrence per (b, d, t): per state n, exp(delta A) (a multiply
+and an exp), Abar h + (delta u) B (a multiply and an FMA) and C h accumulated into y (an FMA):
+7 flops with an exp counted as one; per (b, d, t) besides, softplus(delta + bias) (4),
+delta u (1), y + D u (2) and the silu(z) gate (5): 12.  The main kernel's share of HBM
+traffic, from rocprofv3 counters taken on this exact kernel source, is `traffic`.
 """
 from __future__ import annotations
 
@@ -25,8 +34,24 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, AMD published peak
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, AMD published peak
 WORKLOAD = "mamba2p8b_bf16"
+FLOPS_PER_STATE_UPDATE = 7
+FLOPS_PER_ROW_STEP = 12
+
+# HBM bytes per launch of the main scan kernel on this workload, from two rocprofv3 --pmc runs
+# of `python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline` (FETCH_SIZE, then WRITE_SIZE),
+# each scaled by what the counter reads for a plain 1 GiB device copy (FETCH_SIZE x2.0,
+# WRITE_SIZE x1.0).  Valid only for the kernel source with this SHA-256 prefix; otherwise
+# traffic is reported as null.
+MAIN_TRAFFIC = {"src_sha256": "78f678bdb32c75f1", "fetch_bytes": 506974989, "write_bytes": 100034168}
+
+
+def kernel_source_digest():
+    import hashlib
+    path = os.path.join(ROOT, "selective_state_space_06_amd", "csrc", "scan_fast.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
 def scan_bytes(Bt, Dn, N, L, es_io=2, with_z=True, last_state=True):
@@ -124,11 +149,14 @@ def main():
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
+    mss.profile_enable(True)
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(k, evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    mss.profile_enable(False)
+    n_calls, carry_ms_tot, main_ms_tot = mss.profile_fwd()
 
     scan_ms = [e[0].elapsed_time(e[1]) for e in evs]
     dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
@@ -138,6 +166,14 @@ def main():
     scan_avg_ms = float(np.mean(scan_ms))
     scan_gbps = sb / (scan_avg_ms * 1e-3) / 1e9
     updates = Bt * Dn * L * N + Bt * Dn * N
+    main_ms = main_ms_tot / max(n_calls, 1)
+    carry_ms = carry_ms_tot / max(n_calls, 1)
+    flops = Bt * Dn * L * (N * FLOPS_PER_STATE_UPDATE + FLOPS_PER_ROW_STEP)
+    achieved = flops / (main_ms * 1e-3) / 1e12
+    traffic = None
+    if MAIN_TRAFFIC["src_sha256"] == kernel_source_digest():
+        traffic = MAIN_TRAFFIC["fetch_bytes"] + MAIN_TRAFFIC["write_bytes"]
+    main_bytes = Bt * Dn * L * 2 * 4 + 2 * Bt * N * L * 4  # u, delta, z in, out; B, C
 
     res = {
         "metric": "selective-scan fwd GB/s + state-updates/s (B*D*L*N/s), % of MI355X HBM peak",
@@ -162,10 +198,16 @@ def main():
                      "gbps": round(scan_gbps, 2), "frac_hbm_peak": round(scan_gbps / HBM_PEAK_GBPS, 4),
                      "state_updates_per_s": round(Bt * Dn * L * N / (scan_avg_ms * 1e-3), 1)},
         "decode_token": {"avg_us": round(float(np.mean(dec_ms)) * 1e3, 2)},
-        "roofline": {"bound": "hbm", "achieved": round(scan_gbps, 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(scan_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "mss_selective_scan_fwd (one call: aggregate, combine and main "
-                               "kernels), timed with HIP events on its stream"},
+        "kernels": {"calls_timed": n_calls, "carry_stage_avg_ms": round(carry_ms, 4),
+                    "main_avg_ms": round(main_ms, 4),
+                    "main_hbm_gbps": round(main_bytes / (main_ms * 1e-3) / 1e9, 2),
+                    "main_frac_hbm_peak": round(main_bytes / (main_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": FP32_VECTOR_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / FP32_VECTOR_PEAK_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel": "scan_main_kernel (the main kernel of mss_selective_scan_fwd), "
+                               "timed by the library's HIP events on its stream",
+                     "algorithmic_flops": flops},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(s, Bt, Dn, N, L)

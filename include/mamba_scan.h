@@ -75,7 +75,10 @@ typedef struct {
  *   softplus_flag  nonzero: delta = softplus(delta_raw + bias); zero: delta_raw + bias
  *   out         (batch, d_inner, L)      dtype of u, written
  *   last_state  (batch, d_inner, d_state) f32, nullable; written with h_L (zeros if L = 0)
- * d_state must be 16.  out must not overlap any input or last_state.
+ * d_state must be 16.  out must not overlap any input or last_state.  A and last_state must
+ * be 16-byte aligned (MSS_ERR_LAYOUT otherwise).  When every row of u / delta / z / out spans
+ * a multiple of 16 bytes and those tensors and B / C start 16-byte aligned, the vectorised
+ * kernels run; any other valid layout takes a slower general path with the same results.
  */
 int mss_selective_scan_fwd(const mss_tensor_t* u, const mss_tensor_t* delta,
                            const mss_tensor_t* A, const mss_tensor_t* B, const mss_tensor_t* C,
@@ -98,7 +101,7 @@ int mss_selective_scan_fwd(const mss_tensor_t* u, const mss_tensor_t* delta,
  *   dt_bias     (d_inner,)               f32, nullable
  *   out         (batch, d_inner)         dtype of x, written
  * d_state must be 16.  out must not overlap any input or the state; the state must not
- * overlap any input.
+ * overlap any input.  state, A, B and C must be 16-byte aligned (MSS_ERR_LAYOUT otherwise).
  */
 int mss_selective_state_update(const mss_tensor_t* state, const mss_tensor_t* x,
                                const mss_tensor_t* dt, const mss_tensor_t* A,
@@ -106,6 +109,22 @@ int mss_selective_state_update(const mss_tensor_t* state, const mss_tensor_t* x,
                                const mss_tensor_t* D, const mss_tensor_t* z,
                                const mss_tensor_t* dt_bias, const mss_tensor_t* out,
                                void* stream);
+
+/*
+ * Launch timing, for measurement only (the results of the calls above do not depend on it).
+ * mss_profile_enable(1) clears the records and makes each later mss_selective_scan_fwd (up to
+ * 1024 calls) record three library-owned HIP events on its stream: before its first kernel,
+ * between the carry stage (the per-segment aggregates of a split sequence) and the main
+ * kernel, and after the main kernel.  mss_profile_enable(0) stops recording (the records stay).
+ * mss_profile_fwd waits for the recorded calls to finish and returns their count and the
+ * summed carry-stage and main-kernel times in milliseconds (a call that did not split its
+ * sequence adds 0 carry time).  Events are created on the device current at the recording
+ * call; record calls of one device at a time.
+ * Returns MSS_OK; MSS_ERR_NULL_ARG for a NULL output pointer; MSS_ERR_HIP when the runtime
+ * reports an error.
+ */
+int mss_profile_enable(int on);
+int mss_profile_fwd(int* calls, double* carry_ms, double* main_ms);
 
 /* Static, NUL-terminated name of a status code ("MSS_OK", "MSS_ERR_SHAPE", ...). */
 const char* mss_status_string(int status);

@@ -11,6 +11,8 @@ from ._binding import (  # noqa: F401
     MssError,
     Tensor,
     load_library,
+    profile_enable,
+    profile_fwd,
     scan_fwd_raw,
     selective_scan_fwd,
     selective_state_update,

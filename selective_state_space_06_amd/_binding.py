@@ -17,8 +17,8 @@ STATUS = {0: "MSS_OK", -1: "MSS_ERR_NULL_ARG", -2: "MSS_ERR_SHAPE", -3: "MSS_ERR
           -4: "MSS_ERR_LAYOUT", -5: "MSS_ERR_ALIAS", -6: "MSS_ERR_UNSUPPORTED", -7: "MSS_ERR_HIP"}
 
 # every symbol include/mamba_scan.h declares
-EXPORTS = ("mss_selective_scan_fwd", "mss_selective_state_update", "mss_status_string",
-           "mss_version")
+EXPORTS = ("mss_selective_scan_fwd", "mss_selective_state_update", "mss_profile_enable",
+           "mss_profile_fwd", "mss_status_string", "mss_version")
 
 
 class Tensor(ctypes.Structure):
@@ -74,6 +74,12 @@ def load_library(path: str = LIB_PATH):
             lib.mss_status_string.argtypes = [ctypes.c_int]
             lib.mss_version.restype = ctypes.c_int
             lib.mss_version.argtypes = []
+            lib.mss_profile_enable.restype = ctypes.c_int
+            lib.mss_profile_enable.argtypes = [ctypes.c_int]
+            lib.mss_profile_fwd.restype = ctypes.c_int
+            lib.mss_profile_fwd.argtypes = [ctypes.POINTER(ctypes.c_int),
+                                            ctypes.POINTER(ctypes.c_double),
+                                            ctypes.POINTER(ctypes.c_double)]
             _lib = lib
     return _lib
 
@@ -84,6 +90,22 @@ def status_string(status: int) -> str:
 
 def version() -> int:
     return int(load_library().mss_version())
+
+
+def profile_enable(on: bool = True) -> None:
+    """mss_profile_enable: record launch-timing events around each forward scan's kernels."""
+    st = load_library().mss_profile_enable(1 if on else 0)
+    if st != 0:
+        raise MssError(st, "mss_profile_enable")
+
+
+def profile_fwd():
+    """mss_profile_fwd: (calls, carry_ms_total, main_ms_total) of the recorded forward scans."""
+    n, c, m = ctypes.c_int(), ctypes.c_double(), ctypes.c_double()
+    st = load_library().mss_profile_fwd(ctypes.byref(n), ctypes.byref(c), ctypes.byref(m))
+    if st != 0:
+        raise MssError(st, "mss_profile_fwd")
+    return int(n.value), float(c.value), float(m.value)
 
 
 def _ref(t):

@@ -2,6 +2,7 @@
 // workspace, and dispatch to the gfx950 kernels.  Every check runs before the first HIP call,
 // so invalid arguments never reach the device.
 #include <cstdlib>
+#include <vector>
 #include <initializer_list>
 #include <mutex>
 #include <unordered_map>
@@ -137,6 +138,16 @@ hipError_t workspace(int dev, void* stream, size_t bytes, float** out) {
     *out = static_cast<float*>(w.ptr);
     return hipSuccess;
 }
+
+// Launch timing (mss_profile_enable / mss_profile_fwd): one event triple per recorded call.
+constexpr int kProfMaxCalls = 1024;
+struct Prof {
+    bool on = false;
+    int calls = 0;                 // recorded since enabling
+    std::vector<hipEvent_t> ev;    // 3 per call slot, created on demand
+    std::vector<char> split;       // the call ran a carry stage
+};
+Prof g_prof;
 
 int validate_fwd(const mss_tensor_t* u, const mss_tensor_t* delta, const mss_tensor_t* A,
                  const mss_tensor_t* B, const mss_tensor_t* C, const mss_tensor_t* D,
@@ -290,8 +301,61 @@ int mss_selective_scan_fwd(const mss_tensor_t* u, const mss_tensor_t* delta, con
         float* ws = nullptr;
         if (plan.workspace_bytes > 0 && workspace(dev, stream, plan.workspace_bytes, &ws) != hipSuccess)
             return MSS_ERR_HIP;
+        std::unique_lock<std::mutex> plk(g_mu, std::defer_lock);
+        int slot = -1;
+        if (g_prof.on) {
+            plk.lock();
+            if (g_prof.calls < kProfMaxCalls) {
+                slot = g_prof.calls;
+                if (static_cast<int>(g_prof.split.size()) <= slot) {
+                    for (int k = 0; k < 3; ++k) {
+                        hipEvent_t ev = nullptr;
+                        if (hipEventCreate(&ev) != hipSuccess) return MSS_ERR_HIP;
+                        g_prof.ev.push_back(ev);
+                    }
+                    g_prof.split.push_back(0);
+                }
+                for (int k = 0; k < 3; ++k) a.ev[k] = g_prof.ev[3 * slot + k];
+                g_prof.split[slot] = plan.segments > 1;
+            }
+        }
         const hipError_t e = fast ? mss::launch_scan_fast(a, plan, ws, s) : mss::launch_scan_fwd(a, plan, ws, s);
+        if (slot >= 0 && e == hipSuccess) g_prof.calls = slot + 1;
         return e == hipSuccess ? MSS_OK : MSS_ERR_HIP;
+    } catch (...) {
+        return MSS_ERR_HIP;
+    }
+}
+
+int mss_profile_enable(int on) {
+    try {
+        std::lock_guard<std::mutex> lk(g_mu);
+        g_prof.on = on != 0;
+        if (on) g_prof.calls = 0;
+        return MSS_OK;
+    } catch (...) {
+        return MSS_ERR_HIP;
+    }
+}
+
+int mss_profile_fwd(int* calls, double* carry_ms, double* main_ms) {
+    if (!calls || !carry_ms || !main_ms) return MSS_ERR_NULL_ARG;
+    try {
+        std::lock_guard<std::mutex> lk(g_mu);
+        double c = 0.0, m = 0.0;
+        for (int i = 0; i < g_prof.calls; ++i) {
+            hipEvent_t* e = &g_prof.ev[3 * i];
+            if (hipEventSynchronize(e[2]) != hipSuccess) return MSS_ERR_HIP;
+            float ci = 0.0f, mi = 0.0f;
+            if (hipEventElapsedTime(&ci, e[0], e[1]) != hipSuccess) return MSS_ERR_HIP;
+            if (hipEventElapsedTime(&mi, e[1], e[2]) != hipSuccess) return MSS_ERR_HIP;
+            c += g_prof.split[i] ? ci : 0.0f;
+            m += mi;
+        }
+        *calls = g_prof.calls;
+        *carry_ms = c;
+        *main_ms = m;
+        return MSS_OK;
     } catch (...) {
         return MSS_ERR_HIP;
     }

@@ -26,7 +26,15 @@ struct ScanLaunch {
     int softplus;
     bool bf16;              // storage type of u / delta / z / out
     bool vec_ok;            // rows of u / delta / z / out are 16-byte aligned
+    // Optional timing events (all null or all valid): recorded on the stream before the first
+    // kernel, before the main kernel and after it.
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
 };
+
+// Records launch-timing event k of `a` on `stream` when timing is on.
+inline void mark(const ScanLaunch& a, int k, hipStream_t stream) {
+    if (a.ev[k]) (void)hipEventRecord(a.ev[k], stream);
+}
 
 struct DecodeLaunch {
     float* state;           // (Bt, Dn, N), in/out

@@ -555,13 +555,16 @@ hipError_t launch_fast_t(const ScanLaunch& a, const ScanPlan& p, float* ws, hipS
     float* agg = ws;
     const dim3 block(64);
     const unsigned gx = static_cast<unsigned>((a.Dn + 63) / 64);
+    mark(a, 0, stream);
     if (p.segments > 1)
         scan_agg_kernel<E, SOFTPLUS><<<dim3(gx, (unsigned)a.Bt, (unsigned)(p.segments - 1)), block, 0, stream>>>(
             static_cast<const S_t*>(a.u), static_cast<const S_t*>(a.delta), a.A, a.B, a.bias, agg, a.Dn, a.L,
             p.segments);
+    mark(a, 1, stream);
     scan_main_kernel<E, HAS_Z, SOFTPLUS><<<dim3(gx, (unsigned)a.Bt, (unsigned)p.segments), block, 0, stream>>>(
         static_cast<const S_t*>(a.u), static_cast<const S_t*>(a.delta), static_cast<const S_t*>(a.z), a.A, a.B,
         a.C, a.D, a.bias, agg, static_cast<S_t*>(a.out), a.last_state, a.Dn, a.L, p.segments);
+    mark(a, 2, stream);
     return hipGetLastError();
 }
 

@@ -351,15 +351,19 @@ __global__ __launch_bounds__(256) void zero_state_kernel(float* p, int64_t n) {
 constexpr int kTile = 32;
 
 template <class E, bool VEC, bool HAS_Z>
-hipError_t launch_typed(const KArgs& k, int64_t Bt, hipStream_t stream) {
+hipError_t launch_typed(const KArgs& k, const ScanLaunch& a, hipStream_t stream) {
+    const int64_t Bt = a.Bt;
     const dim3 block(kRows);
     const unsigned gx = static_cast<unsigned>((k.Dn + kRows - 1) / kRows);
+    mark(a, 0, stream);
     if (k.S > 1) {
         scan_kernel<E, VEC, HAS_Z, kAgg, kTile><<<dim3(gx, (unsigned)Bt, (unsigned)(k.S - 1)), block, 0, stream>>>(k);
         const int64_t cblocks = (k.rows_total + 255) / 256;
         combine_kernel<<<dim3((unsigned)(cblocks < 65535 ? cblocks : 65535)), dim3(256), 0, stream>>>(k);
     }
+    mark(a, 1, stream);
     scan_kernel<E, VEC, HAS_Z, kMain, kTile><<<dim3(gx, (unsigned)Bt, (unsigned)k.S), block, 0, stream>>>(k);
+    mark(a, 2, stream);
     return hipGetLastError();
 }
 
@@ -413,11 +417,11 @@ hipError_t launch_scan_fwd(const ScanLaunch& a, const ScanPlan& plan, float* wor
     k.S = plan.segments; k.softplus = a.softplus;
     const bool hz = a.z != nullptr;
     if (a.bf16) {
-        if (a.vec_ok) return hz ? launch_typed<BF16, true, true>(k, a.Bt, stream) : launch_typed<BF16, true, false>(k, a.Bt, stream);
-        return hz ? launch_typed<BF16, false, true>(k, a.Bt, stream) : launch_typed<BF16, false, false>(k, a.Bt, stream);
+        if (a.vec_ok) return hz ? launch_typed<BF16, true, true>(k, a, stream) : launch_typed<BF16, true, false>(k, a, stream);
+        return hz ? launch_typed<BF16, false, true>(k, a, stream) : launch_typed<BF16, false, false>(k, a, stream);
     }
-    if (a.vec_ok) return hz ? launch_typed<F32, true, true>(k, a.Bt, stream) : launch_typed<F32, true, false>(k, a.Bt, stream);
-    return hz ? launch_typed<F32, false, true>(k, a.Bt, stream) : launch_typed<F32, false, false>(k, a.Bt, stream);
+    if (a.vec_ok) return hz ? launch_typed<F32, true, true>(k, a, stream) : launch_typed<F32, true, false>(k, a, stream);
+    return hz ? launch_typed<F32, false, true>(k, a, stream) : launch_typed<F32, false, false>(k, a, stream);
 }
 
 }  // namespace mss

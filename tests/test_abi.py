@@ -235,3 +235,21 @@ def test_dec_layout_and_alias(lib):
     assert call_dec(a) == ALIAS
     a = dec_args(n=4)
     assert call_dec(a) == UNSUPPORTED
+
+
+# --------------------------------------------------------------------- launch timing
+
+def test_profile_fwd_without_records(lib):
+    """Enabling clears the records; with no recorded call the totals are zero (no HIP call)."""
+    assert lib.mss_profile_enable(1) == OK
+    n, c, m = ctypes.c_int(-1), ctypes.c_double(-1.0), ctypes.c_double(-1.0)
+    assert lib.mss_profile_fwd(ctypes.byref(n), ctypes.byref(c), ctypes.byref(m)) == OK
+    assert (n.value, c.value, m.value) == (0, 0.0, 0.0)
+    assert lib.mss_profile_enable(0) == OK
+
+
+def test_profile_fwd_null_outputs(lib):
+    n, c = ctypes.c_int(), ctypes.c_double()
+    assert lib.mss_profile_fwd(None, ctypes.byref(c), ctypes.byref(c)) == NULL_ARG
+    assert lib.mss_profile_fwd(ctypes.byref(n), None, ctypes.byref(c)) == NULL_ARG
+    assert lib.mss_profile_fwd(ctypes.byref(n), ctypes.byref(c), None) == NULL_ARG

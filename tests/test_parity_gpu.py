@@ -246,3 +246,23 @@ def test_nondefault_stream(mss, orc):
     st.synchronize()
     ref_out, ref_last = oracle_scan(orc, s)
     assert_close(host64(out), ref_out, what="side stream out", **TOL_F32)
+
+
+def test_launch_timing_records(mss, orc):
+    """The timing hook records each call's kernels without changing its results."""
+    import torch
+    s = scan_inputs(2, 128, 16, 1024, dtype="f32", seed=31)
+    mss.profile_enable(True)
+    try:
+        out, last = run_scan(mss, s)
+        out2, _ = run_scan(mss, s)
+    finally:
+        mss.profile_enable(False)
+    out3, _ = run_scan(mss, s)  # not recorded
+    torch.cuda.synchronize()
+    calls, carry_ms, main_ms = mss.profile_fwd()  # the records outlive disabling
+    assert calls == 2
+    assert main_ms > 0.0 and carry_ms >= 0.0
+    assert torch.equal(out, out2) and torch.equal(out, out3)
+    ref_out, ref_last = oracle_scan(orc, s)
+    assert_close(host64(out), ref_out, what="timed out", **TOL_F32)
