@@ -346,13 +346,34 @@ __device__ __forceinline__ void main_body(
     }
 }
 
-// Segment seg of S: tiles [seg T / S, (seg + 1) T / S) of the T = ceil(L / TT) tiles.
-__device__ __forceinline__ void seg_bounds(int seg, int S, int64_t L, int TT, int64_t& t_begin,
-                                           int64_t& t_end) {
+// Segment seg of S: tiles [seg T / S, (seg + 1) T / S) of the T = ceil(L / TT) tiles.  (Whole
+// tiles keep every tile on a 64-byte boundary of its rows; finer splits were measured slower.)
+template <class E>
+__device__ __forceinline__ void seg_bounds(int seg, int S, int64_t L, int64_t& t_begin, int64_t& t_end) {
+    constexpr int TT = Geo<E>::TT;
     const int64_t T = (L + TT - 1) / TT;
     t_begin = (seg * T / S) * TT;
     const int64_t e = ((seg + 1) * T / S) * TT;
     t_end = e < L ? e : L;
+}
+
+// B at steps j, j + 1 from the aggregate kernel's B block (stride 20 floats per step).
+struct BPair {
+    float b[2][kN];
+};
+
+__device__ __forceinline__ BPair b_pair(const float* sbc, int j) {
+    BPair r;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float4* p = reinterpret_cast<const float4*>(sbc + (j + i) * 20);
+#pragma unroll
+        for (int q = 0; q < kN / 4; ++q) {
+            const float4 v = p[q];
+            r.b[i][4 * q] = v.x; r.b[i][4 * q + 1] = v.y; r.b[i][4 * q + 2] = v.z; r.b[i][4 * q + 3] = v.w;
+        }
+    }
+    return r;
 }
 
 // Folds the aggregates of segments [0, seg) into the starting state of segment seg, four
@@ -405,7 +426,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sc
     const int seg = blockIdx.z;
     const int64_t R = (int64_t)gridDim.y * Dn;
     int64_t t_begin, t_end;
-    seg_bounds(seg, S, L, G::TT, t_begin, t_end);
+    seg_bounds<E>(seg, S, L, t_begin, t_end);
     const int64_t base = rs.row * L;
     const float* Bb = B + (int64_t)blockIdx.y * kN * L;
     const float* Cb = C + (int64_t)blockIdx.y * kN * L;
@@ -464,32 +485,31 @@ __device__ __forceinline__ void agg_body(const RowSetup& rs, const typename E::s
         }
         const int nsteps = static_cast<int>(t_end - t0 < TT ? t_end - t0 : TT);
         if (POW) {
+            // The scalars and the B values of the next pair are read one iteration ahead, so an
+            // iteration does not start by waiting for its own LDS reads (unrolled by two so the
+            // current / next register sets alternate instead of being copied).
             Pair cur = pair_of<E, SOFTPLUS, true, false>(su, sd, nsteps - 2, rs);
-#pragma unroll 1
+            BPair bcur = b_pair(sbc, nsteps - 2);
+#pragma unroll 2
             for (int j = nsteps - 2; j >= 0; j -= 2) {
-                const Pair nxt = pair_of<E, SOFTPLUS, true, false>(su, sd, j >= 2 ? j - 2 : 0, rs);
-                const float4* b0 = reinterpret_cast<const float4*>(sbc + j * 20);
-                const float4* b1 = reinterpret_cast<const float4*>(sbc + (j + 1) * 20);
+                const int jn = j >= 2 ? j - 2 : 0;
+                const Pair nxt = pair_of<E, SOFTPLUS, true, false>(su, sd, jn, rs);
+                const BPair bnxt = b_pair(sbc, jn);
                 // step j + 1 first (backward), then step j
                 const float R1 = Rp;
                 const float R0 = Rp * cur.a[1];
                 Rp = R0 * cur.a[0];
                 float w1 = cur.x[1], w0 = cur.x[0];
 #pragma unroll
-                for (int q = 0; q < kN / 4; ++q) {
-                    const float4 x1 = b1[q], x0 = b0[q];
-                    const float c1[4] = {x1.x, x1.y, x1.z, x1.w};
-                    const float c0[4] = {x0.x, x0.y, x0.z, x0.w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        w1 *= R1;
-                        w0 *= R0;
-                        acc[4 * q + i] = fmaf(c1[i], w1, acc[4 * q + i]);
-                        acc[4 * q + i] = fmaf(c0[i], w0, acc[4 * q + i]);
-                    }
+                for (int n = 0; n < kN; ++n) {
+                    w1 *= R1;
+                    w0 *= R0;
+                    acc[n] = fmaf(bcur.b[1][n], w1, acc[n]);
+                    acc[n] = fmaf(bcur.b[0][n], w0, acc[n]);
                 }
                 dsum += cur.d[1] + cur.d[0];
                 cur = nxt;
+                bcur = bnxt;
             }
         } else {
 #pragma unroll 1
@@ -533,7 +553,7 @@ __global__ __launch_bounds__(64) void scan_agg_kernel(
     const int seg = blockIdx.z;
     const int64_t R = (int64_t)gridDim.y * Dn;
     int64_t t_begin, t_end;
-    seg_bounds(seg, S, L, G::TT, t_begin, t_end);
+    seg_bounds<E>(seg, S, L, t_begin, t_end);
     const int64_t base = rs.row * L;
     const float* Bb = B + (int64_t)blockIdx.y * kN * L;
     float acc[kN], dsum;
@@ -577,14 +597,15 @@ hipError_t launch_fast_e(const ScanLaunch& a, const ScanPlan& p, float* ws, hipS
 
 }  // namespace
 
-// Segments per channel group: enough wavefronts to give each SIMD about 2.5 (the main kernel
-// holds 3 per SIMD), at most one per tile.  MSS_SCAN_SEGMENTS overrides.
+// Segments per channel group: about ten wavefronts per CU for bf16 rows and six for fp32 rows
+// (the main kernel holds 12), which measured best on the Mamba-2.8B (bf16) and Mamba-130M (fp32)
+// layer shapes; at most one per tile.  MSS_SCAN_SEGMENTS overrides.
 ScanPlan plan_fast(const ScanLaunch& a, int num_cus) {
     ScanPlan p;
     const int TT = kFastTileBytes / (a.bf16 ? 2 : 4);
     const int64_t groups = a.Bt * ((a.Dn + 63) / 64);
     const int64_t tiles = (a.L + TT - 1) / TT;
-    const int64_t target = 10LL * (num_cus > 0 ? num_cus : 256);
+    const int64_t target = (a.bf16 ? 10LL : 6LL) * (num_cus > 0 ? num_cus : 256);
     int64_t S = (target + groups / 2) / groups;
     const char* env = getenv("MSS_SCAN_SEGMENTS");
     if (env && atoi(env) > 0) S = atoi(env);
