@@ -266,3 +266,42 @@ def test_launch_timing_records(mss, orc):
     assert torch.equal(out, out2) and torch.equal(out, out3)
     ref_out, ref_last = oracle_scan(orc, s)
     assert_close(host64(out), ref_out, what="timed out", **TOL_F32)
+
+
+def test_decode_graph_replays_match_eager(mss):
+    """A captured HIP graph of chained decode steps gives the eager results on every replay."""
+    import torch
+    dev = torch.device("cuda:0")
+    d = decode_inputs(4, 256, 16, 8, dtype="bf16", with_z=True, seed=41)
+    up = lambda a, bf=False: (torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)
+                              if bf else torch.from_numpy(np.ascontiguousarray(a)).to(dev))
+    X, DT, Z, Bs, Cs = up(d.x, True), up(d.dt, True), up(d.z, True), up(d.B), up(d.C)
+    A, D, bias = up(d.A), up(d.D), up(d.dt_bias)
+    state = torch.zeros((4, 256, 16), dtype=torch.float32, device=dev)
+    outs = torch.empty((8, 4, 256), dtype=torch.bfloat16, device=dev)
+
+    def chain():
+        for k in range(8):
+            mss.selective_state_update(state, X[k], DT[k], A, Bs[k], Cs[k], D=D, z=Z[k],
+                                       dt_bias=bias, out=outs[k])
+
+    chain()
+    torch.cuda.synchronize()
+    ref_state, ref_outs = state.clone(), outs.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        state.zero_()
+        chain()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        chain()
+    for rep in range(3):
+        state.zero_()
+        outs.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(state, ref_state), f"replay {rep}: state"
+        assert torch.equal(outs, ref_outs), f"replay {rep}: out"
