@@ -49,7 +49,7 @@ def _load():
             lib.oracle_selective_scan.restype = ctypes.c_int
             lib.oracle_selective_scan.argtypes = [
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i64p,
-                _d, _d, _d, _d, _d, _d, _d, _d, ctypes.c_int, _d, _d, ctypes.c_int]
+                _d, _d, _d, _d, _d, _d, _d, _d, ctypes.c_int, _d, _d, _d, ctypes.c_int]
             lib.oracle_state_update.restype = ctypes.c_int
             lib.oracle_state_update.argtypes = [
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i64p,
@@ -93,11 +93,12 @@ def silu(x) -> np.ndarray:
 
 
 def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus_flag=True,
-                   rows=None, nthreads: int = 0):
+                   rows=None, nthreads: int = 0, h0=None):
     """Run the fp64 scan.
 
     u, delta, z: (batch, d_inner, L); A: (d_inner, d_state); B, C: (batch, d_state, L);
     D, delta_bias: (d_inner,).  Any float dtype; values are taken exactly as float64.
+    h0: optional starting state (batch, d_inner, d_state) (default zeros).
     rows: optional flat row indices r = b * d_inner + d to compute (default: all rows).
     Returns (out, last_state): (batch, d_inner, L) and (batch, d_inner, d_state) when rows
     is None, else (len(rows), L) and (len(rows), d_state).
@@ -120,12 +121,13 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus_
     D_r = None if D is None else _f64(np.asarray(D)[ch])
     b_r = None if delta_bias is None else _f64(np.asarray(delta_bias)[ch])
     Bm, Cm = _f64(B), _f64(C)
+    h0_r = None if h0 is None else _f64(np.asarray(h0).reshape(Bt * Dn, N)[sel])
     R = sel.size
     out = np.empty((R, L), np.float64)
     last = np.empty((R, N), np.float64)
     rc = _load().oracle_selective_scan(
         R, N, L, Bt, rb.ctypes.data_as(_i64p), _ptr(u_r), _ptr(dl_r), _ptr(z_r), _ptr(A_r),
-        _ptr(Bm), _ptr(Cm), _ptr(D_r), _ptr(b_r), int(bool(softplus_flag)), _ptr(out),
+        _ptr(Bm), _ptr(Cm), _ptr(D_r), _ptr(b_r), int(bool(softplus_flag)), _ptr(h0_r), _ptr(out),
         _ptr(last), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_selective_scan rejected its arguments")

@@ -22,6 +22,9 @@
  * Arithmetic is IEEE fp64 throughout, sequential in t; rows (batch, channel) are
  * independent and are the only thing run in parallel.
  *
+ * A scan may also start from a given state h_0 instead of zeros (prefill continued in chunks:
+ * the recurrence itself is unchanged, only its first h_{t-1} differs).
+ *
  * Parity pins (all in tests/test_oracle_pins.py, each independent of this loop): the L = 1
  * closed form; the LTI case against a brute-force convolution with kernel
  * K_k = sum_n C_n exp(k delta A_n) delta B_n; the unrolled time-varying sum with exponents
@@ -86,7 +89,7 @@ int oracle_selective_scan(int64_t R, int64_t N, int64_t L, int64_t Bt,
                           const double* u, const double* delta, const double* z,
                           const double* A, const double* Bm, const double* Cm,
                           const double* D, const double* bias, int softplus_flag,
-                          double* out, double* last_state, int nthreads) {
+                          const double* h0, double* out, double* last_state, int nthreads) {
     if (R < 0 || N <= 0 || L < 0 || Bt <= 0) return -1;
     set_threads(nthreads);
     int bad = 0;
@@ -94,8 +97,10 @@ int oracle_selective_scan(int64_t R, int64_t N, int64_t L, int64_t Bt,
     for (int64_t r = 0; r < R; ++r) {
         const int64_t b = row_batch[r];
         if (b < 0 || b >= Bt) { bad = 1; continue; }
-        double* h = (double*)calloc((size_t)N, sizeof(double)); /* h_0 = 0 */
+        double* h = (double*)calloc((size_t)N, sizeof(double)); /* h_0 = 0 ... */
         if (!h) { bad = 1; continue; }
+        if (h0)                                                  /* ... or the given state */
+            for (int64_t n = 0; n < N; ++n) h[n] = h0[r * N + n];
         const double* Ar = A + r * N;
         const double* Bb = Bm + b * N * L;
         const double* Cb = Cm + b * N * L;

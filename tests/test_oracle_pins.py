@@ -280,6 +280,68 @@ def test_scan_then_decode_continues(oracle_mod):
     _close(state, last)
 
 
+# ---------------------------------------------------------------- given starting state
+
+def test_initial_state_unrolled_sum(oracle_mod):
+    """From a given h_0: h_t[n] = exp(A_n sum_{r<=t} delta_r) h_0[n] + the zero-state sum."""
+    s = _small(seed=23, Bt=2, Dn=3, N=5, L=17)
+    rng = np.random.default_rng(123)
+    h0 = rng.standard_normal((2, 3, 5))
+    out, last = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias,
+                                          h0=h0)
+    Bt, Dn, L = s.u.shape
+    for b in range(Bt):
+        for d in range(Dn):
+            dl = _np_softplus(s.delta[b, d].astype(np.float64) + s.delta_bias[d])
+            u = s.u[b, d].astype(np.float64)
+            A = s.A[d].astype(np.float64)
+            for t in range(L):
+                h = np.exp(A * np.sum(dl[: t + 1])) * h0[b, d]
+                for s_ in range(t + 1):
+                    h = h + np.exp(A * np.sum(dl[s_ + 1: t + 1])) * dl[s_] * s.B[b, :, s_] * u[s_]
+                y = (np.dot(s.C[b, :, t], h) + s.D[d] * u[t]) * _np_silu(float(s.z[b, d, t]))
+                np.testing.assert_allclose(out[b, d, t], y, rtol=1e-11, atol=1e-13)
+            np.testing.assert_allclose(last[b, d], h, rtol=1e-11, atol=1e-13)
+
+
+def test_initial_state_free_response(oracle_mod):
+    """u = 0: only h_0 drives the output, y_t = sum_n C_t[n] exp(A_n cumsum(delta)_t) h_0[n]."""
+    s = _small(seed=24, Bt=1, Dn=4, N=6, L=25, with_z=False)
+    h0 = np.random.default_rng(5).standard_normal((1, 4, 6))
+    u0 = np.zeros_like(s.u)
+    out, last = oracle_mod.selective_scan(u0, s.delta, s.A, s.B, s.C, s.D, None, s.delta_bias,
+                                          h0=h0)
+    dl = _np_softplus(s.delta[0].astype(np.float64) + s.delta_bias[:, None])   # (Dn, L)
+    cum = np.cumsum(dl, axis=1)                                                # (Dn, L)
+    H = np.exp(s.A[:, :, None].astype(np.float64) * cum[:, None, :]) * h0[0][:, :, None]
+    y = np.einsum("dnl,nl->dl", H, s.C[0].astype(np.float64))
+    _close(out[0], y, rtol=1e-12, atol=1e-14)
+    _close(last[0], H[..., -1], rtol=1e-12, atol=1e-14)
+
+
+def test_zero_initial_state_is_default(oracle_mod):
+    s = _small(seed=25, L=13)
+    a = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias)
+    b = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias,
+                                  h0=np.zeros((2, 3, 5)))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("cut", [0, 1, 9, 20])
+def test_chunked_scan_equals_one_scan(oracle_mod, cut):
+    """scan(u[:cut]) then scan(u[cut:]) from its last state = scan(u), outputs and final state."""
+    s = _small(seed=26, Bt=2, Dn=3, N=5, L=20)
+    out, last = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias)
+    sl = (Ellipsis, slice(0, cut))
+    o1, h = oracle_mod.selective_scan(s.u[sl], s.delta[sl], s.A, s.B[sl], s.C[sl], s.D,
+                                      s.z[sl], s.delta_bias)
+    sr = (Ellipsis, slice(cut, None))
+    o2, h2 = oracle_mod.selective_scan(s.u[sr], s.delta[sr], s.A, s.B[sr], s.C[sr], s.D,
+                                       s.z[sr], s.delta_bias, h0=h)
+    _close(np.concatenate([o1, o2], axis=-1), out, rtol=1e-12, atol=1e-14)
+    _close(h2, last, rtol=1e-12, atol=1e-14)
+
+
 # ---------------------------------------------------------------- input generator
 
 def test_inputs_are_deterministic_and_seeded():
