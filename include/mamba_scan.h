@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MSS_VERSION 10000 /* major * 10000 + minor * 100 + patch */
+#define MSS_VERSION 10100 /* major * 10000 + minor * 100 + patch */
 
 typedef enum { MSS_F32 = 0, MSS_BF16 = 1 } mss_dtype_t;
 
@@ -88,6 +88,29 @@ int mss_selective_scan_fwd(const mss_tensor_t* u, const mss_tensor_t* delta,
                            void* stream);
 
 /*
+ * The same forward scan continued from a given state instead of h_0 = 0: the recurrence runs
+ * unchanged with h_{t-1} at t = 1 taken from initial_state.  Cutting a sequence anywhere and
+ * scanning the second part from the first part's last_state gives the outputs and final state
+ * of one scan over the whole sequence (prefill in chunks, or a prompt appended to a cached
+ * state), since each step depends on the past only through h_{t-1} (the tutorial page's
+ * "Going from continuous spaces to discrete spaces" part: the hidden state is handed on to
+ * the next input as in an RNN; the mamba-jax README's recurrent `--scan` generation).
+ *   initial_state  (batch, d_inner, d_state) f32, nullable (then exactly mss_selective_scan_fwd)
+ *   every other argument as for mss_selective_scan_fwd; with L = 0, last_state receives a copy
+ *   of initial_state.
+ * initial_state must be 16-byte aligned (MSS_ERR_LAYOUT otherwise) and must not overlap out or
+ * last_state (MSS_ERR_ALIAS): the kernels of a split sequence read it while others write
+ * last_state, so an in-place update needs a second buffer.
+ */
+int mss_selective_scan_fwd_with_state(const mss_tensor_t* u, const mss_tensor_t* delta,
+                                      const mss_tensor_t* A, const mss_tensor_t* B,
+                                      const mss_tensor_t* C, const mss_tensor_t* D,
+                                      const mss_tensor_t* z, const mss_tensor_t* delta_bias,
+                                      const mss_tensor_t* initial_state, int softplus_flag,
+                                      const mss_tensor_t* out, const mss_tensor_t* last_state,
+                                      void* stream);
+
+/*
  * One recurrent (decode) step: the same equations for a single token, continuing from
  * `state`, which is updated in place (the recurrent mode the mamba-jax README's `--scan`
  * generation loop and the upstream README's generation benchmark run token by token).
@@ -112,8 +135,8 @@ int mss_selective_state_update(const mss_tensor_t* state, const mss_tensor_t* x,
 
 /*
  * Launch timing, for measurement only (the results of the calls above do not depend on it).
- * mss_profile_enable(1) clears the records and makes each later mss_selective_scan_fwd (up to
- * 1024 calls) record three library-owned HIP events on its stream: before its first kernel,
+ * mss_profile_enable(1) clears the records and makes each later mss_selective_scan_fwd or
+ * mss_selective_scan_fwd_with_state (up to 1024 calls) record three library-owned HIP events on its stream: before its first kernel,
  * between the carry stage (the per-segment aggregates of a split sequence) and the main
  * kernel, and after the main kernel.  mss_profile_enable(0) stops recording (the records stay).
  * mss_profile_fwd waits for the recorded calls to finish and returns their count and the

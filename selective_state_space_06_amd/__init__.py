@@ -14,7 +14,9 @@ from ._binding import (  # noqa: F401
     profile_enable,
     profile_fwd,
     scan_fwd_raw,
+    scan_fwd_with_state_raw,
     selective_scan_fwd,
+    selective_scan_fwd_with_state,
     selective_state_update,
     state_update_raw,
     status_string,

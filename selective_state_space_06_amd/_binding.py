@@ -17,8 +17,9 @@ STATUS = {0: "MSS_OK", -1: "MSS_ERR_NULL_ARG", -2: "MSS_ERR_SHAPE", -3: "MSS_ERR
           -4: "MSS_ERR_LAYOUT", -5: "MSS_ERR_ALIAS", -6: "MSS_ERR_UNSUPPORTED", -7: "MSS_ERR_HIP"}
 
 # every symbol include/mamba_scan.h declares
-EXPORTS = ("mss_selective_scan_fwd", "mss_selective_state_update", "mss_profile_enable",
-           "mss_profile_fwd", "mss_status_string", "mss_version")
+EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_fwd_with_state",
+           "mss_selective_state_update", "mss_profile_enable", "mss_profile_fwd",
+           "mss_status_string", "mss_version")
 
 
 class Tensor(ctypes.Structure):
@@ -67,6 +68,9 @@ def load_library(path: str = LIB_PATH):
             lib.mss_selective_scan_fwd.restype = ctypes.c_int
             lib.mss_selective_scan_fwd.argtypes = [_TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP,
                                                    ctypes.c_int, _TP, _TP, ctypes.c_void_p]
+            lib.mss_selective_scan_fwd_with_state.restype = ctypes.c_int
+            lib.mss_selective_scan_fwd_with_state.argtypes = [
+                _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, ctypes.c_int, _TP, _TP, ctypes.c_void_p]
             lib.mss_selective_state_update.restype = ctypes.c_int
             lib.mss_selective_state_update.argtypes = [_TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP,
                                                        _TP, _TP, ctypes.c_void_p]
@@ -119,6 +123,14 @@ def scan_fwd_raw(u, delta, A, B, C, D, z, delta_bias, softplus_flag, out, last_s
         int(softplus_flag), _ref(out), _ref(last_state), stream)
 
 
+def scan_fwd_with_state_raw(u, delta, A, B, C, D, z, delta_bias, initial_state, softplus_flag,
+                            out, last_state, stream) -> int:
+    """Direct call of mss_selective_scan_fwd_with_state with Tensor descriptors (or None)."""
+    return load_library().mss_selective_scan_fwd_with_state(
+        _ref(u), _ref(delta), _ref(A), _ref(B), _ref(C), _ref(D), _ref(z), _ref(delta_bias),
+        _ref(initial_state), int(softplus_flag), _ref(out), _ref(last_state), stream)
+
+
 def state_update_raw(state, x, dt, A, B, C, D, z, dt_bias, out, stream) -> int:
     """Direct call of mss_selective_state_update with Tensor descriptors (or None)."""
     return load_library().mss_selective_state_update(
@@ -160,6 +172,28 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
     if st != 0:
         raise MssError(st, "mss_selective_scan_fwd")
     return (out, last_state) if return_last_state else out
+
+
+def selective_scan_fwd_with_state(u, delta, A, B, C, initial_state, D=None, z=None,
+                                  delta_bias=None, delta_softplus=True, out=None, last_state=None):
+    """Forward selective scan continued from `initial_state` (batch, d_inner, 16) float32
+    (None: from zeros).  Other arguments as selective_scan_fwd; returns (out, last_state).
+    last_state must be a different buffer from initial_state."""
+    import torch
+    if out is None:
+        out = torch.empty_like(u, memory_format=torch.contiguous_format)
+    if last_state is None:
+        last_state = torch.empty((u.shape[0], u.shape[1], A.shape[1]), dtype=torch.float32,
+                                 device=u.device)
+    with torch.cuda.device(u.device):
+        stream = torch.cuda.current_stream(u.device).cuda_stream
+        st = scan_fwd_with_state_raw(_desc(u), _desc(delta), _desc(A), _desc(B), _desc(C),
+                                     _desc(D), _desc(z), _desc(delta_bias), _desc(initial_state),
+                                     1 if delta_softplus else 0, _desc(out), _desc(last_state),
+                                     stream)
+    if st != 0:
+        raise MssError(st, "mss_selective_scan_fwd_with_state")
+    return out, last_state
 
 
 def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None):

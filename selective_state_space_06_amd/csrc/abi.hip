@@ -151,11 +151,11 @@ Prof g_prof;
 
 int validate_fwd(const mss_tensor_t* u, const mss_tensor_t* delta, const mss_tensor_t* A,
                  const mss_tensor_t* B, const mss_tensor_t* C, const mss_tensor_t* D,
-                 const mss_tensor_t* z, const mss_tensor_t* bias, const mss_tensor_t* out,
-                 const mss_tensor_t* last) {
+                 const mss_tensor_t* z, const mss_tensor_t* bias, const mss_tensor_t* h0,
+                 const mss_tensor_t* out, const mss_tensor_t* last) {
     {
         const mss_tensor_t* const req[] = {u, delta, A, B, C, out};
-        const int s = check_descs(req, {D, z, bias, last});
+        const int s = check_descs(req, {D, z, bias, h0, last});
         if (s != MSS_OK) return s;
     }
     if (u->ndim != 3 || A->ndim != 2) return MSS_ERR_SHAPE;
@@ -168,22 +168,25 @@ int validate_fwd(const mss_tensor_t* u, const mss_tensor_t* delta, const mss_ten
     if (D && !shape_is(*D, 1, Dn)) return MSS_ERR_SHAPE;
     if (bias && !shape_is(*bias, 1, Dn)) return MSS_ERR_SHAPE;
     if (last && !shape_is(*last, 3, Bt, Dn, N)) return MSS_ERR_SHAPE;
+    if (h0 && !shape_is(*h0, 3, Bt, Dn, N)) return MSS_ERR_SHAPE;
 
     if (u->dtype != MSS_F32 && u->dtype != MSS_BF16) return MSS_ERR_DTYPE;
     if (delta->dtype != u->dtype || out->dtype != u->dtype || (z && z->dtype != u->dtype))
         return MSS_ERR_DTYPE;
     if (A->dtype != MSS_F32 || B->dtype != MSS_F32 || C->dtype != MSS_F32) return MSS_ERR_DTYPE;
-    if ((D && D->dtype != MSS_F32) || (bias && bias->dtype != MSS_F32) || (last && last->dtype != MSS_F32))
+    if ((D && D->dtype != MSS_F32) || (bias && bias->dtype != MSS_F32) || (last && last->dtype != MSS_F32) ||
+        (h0 && h0->dtype != MSS_F32))
         return MSS_ERR_DTYPE;
 
-    const mss_tensor_t* all[] = {u, delta, A, B, C, D, z, bias, out, last};
+    const mss_tensor_t* all[] = {u, delta, A, B, C, D, z, bias, h0, out, last};
     for (const mss_tensor_t* t : all) {
         if (!t) continue;
         if (!dense(*t) || !aligned(*t, elem_size(t->dtype))) return MSS_ERR_LAYOUT;
     }
-    if (!aligned(*A, 16) || (last && !aligned(*last, 16))) return MSS_ERR_LAYOUT;
+    if (!aligned(*A, 16) || (last && !aligned(*last, 16)) || (h0 && !aligned(*h0, 16)))
+        return MSS_ERR_LAYOUT;
 
-    const mss_tensor_t* ins[] = {u, delta, A, B, C, D, z, bias};
+    const mss_tensor_t* ins[] = {u, delta, A, B, C, D, z, bias, h0};
     for (const mss_tensor_t* t : ins) {
         if (overlap(out, t)) return MSS_ERR_ALIAS;
         if (last && overlap(last, t)) return MSS_ERR_ALIAS;
@@ -265,8 +268,19 @@ int mss_selective_scan_fwd(const mss_tensor_t* u, const mss_tensor_t* delta, con
                            const mss_tensor_t* B, const mss_tensor_t* C, const mss_tensor_t* D,
                            const mss_tensor_t* z, const mss_tensor_t* delta_bias, int softplus_flag,
                            const mss_tensor_t* out, const mss_tensor_t* last_state, void* stream) {
+    return mss_selective_scan_fwd_with_state(u, delta, A, B, C, D, z, delta_bias, nullptr, softplus_flag,
+                                             out, last_state, stream);
+}
+
+int mss_selective_scan_fwd_with_state(const mss_tensor_t* u, const mss_tensor_t* delta,
+                                      const mss_tensor_t* A, const mss_tensor_t* B,
+                                      const mss_tensor_t* C, const mss_tensor_t* D,
+                                      const mss_tensor_t* z, const mss_tensor_t* delta_bias,
+                                      const mss_tensor_t* initial_state, int softplus_flag,
+                                      const mss_tensor_t* out, const mss_tensor_t* last_state,
+                                      void* stream) {
     try {
-        const int st = validate_fwd(u, delta, A, B, C, D, z, delta_bias, out, last_state);
+        const int st = validate_fwd(u, delta, A, B, C, D, z, delta_bias, initial_state, out, last_state);
         if (st != MSS_OK) return st;
         mss::ScanLaunch a;
         a.u = u->data; a.delta = delta->data; a.z = z ? z->data : nullptr;
@@ -277,6 +291,7 @@ int mss_selective_scan_fwd(const mss_tensor_t* u, const mss_tensor_t* delta, con
         a.bias = delta_bias ? static_cast<const float*>(delta_bias->data) : nullptr;
         a.out = out->data;
         a.last_state = last_state ? static_cast<float*>(last_state->data) : nullptr;
+        a.h0 = initial_state ? static_cast<const float*>(initial_state->data) : nullptr;
         a.Bt = u->shape[0]; a.Dn = u->shape[1]; a.L = u->shape[2];
         a.softplus = softplus_flag ? 1 : 0;
         a.bf16 = u->dtype == MSS_BF16;

@@ -22,6 +22,7 @@ struct ScanLaunch {
     const float* bias;      // nullable
     void* out;
     float* last_state;      // nullable
+    const float* h0;        // nullable: starting state (Bt, Dn, N), zeros when null
     int64_t Bt, Dn, L;
     int softplus;
     bool bf16;              // storage type of u / delta / z / out

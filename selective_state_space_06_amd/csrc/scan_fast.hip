@@ -26,6 +26,8 @@
 //     per segment, the pair (sum of delta, local end state from h = 0); the main kernel folds
 //     the pairs of the preceding segments with the associative operator
 //     (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2) into its starting state and runs the segment.
+//     A scan continued from a given state h0 starts that fold from h0 instead of zeros (the
+//     aggregates do not depend on it).
 //
 // exp is exp2 of a log2(e)-prescaled argument.  When every row of a wave satisfies
 // A[d, n] == (n + 1) A[d, 0] exactly (the S4D-real A = -(1..N) of the tutorial's init),
@@ -378,14 +380,23 @@ __device__ __forceinline__ BPair b_pair(const float* sbc, int j) {
 
 // Folds the aggregates of segments [0, seg) into the starting state of segment seg, four
 // segments per round: the 68 loads of a round are issued together, so a round costs one memory
-// round trip.
+// round trip.  The fold starts from the row's h0 when one is given, else from zeros.
 template <bool POW>
 __device__ __forceinline__ void fold_carry(float (&h)[kN], const float (&A2)[kN],
-                                           const float* __restrict__ agg, int seg, int64_t R,
-                                           int64_t row) {
+                                           const float* __restrict__ agg, const float* __restrict__ h0,
+                                           int seg, int64_t R, int64_t row) {
     constexpr int kRound = 4;
+    if (h0) {
+        const float4* src = reinterpret_cast<const float4*>(h0 + row * kN);
 #pragma unroll
-    for (int n = 0; n < kN; ++n) h[n] = 0.0f;
+        for (int q = 0; q < kN / 4; ++q) {
+            const float4 v = src[q];
+            h[4 * q] = v.x; h[4 * q + 1] = v.y; h[4 * q + 2] = v.z; h[4 * q + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) h[n] = 0.0f;
+    }
     for (int s0 = 0; s0 < seg; s0 += kRound) {
         float v[kRound][kN + 1];
 #pragma unroll
@@ -417,8 +428,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sc
     const typename E::storage* __restrict__ u, const typename E::storage* __restrict__ delta,
     const typename E::storage* __restrict__ z, const float* __restrict__ A,
     const float* __restrict__ B, const float* __restrict__ C, const float* __restrict__ D,
-    const float* __restrict__ bias, const float* __restrict__ agg, typename E::storage* __restrict__ out,
-    float* __restrict__ last_state, int64_t Dn, int64_t L, int S) {
+    const float* __restrict__ bias, const float* __restrict__ agg, const float* __restrict__ h0,
+    typename E::storage* __restrict__ out, float* __restrict__ last_state, int64_t Dn, int64_t L, int S) {
     using G = Geo<E>;
     __shared__ uint32_t srow[G::kRowWords];
     __shared__ __align__(16) float sbc[G::TT * 36];
@@ -433,11 +444,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sc
     const typename E::storage* zp = z ? z + base : nullptr;
     float h[kN];
     if (__all(rs.pow_ok)) {
-        fold_carry<true>(h, rs.A2, agg, seg, R, rs.row);
+        fold_carry<true>(h, rs.A2, agg, h0, seg, R, rs.row);
         main_body<E, HAS_Z, SOFTPLUS, true>(rs, h, u + base, delta + base, zp, out + base, Bb, Cb, L,
                                             srow, sbc, t_begin, t_end);
     } else {
-        fold_carry<false>(h, rs.A2, agg, seg, R, rs.row);
+        fold_carry<false>(h, rs.A2, agg, h0, seg, R, rs.row);
         main_body<E, HAS_Z, SOFTPLUS, false>(rs, h, u + base, delta + base, zp, out + base, Bb, Cb, L,
                                              srow, sbc, t_begin, t_end);
     }
@@ -583,7 +594,7 @@ hipError_t launch_fast_t(const ScanLaunch& a, const ScanPlan& p, float* ws, hipS
     mark(a, 1, stream);
     scan_main_kernel<E, HAS_Z, SOFTPLUS><<<dim3(gx, (unsigned)a.Bt, (unsigned)p.segments), block, 0, stream>>>(
         static_cast<const S_t*>(a.u), static_cast<const S_t*>(a.delta), static_cast<const S_t*>(a.z), a.A, a.B,
-        a.C, a.D, a.bias, agg, static_cast<S_t*>(a.out), a.last_state, a.Dn, a.L, p.segments);
+        a.C, a.D, a.bias, agg, a.h0, static_cast<S_t*>(a.out), a.last_state, a.Dn, a.L, p.segments);
     mark(a, 2, stream);
     return hipGetLastError();
 }

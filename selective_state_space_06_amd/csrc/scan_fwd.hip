@@ -4,7 +4,8 @@
 // coded on the Keras/TensorFlow Mamba tutorial page in `selective_scan` and
 // `MambaBlock.ssm`; the upstream mamba README's "Selective SSM" layer):
 //   delta_t = softplus(delta_raw_t + bias_d)   Abar = exp(delta_t A_dn)
-//   h_t = Abar h_{t-1} + delta_t B_nt u_t (h_0 = 0)   out_t = (sum_n C_nt h_t + D_d u_t) silu(z_t)
+//   h_t = Abar h_{t-1} + delta_t B_nt u_t (h_0 = 0, or a given state)
+//   out_t = (sum_n C_nt h_t + D_d u_t) silu(z_t)
 //
 // Work decomposition (one wavefront per workgroup):
 //   * a lane owns one channel (row b, d) and keeps its 16 states in VGPRs, sequential in t;
@@ -20,6 +21,7 @@
 //     the associative operator (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2) -- the parallel
 //     associative scan the tutorial page and the mamba-jax README describe -- into each
 //     segment's starting state; the main pass then runs every segment from its true start.
+//     A given starting state h0 enters only through segment 0 and the start of that fold.
 //
 // exp(delta A) = exp2(delta * A log2e) with A log2e formed once per (d, n).  When a row
 // satisfies A[d, n] == (n + 1) A[d, 0] exactly (the S4D-real initialisation A = -(1..N) the
@@ -46,6 +48,7 @@ struct KArgs {
     const float* bias;
     void* out;
     float* last_state;
+    const float* h0;      // nullable starting state, (rows_total, kN)
     float* ws;            // [S][kN + 1][rows_total] carry workspace
     int64_t Dn, L, seg_len, rows_total;
     int S;
@@ -304,6 +307,9 @@ __global__ __launch_bounds__(kRows) void scan_kernel(KArgs a) {
         const float* ws = a.ws + (int64_t)(seg - 1) * (kN + 1) * a.rows_total + row;
 #pragma unroll
         for (int n = 0; n < kN; ++n) h[n] = ws[(int64_t)n * a.rows_total];
+    } else if (MODE == kMain && a.h0 && active) {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) h[n] = a.h0[row * kN + n];
     } else {
 #pragma unroll
         for (int n = 0; n < kN; ++n) h[n] = 0.0f;
@@ -318,7 +324,7 @@ __global__ __launch_bounds__(kRows) void scan_kernel(KArgs a) {
 }
 
 // Folds the per-segment pairs (sum delta_s, local end state e_s) into inclusive end states:
-// H_s = exp(A * sum delta_s) H_{s-1} + e_s, H_{-1} = 0, written over e_s.
+// H_s = exp(A * sum delta_s) H_{s-1} + e_s, H_{-1} = h0 (zeros without one), written over e_s.
 __global__ __launch_bounds__(256) void combine_kernel(KArgs a) {
     const int64_t R = a.rows_total;
     for (int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; row < R;
@@ -328,7 +334,7 @@ __global__ __launch_bounds__(256) void combine_kernel(KArgs a) {
 #pragma unroll
         for (int n = 0; n < kN; ++n) {
             A2[n] = a.A[d * kN + n] * kLog2e;
-            h[n] = 0.0f;
+            h[n] = a.h0 ? a.h0[row * kN + n] : 0.0f;
         }
         for (int s = 0; s + 1 < a.S; ++s) {
             float* ws = a.ws + (int64_t)s * (kN + 1) * R + row;
@@ -342,10 +348,11 @@ __global__ __launch_bounds__(256) void combine_kernel(KArgs a) {
     }
 }
 
-__global__ __launch_bounds__(256) void zero_state_kernel(float* p, int64_t n) {
+// L = 0: the final state is the starting state (h0, or zeros).
+__global__ __launch_bounds__(256) void start_state_kernel(float* p, const float* h0, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = 0.0f;
+        p[i] = h0 ? h0[i] : 0.0f;
 }
 
 constexpr int kTile = 32;
@@ -405,14 +412,15 @@ hipError_t launch_scan_fwd(const ScanLaunch& a, const ScanPlan& plan, float* wor
         if (a.last_state) {
             const int64_t n = rows * kN;
             const int64_t blocks = (n + 255) / 256;
-            zero_state_kernel<<<dim3((unsigned)(blocks < 65535 ? blocks : 65535)), dim3(256), 0, stream>>>(a.last_state, n);
+            start_state_kernel<<<dim3((unsigned)(blocks < 65535 ? blocks : 65535)), dim3(256), 0, stream>>>(
+                a.last_state, a.h0, n);
             return hipGetLastError();
         }
         return hipSuccess;
     }
     KArgs k;
     k.u = a.u; k.delta = a.delta; k.z = a.z; k.A = a.A; k.B = a.B; k.C = a.C; k.D = a.D;
-    k.bias = a.bias; k.out = a.out; k.last_state = a.last_state; k.ws = workspace;
+    k.bias = a.bias; k.out = a.out; k.last_state = a.last_state; k.h0 = a.h0; k.ws = workspace;
     k.Dn = a.Dn; k.L = a.L; k.seg_len = plan.seg_len; k.rows_total = rows;
     k.S = plan.segments; k.softplus = a.softplus;
     const bool hz = a.z != nullptr;

@@ -171,6 +171,76 @@ def test_fwd_empty_batch_is_ok(lib):
     assert call_fwd(a) == OK
 
 
+# ------------------------------------------------------------ scan from a given state
+
+def call_fwd_state(a, h0):
+    return mss.scan_fwd_with_state_raw(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                       a["delta_bias"], h0, a["softplus_flag"], a["out"],
+                                       a["last_state"], a["stream"])
+
+
+def h0_desc(n=N):
+    return Tensor.make(addr(BT * DN * n * 4), MSS_F32, [BT, DN, n])
+
+
+def test_fwd_state_null_descriptor_is_plain_forward(lib):
+    """initial_state NULL validates exactly like mss_selective_scan_fwd."""
+    a = fwd_args()
+    a["A"].data += 4
+    assert call_fwd_state(a, None) == LAYOUT
+    a = fwd_args(n=8)
+    assert call_fwd_state(a, None) == UNSUPPORTED
+
+
+def test_fwd_state_null_data(lib):
+    h = h0_desc()
+    h.data = None
+    assert call_fwd_state(fwd_args(), h) == NULL_ARG
+
+
+@pytest.mark.parametrize("shape", [[BT, DN, N - 1], [BT + 1, DN, N], [BT, DN], [BT, DN, N, 1]])
+def test_fwd_state_shape(lib, shape):
+    h = h0_desc()
+    h = Tensor.make(h.data, MSS_F32, shape[:3])
+    if len(shape) == 4:
+        h.ndim = 4
+    expect = SHAPE
+    assert call_fwd_state(fwd_args(), h) == expect
+
+
+def test_fwd_state_dtype_and_layout(lib):
+    h = h0_desc()
+    h.dtype = MSS_BF16
+    assert call_fwd_state(fwd_args(), h) == DTYPE
+    h = h0_desc()
+    h.data += 4                                  # f32-aligned but not 16-byte aligned
+    assert call_fwd_state(fwd_args(), h) == LAYOUT
+    h = h0_desc()
+    h.stride[0], h.stride[1] = DN, 1             # transposed, not dense
+    h.stride[2] = BT * DN
+    assert call_fwd_state(fwd_args(), h) == LAYOUT
+
+
+@pytest.mark.parametrize("victim", ["out", "last_state"])
+def test_fwd_state_output_alias(lib, victim):
+    a = fwd_args()
+    h = h0_desc()
+    h.data = a[victim].data
+    assert call_fwd_state(a, h) == ALIAS
+
+
+def test_fwd_state_may_share_inputs(lib):
+    """initial_state is read-only: overlapping another input is allowed (empty batch, no launch)."""
+    a = fwd_args()
+    for k in ("u", "delta", "z", "out"):
+        a[k] = Tensor.make(a[k].data, MSS_F32, [0, DN, L])
+    for k in ("B", "C"):
+        a[k] = Tensor.make(a[k].data, MSS_F32, [0, N, L])
+    a["last_state"] = Tensor.make(a["last_state"].data, MSS_F32, [0, DN, N])
+    h = Tensor.make(a["B"].data, MSS_F32, [0, DN, N])
+    assert call_fwd_state(a, h) == OK
+
+
 # --------------------------------------------------------------------- decode step
 
 def dec_args(dtype=MSS_BF16, n=N):
