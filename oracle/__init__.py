@@ -50,6 +50,11 @@ def _load():
             lib.oracle_selective_scan.argtypes = [
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i64p,
                 _d, _d, _d, _d, _d, _d, _d, _d, ctypes.c_int, _d, _d, _d, ctypes.c_int]
+            lib.oracle_selective_scan_bwd.restype = ctypes.c_int
+            lib.oracle_selective_scan_bwd.argtypes = [
+                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i64p,
+                _d, _d, _d, _d, _d, _d, _d, _d, ctypes.c_int, _d,
+                _d, _d, _d, _d, _d, _d, _d, _d, ctypes.c_int, ctypes.c_int]
             lib.oracle_state_update.restype = ctypes.c_int
             lib.oracle_state_update.argtypes = [
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i64p,
@@ -134,6 +139,54 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus_
     if rows is None:
         return out.reshape(Bt, Dn, L), last.reshape(Bt, Dn, N)
     return out, last
+
+
+def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus_flag=True,
+                       dout=None, rows=None, nthreads: int = 0, magnitude: bool = False):
+    """fp64 gradients of L = sum(dout * out) for the forward scan from h_0 = 0.
+
+    Inputs as selective_scan, plus dout (batch, d_inner, L).  Returns a dict:
+      du, ddelta, dz (None without z): (batch, d_inner, L), or (len(rows), L) with rows;
+      dA: (d_inner, d_state); dD, ddelta_bias: (d_inner,) -- each summed over the selected
+      rows of that channel (with rows given: per-row arrays (len(rows), d_state) / (len(rows),));
+      dB, dC: (batch, d_state, L), summed over the selected rows.
+    dD / ddelta_bias are the gradients at D = 0 / bias = 0 when those are None.
+    magnitude=True returns, in the same layout, the sum of |terms| behind each element.
+    """
+    u = np.asarray(u)
+    Bt, Dn, L = u.shape
+    N = np.asarray(A).shape[1]
+    if rows is None:
+        sel = np.arange(Bt * Dn, dtype=np.int64)
+    else:
+        sel = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    ch = sel % Dn
+    rb = np.ascontiguousarray(sel // Dn)
+
+    def rows_of(a):
+        return None if a is None else _f64(np.asarray(a).reshape(Bt * Dn, L)[sel])
+
+    R = sel.size
+    du = np.empty((R, L)); dd = np.empty((R, L))
+    dz = np.empty((R, L)) if z is not None else None
+    dA = np.empty((R, N)); dD = np.empty(R); db = np.empty(R)
+    dB = np.empty((Bt, N, L)); dC = np.empty((Bt, N, L))
+    rc = _load().oracle_selective_scan_bwd(
+        R, N, L, Bt, rb.ctypes.data_as(_i64p), _ptr(rows_of(u)), _ptr(rows_of(delta)),
+        _ptr(rows_of(z)), _ptr(_f64(np.asarray(A)[ch])), _ptr(_f64(B)), _ptr(_f64(C)),
+        _ptr(None if D is None else _f64(np.asarray(D)[ch])),
+        _ptr(None if delta_bias is None else _f64(np.asarray(delta_bias)[ch])),
+        int(bool(softplus_flag)), _ptr(rows_of(dout)), _ptr(du), _ptr(dd), _ptr(dz), _ptr(dA),
+        _ptr(dB), _ptr(dC), _ptr(dD), _ptr(db), int(bool(magnitude)), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_selective_scan_bwd rejected its arguments")
+    if rows is not None:
+        return dict(du=du, ddelta=dd, dz=dz, dA=dA, dB=dB, dC=dC, dD=dD, ddelta_bias=db)
+    sh = (Bt, Dn, L)
+    return dict(du=du.reshape(sh), ddelta=dd.reshape(sh),
+                dz=None if dz is None else dz.reshape(sh),
+                dA=dA.reshape(Bt, Dn, N).sum(0), dB=dB, dC=dC,
+                dD=dD.reshape(Bt, Dn).sum(0), ddelta_bias=db.reshape(Bt, Dn).sum(0))
 
 
 def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,

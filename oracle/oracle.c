@@ -127,6 +127,142 @@ int oracle_selective_scan(int64_t R, int64_t N, int64_t L, int64_t Bt,
 }
 
 /*
+ * Gradients of the forward scan (h_0 = 0): given dout = dL/dout for a scalar loss L, the
+ * adjoint (reverse-mode) pass of the recurrence above, written out step by step.  The pages
+ * define only the forward; this is its derivative, taken by the chain rule through
+ *   pre = delta_raw + bias,  dt = softplus(pre) (d dt / d pre = sigmoid(pre)) or dt = pre,
+ *   abar_n = exp(dt A_n),  h_t = abar h_{t-1} + dt B_t u_t,  y_t = C_t.h_t + D u_t,
+ *   out_t = y_t silu(z_t)   (d silu / dz = s (1 + z (1 - s)), s = sigmoid(z)).
+ * With G_t = dL/dh_t (total), G_t = dy_t C_t + abar_{t+1} G_{t+1}; every input's gradient
+ * collects its terms from the steps that use it.  h_t is stored for the whole row (the
+ * plainest route; no recomputation).
+ *
+ * Outputs, all overwritten:
+ *   du, ddelta         R x L   (ddelta is w.r.t. delta_raw)
+ *   dz                 R x L   (only when z is given)
+ *   dA                 R x N   row's contribution (the channel's gradient sums its rows)
+ *   dD, dbias          R       row's contribution (computed even when D / bias is NULL,
+ *                              i.e. the gradient at D = 0 / bias = 0)
+ *   dB, dC             Bt x N x L, summed over the R rows
+ * magnitude != 0 replaces every term added into an output by its absolute value (G and h
+ * themselves stay signed), giving sum |terms| per output element: the scale a rounding-error
+ * bound for a re-associated fp32 evaluation of the same sums is proportional to.
+ * Not pinned by the pages (they print no gradient); pinned in the tests by central finite
+ * differences of the forward above, an L = 1 closed form and linearity in dout.
+ */
+int oracle_selective_scan_bwd(int64_t R, int64_t N, int64_t L, int64_t Bt,
+                              const int64_t* row_batch,
+                              const double* u, const double* delta, const double* z,
+                              const double* A, const double* Bm, const double* Cm,
+                              const double* D, const double* bias, int softplus_flag,
+                              const double* dout, double* du, double* ddelta, double* dz,
+                              double* dA, double* dB, double* dC, double* dD, double* dbias,
+                              int magnitude, int nthreads) {
+    if (R < 0 || N <= 0 || L < 0 || Bt <= 0) return -1;
+    set_threads(nthreads);
+    const size_t nbc = (size_t)(Bt * N * L);
+    const int nt = oracle_max_threads();
+    /* each thread's share of dB / dC, added into the outputs in thread order at the end */
+    double* shares = (double*)calloc((size_t)nt * 2 * (nbc ? nbc : 1), sizeof(double));
+    if (!shares) return -1;
+    int bad = 0;
+#pragma omp parallel reduction(| : bad)
+    {
+#ifdef _OPENMP
+        const int tid = omp_get_thread_num();
+#else
+        const int tid = 0;
+#endif
+        double* accB = shares + (size_t)tid * 2 * (nbc ? nbc : 1);
+        double* accC = accB + (nbc ? nbc : 1);
+        double* hs = (double*)malloc((size_t)((L + 1) * N) * sizeof(double)); /* h_0 .. h_L */
+        double* ys = (double*)malloc((size_t)(L ? L : 1) * sizeof(double));
+        double* g = (double*)malloc((size_t)N * sizeof(double));
+        if (tid >= nt || !hs || !ys || !g) bad = 1;
+#define ACC(dst, term) ((dst) += magnitude ? fabs(term) : (term))
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < R; ++r) {
+            if (bad) continue;
+            const int64_t b = row_batch[r];
+            if (b < 0 || b >= Bt) { bad = 1; continue; }
+            const double* Ar = A + r * N;
+            const double* Bb = Bm + b * N * L;
+            const double* Cb = Cm + b * N * L;
+            const double Dr = D ? D[r] : 0.0;
+            const double br = bias ? bias[r] : 0.0;
+            /* forward, keeping every h_t and y_t (for magnitude: y's sum of |terms|) */
+            for (int64_t n = 0; n < N; ++n) hs[n] = 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                const double ut = u[r * L + t];
+                const double pre = delta[r * L + t] + br;
+                const double dt = softplus_flag ? sp(pre) : pre;
+                const double* hp = hs + t * N;
+                double* hc = hs + (t + 1) * N;
+                double y = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    hc[n] = exp(dt * Ar[n]) * hp[n] + dt * Bb[n * L + t] * ut;
+                    ACC(y, Cb[n * L + t] * hc[n]);
+                }
+                ACC(y, Dr * ut);
+                ys[t] = y;
+            }
+            /* reverse */
+            double dDr = 0.0, dbr = 0.0;
+            for (int64_t n = 0; n < N; ++n) { g[n] = 0.0; dA[r * N + n] = 0.0; }
+            for (int64_t t = L - 1; t >= 0; --t) {
+                const double ut = u[r * L + t];
+                const double pre = delta[r * L + t] + br;
+                const double dt = softplus_flag ? sp(pre) : pre;
+                const double dsp = softplus_flag ? 1.0 / (1.0 + exp(-pre)) : 1.0;
+                const double go = dout[r * L + t];
+                double dy = go;
+                if (z) {
+                    const double zt = z[r * L + t];
+                    const double s = 1.0 / (1.0 + exp(-zt));
+                    dy = go * zt * s;                                   /* dout silu(z) */
+                    const double dgate = go * s * (1.0 + zt * (1.0 - s)); /* dout silu'(z) */
+                    dz[r * L + t] = magnitude ? fabs(dgate) * ys[t] : dgate * ys[t];
+                }
+                double dut = 0.0, ddt = 0.0;
+                ACC(dut, Dr * dy);
+                ACC(dDr, dy * ut);
+                const double* hp = hs + t * N;        /* h_{t-1} */
+                const double* hc = hs + (t + 1) * N;  /* h_t     */
+                for (int64_t n = 0; n < N; ++n) {
+                    const double Bn = Bb[n * L + t], Cn = Cb[n * L + t];
+                    const double G = dy * Cn + g[n];  /* dL/dh_t */
+                    const double abar = exp(dt * Ar[n]);
+                    const double ah = abar * hp[n];
+                    ACC(ddt, G * Ar[n] * ah);         /* through abar = exp(dt A) */
+                    ACC(ddt, G * Bn * ut);            /* through dt B u           */
+                    ACC(dA[r * N + n], G * dt * ah);
+                    ACC(accB[(b * N + n) * L + t], G * dt * ut);
+                    ACC(accC[(b * N + n) * L + t], dy * hc[n]);
+                    ACC(dut, G * dt * Bn);
+                    g[n] = abar * G;                  /* dL/dh_{t-1} from this step */
+                }
+                du[r * L + t] = dut;
+                const double dpre = ddt * dsp;
+                ddelta[r * L + t] = dpre;
+                dbr += dpre;
+            }
+            if (dD) dD[r] = dDr;
+            if (dbias) dbias[r] = dbr;
+        }
+#undef ACC
+        free(hs); free(ys); free(g);
+    }
+    for (size_t i = 0; i < nbc; ++i) { dB[i] = 0.0; dC[i] = 0.0; }
+    for (int k = 0; k < nt; ++k) {
+        const double* sB = shares + (size_t)k * 2 * (nbc ? nbc : 1);
+        const double* sC = sB + (nbc ? nbc : 1);
+        for (size_t i = 0; i < nbc; ++i) { dB[i] += sB[i]; dC[i] += sC[i]; }
+    }
+    free(shares);
+    return bad ? -1 : 0;
+}
+
+/*
  * One recurrent (decode) step over R rows, state updated in place.
  *   state      R x N (in/out)
  *   x, dt, z   R (z may be NULL); dt is raw, softplus(dt + dt_bias) is always applied
