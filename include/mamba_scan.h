@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MSS_VERSION 10100 /* major * 10000 + minor * 100 + patch */
+#define MSS_VERSION 10200 /* major * 10000 + minor * 100 + patch */
 
 typedef enum { MSS_F32 = 0, MSS_BF16 = 1 } mss_dtype_t;
 
@@ -109,6 +109,38 @@ int mss_selective_scan_fwd_with_state(const mss_tensor_t* u, const mss_tensor_t*
                                       const mss_tensor_t* initial_state, int softplus_flag,
                                       const mss_tensor_t* out, const mss_tensor_t* last_state,
                                       void* stream);
+
+/*
+ * Gradients of mss_selective_scan_fwd (h_0 = 0) for training: given dout = dL/dout of a scalar
+ * loss L, writes dL/d(every input).  The pages define only the forward; these are its exact
+ * derivatives by the chain rule (reverse mode through the recurrence: with dy = dout silu(z),
+ * G_t = dL/dh_t = dy_t C_t + Abar_{t+1} G_{t+1} is carried backward over t).  The forward
+ * states are recomputed, not stored: the call needs only the forward's inputs.
+ *   u, delta, A, B, C, D, z, delta_bias, softplus_flag   exactly as passed to the forward
+ *   dout        (batch, d_inner, L)      dtype of u
+ *   du, ddelta  (batch, d_inner, L)      dtype of u, written (ddelta is w.r.t. the raw delta)
+ *   dA          (d_inner, d_state)       f32, written (sum over batch and time)
+ *   dB, dC      (batch, d_state, L)      f32, written (sum over d_inner)
+ *   dD          (d_inner,)               f32, nullable; written with sum dy u (also when D is
+ *                                        NULL: the gradient at D = 0)
+ *   dz          (batch, d_inner, L)      dtype of u, nullable; must be NULL when z is NULL
+ *                                        (MSS_ERR_SHAPE otherwise)
+ *   ddelta_bias (d_inner,)               f32, nullable; written (also when delta_bias is NULL)
+ * Outputs are overwritten, not accumulated.  d_state must be 16; A must be 16-byte aligned;
+ * no output may overlap an input or another output (MSS_ERR_ALIAS).  Sums are taken in a
+ * fixed order: repeated calls give identical results.  Uses the library workspace (long
+ * sequences: about 8 bytes per (batch, d_inner, step) of state checkpoints plus
+ * 128 bytes per (64-channel group, batch, step) of partial dB / dC sums).
+ */
+int mss_selective_scan_bwd(const mss_tensor_t* u, const mss_tensor_t* delta,
+                           const mss_tensor_t* A, const mss_tensor_t* B, const mss_tensor_t* C,
+                           const mss_tensor_t* D, const mss_tensor_t* z,
+                           const mss_tensor_t* delta_bias, int softplus_flag,
+                           const mss_tensor_t* dout, const mss_tensor_t* du,
+                           const mss_tensor_t* ddelta, const mss_tensor_t* dA,
+                           const mss_tensor_t* dB, const mss_tensor_t* dC,
+                           const mss_tensor_t* dD, const mss_tensor_t* dz,
+                           const mss_tensor_t* ddelta_bias, void* stream);
 
 /*
  * One recurrent (decode) step: the same equations for a single token, continuing from

@@ -13,8 +13,10 @@ from ._binding import (  # noqa: F401
     load_library,
     profile_enable,
     profile_fwd,
+    scan_bwd_raw,
     scan_fwd_raw,
     scan_fwd_with_state_raw,
+    selective_scan_bwd,
     selective_scan_fwd,
     selective_scan_fwd_with_state,
     selective_state_update,

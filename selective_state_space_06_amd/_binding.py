@@ -17,7 +17,7 @@ STATUS = {0: "MSS_OK", -1: "MSS_ERR_NULL_ARG", -2: "MSS_ERR_SHAPE", -3: "MSS_ERR
           -4: "MSS_ERR_LAYOUT", -5: "MSS_ERR_ALIAS", -6: "MSS_ERR_UNSUPPORTED", -7: "MSS_ERR_HIP"}
 
 # every symbol include/mamba_scan.h declares
-EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_fwd_with_state",
+EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_fwd_with_state", "mss_selective_scan_bwd",
            "mss_selective_state_update", "mss_profile_enable", "mss_profile_fwd",
            "mss_status_string", "mss_version")
 
@@ -71,6 +71,10 @@ def load_library(path: str = LIB_PATH):
             lib.mss_selective_scan_fwd_with_state.restype = ctypes.c_int
             lib.mss_selective_scan_fwd_with_state.argtypes = [
                 _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, ctypes.c_int, _TP, _TP, ctypes.c_void_p]
+            lib.mss_selective_scan_bwd.restype = ctypes.c_int
+            lib.mss_selective_scan_bwd.argtypes = [
+                _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, ctypes.c_int, _TP,
+                _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, ctypes.c_void_p]
             lib.mss_selective_state_update.restype = ctypes.c_int
             lib.mss_selective_state_update.argtypes = [_TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP,
                                                        _TP, _TP, ctypes.c_void_p]
@@ -131,6 +135,15 @@ def scan_fwd_with_state_raw(u, delta, A, B, C, D, z, delta_bias, initial_state, 
         _ref(initial_state), int(softplus_flag), _ref(out), _ref(last_state), stream)
 
 
+def scan_bwd_raw(u, delta, A, B, C, D, z, delta_bias, softplus_flag, dout, du, ddelta, dA, dB, dC,
+                 dD, dz, ddelta_bias, stream) -> int:
+    """Direct call of mss_selective_scan_bwd with Tensor descriptors (or None)."""
+    return load_library().mss_selective_scan_bwd(
+        _ref(u), _ref(delta), _ref(A), _ref(B), _ref(C), _ref(D), _ref(z), _ref(delta_bias),
+        int(softplus_flag), _ref(dout), _ref(du), _ref(ddelta), _ref(dA), _ref(dB), _ref(dC),
+        _ref(dD), _ref(dz), _ref(ddelta_bias), stream)
+
+
 def state_update_raw(state, x, dt, A, B, C, D, z, dt_bias, out, stream) -> int:
     """Direct call of mss_selective_state_update with Tensor descriptors (or None)."""
     return load_library().mss_selective_state_update(
@@ -172,6 +185,34 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
     if st != 0:
         raise MssError(st, "mss_selective_scan_fwd")
     return (out, last_state) if return_last_state else out
+
+
+def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
+                       delta_softplus=True):
+    """Gradients of selective_scan_fwd (from h = 0) for L = sum(dout * out), on the current
+    stream.  Returns a dict: du, ddelta, dz (None without z) in u's dtype; dA, dB, dC, dD,
+    ddelta_bias in float32 (dD / ddelta_bias also when D / delta_bias is None)."""
+    import torch
+    dev_ = u.device
+    Bt, Dn, L = u.shape
+    N = A.shape[1]
+    f32 = dict(dtype=torch.float32, device=dev_)
+    g = dict(du=torch.empty((Bt, Dn, L), dtype=u.dtype, device=dev_),
+             ddelta=torch.empty((Bt, Dn, L), dtype=u.dtype, device=dev_),
+             dz=None if z is None else torch.empty((Bt, Dn, L), dtype=u.dtype, device=dev_),
+             dA=torch.empty((Dn, N), **f32), dB=torch.empty((Bt, N, L), **f32),
+             dC=torch.empty((Bt, N, L), **f32), dD=torch.empty((Dn,), **f32),
+             ddelta_bias=torch.empty((Dn,), **f32))
+    with torch.cuda.device(dev_):
+        stream = torch.cuda.current_stream(dev_).cuda_stream
+        st = scan_bwd_raw(_desc(u), _desc(delta), _desc(A), _desc(B), _desc(C), _desc(D),
+                          _desc(z), _desc(delta_bias), 1 if delta_softplus else 0, _desc(dout),
+                          _desc(g["du"]), _desc(g["ddelta"]), _desc(g["dA"]), _desc(g["dB"]),
+                          _desc(g["dC"]), _desc(g["dD"]), _desc(g["dz"]), _desc(g["ddelta_bias"]),
+                          stream)
+    if st != 0:
+        raise MssError(st, "mss_selective_scan_bwd")
+    return g
 
 
 def selective_scan_fwd_with_state(u, delta, A, B, C, initial_state, D=None, z=None,

@@ -244,6 +244,57 @@ int validate_decode(const mss_tensor_t* state, const mss_tensor_t* x, const mss_
     return MSS_OK;
 }
 
+int validate_bwd(const mss_tensor_t* u, const mss_tensor_t* delta, const mss_tensor_t* A,
+                 const mss_tensor_t* B, const mss_tensor_t* C, const mss_tensor_t* D,
+                 const mss_tensor_t* z, const mss_tensor_t* bias, const mss_tensor_t* dout,
+                 const mss_tensor_t* du, const mss_tensor_t* ddelta, const mss_tensor_t* dA,
+                 const mss_tensor_t* dB, const mss_tensor_t* dC, const mss_tensor_t* dD,
+                 const mss_tensor_t* dz, const mss_tensor_t* dbias) {
+    {
+        const mss_tensor_t* const req[] = {u, delta, A, B, C, dout, du, ddelta, dA, dB, dC};
+        const int s = check_descs(req, {D, z, bias, dD, dz, dbias});
+        if (s != MSS_OK) return s;
+    }
+    if (u->ndim != 3 || A->ndim != 2) return MSS_ERR_SHAPE;
+    const int64_t Bt = u->shape[0], Dn = u->shape[1], L = u->shape[2], N = A->shape[1];
+    if (Bt < 0 || Dn < 0 || L < 0 || N < 0) return MSS_ERR_SHAPE;
+    for (const mss_tensor_t* t : {delta, dout, du, ddelta})
+        if (!shape_is(*t, 3, Bt, Dn, L)) return MSS_ERR_SHAPE;
+    if (z && !shape_is(*z, 3, Bt, Dn, L)) return MSS_ERR_SHAPE;
+    if (dz && (!z || !shape_is(*dz, 3, Bt, Dn, L))) return MSS_ERR_SHAPE;  // no gate, no dz
+    if (!shape_is(*A, 2, Dn, N) || !shape_is(*dA, 2, Dn, N)) return MSS_ERR_SHAPE;
+    for (const mss_tensor_t* t : {B, C, dB, dC})
+        if (!shape_is(*t, 3, Bt, N, L)) return MSS_ERR_SHAPE;
+    for (const mss_tensor_t* t : {D, bias, dD, dbias})
+        if (t && !shape_is(*t, 1, Dn)) return MSS_ERR_SHAPE;
+
+    if (u->dtype != MSS_F32 && u->dtype != MSS_BF16) return MSS_ERR_DTYPE;
+    for (const mss_tensor_t* t : {delta, dout, du, ddelta, z, dz})
+        if (t && t->dtype != u->dtype) return MSS_ERR_DTYPE;
+    for (const mss_tensor_t* t : {A, B, C, D, bias, dA, dB, dC, dD, dbias})
+        if (t && t->dtype != MSS_F32) return MSS_ERR_DTYPE;
+
+    const mss_tensor_t* all[] = {u, delta, A, B, C, D, z, bias, dout, du, ddelta, dA, dB, dC, dD, dz, dbias};
+    for (const mss_tensor_t* t : all) {
+        if (!t) continue;
+        if (!dense(*t) || !aligned(*t, elem_size(t->dtype))) return MSS_ERR_LAYOUT;
+    }
+    if (!aligned(*A, 16)) return MSS_ERR_LAYOUT;
+
+    const mss_tensor_t* ins[] = {u, delta, A, B, C, D, z, bias, dout};
+    const mss_tensor_t* outs[] = {du, ddelta, dA, dB, dC, dD, dz, dbias};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const mss_tensor_t* t : ins)
+            if (overlap(outs[i], t)) return MSS_ERR_ALIAS;
+        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+            if (overlap(outs[i], outs[j])) return MSS_ERR_ALIAS;
+    }
+
+    if (N != kN) return MSS_ERR_UNSUPPORTED;
+    if (Bt > 65535) return MSS_ERR_UNSUPPORTED;
+    return MSS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -337,6 +388,54 @@ int mss_selective_scan_fwd_with_state(const mss_tensor_t* u, const mss_tensor_t*
         const hipError_t e = fast ? mss::launch_scan_fast(a, plan, ws, s) : mss::launch_scan_fwd(a, plan, ws, s);
         if (slot >= 0 && e == hipSuccess) g_prof.calls = slot + 1;
         return e == hipSuccess ? MSS_OK : MSS_ERR_HIP;
+    } catch (...) {
+        return MSS_ERR_HIP;
+    }
+}
+
+int mss_selective_scan_bwd(const mss_tensor_t* u, const mss_tensor_t* delta, const mss_tensor_t* A,
+                           const mss_tensor_t* B, const mss_tensor_t* C, const mss_tensor_t* D,
+                           const mss_tensor_t* z, const mss_tensor_t* delta_bias, int softplus_flag,
+                           const mss_tensor_t* dout, const mss_tensor_t* du, const mss_tensor_t* ddelta,
+                           const mss_tensor_t* dA, const mss_tensor_t* dB, const mss_tensor_t* dC,
+                           const mss_tensor_t* dD, const mss_tensor_t* dz,
+                           const mss_tensor_t* ddelta_bias, void* stream) {
+    try {
+        const int st = validate_bwd(u, delta, A, B, C, D, z, delta_bias, dout, du, ddelta, dA, dB, dC, dD,
+                                    dz, ddelta_bias);
+        if (st != MSS_OK) return st;
+        mss::BwdLaunch a;
+        a.u = u->data; a.delta = delta->data; a.z = z ? z->data : nullptr; a.dout = dout->data;
+        a.A = static_cast<const float*>(A->data);
+        a.B = static_cast<const float*>(B->data);
+        a.C = static_cast<const float*>(C->data);
+        a.D = D ? static_cast<const float*>(D->data) : nullptr;
+        a.bias = delta_bias ? static_cast<const float*>(delta_bias->data) : nullptr;
+        a.du = du->data; a.ddelta = ddelta->data; a.dz = dz ? dz->data : nullptr;
+        a.dA = static_cast<float*>(dA->data);
+        a.dB = static_cast<float*>(dB->data);
+        a.dC = static_cast<float*>(dC->data);
+        a.dD = dD ? static_cast<float*>(dD->data) : nullptr;
+        a.dbias = ddelta_bias ? static_cast<float*>(ddelta_bias->data) : nullptr;
+        a.Bt = u->shape[0]; a.Dn = u->shape[1]; a.L = u->shape[2];
+        a.softplus = softplus_flag ? 1 : 0;
+        a.bf16 = u->dtype == MSS_BF16;
+        const size_t es = elem_size(u->dtype);
+        a.vec_ok = (a.L * static_cast<int64_t>(es)) % 16 == 0 && aligned(*u, 16) && aligned(*delta, 16) &&
+                   aligned(*dout, 16) && aligned(*du, 16) && aligned(*ddelta, 16) && (!z || aligned(*z, 16)) &&
+                   (!dz || aligned(*dz, 16)) && aligned(*B, 16) && aligned(*C, 16);
+        const int64_t elems = a.Dn * kN + a.Bt * kN * a.L + a.Dn;
+        if (elems == 0) return MSS_OK;  // nothing to write
+
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return MSS_ERR_HIP;
+        if (device_cus(dev, &cus) != hipSuccess) return MSS_ERR_HIP;
+        const int segments = mss::plan_bwd_segments(a, cus);
+        const size_t bytes = mss::bwd_workspace_bytes(a, segments);
+        float* ws = nullptr;
+        if (bytes > 0 && workspace(dev, stream, bytes, &ws) != hipSuccess) return MSS_ERR_HIP;
+        return mss::launch_scan_bwd(a, segments, ws, s) == hipSuccess ? MSS_OK : MSS_ERR_HIP;
     } catch (...) {
         return MSS_ERR_HIP;
     }

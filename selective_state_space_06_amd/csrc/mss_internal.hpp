@@ -52,6 +52,30 @@ struct DecodeLaunch {
     bool bf16;
 };
 
+struct BwdLaunch {
+    const void* u;
+    const void* delta;
+    const void* z;          // nullable
+    const void* dout;
+    const float* A;
+    const float* B;
+    const float* C;
+    const float* D;         // nullable
+    const float* bias;      // nullable
+    void* du;
+    void* ddelta;
+    void* dz;               // nullable (also when z is null)
+    float* dA;              // (Dn, N)
+    float* dB;              // (Bt, N, L)
+    float* dC;              // (Bt, N, L)
+    float* dD;              // nullable
+    float* dbias;           // nullable
+    int64_t Bt, Dn, L;
+    int softplus;
+    bool bf16;
+    bool vec_ok;            // rows of u / delta / z / dout / du / ddelta / dz and B / C 16-byte aligned
+};
+
 // How the forward scan is decomposed along L: `segments` workgroup-rows per channel
 // group, each covering `seg_len` steps (a multiple of the time tile).
 struct ScanPlan {
@@ -74,5 +98,9 @@ size_t fast_workspace_bytes(const ScanLaunch& a, int segments);
 hipError_t launch_scan_fast(const ScanLaunch& a, const ScanPlan& plan, float* workspace,
                             hipStream_t stream);
 hipError_t launch_state_update(const DecodeLaunch& a, hipStream_t stream);
+// Backward scan: scan_bwd.hip.
+int plan_bwd_segments(const BwdLaunch& a, int num_cus);
+size_t bwd_workspace_bytes(const BwdLaunch& a, int segments);
+hipError_t launch_scan_bwd(const BwdLaunch& a, int segments, void* workspace, hipStream_t stream);
 
 }  // namespace mss

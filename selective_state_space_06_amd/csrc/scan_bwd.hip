@@ -1,0 +1,612 @@
+// scan_bwd.hip -- gradients of the forward selective scan (S6) for gfx950.
+//
+// The forward (Keras/TensorFlow Mamba tutorial page, `selective_scan` and `MambaBlock.ssm` /
+// `MambaBlock.call`; Mamba paper Section 3 as that page restates it):
+//   pre = delta_raw + bias, dt = softplus(pre) (or pre), abar_n = exp(dt A_n),
+//   h_t = abar_t h_{t-1} + dt_t B_t u_t (h_0 = 0), y_t = C_t.h_t + D u_t, out_t = y_t silu(z_t).
+// The pages give no backward; this is the forward's reverse-mode derivative by the chain
+// rule.  With dy_t = dout_t silu(z_t) and G_t = dL/dh_t = dy_t C_t + abar_{t+1} G_{t+1}:
+//   du_t     = dt_t sum_n G_tn B_tn + D dy_t
+//   ddelta_t = sigmoid(pre_t) sum_n G_tn (A_n abar_tn h_{t-1,n} + B_tn u_t)   (softplus on)
+//   dz_t     = dout_t y_t silu'(z_t),  silu'(z) = s (1 + z (1 - s)), s = sigmoid(z)
+//   dA_dn    = sum_{b,t} G_tn dt_t abar_tn h_{t-1,n},  dD_d = sum dy u,  dbias_d = sum ddelta
+//   dB_bnt   = sum_d G_tn dt_t u_t,  dC_bnt = sum_d dy_t h_tn
+// abar h_{t-1} is taken as h_t - dt B u (no second copy of the state), exp as exp2 of a
+// log2(e)-prescaled argument, and A = (n + 1) A_0 rows use abar_n = abar_0^(n+1) as in the
+// forward.
+//
+// Decomposition (one wavefront per workgroup; lane = channel, 16 states in VGPRs):
+//   * each channel row is cut into S segments of whole 8-step tiles.  An aggregate kernel
+//     gives each segment its forward carry (sum of dt, end state from h = 0) and its adjoint
+//     carry Lambda = sum_t (prod of abar over the segment's steps up to t) dy_t C_t, the part of
+//     dL/dh that flows out of the segment's first step into the one before;
+//   * the main kernel folds the forward carries of the earlier segments into its start state
+//     and the adjoint carries of the later segments (the same associative operator, taken in
+//     reverse order) into the adjoint entering its last step.  It walks its tiles forward once
+//     storing h at each tile start in a workspace checkpoint, then walks them backward: a
+//     tile's 8 states are recomputed from its checkpoint into LDS and consumed in reverse;
+//   * dB and dC sum over channels: per step the wave's 64 x 32 terms go through LDS and are
+//     summed per wave; a reduction kernel adds the per-wave sums of the channel groups.
+//     dA / dD / dbias are per-lane sums, added over segments and batches by a second kernel.
+// Every sum is taken in a fixed order, so results do not vary from run to run.
+#include <cstdlib>
+
+#include "device_math.hpp"
+#include "mss_internal.hpp"
+
+namespace mss {
+namespace {
+
+constexpr int kBT = 8;            // steps per tile
+constexpr int kAggW = 2 * kN + 1; // aggregate words per (segment, row): sum dt | H[16] | Lambda[16]
+constexpr int kParW = kN + 2;     // partial words per (segment, row): dA[16] | dD | dbias
+constexpr int kBCs = 2 * kN + 4;  // LDS words per step of B | C (16-byte pad)
+constexpr int kRedS = 2 * kN + 4; // LDS row stride of the dB / dC reduction buffer
+
+struct BwdArgs {
+    const void* u;
+    const void* delta;
+    const void* z;
+    const void* dout;
+    const float* A;
+    const float* B;
+    const float* C;
+    const float* D;
+    const float* bias;
+    void* du;
+    void* ddelta;
+    void* dz;
+    float* agg;   // [S][kAggW][R]
+    float* ck;    // [ntiles][kN][R]
+    float* part;  // [G][Bt][2 kN][tpad]
+    float* par;   // [S][kParW][R]
+    int64_t Dn, L, R, ntiles, tpad;
+    int S, G, Bt;
+};
+
+struct Row {
+    int64_t row;      // flat (b, d) row, clamped to a valid row for inactive lanes
+    bool active;
+    float A2[kN];     // A * log2(e)
+    float An[kN];     // A
+    float bias, dskip;
+    bool pow_ok;
+};
+
+__device__ __forceinline__ Row row_of(const BwdArgs& a) {
+    Row r;
+    const int64_t d = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    r.active = d < a.Dn;
+    const int64_t dc = r.active ? d : a.Dn - 1;
+    r.row = (int64_t)blockIdx.y * a.Dn + dc;
+    const float4* Ar = reinterpret_cast<const float4*>(a.A + dc * kN);
+#pragma unroll
+    for (int q = 0; q < kN / 4; ++q) {
+        const float4 v = Ar[q];
+        r.An[4 * q] = v.x; r.An[4 * q + 1] = v.y; r.An[4 * q + 2] = v.z; r.An[4 * q + 3] = v.w;
+    }
+    r.pow_ok = true;
+#pragma unroll
+    for (int n = 0; n < kN; ++n) {
+        r.A2[n] = r.An[n] * kLog2e;
+        r.pow_ok = r.pow_ok && (r.An[n] == static_cast<float>(n + 1) * r.An[0]);
+    }
+    r.bias = a.bias ? a.bias[dc] : 0.0f;
+    r.dskip = a.D ? a.D[dc] : 0.0f;
+    return r;
+}
+
+// abar_n for one step: exp2(dt A2_n), or abar_0^(n+1) by a product tree on the power path.
+template <bool POW>
+__device__ __forceinline__ void abar16(float dt, const float (&A2)[kN], float (&p)[kN]) {
+    if (POW) {
+        const float a = fast_exp2(dt * A2[0]);
+        p[0] = a;
+        p[1] = a * a;
+        p[2] = p[1] * a;
+        p[3] = p[1] * p[1];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) p[4 + k] = p[3] * p[k];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) p[8 + k] = p[7] * p[k];
+    } else {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) p[n] = fast_exp2(dt * A2[n]);
+    }
+}
+
+__device__ __forceinline__ float sigmoid(float v) { return fast_rcp(1.0f + fast_exp2(-v * kLog2e)); }
+
+// One tile (kBT steps from t0) of the lane's row; steps at or past L read as 0.  VEC: whole
+// 16-byte vectors (L is then a multiple of the vector length, so a vector is entirely valid or
+// entirely past the end).
+template <class E, bool VEC>
+__device__ __forceinline__ void load_tile(const void* base, int64_t off, int64_t t0, int64_t L,
+                                          float (&v)[kBT]) {
+    const typename E::storage* p = static_cast<const typename E::storage*>(base) + off;
+    if (VEC) {
+        constexpr int V = E::kPerVec;
+#pragma unroll
+        for (int q = 0; q < kBT / V; ++q) {
+            float w[V];
+            if (t0 + q * V < L) {
+                E::unpack(*reinterpret_cast<const uint4*>(p + t0 + q * V), w);
+            } else {
+#pragma unroll
+                for (int e = 0; e < V; ++e) w[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < V; ++e) v[q * V + e] = w[e];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kBT; ++i) v[i] = (t0 + i < L) ? E::load1(p, t0 + i) : 0.0f;
+    }
+}
+
+template <class E, bool VEC>
+__device__ __forceinline__ void store_tile(void* base, int64_t off, int64_t t0, int64_t L,
+                                           const float (&v)[kBT]) {
+    typename E::storage* p = static_cast<typename E::storage*>(base) + off;
+    if (VEC) {
+        constexpr int V = E::kPerVec;
+#pragma unroll
+        for (int q = 0; q < kBT / V; ++q)
+            if (t0 + q * V < L) *reinterpret_cast<uint4*>(p + t0 + q * V) = E::pack(&v[q * V]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kBT; ++i)
+            if (t0 + i < L) E::store1(p, t0 + i, v[i]);
+    }
+}
+
+// B and C of steps [t0, t0 + kBT) of batch b into LDS, time-major: sbc[t][n] = B, sbc[t][16 + n]
+// = C.  Lanes 0..31 load B, 32..63 load C, four steps of one state each.
+template <bool VEC>
+__device__ __forceinline__ void stage_bc(const float* __restrict__ B, const float* __restrict__ C, int b,
+                                         int64_t t0, int64_t L, float* sbc) {
+    const int lane = threadIdx.x;
+    const int half = lane & 1;
+    const int n = (lane >> 1) & (kN - 1);
+    const bool isC = lane >= 32;
+    const float* src = (isC ? C : B) + ((int64_t)b * kN + n) * L;
+    const int col = (isC ? kN : 0) + n;
+    const int64_t tb = t0 + 4 * half;
+    float v[4];
+    if (VEC) {
+        if (tb < L) {
+            const float4 w = *reinterpret_cast<const float4*>(src + tb);
+            v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+        } else {
+            v[0] = v[1] = v[2] = v[3] = 0.0f;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (tb + e < L) ? src[tb + e] : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sbc[(4 * half + e) * kBCs + col] = v[e];
+}
+
+__device__ __forceinline__ void read_bc(const float* sbc, int j, float (&bv)[kN], float (&cv)[kN]) {
+    const float4* b4 = reinterpret_cast<const float4*>(sbc + j * kBCs);
+#pragma unroll
+    for (int q = 0; q < kN / 4; ++q) {
+        const float4 x = b4[q], y = b4[kN / 4 + q];
+        bv[4 * q] = x.x; bv[4 * q + 1] = x.y; bv[4 * q + 2] = x.z; bv[4 * q + 3] = x.w;
+        cv[4 * q] = y.x; cv[4 * q + 1] = y.y; cv[4 * q + 2] = y.z; cv[4 * q + 3] = y.w;
+    }
+}
+
+// Per-step scalars of one lane.  Inactive lanes and steps past L get dt = x = dy = 0, which
+// makes their steps identities and their dB / dC terms exact zeros.
+struct StepVals {
+    float dt[kBT], x[kBT], dsp[kBT], dy[kBT], dg[kBT], u[kBT];
+};
+
+template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z>
+__device__ __forceinline__ void step_vals(const BwdArgs& a, const Row& r, int64_t t0, StepVals& s) {
+    const int64_t off = r.row * a.L;
+    float dv[kBT], gv[kBT], zv[kBT];
+    load_tile<E, VEC>(a.u, off, t0, a.L, s.u);
+    load_tile<E, VEC>(a.delta, off, t0, a.L, dv);
+    load_tile<E, VEC>(a.dout, off, t0, a.L, gv);
+    if (HAS_Z) load_tile<E, VEC>(a.z, off, t0, a.L, zv);
+#pragma unroll
+    for (int j = 0; j < kBT; ++j) {
+        const bool ok = r.active && t0 + j < a.L;
+        const float pre = dv[j] + r.bias;
+        const float dt = SOFTPLUS ? softplus(pre) : pre;
+        s.dt[j] = ok ? dt : 0.0f;
+        s.dsp[j] = SOFTPLUS ? sigmoid(pre) : 1.0f;
+        s.u[j] = ok ? s.u[j] : 0.0f;
+        s.x[j] = s.dt[j] * s.u[j];
+        if (HAS_Z) {
+            const float zz = zv[j];
+            const float sg = sigmoid(zz);
+            s.dy[j] = ok ? gv[j] * zz * sg : 0.0f;
+            s.dg[j] = gv[j] * sg * fmaf(zz, 1.0f - sg, 1.0f);
+        } else {
+            s.dy[j] = ok ? gv[j] : 0.0f;
+            s.dg[j] = 0.0f;
+        }
+    }
+}
+
+__device__ __forceinline__ void seg_tiles(int s, int S, int64_t ntiles, int64_t& tb, int64_t& te) {
+    tb = (int64_t)s * ntiles / S;
+    te = (int64_t)(s + 1) * ntiles / S;
+}
+
+// ---------------------------------------------------------------- aggregate kernel
+
+template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z, bool POW>
+__device__ __forceinline__ void agg_body(const BwdArgs& a, const Row& r, float* sbc) {
+    const int s = blockIdx.z;
+    int64_t tb, te;
+    seg_tiles(s, a.S, a.ntiles, tb, te);
+    float H[kN], Lam[kN], Rp[kN];
+#pragma unroll
+    for (int n = 0; n < kN; ++n) { H[n] = 0.0f; Lam[n] = 0.0f; Rp[n] = 1.0f; }
+    float dsum = 0.0f;
+    for (int64_t tile = tb; tile < te; ++tile) {
+        const int64_t t0 = tile * kBT;
+        StepVals v;
+        step_vals<E, VEC, SOFTPLUS, HAS_Z>(a, r, t0, v);
+        __syncthreads();  // readers of the previous tile's B / C are done
+        stage_bc<VEC>(a.B, a.C, blockIdx.y, t0, a.L, sbc);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kBT; ++j) {
+            if (t0 + j >= a.L) break;
+            float bv[kN], cv[kN], p[kN];
+            read_bc(sbc, j, bv, cv);
+            abar16<POW>(v.dt[j], r.A2, p);
+            dsum += v.dt[j];
+#pragma unroll
+            for (int n = 0; n < kN; ++n) {
+                H[n] = fmaf(p[n], H[n], v.x[j] * bv[n]);
+                Rp[n] *= p[n];
+                Lam[n] = fmaf(Rp[n], v.dy[j] * cv[n], Lam[n]);
+            }
+        }
+    }
+    if (r.active) {
+        float* o = a.agg + (int64_t)s * kAggW * a.R + r.row;
+        o[0] = dsum;
+#pragma unroll
+        for (int n = 0; n < kN; ++n) {
+            o[(int64_t)(1 + n) * a.R] = H[n];
+            o[(int64_t)(1 + kN + n) * a.R] = Lam[n];
+        }
+    }
+}
+
+template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z>
+__global__ __launch_bounds__(64) void bwd_agg_kernel(BwdArgs a) {
+    __shared__ __align__(16) float sbc[kBT * kBCs];
+    const Row r = row_of(a);
+    if (__all(r.pow_ok)) agg_body<E, VEC, SOFTPLUS, HAS_Z, true>(a, r, sbc);
+    else agg_body<E, VEC, SOFTPLUS, HAS_Z, false>(a, r, sbc);
+}
+
+// ---------------------------------------------------------------- main kernel
+
+// Segment carries: the forward state entering segment s (fold of segments 0..s-1) and the
+// adjoint entering its last step from the later segments (fold of S-1 down to s+1).
+template <bool POW>
+__device__ __forceinline__ void carries(const BwdArgs& a, const Row& r, int s, float (&h)[kN],
+                                        float (&gc)[kN]) {
+#pragma unroll
+    for (int n = 0; n < kN; ++n) { h[n] = 0.0f; gc[n] = 0.0f; }
+    for (int k = 0; k < s; ++k) {
+        const float* g = a.agg + (int64_t)k * kAggW * a.R + r.row;
+        float p[kN];
+        abar16<POW>(g[0], r.A2, p);
+#pragma unroll
+        for (int n = 0; n < kN; ++n) h[n] = fmaf(p[n], h[n], g[(int64_t)(1 + n) * a.R]);
+    }
+    for (int k = a.S - 1; k > s; --k) {
+        const float* g = a.agg + (int64_t)k * kAggW * a.R + r.row;
+        float p[kN];
+        abar16<POW>(g[0], r.A2, p);
+#pragma unroll
+        for (int n = 0; n < kN; ++n) gc[n] = fmaf(p[n], gc[n], g[(int64_t)(1 + kN + n) * a.R]);
+    }
+}
+
+template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z, bool POW>
+__device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float* sbc, float* hbuf,
+                                          float* red) {
+    const int s = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int b = blockIdx.y;
+    int64_t tb, te;
+    seg_tiles(s, a.S, a.ntiles, tb, te);
+    float h[kN], gc[kN];
+    carries<POW>(a, r, s, h, gc);
+
+    // forward walk: checkpoint h at every tile start
+    for (int64_t tile = tb; tile < te; ++tile) {
+        const int64_t t0 = tile * kBT;
+        if (r.active) {
+            float* ck = a.ck + tile * kN * a.R + r.row;
+#pragma unroll
+            for (int n = 0; n < kN; ++n) ck[(int64_t)n * a.R] = h[n];
+        }
+        if (tile + 1 == te) break;  // the last tile's end state is not needed
+        StepVals v;
+        step_vals<E, VEC, SOFTPLUS, HAS_Z>(a, r, t0, v);
+        __syncthreads();
+        stage_bc<VEC>(a.B, a.C, b, t0, a.L, sbc);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kBT; ++j) {
+            if (t0 + j >= a.L) break;
+            float bv[kN], cv[kN], p[kN];
+            read_bc(sbc, j, bv, cv);
+            abar16<POW>(v.dt[j], r.A2, p);
+#pragma unroll
+            for (int n = 0; n < kN; ++n) h[n] = fmaf(p[n], h[n], v.x[j] * bv[n]);
+        }
+    }
+
+    // backward walk
+    float dA[kN];
+#pragma unroll
+    for (int n = 0; n < kN; ++n) dA[n] = 0.0f;
+    float dDacc = 0.0f, dbacc = 0.0f;
+    const int jj = lane & (2 * kN - 1), hh = lane >> 5;
+    for (int64_t tile = te - 1; tile >= tb; --tile) {
+        const int64_t t0 = tile * kBT;
+        StepVals v;
+        step_vals<E, VEC, SOFTPLUS, HAS_Z>(a, r, t0, v);
+        __syncthreads();
+        stage_bc<VEC>(a.B, a.C, b, t0, a.L, sbc);
+        __syncthreads();
+        {   // recompute the tile's states into LDS (lane-private columns)
+            const float* ck = a.ck + tile * kN * a.R + r.row;
+            float hs[kN];
+#pragma unroll
+            for (int n = 0; n < kN; ++n) hs[n] = ck[(int64_t)n * a.R];
+#pragma unroll
+            for (int j = 0; j < kBT; ++j) {
+                if (t0 + j >= a.L) break;
+                float bv[kN], cv[kN], p[kN];
+                read_bc(sbc, j, bv, cv);
+                abar16<POW>(v.dt[j], r.A2, p);
+#pragma unroll
+                for (int n = 0; n < kN; ++n) {
+                    hs[n] = fmaf(p[n], hs[n], v.x[j] * bv[n]);
+                    hbuf[(j * kN + n) * 64 + lane] = hs[n];
+                }
+            }
+        }
+        float gdu[kBT], gdd[kBT], gdz[kBT], bcs[kBT];
+#pragma unroll
+        for (int j = kBT - 1; j >= 0; --j) {
+            gdu[j] = gdd[j] = gdz[j] = bcs[j] = 0.0f;
+            if (t0 + j >= a.L) continue;
+            float bv[kN], cv[kN], p[kN], hc[kN];
+            read_bc(sbc, j, bv, cv);
+            abar16<POW>(v.dt[j], r.A2, p);
+#pragma unroll
+            for (int n = 0; n < kN; ++n) hc[n] = hbuf[(j * kN + n) * 64 + lane];
+            float y = 0.0f, gb = 0.0f, qa = 0.0f;
+            float4* rrow = reinterpret_cast<float4*>(red + lane * kRedS);
+#pragma unroll
+            for (int q = 0; q < kN / 4; ++q) {
+                float cB[4], cC[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int n = 4 * q + e;
+                    const float G = fmaf(v.dy[j], cv[n], gc[n]);       // dL/dh_t
+                    y = fmaf(cv[n], hc[n], y);
+                    const float ah = fmaf(-v.x[j], bv[n], hc[n]);      // abar h_{t-1}
+                    const float qn = G * ah;
+                    qa = fmaf(POW ? static_cast<float>(n + 1) : r.An[n], qn, qa);
+                    gb = fmaf(G, bv[n], gb);
+                    dA[n] = fmaf(v.dt[j], qn, dA[n]);
+                    cB[e] = G * v.x[j];
+                    cC[e] = v.dy[j] * hc[n];
+                    gc[n] = p[n] * G;                                  // toward h_{t-1}
+                }
+                rrow[q] = make_float4(cB[0], cB[1], cB[2], cB[3]);
+                rrow[kN / 4 + q] = make_float4(cC[0], cC[1], cC[2], cC[3]);
+            }
+            if (POW) qa *= r.An[0];
+            gdu[j] = fmaf(v.dt[j], gb, r.dskip * v.dy[j]);
+            gdd[j] = fmaf(v.u[j], gb, qa) * v.dsp[j];
+            gdz[j] = v.dg[j] * fmaf(r.dskip, v.u[j], y);
+            dDacc = fmaf(v.dy[j], v.u[j], dDacc);
+            dbacc += r.active ? gdd[j] : 0.0f;
+            __syncthreads();
+            // lane (hh, jj) sums term jj over lanes 32 hh .. 32 hh + 31; the halves then meet
+            float sum = 0.0f;
+#pragma unroll 8
+            for (int i = 0; i < 32; ++i) sum += red[(32 * hh + i) * kRedS + jj];
+            sum += __shfl_xor(sum, 32);
+            bcs[j] = sum;
+            __syncthreads();
+        }
+        if (r.active) {
+            const int64_t off = r.row * a.L;
+            store_tile<E, VEC>(a.du, off, t0, a.L, gdu);
+            store_tile<E, VEC>(a.ddelta, off, t0, a.L, gdd);
+            if (HAS_Z && a.dz) store_tile<E, VEC>(a.dz, off, t0, a.L, gdz);
+        }
+        if (lane < 2 * kN) {
+            float4* o = reinterpret_cast<float4*>(
+                a.part + (((int64_t)blockIdx.x * a.Bt + b) * (2 * kN) + lane) * a.tpad + t0);
+            o[0] = make_float4(bcs[0], bcs[1], bcs[2], bcs[3]);
+            o[1] = make_float4(bcs[4], bcs[5], bcs[6], bcs[7]);
+        }
+    }
+    if (r.active) {
+        float* o = a.par + (int64_t)s * kParW * a.R + r.row;
+#pragma unroll
+        for (int n = 0; n < kN; ++n) o[(int64_t)n * a.R] = dA[n];
+        o[(int64_t)kN * a.R] = dDacc;
+        o[(int64_t)(kN + 1) * a.R] = dbacc;
+    }
+}
+
+template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z>
+__global__ __launch_bounds__(64) void bwd_main_kernel(BwdArgs a) {
+    __shared__ __align__(16) float sbc[kBT * kBCs];
+    __shared__ __align__(16) float hbuf[kBT * kN * 64];
+    __shared__ __align__(16) float red[64 * kRedS];
+    const Row r = row_of(a);
+    if (__all(r.pow_ok)) main_body<E, VEC, SOFTPLUS, HAS_Z, true>(a, r, sbc, hbuf, red);
+    else main_body<E, VEC, SOFTPLUS, HAS_Z, false>(a, r, sbc, hbuf, red);
+}
+
+// ---------------------------------------------------------------- reductions
+
+// dB[b][n][t] = sum_g part[g][b][n][t], dC[b][n][t] = sum_g part[g][b][16 + n][t].
+__global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ part, float* __restrict__ dB,
+                                                            float* __restrict__ dC, int G, int Bt, int64_t L,
+                                                            int64_t tpad) {
+    const int64_t total = (int64_t)Bt * 2 * kN * L;
+    const int64_t gstride = (int64_t)Bt * 2 * kN * tpad;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = i % L;
+        const int64_t bk = i / L;           // b * 32 + k
+        const int k = static_cast<int>(bk % (2 * kN));
+        const int64_t b = bk / (2 * kN);
+        const float* p = part + bk * tpad + t;
+        float s = 0.0f;
+        for (int g = 0; g < G; ++g) s += p[(int64_t)g * gstride];
+        if (k < kN) dB[(b * kN + k) * L + t] = s;
+        else dC[(b * kN + (k - kN)) * L + t] = s;
+    }
+}
+
+// dA[d][n], dD[d], dbias[d]: sums of the per-(segment, row) partials over segments and batches.
+__global__ __launch_bounds__(256) void bwd_reduce_par_kernel(const float* __restrict__ par, float* __restrict__ dA,
+                                                             float* __restrict__ dD, float* __restrict__ dbias,
+                                                             int S, int Bt, int64_t Dn, int64_t R) {
+    const int64_t total = (int64_t)kParW * Dn;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int k = static_cast<int>(i / Dn);
+        const int64_t d = i % Dn;
+        float s = 0.0f;
+        for (int sg = 0; sg < S; ++sg)
+            for (int b = 0; b < Bt; ++b) s += par[((int64_t)sg * kParW + k) * R + (int64_t)b * Dn + d];
+        if (k < kN) dA[d * kN + k] = s;
+        else if (k == kN) { if (dD) dD[d] = s; }
+        else if (dbias) dbias[d] = s;
+    }
+}
+
+__global__ __launch_bounds__(256) void bwd_zero_kernel(float* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0.0f;
+}
+
+unsigned grid_for(int64_t n) {
+    const int64_t b = (n + 255) / 256;
+    return static_cast<unsigned>(b < 1 ? 1 : (b > 65535 ? 65535 : b));
+}
+
+hipError_t zero(float* p, int64_t n, hipStream_t s) {
+    if (!p || n <= 0) return hipSuccess;
+    bwd_zero_kernel<<<dim3(grid_for(n)), dim3(256), 0, s>>>(p, n);
+    return hipGetLastError();
+}
+
+template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z>
+hipError_t launch_t(const BwdArgs& k, const BwdLaunch& a, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(k.G), static_cast<unsigned>(k.Bt), static_cast<unsigned>(k.S));
+    if (k.S > 1) bwd_agg_kernel<E, VEC, SOFTPLUS, HAS_Z><<<grid, dim3(64), 0, stream>>>(k);
+    bwd_main_kernel<E, VEC, SOFTPLUS, HAS_Z><<<grid, dim3(64), 0, stream>>>(k);
+    const int64_t nbc = (int64_t)k.Bt * 2 * kN * k.L;
+    bwd_reduce_bc_kernel<<<dim3(grid_for(nbc)), dim3(256), 0, stream>>>(k.part, a.dB, a.dC, k.G, k.Bt, k.L, k.tpad);
+    bwd_reduce_par_kernel<<<dim3(grid_for((int64_t)kParW * k.Dn)), dim3(256), 0, stream>>>(
+        k.par, a.dA, a.dD, a.dbias, k.S, k.Bt, k.Dn, k.R);
+    return hipGetLastError();
+}
+
+template <class E, bool VEC>
+hipError_t launch_e(const BwdArgs& k, const BwdLaunch& a, hipStream_t stream) {
+    const bool hz = a.z != nullptr;
+    if (a.softplus) return hz ? launch_t<E, VEC, true, true>(k, a, stream) : launch_t<E, VEC, true, false>(k, a, stream);
+    return hz ? launch_t<E, VEC, false, true>(k, a, stream) : launch_t<E, VEC, false, false>(k, a, stream);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct Layout {
+    size_t agg, ck, part, par, total;
+};
+
+Layout layout_of(const BwdLaunch& a, int S) {
+    const int64_t R = a.Bt * a.Dn;
+    const int64_t ntiles = (a.L + kBT - 1) / kBT;
+    const int64_t G = (a.Dn + 63) / 64;
+    Layout l;
+    l.agg = 0;
+    l.ck = l.agg + align256(static_cast<size_t>(S) * kAggW * R * sizeof(float));
+    l.part = l.ck + align256(static_cast<size_t>(ntiles) * kN * R * sizeof(float));
+    l.par = l.part + align256(static_cast<size_t>(G) * a.Bt * 2 * kN * ntiles * kBT * sizeof(float));
+    l.total = l.par + align256(static_cast<size_t>(S) * kParW * R * sizeof(float));
+    return l;
+}
+
+}  // namespace
+
+// Segments per channel group: about three wavefronts per CU over the launch (the main kernel's
+// LDS holds three per CU), at most one per tile.  MSS_BWD_SEGMENTS overrides.
+int plan_bwd_segments(const BwdLaunch& a, int num_cus) {
+    const int64_t groups = a.Bt * ((a.Dn + 63) / 64);
+    const int64_t ntiles = (a.L + kBT - 1) / kBT;
+    const int64_t target = 3LL * (num_cus > 0 ? num_cus : 256);
+    int64_t S = groups > 0 ? (target + groups - 1) / groups : 1;
+    const char* env = getenv("MSS_BWD_SEGMENTS");
+    if (env && atoi(env) > 0) S = atoi(env);
+    if (S > ntiles) S = ntiles;
+    if (S > 65535) S = 65535;
+    if (S < 1) S = 1;
+    return static_cast<int>(S);
+}
+
+size_t bwd_workspace_bytes(const BwdLaunch& a, int segments) {
+    if (a.L == 0 || a.Bt * a.Dn == 0) return 0;
+    return layout_of(a, segments).total;
+}
+
+hipError_t launch_scan_bwd(const BwdLaunch& a, int segments, void* workspace, hipStream_t stream) {
+    const int64_t R = a.Bt * a.Dn;
+    if (a.L == 0 || R == 0) {
+        // empty sums: every reduced gradient is zero (du / ddelta / dz have no elements)
+        hipError_t e = zero(a.dA, a.Dn * kN, stream);
+        if (e == hipSuccess) e = zero(a.dD, a.Dn, stream);
+        if (e == hipSuccess) e = zero(a.dbias, a.Dn, stream);
+        if (e == hipSuccess) e = zero(a.dB, a.Bt * kN * a.L, stream);
+        if (e == hipSuccess) e = zero(a.dC, a.Bt * kN * a.L, stream);
+        return e;
+    }
+    const Layout l = layout_of(a, segments);
+    char* ws = static_cast<char*>(workspace);
+    BwdArgs k;
+    k.u = a.u; k.delta = a.delta; k.z = a.z; k.dout = a.dout;
+    k.A = a.A; k.B = a.B; k.C = a.C; k.D = a.D; k.bias = a.bias;
+    k.du = a.du; k.ddelta = a.ddelta; k.dz = a.dz;
+    k.agg = reinterpret_cast<float*>(ws + l.agg);
+    k.ck = reinterpret_cast<float*>(ws + l.ck);
+    k.part = reinterpret_cast<float*>(ws + l.part);
+    k.par = reinterpret_cast<float*>(ws + l.par);
+    k.Dn = a.Dn; k.L = a.L; k.R = R;
+    k.ntiles = (a.L + kBT - 1) / kBT;
+    k.tpad = k.ntiles * kBT;
+    k.S = segments;
+    k.G = static_cast<int>((a.Dn + 63) / 64);
+    k.Bt = static_cast<int>(a.Bt);
+    if (a.bf16) return a.vec_ok ? launch_e<BF16, true>(k, a, stream) : launch_e<BF16, false>(k, a, stream);
+    return a.vec_ok ? launch_e<F32, true>(k, a, stream) : launch_e<F32, false>(k, a, stream);
+}
+
+}  // namespace mss

@@ -241,6 +241,103 @@ def test_fwd_state_may_share_inputs(lib):
     assert call_fwd_state(a, h) == OK
 
 
+# --------------------------------------------------------------------- backward scan
+
+def bwd_args(dtype=MSS_F32, n=N):
+    es = 2 if dtype == MSS_BF16 else 4
+    big = BT * DN * L
+    a = fwd_args(dtype, n)
+    del a["out"], a["last_state"]
+    a.update(
+        dout=Tensor.make(addr(big * es), dtype, [BT, DN, L]),
+        du=Tensor.make(addr(big * es), dtype, [BT, DN, L]),
+        ddelta=Tensor.make(addr(big * es), dtype, [BT, DN, L]),
+        dA=Tensor.make(addr(DN * n * 4), MSS_F32, [DN, n]),
+        dB=Tensor.make(addr(BT * n * L * 4), MSS_F32, [BT, n, L]),
+        dC=Tensor.make(addr(BT * n * L * 4), MSS_F32, [BT, n, L]),
+        dD=Tensor.make(addr(DN * 4), MSS_F32, [DN]),
+        dz=Tensor.make(addr(big * es), dtype, [BT, DN, L]),
+        ddelta_bias=Tensor.make(addr(DN * 4), MSS_F32, [DN]))
+    return a
+
+
+def call_bwd(a):
+    return mss.scan_bwd_raw(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                            a["delta_bias"], a["softplus_flag"], a["dout"], a["du"], a["ddelta"],
+                            a["dA"], a["dB"], a["dC"], a["dD"], a["dz"], a["ddelta_bias"], a["stream"])
+
+
+@pytest.mark.parametrize("name", ["u", "delta", "A", "B", "C", "dout", "du", "ddelta", "dA", "dB", "dC"])
+def test_bwd_null_required(lib, name):
+    a = bwd_args()
+    a[name] = None
+    assert call_bwd(a) == NULL_ARG
+
+
+@pytest.mark.parametrize("name,shape", [
+    ("dout", [BT, DN, L - 1]), ("du", [BT, DN + 1, L]), ("ddelta", [1, DN, L]), ("dA", [DN, N + 1]),
+    ("dB", [BT, N, L + 1]), ("dC", [BT + 1, N, L]), ("dD", [DN - 1]), ("dz", [BT, DN, 3]),
+    ("ddelta_bias", [DN, 1])])
+def test_bwd_shape(lib, name, shape):
+    a = bwd_args()
+    t = a[name]
+    a[name] = Tensor.make(t.data, t.dtype, shape)
+    assert call_bwd(a) == SHAPE
+
+
+def test_bwd_dz_without_gate(lib):
+    a = bwd_args()
+    a["z"] = None
+    assert call_bwd(a) == SHAPE
+
+
+@pytest.mark.parametrize("name,dtype", [
+    ("dout", MSS_BF16), ("du", MSS_BF16), ("dz", MSS_BF16), ("dA", MSS_BF16), ("dB", MSS_BF16),
+    ("dD", MSS_BF16), ("ddelta_bias", MSS_BF16)])
+def test_bwd_dtype(lib, name, dtype):
+    a = bwd_args()
+    a[name].dtype = dtype
+    assert call_bwd(a) == DTYPE
+
+
+def test_bwd_layout(lib):
+    a = bwd_args()
+    a["dB"].stride[0], a["dB"].stride[1] = L, BT * L
+    assert call_bwd(a) == LAYOUT
+    a = bwd_args()
+    a["A"].data += 4
+    assert call_bwd(a) == LAYOUT
+    a = bwd_args(MSS_BF16)
+    a["du"].data += 1
+    assert call_bwd(a) == LAYOUT
+
+
+@pytest.mark.parametrize("out,other", [
+    ("du", "u"), ("ddelta", "dout"), ("dA", "A"), ("dB", "B"), ("dC", "C"), ("dz", "z"),
+    ("dD", "delta_bias"), ("du", "ddelta"), ("dB", "dC"), ("dD", "ddelta_bias")])
+def test_bwd_alias(lib, out, other):
+    a = bwd_args()
+    a[out].data = a[other].data
+    assert call_bwd(a) == ALIAS
+
+
+def test_bwd_unsupported_dstate(lib):
+    assert call_bwd(bwd_args(n=32)) == UNSUPPORTED
+
+
+def test_bwd_nothing_to_write_is_ok(lib):
+    a = bwd_args()
+    for k in ("u", "delta", "z", "dout", "du", "ddelta", "dz"):
+        a[k] = Tensor.make(a[k].data, MSS_F32, [0, 0, L])
+    for k in ("B", "C", "dB", "dC"):
+        a[k] = Tensor.make(a[k].data, MSS_F32, [0, N, L])
+    for k in ("A", "dA"):
+        a[k] = Tensor.make(a[k].data, MSS_F32, [0, N])
+    for k in ("D", "delta_bias", "dD", "ddelta_bias"):
+        a[k] = Tensor.make(a[k].data, MSS_F32, [0])
+    assert call_bwd(a) == OK
+
+
 # --------------------------------------------------------------------- decode step
 
 def dec_args(dtype=MSS_BF16, n=N):
