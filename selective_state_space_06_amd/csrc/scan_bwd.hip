@@ -41,7 +41,6 @@ constexpr int kBT = 8;            // steps per tile
 constexpr int kAggW = 2 * kN + 1; // aggregate words per (segment, row): sum dt | H[16] | Lambda[16]
 constexpr int kParW = kN + 2;     // partial words per (segment, row): dA[16] | dD | dbias
 constexpr int kBCs = 2 * kN + 4;  // LDS words per step of B | C (16-byte pad)
-constexpr int kRedS = 2 * kN + 4; // LDS row stride of the dB / dC reduction buffer
 
 struct BwdArgs {
     const void* u;
@@ -115,6 +114,30 @@ __device__ __forceinline__ void abar16(float dt, const float (&A2)[kN], float (&
     }
 }
 
+constexpr int kH = kN / 2;  // states per half-pass of the backward walk
+
+// abar for the 8 states kH * hf .. kH * hf + 7 of one step.
+template <bool POW>
+__device__ __forceinline__ void abar8(float dt, const float (&A2)[kN], int hf, float (&p)[kH]) {
+    if (POW) {
+        const float a = fast_exp2(dt * A2[0]);
+        p[0] = a;
+        p[1] = a * a;
+        p[2] = p[1] * a;
+        p[3] = p[1] * p[1];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) p[4 + k] = p[3] * p[k];
+        if (hf) {
+            const float a8 = p[7];
+#pragma unroll
+            for (int k = 0; k < kH; ++k) p[k] *= a8;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < kH; ++k) p[k] = fast_exp2(dt * A2[kH * hf + k]);
+    }
+}
+
 __device__ __forceinline__ float sigmoid(float v) { return fast_rcp(1.0f + fast_exp2(-v * kLog2e)); }
 
 // One tile (kBT steps from t0) of the lane's row; steps at or past L read as 0.  VEC: whole
@@ -160,34 +183,6 @@ __device__ __forceinline__ void store_tile(void* base, int64_t off, int64_t t0, 
     }
 }
 
-// B and C of steps [t0, t0 + kBT) of batch b into LDS, time-major: sbc[t][n] = B, sbc[t][16 + n]
-// = C.  Lanes 0..31 load B, 32..63 load C, four steps of one state each.
-template <bool VEC>
-__device__ __forceinline__ void stage_bc(const float* __restrict__ B, const float* __restrict__ C, int b,
-                                         int64_t t0, int64_t L, float* sbc) {
-    const int lane = threadIdx.x;
-    const int half = lane & 1;
-    const int n = (lane >> 1) & (kN - 1);
-    const bool isC = lane >= 32;
-    const float* src = (isC ? C : B) + ((int64_t)b * kN + n) * L;
-    const int col = (isC ? kN : 0) + n;
-    const int64_t tb = t0 + 4 * half;
-    float v[4];
-    if (VEC) {
-        if (tb < L) {
-            const float4 w = *reinterpret_cast<const float4*>(src + tb);
-            v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
-        } else {
-            v[0] = v[1] = v[2] = v[3] = 0.0f;
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (tb + e < L) ? src[tb + e] : 0.0f;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sbc[(4 * half + e) * kBCs + col] = v[e];
-}
-
 __device__ __forceinline__ void read_bc(const float* sbc, int j, float (&bv)[kN], float (&cv)[kN]) {
     const float4* b4 = reinterpret_cast<const float4*>(sbc + j * kBCs);
 #pragma unroll
@@ -198,6 +193,85 @@ __device__ __forceinline__ void read_bc(const float* sbc, int j, float (&bv)[kN]
     }
 }
 
+// B and C of the 8 states of half hf at tile step j.
+__device__ __forceinline__ void read_bc_half(const float* sbc, int j, int hf, float (&bv)[kH], float (&cv)[kH]) {
+    const float4* b4 = reinterpret_cast<const float4*>(sbc + j * kBCs + kH * hf);
+    const float4* c4 = reinterpret_cast<const float4*>(sbc + j * kBCs + kN + kH * hf);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const float4 x = b4[q], y = c4[q];
+        bv[4 * q] = x.x; bv[4 * q + 1] = x.y; bv[4 * q + 2] = x.z; bv[4 * q + 3] = x.w;
+        cv[4 * q] = y.x; cv[4 * q + 1] = y.y; cv[4 * q + 2] = y.z; cv[4 * q + 3] = y.w;
+    }
+}
+
+// One tile of the lane's inputs as loaded (VEC: the 16-byte vectors, converted when used, so the
+// loads of the next tile can be in flight while this one is computed), plus the lane's four
+// B or C values for the tile's LDS block.
+template <class E, bool VEC>
+struct Raw {
+    static constexpr int NV = kBT * static_cast<int>(sizeof(typename E::storage)) / 16;
+    uint4 u[NV], d[NV], g[NV], z[NV];
+    float bc[4];
+};
+template <class E>
+struct Raw<E, false> {
+    float u[kBT], d[kBT], g[kBT], z[kBT];
+    float bc[4];
+};
+
+template <class E, bool VEC>
+__device__ __forceinline__ void raw_row(const void* base, int64_t off, int64_t t0, int64_t L,
+                                        uint4 (&w)[Raw<E, true>::NV]) {
+    const typename E::storage* p = static_cast<const typename E::storage*>(base) + off;
+    constexpr int V = E::kPerVec;
+#pragma unroll
+    for (int q = 0; q < Raw<E, true>::NV; ++q)
+        w[q] = (t0 + q * V < L) ? *reinterpret_cast<const uint4*>(p + t0 + q * V) : make_uint4(0, 0, 0, 0);
+}
+
+template <class E, bool VEC, bool HAS_Z>
+__device__ __forceinline__ void load_raw(const BwdArgs& a, const Row& r, int64_t t0, Raw<E, VEC>& w) {
+    const int64_t off = r.row * a.L;
+    if constexpr (VEC) {
+        raw_row<E, VEC>(a.u, off, t0, a.L, w.u);
+        raw_row<E, VEC>(a.delta, off, t0, a.L, w.d);
+        raw_row<E, VEC>(a.dout, off, t0, a.L, w.g);
+        if (HAS_Z) raw_row<E, VEC>(a.z, off, t0, a.L, w.z);
+    } else {
+        load_tile<E, false>(a.u, off, t0, a.L, w.u);
+        load_tile<E, false>(a.delta, off, t0, a.L, w.d);
+        load_tile<E, false>(a.dout, off, t0, a.L, w.g);
+        if (HAS_Z) load_tile<E, false>(a.z, off, t0, a.L, w.z);
+    }
+    // B or C: lanes 0..31 load B, 32..63 load C, four steps of one state each
+    const int lane = threadIdx.x;
+    const int half = lane & 1;
+    const int n = (lane >> 1) & (kN - 1);
+    const float* src = (lane >= 32 ? a.C : a.B) + ((int64_t)blockIdx.y * kN + n) * a.L;
+    const int64_t tb = t0 + 4 * half;
+    if (VEC) {
+        if (tb < a.L) {
+            const float4 v = *reinterpret_cast<const float4*>(src + tb);
+            w.bc[0] = v.x; w.bc[1] = v.y; w.bc[2] = v.z; w.bc[3] = v.w;
+        } else {
+            w.bc[0] = w.bc[1] = w.bc[2] = w.bc[3] = 0.0f;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w.bc[e] = (tb + e < a.L) ? src[tb + e] : 0.0f;
+    }
+}
+
+// The tile's B | C block into LDS, time-major: sbc[t][n] = B, sbc[t][16 + n] = C.
+__device__ __forceinline__ void put_bc(const float (&bc)[4], float* sbc) {
+    const int lane = threadIdx.x;
+    const int half = lane & 1;
+    const int col = (lane >= 32 ? kN : 0) + ((lane >> 1) & (kN - 1));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sbc[(4 * half + e) * kBCs + col] = bc[e];
+}
+
 // Per-step scalars of one lane.  Inactive lanes and steps past L get dt = x = dy = 0, which
 // makes their steps identities and their dB / dC terms exact zeros.
 struct StepVals {
@@ -205,13 +279,24 @@ struct StepVals {
 };
 
 template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z>
-__device__ __forceinline__ void step_vals(const BwdArgs& a, const Row& r, int64_t t0, StepVals& s) {
-    const int64_t off = r.row * a.L;
+__device__ __forceinline__ void step_vals(const BwdArgs& a, const Row& r, int64_t t0, const Raw<E, VEC>& w,
+                                          StepVals& s) {
     float dv[kBT], gv[kBT], zv[kBT];
-    load_tile<E, VEC>(a.u, off, t0, a.L, s.u);
-    load_tile<E, VEC>(a.delta, off, t0, a.L, dv);
-    load_tile<E, VEC>(a.dout, off, t0, a.L, gv);
-    if (HAS_Z) load_tile<E, VEC>(a.z, off, t0, a.L, zv);
+    if constexpr (VEC) {
+        constexpr int V = E::kPerVec;
+#pragma unroll
+        for (int q = 0; q < Raw<E, true>::NV; ++q) {
+            E::unpack(w.u[q], &s.u[q * V]);
+            E::unpack(w.d[q], &dv[q * V]);
+            E::unpack(w.g[q], &gv[q * V]);
+            if (HAS_Z) E::unpack(w.z[q], &zv[q * V]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kBT; ++j) {
+            s.u[j] = w.u[j]; dv[j] = w.d[j]; gv[j] = w.g[j]; zv[j] = HAS_Z ? w.z[j] : 0.0f;
+        }
+    }
 #pragma unroll
     for (int j = 0; j < kBT; ++j) {
         const bool ok = r.active && t0 + j < a.L;
@@ -249,12 +334,16 @@ __device__ __forceinline__ void agg_body(const BwdArgs& a, const Row& r, float* 
 #pragma unroll
     for (int n = 0; n < kN; ++n) { H[n] = 0.0f; Lam[n] = 0.0f; Rp[n] = 1.0f; }
     float dsum = 0.0f;
+    Raw<E, VEC> nx;
+    load_raw<E, VEC, HAS_Z>(a, r, tb * kBT, nx);
     for (int64_t tile = tb; tile < te; ++tile) {
         const int64_t t0 = tile * kBT;
+        const Raw<E, VEC> cur = nx;
+        if (tile + 1 < te) load_raw<E, VEC, HAS_Z>(a, r, t0 + kBT, nx);
         StepVals v;
-        step_vals<E, VEC, SOFTPLUS, HAS_Z>(a, r, t0, v);
+        step_vals<E, VEC, SOFTPLUS, HAS_Z>(a, r, t0, cur, v);
         __syncthreads();  // readers of the previous tile's B / C are done
-        stage_bc<VEC>(a.B, a.C, blockIdx.y, t0, a.L, sbc);
+        put_bc(cur.bc, sbc);
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < kBT; ++j) {
@@ -327,6 +416,8 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
     carries<POW>(a, r, s, h, gc);
 
     // forward walk: checkpoint h at every tile start
+    Raw<E, VEC> nx;
+    load_raw<E, VEC, HAS_Z>(a, r, tb * kBT, nx);
     for (int64_t tile = tb; tile < te; ++tile) {
         const int64_t t0 = tile * kBT;
         if (r.active) {
@@ -335,10 +426,12 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
             for (int n = 0; n < kN; ++n) ck[(int64_t)n * a.R] = h[n];
         }
         if (tile + 1 == te) break;  // the last tile's end state is not needed
+        const Raw<E, VEC> cur = nx;
+        if (tile + 2 < te) load_raw<E, VEC, HAS_Z>(a, r, t0 + kBT, nx);
         StepVals v;
-        step_vals<E, VEC, SOFTPLUS, HAS_Z>(a, r, t0, v);
+        step_vals<E, VEC, SOFTPLUS, HAS_Z>(a, r, t0, cur, v);
         __syncthreads();
-        stage_bc<VEC>(a.B, a.C, b, t0, a.L, sbc);
+        put_bc(cur.bc, sbc);
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < kBT; ++j) {
@@ -356,90 +449,113 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
 #pragma unroll
     for (int n = 0; n < kN; ++n) dA[n] = 0.0f;
     float dDacc = 0.0f, dbacc = 0.0f;
-    const int jj = lane & (2 * kN - 1), hh = lane >> 5;
+    float ckn[kN];
+    load_raw<E, VEC, HAS_Z>(a, r, (te - 1) * kBT, nx);
+#pragma unroll
+    for (int n = 0; n < kN; ++n) ckn[n] = r.active ? a.ck[((te - 1) * kN + n) * a.R + r.row] : 0.0f;
     for (int64_t tile = te - 1; tile >= tb; --tile) {
         const int64_t t0 = tile * kBT;
-        StepVals v;
-        step_vals<E, VEC, SOFTPLUS, HAS_Z>(a, r, t0, v);
-        __syncthreads();
-        stage_bc<VEC>(a.B, a.C, b, t0, a.L, sbc);
-        __syncthreads();
-        {   // recompute the tile's states into LDS (lane-private columns)
-            const float* ck = a.ck + tile * kN * a.R + r.row;
-            float hs[kN];
+        const Raw<E, VEC> cur = nx;
+        float ck0[kN];
 #pragma unroll
-            for (int n = 0; n < kN; ++n) hs[n] = ck[(int64_t)n * a.R];
+        for (int n = 0; n < kN; ++n) ck0[n] = ckn[n];
+        if (tile > tb) {
+            load_raw<E, VEC, HAS_Z>(a, r, t0 - kBT, nx);
+#pragma unroll
+            for (int n = 0; n < kN; ++n) ckn[n] = r.active ? a.ck[((tile - 1) * kN + n) * a.R + r.row] : 0.0f;
+        }
+        StepVals v;
+        step_vals<E, VEC, SOFTPLUS, HAS_Z>(a, r, t0, cur, v);
+        __syncthreads();
+        put_bc(cur.bc, sbc);
+        __syncthreads();
+        // The tile's 16 states in two halves of 8 (the states are independent in the recurrence;
+        // only the outputs' sums over n combine the halves): recompute the half's states from
+        // the checkpoint into LDS (lane-private columns), then consume them in reverse.
+        float yacc[kBT], gbacc[kBT], qaacc[kBT];
+#pragma unroll
+        for (int j = 0; j < kBT; ++j) yacc[j] = gbacc[j] = qaacc[j] = 0.0f;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            float hs[kH];
+#pragma unroll
+            for (int k = 0; k < kH; ++k) hs[k] = ck0[kH * hf + k];
 #pragma unroll
             for (int j = 0; j < kBT; ++j) {
                 if (t0 + j >= a.L) break;
-                float bv[kN], cv[kN], p[kN];
-                read_bc(sbc, j, bv, cv);
-                abar16<POW>(v.dt[j], r.A2, p);
+                float bv[kH], cv[kH], p[kH];
+                read_bc_half(sbc, j, hf, bv, cv);
+                abar8<POW>(v.dt[j], r.A2, hf, p);
 #pragma unroll
-                for (int n = 0; n < kN; ++n) {
-                    hs[n] = fmaf(p[n], hs[n], v.x[j] * bv[n]);
-                    hbuf[(j * kN + n) * 64 + lane] = hs[n];
+                for (int k = 0; k < kH; ++k) {
+                    hs[k] = fmaf(p[k], hs[k], v.x[j] * bv[k]);
+                    hbuf[(j * kH + k) * 64 + lane] = hs[k];
                 }
             }
-        }
-        float gdu[kBT], gdd[kBT], gdz[kBT], bcs[kBT];
+            float bcs[kBT];
 #pragma unroll
-        for (int j = kBT - 1; j >= 0; --j) {
-            gdu[j] = gdd[j] = gdz[j] = bcs[j] = 0.0f;
-            if (t0 + j >= a.L) continue;
-            float bv[kN], cv[kN], p[kN], hc[kN];
-            read_bc(sbc, j, bv, cv);
-            abar16<POW>(v.dt[j], r.A2, p);
+            for (int j = kBT - 1; j >= 0; --j) {
+                bcs[j] = 0.0f;
+                if (t0 + j >= a.L) continue;
+                float bv[kH], cv[kH], p[kH], hc[kH];
+                read_bc_half(sbc, j, hf, bv, cv);
+                abar8<POW>(v.dt[j], r.A2, hf, p);
 #pragma unroll
-            for (int n = 0; n < kN; ++n) hc[n] = hbuf[(j * kN + n) * 64 + lane];
-            float y = 0.0f, gb = 0.0f, qa = 0.0f;
-            float4* rrow = reinterpret_cast<float4*>(red + lane * kRedS);
+                for (int k = 0; k < kH; ++k) hc[k] = hbuf[(j * kH + k) * 64 + lane];
+                float y = 0.0f, gb = 0.0f, qa = 0.0f;
 #pragma unroll
-            for (int q = 0; q < kN / 4; ++q) {
-                float cB[4], cC[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int n = 4 * q + e;
-                    const float G = fmaf(v.dy[j], cv[n], gc[n]);       // dL/dh_t
-                    y = fmaf(cv[n], hc[n], y);
-                    const float ah = fmaf(-v.x[j], bv[n], hc[n]);      // abar h_{t-1}
+                for (int k = 0; k < kH; ++k) {
+                    const int n = kH * hf + k;
+                    const float G = fmaf(v.dy[j], cv[k], gc[n]);       // dL/dh_t
+                    y = fmaf(cv[k], hc[k], y);
+                    const float ah = fmaf(-v.x[j], bv[k], hc[k]);      // abar h_{t-1}
                     const float qn = G * ah;
                     qa = fmaf(POW ? static_cast<float>(n + 1) : r.An[n], qn, qa);
-                    gb = fmaf(G, bv[n], gb);
+                    gb = fmaf(G, bv[k], gb);
                     dA[n] = fmaf(v.dt[j], qn, dA[n]);
-                    cB[e] = G * v.x[j];
-                    cC[e] = v.dy[j] * hc[n];
-                    gc[n] = p[n] * G;                                  // toward h_{t-1}
+                    red[k * 64 + lane] = G * v.x[j];                   // dB term
+                    red[(kH + k) * 64 + lane] = v.dy[j] * hc[k];       // dC term
+                    gc[n] = p[k] * G;                                  // toward h_{t-1}
                 }
-                rrow[q] = make_float4(cB[0], cB[1], cB[2], cB[3]);
-                rrow[kN / 4 + q] = make_float4(cC[0], cC[1], cC[2], cC[3]);
+                yacc[j] += y;
+                gbacc[j] += gb;
+                qaacc[j] += qa;
+                __syncthreads();
+                // lane (qq, jj) sums term jj over lanes 16 qq .. 16 qq + 15; the quarters then meet
+                const float4* rr = reinterpret_cast<const float4*>(red + (lane & 15) * 64 + 16 * (lane >> 4));
+                const float4 w0 = rr[0], w1 = rr[1], w2 = rr[2], w3 = rr[3];
+                float sum = ((w0.x + w0.y) + (w0.z + w0.w)) + ((w1.x + w1.y) + (w1.z + w1.w)) +
+                            (((w2.x + w2.y) + (w2.z + w2.w)) + ((w3.x + w3.y) + (w3.z + w3.w)));
+                sum += __shfl_xor(sum, 16);
+                sum += __shfl_xor(sum, 32);
+                bcs[j] = sum;
+                __syncthreads();
             }
-            if (POW) qa *= r.An[0];
-            gdu[j] = fmaf(v.dt[j], gb, r.dskip * v.dy[j]);
-            gdd[j] = fmaf(v.u[j], gb, qa) * v.dsp[j];
-            gdz[j] = v.dg[j] * fmaf(r.dskip, v.u[j], y);
-            dDacc = fmaf(v.dy[j], v.u[j], dDacc);
-            dbacc += r.active ? gdd[j] : 0.0f;
-            __syncthreads();
-            // lane (hh, jj) sums term jj over lanes 32 hh .. 32 hh + 31; the halves then meet
-            float sum = 0.0f;
-#pragma unroll 8
-            for (int i = 0; i < 32; ++i) sum += red[(32 * hh + i) * kRedS + jj];
-            sum += __shfl_xor(sum, 32);
-            bcs[j] = sum;
-            __syncthreads();
+            if (lane < 2 * kH) {   // term lane: dB of state kH hf + lane, or dC of state kH hf + lane - kH
+                const int idx = lane < kH ? kH * hf + lane : kN + kH * hf + (lane - kH);
+                float4* o = reinterpret_cast<float4*>(
+                    a.part + (((int64_t)blockIdx.x * a.Bt + b) * (2 * kN) + idx) * a.tpad + t0);
+                o[0] = make_float4(bcs[0], bcs[1], bcs[2], bcs[3]);
+                o[1] = make_float4(bcs[4], bcs[5], bcs[6], bcs[7]);
+            }
+        }
+        float gdu[kBT], gdd[kBT], gdz[kBT];
+#pragma unroll
+        for (int j = 0; j < kBT; ++j) {
+            const float qa = POW ? qaacc[j] * r.An[0] : qaacc[j];
+            gdu[j] = fmaf(v.dt[j], gbacc[j], r.dskip * v.dy[j]);
+            gdd[j] = fmaf(v.u[j], gbacc[j], qa) * v.dsp[j];
+            gdz[j] = v.dg[j] * fmaf(r.dskip, v.u[j], yacc[j]);
+            if (t0 + j < a.L) {
+                dDacc = fmaf(v.dy[j], v.u[j], dDacc);
+                dbacc += r.active ? gdd[j] : 0.0f;
+            }
         }
         if (r.active) {
             const int64_t off = r.row * a.L;
             store_tile<E, VEC>(a.du, off, t0, a.L, gdu);
             store_tile<E, VEC>(a.ddelta, off, t0, a.L, gdd);
             if (HAS_Z && a.dz) store_tile<E, VEC>(a.dz, off, t0, a.L, gdz);
-        }
-        if (lane < 2 * kN) {
-            float4* o = reinterpret_cast<float4*>(
-                a.part + (((int64_t)blockIdx.x * a.Bt + b) * (2 * kN) + lane) * a.tpad + t0);
-            o[0] = make_float4(bcs[0], bcs[1], bcs[2], bcs[3]);
-            o[1] = make_float4(bcs[4], bcs[5], bcs[6], bcs[7]);
         }
     }
     if (r.active) {
@@ -452,10 +568,10 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
 }
 
 template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z>
-__global__ __launch_bounds__(64) void bwd_main_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_main_kernel(BwdArgs a) {
     __shared__ __align__(16) float sbc[kBT * kBCs];
-    __shared__ __align__(16) float hbuf[kBT * kN * 64];
-    __shared__ __align__(16) float red[64 * kRedS];
+    __shared__ __align__(16) float hbuf[kBT * kH * 64];
+    __shared__ __align__(16) float red[2 * kH * 64];
     const Row r = row_of(a);
     if (__all(r.pow_ok)) main_body<E, VEC, SOFTPLUS, HAS_Z, true>(a, r, sbc, hbuf, red);
     else main_body<E, VEC, SOFTPLUS, HAS_Z, false>(a, r, sbc, hbuf, red);
@@ -558,13 +674,14 @@ Layout layout_of(const BwdLaunch& a, int S) {
 
 }  // namespace
 
-// Segments per channel group: about three wavefronts per CU over the launch (the main kernel's
-// LDS holds three per CU), at most one per tile.  MSS_BWD_SEGMENTS overrides.
+// Segments per channel group: as many wavefronts as fit on the chip at once (the main kernel's
+// 21 KB of LDS and 256 VGPRs allow seven per CU), at most one per tile.  MSS_BWD_SEGMENTS
+// overrides.
 int plan_bwd_segments(const BwdLaunch& a, int num_cus) {
     const int64_t groups = a.Bt * ((a.Dn + 63) / 64);
     const int64_t ntiles = (a.L + kBT - 1) / kBT;
-    const int64_t target = 3LL * (num_cus > 0 ? num_cus : 256);
-    int64_t S = groups > 0 ? (target + groups - 1) / groups : 1;
+    const int64_t target = 7LL * (num_cus > 0 ? num_cus : 256);
+    int64_t S = groups > 0 ? target / groups : 1;  // one round: every wavefront resident at once
     const char* env = getenv("MSS_BWD_SEGMENTS");
     if (env && atoi(env) > 0) S = atoi(env);
     if (S > ntiles) S = ntiles;
