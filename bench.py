@@ -148,6 +148,44 @@ def decode_chain(mss, torch, devc, steps=1024, pool=64):
             "note": "state (21 MB) stays resident in the 256 MB Infinity Cache across steps"}
 
 
+def bwd_bytes(Bt, Dn, N, L, es_io=2):
+    """Algorithmic bytes of one backward call: u, delta, z, dout read and du, ddelta, dz
+    written once (dtype of u); B, C read and dB, dC written (fp32); A, D, bias read and dA, dD,
+    dbias written."""
+    io = Bt * Dn * L * es_io
+    return 7 * io + 4 * Bt * N * L * 4 + 2 * (Dn * N * 4 + 2 * Dn * 4)
+
+
+def backward_leg(mss, torch, sets, A, D, bias, Bt, Dn, N, L, fwd_ms, calls=10, warmup=2):
+    """mss_selective_scan_bwd on the same workload (gradients of the forward for a random dout),
+    timed with events on the stream it runs on; input sets rotated as in the forward steps."""
+    gen = torch.Generator(device="cuda:0").manual_seed(1)
+    douts = [torch.randn(p["u"].shape, generator=gen, device="cuda:0").to(torch.bfloat16) for p in sets]
+
+    def call(k):
+        p = sets[k % len(sets)]
+        return mss.selective_scan_bwd(p["u"], p["delta"], A, p["B"], p["C"], douts[k % len(sets)],
+                                      D=D, z=p["z"], delta_bias=bias)
+
+    for k in range(warmup):
+        call(k)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for k in range(calls):
+        ev[k][0].record(stream)
+        call(k)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    avg = sum(ms) / len(ms)
+    nb = bwd_bytes(Bt, Dn, N, L)
+    return {"avg_ms": round(avg, 4), "min_ms": round(min(ms), 4), "calls": calls,
+            "gbps": round(nb / (avg * 1e-3) / 1e9, 2), "algorithmic_bytes": nb,
+            "ratio_to_fwd": round(avg / fwd_ms, 2),
+            "outputs": "du, ddelta, dz (bf16); dA, dB, dC, dD, ddelta_bias (fp32)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +194,7 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="input sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-chain", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build runs the scan on a single MI355X "
@@ -269,6 +308,8 @@ def main():
                                "timed by the library's HIP events on its stream",
                      "algorithmic_flops": flops},
     }
+    if not args.no_bwd:
+        res["scan_bwd"] = backward_leg(mss, torch, sets, A, D, bias, Bt, Dn, N, L, scan_avg_ms)
     if not args.no_decode_chain:
         res["decode_chain"] = decode_chain(mss, torch, devc)
     if not args.no_cpu_baseline:

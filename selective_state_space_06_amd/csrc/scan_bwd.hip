@@ -16,15 +16,18 @@
 // forward.
 //
 // Decomposition (one wavefront per workgroup; lane = channel, 16 states in VGPRs):
-//   * each channel row is cut into S segments of whole 8-step tiles.  An aggregate kernel
-//     gives each segment its forward carry (sum of dt, end state from h = 0) and its adjoint
-//     carry Lambda = sum_t (prod of abar over the segment's steps up to t) dy_t C_t, the part of
+//   * each channel row is cut into S segments of whole 8-step tiles.  An aggregate kernel walks
+//     every segment forward from h = 0 and writes, per tile, a checkpoint (the tile's start
+//     state from h = 0 at the segment start, and the sum of dt so far), and per segment its
+//     forward carry (sum of dt, end state) and its adjoint carry
+//     Lambda = sum_t (prod of abar over the segment's steps up to t) dy_t C_t, the part of
 //     dL/dh that flows out of the segment's first step into the one before;
-//   * the main kernel folds the forward carries of the earlier segments into its start state
-//     and the adjoint carries of the later segments (the same associative operator, taken in
-//     reverse order) into the adjoint entering its last step.  It walks its tiles forward once
-//     storing h at each tile start in a workspace checkpoint, then walks them backward: a
-//     tile's 8 states are recomputed from its checkpoint into LDS and consumed in reverse;
+//   * the main kernel folds the forward carries of the earlier segments into the state h_in
+//     entering its segment and the adjoint carries of the later segments (the same associative
+//     operator, taken in reverse order) into the adjoint entering its last step, then walks its
+//     tiles backward.  A tile's true start state is exp(A sum dt) h_in + its checkpoint (the
+//     recurrence is linear); its states are recomputed from there into LDS, 8 at a time, and
+//     consumed in reverse;
 //   * dB and dC sum over channels: per step the wave's 64 x 32 terms go through LDS and are
 //     summed per wave; a reduction kernel adds the per-wave sums of the channel groups.
 //     dA / dD / dbias are per-lane sums, added over segments and batches by a second kernel.
@@ -41,6 +44,7 @@ constexpr int kBT = 8;            // steps per tile
 constexpr int kAggW = 2 * kN + 1; // aggregate words per (segment, row): sum dt | H[16] | Lambda[16]
 constexpr int kParW = kN + 2;     // partial words per (segment, row): dA[16] | dD | dbias
 constexpr int kBCs = 2 * kN + 4;  // LDS words per step of B | C (16-byte pad)
+constexpr int kCkW = kN + 1;      // checkpoint words per (tile, row): local state[16] | sum dt
 
 struct BwdArgs {
     const void* u;
@@ -56,7 +60,7 @@ struct BwdArgs {
     void* ddelta;
     void* dz;
     float* agg;   // [S][kAggW][R]
-    float* ck;    // [ntiles][kN][R]
+    float* ck;    // [ntiles][kCkW][R]
     float* part;  // [G][Bt][2 kN][tpad]
     float* par;   // [S][kParW][R]
     int64_t Dn, L, R, ntiles, tpad;
@@ -116,11 +120,12 @@ __device__ __forceinline__ void abar16(float dt, const float (&A2)[kN], float (&
 
 constexpr int kH = kN / 2;  // states per half-pass of the backward walk
 
-// abar for the 8 states kH * hf .. kH * hf + 7 of one step.
+// exp2(dt A2_n) for the 8 states kH * hf .. kH * hf + 7; on the power path from a0 = exp2(dt A2_0)
+// by multiplications.
 template <bool POW>
-__device__ __forceinline__ void abar8(float dt, const float (&A2)[kN], int hf, float (&p)[kH]) {
+__device__ __forceinline__ void abar8(float dt, float a0, const float (&A2)[kN], int hf, float (&p)[kH]) {
     if (POW) {
-        const float a = fast_exp2(dt * A2[0]);
+        const float a = a0;
         p[0] = a;
         p[1] = a * a;
         p[2] = p[1] * a;
@@ -338,6 +343,12 @@ __device__ __forceinline__ void agg_body(const BwdArgs& a, const Row& r, float* 
     load_raw<E, VEC, HAS_Z>(a, r, tb * kBT, nx);
     for (int64_t tile = tb; tile < te; ++tile) {
         const int64_t t0 = tile * kBT;
+        if (r.active) {  // checkpoint: the tile's start state from h = 0 at the segment start, sum dt
+            float* ck = a.ck + tile * kCkW * a.R + r.row;
+#pragma unroll
+            for (int n = 0; n < kN; ++n) ck[(int64_t)n * a.R] = H[n];
+            ck[(int64_t)kN * a.R] = dsum;
+        }
         const Raw<E, VEC> cur = nx;
         if (tile + 1 < te) load_raw<E, VEC, HAS_Z>(a, r, t0 + kBT, nx);
         StepVals v;
@@ -406,66 +417,36 @@ __device__ __forceinline__ void carries(const BwdArgs& a, const Row& r, int s, f
 
 template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z, bool POW>
 __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float* sbc, float* hbuf,
-                                          float* red) {
+                                          float* red, float* hin) {
     const int s = blockIdx.z;
     const int lane = threadIdx.x;
     const int b = blockIdx.y;
     int64_t tb, te;
     seg_tiles(s, a.S, a.ntiles, tb, te);
-    float h[kN], gc[kN];
+    float h[kN], gc[kN];  // state entering the segment; adjoint entering its last step
     carries<POW>(a, r, s, h, gc);
-
-    // forward walk: checkpoint h at every tile start
-    Raw<E, VEC> nx;
-    load_raw<E, VEC, HAS_Z>(a, r, tb * kBT, nx);
-    for (int64_t tile = tb; tile < te; ++tile) {
-        const int64_t t0 = tile * kBT;
-        if (r.active) {
-            float* ck = a.ck + tile * kN * a.R + r.row;
-#pragma unroll
-            for (int n = 0; n < kN; ++n) ck[(int64_t)n * a.R] = h[n];
-        }
-        if (tile + 1 == te) break;  // the last tile's end state is not needed
-        const Raw<E, VEC> cur = nx;
-        if (tile + 2 < te) load_raw<E, VEC, HAS_Z>(a, r, t0 + kBT, nx);
-        StepVals v;
-        step_vals<E, VEC, SOFTPLUS, HAS_Z>(a, r, t0, cur, v);
-        __syncthreads();
-        put_bc(cur.bc, sbc);
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < kBT; ++j) {
-            if (t0 + j >= a.L) break;
-            float bv[kN], cv[kN], p[kN];
-            read_bc(sbc, j, bv, cv);
-            abar16<POW>(v.dt[j], r.A2, p);
-#pragma unroll
-            for (int n = 0; n < kN; ++n) h[n] = fmaf(p[n], h[n], v.x[j] * bv[n]);
-        }
-    }
 
     // backward walk
     float dA[kN];
 #pragma unroll
     for (int n = 0; n < kN; ++n) dA[n] = 0.0f;
     float dDacc = 0.0f, dbacc = 0.0f;
-    float ckn[kN];
+    Raw<E, VEC> nx;
     load_raw<E, VEC, HAS_Z>(a, r, (te - 1) * kBT, nx);
 #pragma unroll
-    for (int n = 0; n < kN; ++n) ckn[n] = r.active ? a.ck[((te - 1) * kN + n) * a.R + r.row] : 0.0f;
+    for (int n = 0; n < kN; ++n) hin[n * 64 + lane] = h[n];  // h_in waits in LDS: fewer live VGPRs
     for (int64_t tile = te - 1; tile >= tb; --tile) {
         const int64_t t0 = tile * kBT;
         const Raw<E, VEC> cur = nx;
-        float ck0[kN];
+        float ck0[kCkW];  // loaded here, used after the tile's set-up
 #pragma unroll
-        for (int n = 0; n < kN; ++n) ck0[n] = ckn[n];
-        if (tile > tb) {
-            load_raw<E, VEC, HAS_Z>(a, r, t0 - kBT, nx);
-#pragma unroll
-            for (int n = 0; n < kN; ++n) ckn[n] = r.active ? a.ck[((tile - 1) * kN + n) * a.R + r.row] : 0.0f;
-        }
+        for (int n = 0; n < kCkW; ++n) ck0[n] = r.active ? a.ck[(tile * kCkW + n) * a.R + r.row] : 0.0f;
+        if (tile > tb) load_raw<E, VEC, HAS_Z>(a, r, t0 - kBT, nx);
         StepVals v;
         step_vals<E, VEC, SOFTPLUS, HAS_Z>(a, r, t0, cur, v);
+        float a0[kBT];  // abar_0 of each step (power path)
+#pragma unroll
+        for (int j = 0; j < kBT; ++j) a0[j] = POW ? fast_exp2(v.dt[j] * r.A2[0]) : 0.0f;
         __syncthreads();
         put_bc(cur.bc, sbc);
         __syncthreads();
@@ -477,15 +458,16 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
         for (int j = 0; j < kBT; ++j) yacc[j] = gbacc[j] = qaacc[j] = 0.0f;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            float hs[kH];
+            float hs[kH], pc[kH];  // tile start: exp(A sum dt) h_in + the local checkpoint
+            abar8<POW>(ck0[kN], POW ? fast_exp2(ck0[kN] * r.A2[0]) : 0.0f, r.A2, hf, pc);
 #pragma unroll
-            for (int k = 0; k < kH; ++k) hs[k] = ck0[kH * hf + k];
+            for (int k = 0; k < kH; ++k) hs[k] = fmaf(pc[k], hin[(kH * hf + k) * 64 + lane], ck0[kH * hf + k]);
 #pragma unroll
             for (int j = 0; j < kBT; ++j) {
                 if (t0 + j >= a.L) break;
                 float bv[kH], cv[kH], p[kH];
                 read_bc_half(sbc, j, hf, bv, cv);
-                abar8<POW>(v.dt[j], r.A2, hf, p);
+                abar8<POW>(v.dt[j], a0[j], r.A2, hf, p);
 #pragma unroll
                 for (int k = 0; k < kH; ++k) {
                     hs[k] = fmaf(p[k], hs[k], v.x[j] * bv[k]);
@@ -499,7 +481,7 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
                 if (t0 + j >= a.L) continue;
                 float bv[kH], cv[kH], p[kH], hc[kH];
                 read_bc_half(sbc, j, hf, bv, cv);
-                abar8<POW>(v.dt[j], r.A2, hf, p);
+                abar8<POW>(v.dt[j], a0[j], r.A2, hf, p);
 #pragma unroll
                 for (int k = 0; k < kH; ++k) hc[k] = hbuf[(j * kH + k) * 64 + lane];
                 float y = 0.0f, gb = 0.0f, qa = 0.0f;
@@ -572,9 +554,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     __shared__ __align__(16) float sbc[kBT * kBCs];
     __shared__ __align__(16) float hbuf[kBT * kH * 64];
     __shared__ __align__(16) float red[2 * kH * 64];
+    __shared__ __align__(16) float hin[kN * 64];
     const Row r = row_of(a);
-    if (__all(r.pow_ok)) main_body<E, VEC, SOFTPLUS, HAS_Z, true>(a, r, sbc, hbuf, red);
-    else main_body<E, VEC, SOFTPLUS, HAS_Z, false>(a, r, sbc, hbuf, red);
+    if (__all(r.pow_ok)) main_body<E, VEC, SOFTPLUS, HAS_Z, true>(a, r, sbc, hbuf, red, hin);
+    else main_body<E, VEC, SOFTPLUS, HAS_Z, false>(a, r, sbc, hbuf, red, hin);
 }
 
 // ---------------------------------------------------------------- reductions
@@ -637,7 +620,7 @@ hipError_t zero(float* p, int64_t n, hipStream_t s) {
 template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z>
 hipError_t launch_t(const BwdArgs& k, const BwdLaunch& a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(k.G), static_cast<unsigned>(k.Bt), static_cast<unsigned>(k.S));
-    if (k.S > 1) bwd_agg_kernel<E, VEC, SOFTPLUS, HAS_Z><<<grid, dim3(64), 0, stream>>>(k);
+    bwd_agg_kernel<E, VEC, SOFTPLUS, HAS_Z><<<grid, dim3(64), 0, stream>>>(k);
     bwd_main_kernel<E, VEC, SOFTPLUS, HAS_Z><<<grid, dim3(64), 0, stream>>>(k);
     const int64_t nbc = (int64_t)k.Bt * 2 * kN * k.L;
     bwd_reduce_bc_kernel<<<dim3(grid_for(nbc)), dim3(256), 0, stream>>>(k.part, a.dB, a.dC, k.G, k.Bt, k.L, k.tpad);
@@ -666,7 +649,7 @@ Layout layout_of(const BwdLaunch& a, int S) {
     Layout l;
     l.agg = 0;
     l.ck = l.agg + align256(static_cast<size_t>(S) * kAggW * R * sizeof(float));
-    l.part = l.ck + align256(static_cast<size_t>(ntiles) * kN * R * sizeof(float));
+    l.part = l.ck + align256(static_cast<size_t>(ntiles) * kCkW * R * sizeof(float));
     l.par = l.part + align256(static_cast<size_t>(G) * a.Bt * 2 * kN * ntiles * kBT * sizeof(float));
     l.total = l.par + align256(static_cast<size_t>(S) * kParW * R * sizeof(float));
     return l;
@@ -675,12 +658,12 @@ Layout layout_of(const BwdLaunch& a, int S) {
 }  // namespace
 
 // Segments per channel group: as many wavefronts as fit on the chip at once (the main kernel's
-// 21 KB of LDS and 256 VGPRs allow seven per CU), at most one per tile.  MSS_BWD_SEGMENTS
+// 26 KB of LDS and 256 VGPRs allow six per CU), at most one per tile.  MSS_BWD_SEGMENTS
 // overrides.
 int plan_bwd_segments(const BwdLaunch& a, int num_cus) {
     const int64_t groups = a.Bt * ((a.Dn + 63) / 64);
     const int64_t ntiles = (a.L + kBT - 1) / kBT;
-    const int64_t target = 7LL * (num_cus > 0 ? num_cus : 256);
+    const int64_t target = 6LL * (num_cus > 0 ? num_cus : 256);
     int64_t S = groups > 0 ? target / groups : 1;  // one round: every wavefront resident at once
     const char* env = getenv("MSS_BWD_SEGMENTS");
     if (env && atoi(env) > 0) S = atoi(env);
