@@ -55,6 +55,10 @@ def _load():
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i64p,
                 _d, _d, _d, _d, _d, _d, _d, _d, ctypes.c_int, _d,
                 _d, _d, _d, _d, _d, _d, _d, _d, ctypes.c_int, ctypes.c_int]
+            lib.oracle_causal_conv1d.restype = ctypes.c_int
+            lib.oracle_causal_conv1d.argtypes = [
+                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _d, _d, _d, _d, ctypes.c_int,
+                _d, _d, ctypes.c_int]
             lib.oracle_state_update.restype = ctypes.c_int
             lib.oracle_state_update.argtypes = [
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i64p,
@@ -187,6 +191,34 @@ def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softp
                 dz=None if dz is None else dz.reshape(sh),
                 dA=dA.reshape(Bt, Dn, N).sum(0), dB=dB, dC=dC,
                 dD=dD.reshape(Bt, Dn).sum(0), ddelta_bias=db.reshape(Bt, Dn).sum(0))
+
+
+def causal_conv1d(x, weight, bias=None, state=None, silu=True, rows=None, nthreads: int = 0):
+    """fp64 causal depthwise conv1d (+ silu).
+
+    x: (batch, d_inner, L); weight: (d_inner, K); bias: (d_inner,); state: the K - 1 inputs before
+    t = 0, (batch, d_inner, K - 1), oldest first (default zeros).  Returns (out, final_state):
+    (batch, d_inner, L) and (batch, d_inner, K - 1) -- or (len(rows), ...) with rows.
+    """
+    x = np.asarray(x)
+    Bt, Dn, L = x.shape
+    K = np.asarray(weight).shape[1]
+    sel = np.arange(Bt * Dn, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    ch = sel % Dn
+    xr = _f64(x.reshape(Bt * Dn, L)[sel])
+    st = None if state is None else _f64(np.asarray(state).reshape(Bt * Dn, K - 1)[sel])
+    R = sel.size
+    out = np.empty((R, L))
+    fin = np.empty((R, max(K - 1, 0)))
+    rc = _load().oracle_causal_conv1d(
+        R, L, K, _ptr(xr), _ptr(_f64(np.asarray(weight)[ch])),
+        _ptr(None if bias is None else _f64(np.asarray(bias)[ch])), _ptr(st), int(bool(silu)),
+        _ptr(out), _ptr(fin), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_causal_conv1d rejected its arguments")
+    if rows is None:
+        return out.reshape(Bt, Dn, L), fin.reshape(Bt, Dn, K - 1)
+    return out, fin
 
 
 def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,

@@ -263,6 +263,44 @@ int oracle_selective_scan_bwd(int64_t R, int64_t N, int64_t L, int64_t Bt,
 }
 
 /*
+ * Causal depthwise conv1d with optional silu, the step in front of the scan in the tutorial
+ * page's `MambaBlock` (a Keras Conv1D with groups = channels, kernel_size 4, bias, channels-first
+ * data and padding='causal', then swish; the upstream README's d_conv = 4 "local convolution
+ * width").  Keras's Conv1D is a cross-correlation and 'causal' pads K - 1 zeros on the left, so
+ *     y[t] = bias + sum_{k=0}^{K-1} w[k] * x[t - (K-1) + k],   x[t < 0] = state (else 0)
+ * and w[K-1] multiplies the current input.  Over R rows of length L:
+ *   x, out       R x L
+ *   w            R x K (the row's channel weights), bias R (may be NULL)
+ *   state_in     R x (K-1): the inputs before t = 0, oldest first (NULL: zeros)
+ *   state_out    R x (K-1): the last K-1 inputs (from state_in too when L < K-1), or NULL
+ *   silu_flag    nonzero: out = silu(y)
+ */
+int oracle_causal_conv1d(int64_t R, int64_t L, int64_t K, const double* x, const double* w,
+                         const double* bias, const double* state_in, int silu_flag, double* out,
+                         double* state_out, int nthreads) {
+    if (R < 0 || L < 0 || K < 1) return -1;
+    set_threads(nthreads);
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t r = 0; r < R; ++r) {
+        /* the row with its K - 1 predecessors in front: ext[j] = x[j - (K-1)] */
+        double* ext = (double*)malloc((size_t)(L + K - 1) * sizeof(double));
+        if (!ext) { bad = 1; continue; }
+        for (int64_t j = 0; j < K - 1; ++j) ext[j] = state_in ? state_in[r * (K - 1) + j] : 0.0;
+        for (int64_t t = 0; t < L; ++t) ext[K - 1 + t] = x[r * L + t];
+        for (int64_t t = 0; t < L; ++t) {
+            double y = bias ? bias[r] : 0.0;
+            for (int64_t k = 0; k < K; ++k) y += w[r * K + k] * ext[t + k];
+            out[r * L + t] = silu_flag ? silu(y) : y;
+        }
+        if (state_out)
+            for (int64_t j = 0; j < K - 1; ++j) state_out[r * (K - 1) + j] = ext[L + j];
+        free(ext);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
  * One recurrent (decode) step over R rows, state updated in place.
  *   state      R x N (in/out)
  *   x, dt, z   R (z may be NULL); dt is raw, softplus(dt + dt_bias) is always applied
