@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MSS_VERSION 10200 /* major * 10000 + minor * 100 + patch */
+#define MSS_VERSION 10300 /* major * 10000 + minor * 100 + patch */
 
 typedef enum { MSS_F32 = 0, MSS_BF16 = 1 } mss_dtype_t;
 
@@ -164,6 +164,43 @@ int mss_selective_state_update(const mss_tensor_t* state, const mss_tensor_t* x,
                                const mss_tensor_t* D, const mss_tensor_t* z,
                                const mss_tensor_t* dt_bias, const mss_tensor_t* out,
                                void* stream);
+
+/*
+ * Causal depthwise conv1d (+ silu): the step in front of the scan in the tutorial page's
+ * `MambaBlock` (a Conv1D with one filter per channel, kernel size 4, bias, channels-first data,
+ * causal padding, then swish; the upstream README's d_conv = 4).  Per channel d and step t,
+ *     y[t] = bias[d] + sum_{k=0}^{K-1} weight[d][k] * x[t - (K-1) + k],   out = silu(y) or y,
+ * a cross-correlation whose last tap meets the current input; inputs before t = 0 come from
+ * initial_state (zeros when NULL).
+ *   x              (batch, d_inner, L)        f32 or bf16
+ *   weight         (d_inner, K)               f32, 1 <= K <= 4 (MSS_ERR_UNSUPPORTED above)
+ *   bias           (d_inner,)                 f32, nullable (0)
+ *   initial_state  (batch, d_inner, K - 1)    dtype of x, nullable: the K - 1 inputs before t = 0,
+ *                                             oldest first
+ *   silu_flag      nonzero: out = silu(y)
+ *   out            (batch, d_inner, L)        dtype of x, written
+ *   final_state    (batch, d_inner, K - 1)    dtype of x, nullable: written with the last K - 1
+ *                                             inputs (older ones from initial_state when L < K - 1)
+ * Chunked prefill: pass one chunk's final_state as the next chunk's initial_state (a different
+ * buffer: out and final_state may not overlap an input or each other, MSS_ERR_ALIAS).
+ */
+int mss_causal_conv1d_fwd(const mss_tensor_t* x, const mss_tensor_t* weight,
+                          const mss_tensor_t* bias, const mss_tensor_t* initial_state,
+                          int silu_flag, const mss_tensor_t* out,
+                          const mss_tensor_t* final_state, void* stream);
+
+/*
+ * The same conv for one token per row, with the K - 1 previous inputs kept in `state`, which is
+ * updated in place (the window moves by one: the oldest input drops out, x comes in).
+ *   state   (batch, d_inner, K - 1)   dtype of x, read and written
+ *   x       (batch, d_inner)          f32 or bf16
+ *   weight  (d_inner, K) f32; bias (d_inner,) f32 nullable; silu_flag as above
+ *   out     (batch, d_inner)          dtype of x, written
+ * out and the state may not overlap an input or each other.
+ */
+int mss_causal_conv1d_update(const mss_tensor_t* state, const mss_tensor_t* x,
+                             const mss_tensor_t* weight, const mss_tensor_t* bias, int silu_flag,
+                             const mss_tensor_t* out, void* stream);
 
 /*
  * Launch timing, for measurement only (the results of the calls above do not depend on it).

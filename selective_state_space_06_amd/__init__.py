@@ -9,6 +9,10 @@ from ._binding import (  # noqa: F401
     MSS_BF16,
     MSS_F32,
     MssError,
+    causal_conv1d_fwd,
+    causal_conv1d_update,
+    conv1d_fwd_raw,
+    conv1d_update_raw,
     Tensor,
     load_library,
     profile_enable,

@@ -18,7 +18,7 @@ STATUS = {0: "MSS_OK", -1: "MSS_ERR_NULL_ARG", -2: "MSS_ERR_SHAPE", -3: "MSS_ERR
 
 # every symbol include/mamba_scan.h declares
 EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_fwd_with_state", "mss_selective_scan_bwd",
-           "mss_selective_state_update", "mss_profile_enable", "mss_profile_fwd",
+           "mss_selective_state_update", "mss_causal_conv1d_fwd", "mss_causal_conv1d_update", "mss_profile_enable", "mss_profile_fwd",
            "mss_status_string", "mss_version")
 
 
@@ -75,6 +75,12 @@ def load_library(path: str = LIB_PATH):
             lib.mss_selective_scan_bwd.argtypes = [
                 _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, ctypes.c_int, _TP,
                 _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, ctypes.c_void_p]
+            lib.mss_causal_conv1d_fwd.restype = ctypes.c_int
+            lib.mss_causal_conv1d_fwd.argtypes = [_TP, _TP, _TP, _TP, ctypes.c_int, _TP, _TP,
+                                                  ctypes.c_void_p]
+            lib.mss_causal_conv1d_update.restype = ctypes.c_int
+            lib.mss_causal_conv1d_update.argtypes = [_TP, _TP, _TP, _TP, ctypes.c_int, _TP,
+                                                     ctypes.c_void_p]
             lib.mss_selective_state_update.restype = ctypes.c_int
             lib.mss_selective_state_update.argtypes = [_TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP,
                                                        _TP, _TP, ctypes.c_void_p]
@@ -144,6 +150,19 @@ def scan_bwd_raw(u, delta, A, B, C, D, z, delta_bias, softplus_flag, dout, du, d
         _ref(dD), _ref(dz), _ref(ddelta_bias), stream)
 
 
+def conv1d_fwd_raw(x, weight, bias, initial_state, silu_flag, out, final_state, stream) -> int:
+    """Direct call of mss_causal_conv1d_fwd with Tensor descriptors (or None)."""
+    return load_library().mss_causal_conv1d_fwd(
+        _ref(x), _ref(weight), _ref(bias), _ref(initial_state), int(silu_flag), _ref(out),
+        _ref(final_state), stream)
+
+
+def conv1d_update_raw(state, x, weight, bias, silu_flag, out, stream) -> int:
+    """Direct call of mss_causal_conv1d_update with Tensor descriptors (or None)."""
+    return load_library().mss_causal_conv1d_update(
+        _ref(state), _ref(x), _ref(weight), _ref(bias), int(silu_flag), _ref(out), stream)
+
+
 def state_update_raw(state, x, dt, A, B, C, D, z, dt_bias, out, stream) -> int:
     """Direct call of mss_selective_state_update with Tensor descriptors (or None)."""
     return load_library().mss_selective_state_update(
@@ -185,6 +204,42 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
     if st != 0:
         raise MssError(st, "mss_selective_scan_fwd")
     return (out, last_state) if return_last_state else out
+
+
+def causal_conv1d_fwd(x, weight, bias=None, initial_state=None, silu=True, out=None,
+                      return_final_state=False, final_state=None):
+    """Causal depthwise conv1d (+ silu) on the current stream.  x: (batch, d_inner, L) float32
+    or bfloat16; weight: (d_inner, K) float32, K <= 4; bias: (d_inner,) float32; initial_state:
+    (batch, d_inner, K - 1) in x's dtype.  Returns out, or (out, final_state)."""
+    import torch
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    if return_final_state and final_state is None:
+        final_state = torch.empty((x.shape[0], x.shape[1], weight.shape[1] - 1), dtype=x.dtype,
+                                  device=x.device)
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        st = conv1d_fwd_raw(_desc(x), _desc(weight), _desc(bias), _desc(initial_state),
+                            1 if silu else 0, _desc(out),
+                            _desc(final_state) if return_final_state else None, stream)
+    if st != 0:
+        raise MssError(st, "mss_causal_conv1d_fwd")
+    return (out, final_state) if return_final_state else out
+
+
+def causal_conv1d_update(state, x, weight, bias=None, silu=True, out=None):
+    """One token of the conv per row; `state` (batch, d_inner, K - 1) in x's dtype is updated in
+    place.  x: (batch, d_inner).  Returns out (batch, d_inner)."""
+    import torch
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        st = conv1d_update_raw(_desc(state), _desc(x), _desc(weight), _desc(bias),
+                               1 if silu else 0, _desc(out), stream)
+    if st != 0:
+        raise MssError(st, "mss_causal_conv1d_update")
+    return out
 
 
 def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmamba_scan.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["abi.hip", "scan_fwd.hip", "scan_fast.hip", "scan_bwd.hip", "state_update.hip"]
+SOURCES = ["abi.hip", "scan_fwd.hip", "scan_fast.hip", "scan_bwd.hip", "state_update.hip", "conv1d.hip"]
 ARCH = "gfx950"
 
 

@@ -295,6 +295,67 @@ int validate_bwd(const mss_tensor_t* u, const mss_tensor_t* delta, const mss_ten
     return MSS_OK;
 }
 
+constexpr int kMaxConvK = 4;
+
+int validate_conv_fwd(const mss_tensor_t* x, const mss_tensor_t* w, const mss_tensor_t* bias,
+                      const mss_tensor_t* st_in, const mss_tensor_t* out, const mss_tensor_t* st_out) {
+    {
+        const mss_tensor_t* const req[] = {x, w, out};
+        const int s = check_descs(req, {bias, st_in, st_out});
+        if (s != MSS_OK) return s;
+    }
+    if (x->ndim != 3 || w->ndim != 2) return MSS_ERR_SHAPE;
+    const int64_t Bt = x->shape[0], Dn = x->shape[1], L = x->shape[2], K = w->shape[1];
+    if (Bt < 0 || Dn < 0 || L < 0 || K < 1) return MSS_ERR_SHAPE;
+    if (!shape_is(*w, 2, Dn, K) || !shape_is(*out, 3, Bt, Dn, L)) return MSS_ERR_SHAPE;
+    if (bias && !shape_is(*bias, 1, Dn)) return MSS_ERR_SHAPE;
+    for (const mss_tensor_t* t : {st_in, st_out})
+        if (t && !shape_is(*t, 3, Bt, Dn, K - 1)) return MSS_ERR_SHAPE;
+    if (x->dtype != MSS_F32 && x->dtype != MSS_BF16) return MSS_ERR_DTYPE;
+    for (const mss_tensor_t* t : {out, st_in, st_out})
+        if (t && t->dtype != x->dtype) return MSS_ERR_DTYPE;
+    if (w->dtype != MSS_F32 || (bias && bias->dtype != MSS_F32)) return MSS_ERR_DTYPE;
+    for (const mss_tensor_t* t : {x, w, bias, st_in, out, st_out}) {
+        if (!t) continue;
+        if (!dense(*t) || !aligned(*t, elem_size(t->dtype))) return MSS_ERR_LAYOUT;
+    }
+    for (const mss_tensor_t* t : {x, w, bias, st_in}) {
+        if (overlap(out, t)) return MSS_ERR_ALIAS;
+        if (st_out && overlap(st_out, t)) return MSS_ERR_ALIAS;
+    }
+    if (st_out && overlap(st_out, out)) return MSS_ERR_ALIAS;
+    if (K > kMaxConvK) return MSS_ERR_UNSUPPORTED;
+    return MSS_OK;
+}
+
+int validate_conv_update(const mss_tensor_t* st, const mss_tensor_t* x, const mss_tensor_t* w,
+                         const mss_tensor_t* bias, const mss_tensor_t* out) {
+    {
+        const mss_tensor_t* const req[] = {st, x, w, out};
+        const int s = check_descs(req, {bias});
+        if (s != MSS_OK) return s;
+    }
+    if (x->ndim != 2 || w->ndim != 2) return MSS_ERR_SHAPE;
+    const int64_t Bt = x->shape[0], Dn = x->shape[1], K = w->shape[1];
+    if (Bt < 0 || Dn < 0 || K < 1) return MSS_ERR_SHAPE;
+    if (!shape_is(*w, 2, Dn, K) || !shape_is(*out, 2, Bt, Dn) || !shape_is(*st, 3, Bt, Dn, K - 1))
+        return MSS_ERR_SHAPE;
+    if (bias && !shape_is(*bias, 1, Dn)) return MSS_ERR_SHAPE;
+    if (x->dtype != MSS_F32 && x->dtype != MSS_BF16) return MSS_ERR_DTYPE;
+    if (st->dtype != x->dtype || out->dtype != x->dtype) return MSS_ERR_DTYPE;
+    if (w->dtype != MSS_F32 || (bias && bias->dtype != MSS_F32)) return MSS_ERR_DTYPE;
+    for (const mss_tensor_t* t : {st, x, w, bias, out}) {
+        if (!t) continue;
+        if (!dense(*t) || !aligned(*t, elem_size(t->dtype))) return MSS_ERR_LAYOUT;
+    }
+    for (const mss_tensor_t* t : {x, w, bias}) {
+        if (overlap(out, t) || overlap(st, t)) return MSS_ERR_ALIAS;
+    }
+    if (overlap(out, st)) return MSS_ERR_ALIAS;
+    if (K > kMaxConvK) return MSS_ERR_UNSUPPORTED;
+    return MSS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -436,6 +497,54 @@ int mss_selective_scan_bwd(const mss_tensor_t* u, const mss_tensor_t* delta, con
         float* ws = nullptr;
         if (bytes > 0 && workspace(dev, stream, bytes, &ws) != hipSuccess) return MSS_ERR_HIP;
         return mss::launch_scan_bwd(a, segments, ws, s) == hipSuccess ? MSS_OK : MSS_ERR_HIP;
+    } catch (...) {
+        return MSS_ERR_HIP;
+    }
+}
+
+int mss_causal_conv1d_fwd(const mss_tensor_t* x, const mss_tensor_t* weight, const mss_tensor_t* bias,
+                          const mss_tensor_t* initial_state, int silu_flag, const mss_tensor_t* out,
+                          const mss_tensor_t* final_state, void* stream) {
+    try {
+        const int st = validate_conv_fwd(x, weight, bias, initial_state, out, final_state);
+        if (st != MSS_OK) return st;
+        mss::ConvLaunch a;
+        a.x = x->data;
+        a.w = static_cast<const float*>(weight->data);
+        a.bias = bias ? static_cast<const float*>(bias->data) : nullptr;
+        a.state_in = (initial_state && numel(*initial_state) > 0) ? initial_state->data : nullptr;
+        a.out = out->data;
+        a.state_out = (final_state && numel(*final_state) > 0) ? final_state->data : nullptr;
+        a.Dn = x->shape[1]; a.L = x->shape[2]; a.R = x->shape[0] * x->shape[1];
+        a.K = static_cast<int>(weight->shape[1]);
+        a.silu = silu_flag != 0;
+        a.bf16 = x->dtype == MSS_BF16;
+        a.vec_ok = (a.L * static_cast<int64_t>(elem_size(x->dtype))) % 16 == 0 && aligned(*x, 16) &&
+                   aligned(*out, 16);
+        if (a.R == 0) return MSS_OK;
+        return mss::launch_conv1d_fwd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MSS_OK : MSS_ERR_HIP;
+    } catch (...) {
+        return MSS_ERR_HIP;
+    }
+}
+
+int mss_causal_conv1d_update(const mss_tensor_t* state, const mss_tensor_t* x, const mss_tensor_t* weight,
+                             const mss_tensor_t* bias, int silu_flag, const mss_tensor_t* out, void* stream) {
+    try {
+        const int st = validate_conv_update(state, x, weight, bias, out);
+        if (st != MSS_OK) return st;
+        mss::ConvUpdateLaunch a;
+        a.state = state->data;
+        a.x = x->data;
+        a.w = static_cast<const float*>(weight->data);
+        a.bias = bias ? static_cast<const float*>(bias->data) : nullptr;
+        a.out = out->data;
+        a.Dn = x->shape[1]; a.R = x->shape[0] * x->shape[1];
+        a.K = static_cast<int>(weight->shape[1]);
+        a.silu = silu_flag != 0;
+        a.bf16 = x->dtype == MSS_BF16;
+        if (a.R == 0) return MSS_OK;
+        return mss::launch_conv1d_update(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MSS_OK : MSS_ERR_HIP;
     } catch (...) {
         return MSS_ERR_HIP;
     }

@@ -76,6 +76,30 @@ struct BwdLaunch {
     bool vec_ok;            // rows of u / delta / z / dout / du / ddelta / dz and B / C 16-byte aligned
 };
 
+struct ConvLaunch {
+    const void* x;          // (Bt, Dn, L)
+    const float* w;         // (Dn, K)
+    const float* bias;      // nullable
+    const void* state_in;   // (Bt, Dn, K-1), nullable
+    void* out;
+    void* state_out;        // (Bt, Dn, K-1), nullable
+    int64_t Dn, L, R;       // R = Bt * Dn
+    int K;
+    bool silu, bf16;
+    bool vec_ok;            // rows of x / out span whole 16-byte vectors, 16-byte aligned
+};
+
+struct ConvUpdateLaunch {
+    void* state;            // (Bt, Dn, K-1), in/out
+    const void* x;          // (Bt, Dn)
+    const float* w;
+    const float* bias;
+    void* out;
+    int64_t Dn, R;
+    int K;
+    bool silu, bf16;
+};
+
 // How the forward scan is decomposed along L: `segments` workgroup-rows per channel
 // group, each covering `seg_len` steps (a multiple of the time tile).
 struct ScanPlan {
@@ -98,6 +122,9 @@ size_t fast_workspace_bytes(const ScanLaunch& a, int segments);
 hipError_t launch_scan_fast(const ScanLaunch& a, const ScanPlan& plan, float* workspace,
                             hipStream_t stream);
 hipError_t launch_state_update(const DecodeLaunch& a, hipStream_t stream);
+// Causal conv1d: conv1d.hip.
+hipError_t launch_conv1d_fwd(const ConvLaunch& a, hipStream_t stream);
+hipError_t launch_conv1d_update(const ConvUpdateLaunch& a, hipStream_t stream);
 // Backward scan: scan_bwd.hip.
 int plan_bwd_segments(const BwdLaunch& a, int num_cus);
 size_t bwd_workspace_bytes(const BwdLaunch& a, int segments);

@@ -338,6 +338,82 @@ def test_bwd_nothing_to_write_is_ok(lib):
     assert call_bwd(a) == OK
 
 
+# --------------------------------------------------------------------- causal conv1d
+
+def conv_args(dtype=MSS_BF16, K=4):
+    es = 2 if dtype == MSS_BF16 else 4
+    big = BT * DN * L
+    return dict(
+        x=Tensor.make(addr(big * es), dtype, [BT, DN, L]),
+        weight=Tensor.make(addr(DN * K * 4), MSS_F32, [DN, K]),
+        bias=Tensor.make(addr(DN * 4), MSS_F32, [DN]),
+        initial_state=Tensor.make(addr(BT * DN * (K - 1) * es), dtype, [BT, DN, K - 1]),
+        silu_flag=1,
+        out=Tensor.make(addr(big * es), dtype, [BT, DN, L]),
+        final_state=Tensor.make(addr(BT * DN * (K - 1) * es), dtype, [BT, DN, K - 1]),
+        stream=None)
+
+
+def call_conv(a):
+    return mss.conv1d_fwd_raw(a["x"], a["weight"], a["bias"], a["initial_state"], a["silu_flag"],
+                              a["out"], a["final_state"], a["stream"])
+
+
+@pytest.mark.parametrize("name", ["x", "weight", "out"])
+def test_conv_null_required(lib, name):
+    a = conv_args()
+    a[name] = None
+    assert call_conv(a) == NULL_ARG
+
+
+@pytest.mark.parametrize("name,shape", [
+    ("weight", [DN + 1, 4]), ("bias", [DN - 1]), ("initial_state", [BT, DN, 4]),
+    ("out", [BT, DN, L - 1]), ("final_state", [BT, DN, 2])])
+def test_conv_shape(lib, name, shape):
+    a = conv_args()
+    t = a[name]
+    a[name] = Tensor.make(t.data, t.dtype, shape)
+    assert call_conv(a) == SHAPE
+
+
+@pytest.mark.parametrize("name,dtype", [("weight", MSS_BF16), ("bias", MSS_BF16), ("out", MSS_F32),
+                                        ("initial_state", MSS_F32), ("final_state", MSS_F32),
+                                        ("x", 9)])
+def test_conv_dtype(lib, name, dtype):
+    a = conv_args()
+    a[name].dtype = dtype
+    assert call_conv(a) == DTYPE
+
+
+@pytest.mark.parametrize("out,other", [("out", "x"), ("final_state", "initial_state"),
+                                       ("final_state", "out"), ("out", "weight")])
+def test_conv_alias(lib, out, other):
+    a = conv_args()
+    a[out].data = a[other].data
+    assert call_conv(a) == ALIAS
+
+
+def test_conv_wide_kernel_unsupported(lib):
+    assert call_conv(conv_args(K=5)) == UNSUPPORTED
+
+
+def test_conv_update_validation(lib):
+    es = 2
+    rows = BT * DN
+    a = dict(state=Tensor.make(addr(rows * 3 * es), MSS_BF16, [BT, DN, 3]),
+             x=Tensor.make(addr(rows * es), MSS_BF16, [BT, DN]),
+             w=Tensor.make(addr(DN * 16), MSS_F32, [DN, 4]),
+             out=Tensor.make(addr(rows * es), MSS_BF16, [BT, DN]))
+    call = lambda a: mss.conv1d_update_raw(a["state"], a["x"], a["w"], None, 1, a["out"], None)
+    bad = dict(a, state=Tensor.make(a["state"].data, MSS_BF16, [BT, DN, 4]))
+    assert call(bad) == SHAPE
+    bad = dict(a, out=Tensor.make(a["x"].data, MSS_BF16, [BT, DN]))
+    assert call(bad) == ALIAS
+    bad = dict(a, state=Tensor.make(a["state"].data, MSS_F32, [BT, DN, 3]))
+    assert call(bad) == DTYPE
+    assert mss.conv1d_update_raw(None, a["x"], a["w"], None, 1, a["out"], None) == NULL_ARG
+
+
 # --------------------------------------------------------------------- decode step
 
 def dec_args(dtype=MSS_BF16, n=N):
