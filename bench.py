@@ -186,6 +186,40 @@ def backward_leg(mss, torch, sets, A, D, bias, Bt, Dn, N, L, fwd_ms, calls=10, w
             "outputs": "du, ddelta, dz (bf16); dA, dB, dC, dD, ddelta_bias (fp32)"}
 
 
+def conv_leg(mss, torch, devc, Bt, Dn, L, K=4, calls=20, warmup=3, copies=3):
+    """mss_causal_conv1d_fwd (K = 4, bias, silu, final state) on the same layer shape with bf16
+    x / out: a streaming kernel, priced against HBM (x read once, out written once)."""
+    gen = torch.Generator(device=devc).manual_seed(2)
+    xs = [torch.randn((Bt, Dn, L), generator=gen, device=devc).to(torch.bfloat16) for _ in range(copies)]
+    w = torch.randn((Dn, K), generator=gen, device=devc) * 0.5
+    b = torch.randn((Dn,), generator=gen, device=devc)
+    outs = [torch.empty_like(x) for x in xs]
+    fin = torch.empty((Bt, Dn, K - 1), dtype=torch.bfloat16, device=devc)
+
+    def call(k):
+        mss.causal_conv1d_fwd(xs[k % copies], w, b, out=outs[k % copies], return_final_state=True,
+                              final_state=fin)
+
+    for k in range(warmup):
+        call(k)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for k in range(calls):
+        ev[k][0].record(stream)
+        call(k)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(c) for a, c in ev]
+    avg = sum(ms) / len(ms)
+    nb = 2 * Bt * Dn * L * 2 + Dn * K * 4 + Dn * 4 + Bt * Dn * (K - 1) * 2
+    gbps = nb / (avg * 1e-3) / 1e9
+    return {"avg_us": round(avg * 1e3, 2), "min_us": round(min(ms) * 1e3, 2), "calls": calls,
+            "algorithmic_bytes": nb,
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,6 +229,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-chain", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-conv", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build runs the scan on a single MI355X "
@@ -310,6 +345,8 @@ def main():
     }
     if not args.no_bwd:
         res["scan_bwd"] = backward_leg(mss, torch, sets, A, D, bias, Bt, Dn, N, L, scan_avg_ms)
+    if not args.no_conv:
+        res["conv1d"] = conv_leg(mss, torch, devc, Bt, Dn, L)
     if not args.no_decode_chain:
         res["decode_chain"] = decode_chain(mss, torch, devc)
     if not args.no_cpu_baseline:

@@ -11,9 +11,9 @@
 //
 // Forward layout: one thread per 16-byte vector of a row, consecutive threads on consecutive
 // vectors (a wave reads 1 KB of one row in one go), so the conv is a pure streaming kernel: each
-// input read once, each output written once.  A thread's K - 1 left neighbours are the last
-// elements of the previous thread's vector (a cross-lane shuffle); the first lane of a wave
-// reads them from memory, and a row's first vector takes them from the carried state.
+// input read once from memory, each output written once.  A thread's K - 1 left neighbours are
+// the tail of the previous vector, which the thread loads as well (its neighbour's line, already
+// on its way); a row's first vector takes them from the carried state.
 #include <cstdlib>
 
 #include "device_math.hpp"
@@ -41,34 +41,25 @@ __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(ConvArgs a) {
     const int64_t nv = a.L / V;                 // vectors per row
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t total = a.R * nv;
-    const bool live = g < total;
-    const int64_t gc = live ? g : total - 1;     // clamped: every lane takes part in the shuffle
-    const int64_t r = gc / nv, q = gc % nv;
+    if (g >= total) return;
+    const int64_t r = g / nv, q = g % nv;
     const int64_t d = r % a.Dn;
     const auto* xs = static_cast<const typename E::storage*>(a.x);
+    // this thread's vector and the one before it in the row (a cache hit: the neighbouring lane
+    // loads it too), both issued before either is used
     const uint4 raw = *reinterpret_cast<const uint4*>(xs + r * a.L + q * V);
-    float v[V];
+    uint4 praw = make_uint4(0, 0, 0, 0);
+    if (q > 0) praw = *reinterpret_cast<const uint4*>(xs + r * a.L + (q - 1) * V);
+    float v[V], pv[V];
     E::unpack(raw, v);
+    E::unpack(praw, pv);
 
-    // the K - 1 inputs before this vector, oldest first
+    // the K - 1 inputs before this vector, oldest first: the previous vector's tail, or at a row
+    // start the carried state (zeros without one)
     float halo[kMaxK - 1];
-    {
-        float prev[kMaxK - 1];
-        // last K - 1 elements of the previous lane's vector
 #pragma unroll
-        for (int j = 0; j < K - 1; ++j) prev[j] = __shfl_up(v[V - (K - 1) + j], 1);
-        const int lane = threadIdx.x & 63;
-#pragma unroll
-        for (int j = 0; j < K - 1; ++j) {
-            float h = prev[j];
-            if (q == 0) {
-                h = a.state_in ? E::load1(a.state_in, r * (K - 1) + j) : 0.0f;
-            } else if (lane == 0) {
-                h = E::load1(a.x, r * a.L + q * V - (K - 1) + j);
-            }
-            halo[j] = h;
-        }
-    }
+    for (int j = 0; j < K - 1; ++j)
+        halo[j] = q > 0 ? pv[V - (K - 1) + j] : (a.state_in ? E::load1(a.state_in, r * (K - 1) + j) : 0.0f);
     float wk[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) wk[k] = a.w[d * K + k];
@@ -84,7 +75,6 @@ __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(ConvArgs a) {
         }
         o[e] = SILU ? silu(y) : y;
     }
-    if (!live) return;
     auto* os = static_cast<typename E::storage*>(a.out);
     *reinterpret_cast<uint4*>(os + r * a.L + q * V) = E::pack(o);
     if (a.state_out && q == nv - 1) {
