@@ -49,7 +49,7 @@ def _load():
             lib.oracle_selective_scan.restype = ctypes.c_int
             lib.oracle_selective_scan.argtypes = [
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i64p,
-                _d, _d, _d, _d, _d, _d, _d, _d, ctypes.c_int, _d, _d, _d, ctypes.c_int]
+                _d, _d, _d, _d, _d, _d, _d, _d, ctypes.c_int, _d, _i64p, _d, _d, ctypes.c_int]
             lib.oracle_selective_scan_bwd.restype = ctypes.c_int
             lib.oracle_selective_scan_bwd.argtypes = [
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i64p,
@@ -102,12 +102,14 @@ def silu(x) -> np.ndarray:
 
 
 def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus_flag=True,
-                   rows=None, nthreads: int = 0, h0=None):
+                   rows=None, nthreads: int = 0, h0=None, seq_lens=None):
     """Run the fp64 scan.
 
     u, delta, z: (batch, d_inner, L); A: (d_inner, d_state); B, C: (batch, d_state, L);
     D, delta_bias: (d_inner,).  Any float dtype; values are taken exactly as float64.
     h0: optional starting state (batch, d_inner, d_state) (default zeros).
+    seq_lens: optional (batch,) lengths (clamped to [0, L]): steps stop there, outputs past the
+    end are 0 and last_state is the state after the batch's own last step.
     rows: optional flat row indices r = b * d_inner + d to compute (default: all rows).
     Returns (out, last_state): (batch, d_inner, L) and (batch, d_inner, d_state) when rows
     is None, else (len(rows), L) and (len(rows), d_state).
@@ -131,13 +133,15 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus_
     b_r = None if delta_bias is None else _f64(np.asarray(delta_bias)[ch])
     Bm, Cm = _f64(B), _f64(C)
     h0_r = None if h0 is None else _f64(np.asarray(h0).reshape(Bt * Dn, N)[sel])
+    len_r = None if seq_lens is None else np.ascontiguousarray(
+        np.asarray(seq_lens, dtype=np.int64)[rb])
     R = sel.size
     out = np.empty((R, L), np.float64)
     last = np.empty((R, N), np.float64)
     rc = _load().oracle_selective_scan(
         R, N, L, Bt, rb.ctypes.data_as(_i64p), _ptr(u_r), _ptr(dl_r), _ptr(z_r), _ptr(A_r),
-        _ptr(Bm), _ptr(Cm), _ptr(D_r), _ptr(b_r), int(bool(softplus_flag)), _ptr(h0_r), _ptr(out),
-        _ptr(last), int(nthreads))
+        _ptr(Bm), _ptr(Cm), _ptr(D_r), _ptr(b_r), int(bool(softplus_flag)), _ptr(h0_r),
+        None if len_r is None else len_r.ctypes.data_as(_i64p), _ptr(out), _ptr(last), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_selective_scan rejected its arguments")
     if rows is None:

@@ -23,7 +23,9 @@
  * independent and are the only thing run in parallel.
  *
  * A scan may also start from a given state h_0 instead of zeros (prefill continued in chunks:
- * the recurrence itself is unchanged, only its first h_{t-1} differs).
+ * the recurrence itself is unchanged, only its first h_{t-1} differs), and a row may be shorter
+ * than L (row_len[r], sequences of different lengths in one batch): its steps stop there, its
+ * outputs past the end are 0 and last_state is the state after its own last step.
  *
  * Parity pins (all in tests/test_oracle_pins.py, each independent of this loop): the L = 1
  * closed form; the LTI case against a brute-force convolution with kernel
@@ -89,7 +91,8 @@ int oracle_selective_scan(int64_t R, int64_t N, int64_t L, int64_t Bt,
                           const double* u, const double* delta, const double* z,
                           const double* A, const double* Bm, const double* Cm,
                           const double* D, const double* bias, int softplus_flag,
-                          const double* h0, double* out, double* last_state, int nthreads) {
+                          const double* h0, const int64_t* row_len, double* out,
+                          double* last_state, int nthreads) {
     if (R < 0 || N <= 0 || L < 0 || Bt <= 0) return -1;
     set_threads(nthreads);
     int bad = 0;
@@ -106,7 +109,9 @@ int oracle_selective_scan(int64_t R, int64_t N, int64_t L, int64_t Bt,
         const double* Cb = Cm + b * N * L;
         const double Dr = D ? D[r] : 0.0;
         const double br = bias ? bias[r] : 0.0;
-        for (int64_t t = 0; t < L; ++t) {
+        const int64_t Lr = row_len ? (row_len[r] < 0 ? 0 : (row_len[r] > L ? L : row_len[r])) : L;
+        for (int64_t t = Lr; t < L; ++t) out[r * L + t] = 0.0;           /* past the row's end */
+        for (int64_t t = 0; t < Lr; ++t) {
             const double ut = u[r * L + t];
             const double pre = delta[r * L + t] + br;
             const double dt = softplus_flag ? sp(pre) : pre;

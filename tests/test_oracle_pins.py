@@ -342,6 +342,50 @@ def test_chunked_scan_equals_one_scan(oracle_mod, cut):
     _close(h2, last, rtol=1e-12, atol=1e-14)
 
 
+# ---------------------------------------------------------------- sequences of different lengths
+
+def test_varlen_rows_equal_truncated_scans(oracle_mod):
+    """Batch b with length l_b: its outputs are the scan of the first l_b steps, then zeros."""
+    s = _small(seed=31, Bt=4, Dn=3, N=5, L=21)
+    lens = np.array([0, 1, 13, 21])
+    h0 = np.random.default_rng(31).standard_normal((4, 3, 5))
+    out, last = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias,
+                                          h0=h0, seq_lens=lens)
+    for b, lb in enumerate(lens):
+        sl = (slice(b, b + 1), Ellipsis, slice(0, lb))
+        o, h = oracle_mod.selective_scan(s.u[sl], s.delta[sl], s.A, s.B[sl], s.C[sl], s.D,
+                                         s.z[sl], s.delta_bias, h0=h0[b:b + 1])
+        assert np.array_equal(out[b, :, :lb], o[0]) and np.array_equal(last[b], h[0])
+        assert not np.any(out[b, :, lb:])
+    assert np.array_equal(last[0], h0[0])                      # empty sequence: state unchanged
+
+
+def test_varlen_last_state_unrolled(oracle_mod):
+    """last_state of a shortened row against the unrolled sum over its own steps only."""
+    s = _small(seed=32, Bt=2, Dn=2, N=4, L=15)
+    lens = np.array([9, 15])
+    _, last = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias,
+                                        seq_lens=lens)
+    b, lb = 0, 9
+    for d in range(2):
+        dl = _np_softplus(s.delta[b, d].astype(np.float64) + s.delta_bias[d])
+        h = np.zeros(4)
+        for s_ in range(lb):
+            h += np.exp(s.A[d] * np.sum(dl[s_ + 1: lb])) * dl[s_] * s.B[b, :, s_] * s.u[b, d, s_]
+        np.testing.assert_allclose(last[b, d], h, rtol=1e-11, atol=1e-13)
+
+
+def test_varlen_full_and_clamped_lengths(oracle_mod):
+    s = _small(seed=33, L=11)
+    a = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias)
+    b = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias,
+                                  seq_lens=np.array([11, 50]))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    c = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias,
+                                  seq_lens=np.array([-3, 0]))
+    assert not np.any(c[0]) and not np.any(c[1])
+
+
 # ---------------------------------------------------------------- input generator
 
 def test_inputs_are_deterministic_and_seeded():
