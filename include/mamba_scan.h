@@ -40,9 +40,9 @@
 extern "C" {
 #endif
 
-#define MSS_VERSION 10300 /* major * 10000 + minor * 100 + patch */
+#define MSS_VERSION 10400 /* major * 10000 + minor * 100 + patch */
 
-typedef enum { MSS_F32 = 0, MSS_BF16 = 1 } mss_dtype_t;
+typedef enum { MSS_F32 = 0, MSS_BF16 = 1, MSS_I32 = 2 } mss_dtype_t;  /* I32: lengths only */
 
 typedef enum {
     MSS_OK = 0,
@@ -109,6 +109,27 @@ int mss_selective_scan_fwd_with_state(const mss_tensor_t* u, const mss_tensor_t*
                                       const mss_tensor_t* initial_state, int softplus_flag,
                                       const mss_tensor_t* out, const mss_tensor_t* last_state,
                                       void* stream);
+
+/*
+ * mss_selective_scan_fwd_with_state for a batch of sequences of different lengths (prompts of
+ * different lengths prefilled together, each handing its own final state to decode): batch b's
+ * sequence is steps [0, seq_lens[b]) of its rows.  Its steps stop there, last_state[b] is the
+ * state after its own last step, and out[b, :, t] is 0 for t >= seq_lens[b].  Since step t
+ * depends on the past only through h_{t-1}, these are the results of scanning each sequence on
+ * its own (the tutorial page's recurrent view, "Going from continuous spaces to discrete spaces").
+ *   seq_lens  (batch,)   MSS_I32 in device memory, nullable (then all L); values are clamped to
+ *                        [0, L] on the device (they are not read on the host)
+ *   every other argument as for mss_selective_scan_fwd_with_state.
+ * The work done does not shrink with the lengths: steps past a sequence's end run as identity
+ * steps.
+ */
+int mss_selective_scan_fwd_varlen(const mss_tensor_t* u, const mss_tensor_t* delta,
+                                  const mss_tensor_t* A, const mss_tensor_t* B,
+                                  const mss_tensor_t* C, const mss_tensor_t* D,
+                                  const mss_tensor_t* z, const mss_tensor_t* delta_bias,
+                                  const mss_tensor_t* initial_state, const mss_tensor_t* seq_lens,
+                                  int softplus_flag, const mss_tensor_t* out,
+                                  const mss_tensor_t* last_state, void* stream);
 
 /*
  * Gradients of mss_selective_scan_fwd (h_0 = 0) for training: given dout = dL/dout of a scalar

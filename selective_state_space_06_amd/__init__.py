@@ -8,6 +8,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     MSS_BF16,
     MSS_F32,
+    MSS_I32,
     MssError,
     causal_conv1d_fwd,
     causal_conv1d_update,
@@ -19,9 +20,11 @@ from ._binding import (  # noqa: F401
     profile_fwd,
     scan_bwd_raw,
     scan_fwd_raw,
+    scan_fwd_varlen_raw,
     scan_fwd_with_state_raw,
     selective_scan_bwd,
     selective_scan_fwd,
+    selective_scan_fwd_varlen,
     selective_scan_fwd_with_state,
     selective_state_update,
     state_update_raw,

@@ -12,12 +12,13 @@ import threading
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libmamba_scan.so")
 
-MSS_F32, MSS_BF16 = 0, 1
+MSS_F32, MSS_BF16, MSS_I32 = 0, 1, 2
 STATUS = {0: "MSS_OK", -1: "MSS_ERR_NULL_ARG", -2: "MSS_ERR_SHAPE", -3: "MSS_ERR_DTYPE",
           -4: "MSS_ERR_LAYOUT", -5: "MSS_ERR_ALIAS", -6: "MSS_ERR_UNSUPPORTED", -7: "MSS_ERR_HIP"}
 
 # every symbol include/mamba_scan.h declares
-EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_fwd_with_state", "mss_selective_scan_bwd",
+EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_fwd_with_state",
+           "mss_selective_scan_fwd_varlen", "mss_selective_scan_bwd",
            "mss_selective_state_update", "mss_causal_conv1d_fwd", "mss_causal_conv1d_update", "mss_profile_enable", "mss_profile_fwd",
            "mss_status_string", "mss_version")
 
@@ -71,6 +72,9 @@ def load_library(path: str = LIB_PATH):
             lib.mss_selective_scan_fwd_with_state.restype = ctypes.c_int
             lib.mss_selective_scan_fwd_with_state.argtypes = [
                 _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, ctypes.c_int, _TP, _TP, ctypes.c_void_p]
+            lib.mss_selective_scan_fwd_varlen.restype = ctypes.c_int
+            lib.mss_selective_scan_fwd_varlen.argtypes = [
+                _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, ctypes.c_int, _TP, _TP, ctypes.c_void_p]
             lib.mss_selective_scan_bwd.restype = ctypes.c_int
             lib.mss_selective_scan_bwd.argtypes = [
                 _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, ctypes.c_int, _TP,
@@ -141,6 +145,14 @@ def scan_fwd_with_state_raw(u, delta, A, B, C, D, z, delta_bias, initial_state, 
         _ref(initial_state), int(softplus_flag), _ref(out), _ref(last_state), stream)
 
 
+def scan_fwd_varlen_raw(u, delta, A, B, C, D, z, delta_bias, initial_state, seq_lens, softplus_flag,
+                        out, last_state, stream) -> int:
+    """Direct call of mss_selective_scan_fwd_varlen with Tensor descriptors (or None)."""
+    return load_library().mss_selective_scan_fwd_varlen(
+        _ref(u), _ref(delta), _ref(A), _ref(B), _ref(C), _ref(D), _ref(z), _ref(delta_bias),
+        _ref(initial_state), _ref(seq_lens), int(softplus_flag), _ref(out), _ref(last_state), stream)
+
+
 def scan_bwd_raw(u, delta, A, B, C, D, z, delta_bias, softplus_flag, dout, du, ddelta, dA, dB, dC,
                  dD, dz, ddelta_bias, stream) -> int:
     """Direct call of mss_selective_scan_bwd with Tensor descriptors (or None)."""
@@ -178,7 +190,7 @@ def _desc(t):
         return None
     if t.device.type != "cuda":
         raise ValueError("libmamba_scan takes device tensors")
-    dt = {torch.float32: MSS_F32, torch.bfloat16: MSS_BF16}.get(t.dtype, -1)
+    dt = {torch.float32: MSS_F32, torch.bfloat16: MSS_BF16, torch.int32: MSS_I32}.get(t.dtype, -1)
     return Tensor.make(t.data_ptr(), dt, list(t.shape), list(t.stride()))
 
 
@@ -268,6 +280,27 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
     if st != 0:
         raise MssError(st, "mss_selective_scan_bwd")
     return g
+
+
+def selective_scan_fwd_varlen(u, delta, A, B, C, seq_lens, initial_state=None, D=None, z=None,
+                              delta_bias=None, delta_softplus=True, out=None, last_state=None):
+    """Forward scan of sequences of different lengths: seq_lens (batch,) int32 on the device.
+    Outputs past a sequence's end are 0; last_state[b] is the state after step seq_lens[b] - 1.
+    Returns (out, last_state)."""
+    import torch
+    if out is None:
+        out = torch.empty_like(u, memory_format=torch.contiguous_format)
+    if last_state is None:
+        last_state = torch.empty((u.shape[0], u.shape[1], A.shape[1]), dtype=torch.float32,
+                                 device=u.device)
+    with torch.cuda.device(u.device):
+        stream = torch.cuda.current_stream(u.device).cuda_stream
+        st = scan_fwd_varlen_raw(_desc(u), _desc(delta), _desc(A), _desc(B), _desc(C), _desc(D),
+                                 _desc(z), _desc(delta_bias), _desc(initial_state), _desc(seq_lens),
+                                 1 if delta_softplus else 0, _desc(out), _desc(last_state), stream)
+    if st != 0:
+        raise MssError(st, "mss_selective_scan_fwd_varlen")
+    return out, last_state
 
 
 def selective_scan_fwd_with_state(u, delta, A, B, C, initial_state, D=None, z=None,

@@ -391,9 +391,28 @@ int mss_selective_scan_fwd_with_state(const mss_tensor_t* u, const mss_tensor_t*
                                       const mss_tensor_t* initial_state, int softplus_flag,
                                       const mss_tensor_t* out, const mss_tensor_t* last_state,
                                       void* stream) {
+    return mss_selective_scan_fwd_varlen(u, delta, A, B, C, D, z, delta_bias, initial_state, nullptr,
+                                         softplus_flag, out, last_state, stream);
+}
+
+int mss_selective_scan_fwd_varlen(const mss_tensor_t* u, const mss_tensor_t* delta,
+                                  const mss_tensor_t* A, const mss_tensor_t* B,
+                                  const mss_tensor_t* C, const mss_tensor_t* D,
+                                  const mss_tensor_t* z, const mss_tensor_t* delta_bias,
+                                  const mss_tensor_t* initial_state, const mss_tensor_t* seq_lens,
+                                  int softplus_flag, const mss_tensor_t* out,
+                                  const mss_tensor_t* last_state, void* stream) {
     try {
-        const int st = validate_fwd(u, delta, A, B, C, D, z, delta_bias, initial_state, out, last_state);
+        int st = validate_fwd(u, delta, A, B, C, D, z, delta_bias, initial_state, out, last_state);
         if (st != MSS_OK) return st;
+        if (seq_lens) {
+            st = check_desc(seq_lens, false);
+            if (st != MSS_OK) return st;
+            if (!shape_is(*seq_lens, 1, u->shape[0])) return MSS_ERR_SHAPE;
+            if (seq_lens->dtype != MSS_I32) return MSS_ERR_DTYPE;
+            if (!dense(*seq_lens) || !aligned(*seq_lens, 4)) return MSS_ERR_LAYOUT;
+            if (overlap(out, seq_lens) || (last_state && overlap(last_state, seq_lens))) return MSS_ERR_ALIAS;
+        }
         mss::ScanLaunch a;
         a.u = u->data; a.delta = delta->data; a.z = z ? z->data : nullptr;
         a.A = static_cast<const float*>(A->data);
@@ -404,6 +423,7 @@ int mss_selective_scan_fwd_with_state(const mss_tensor_t* u, const mss_tensor_t*
         a.out = out->data;
         a.last_state = last_state ? static_cast<float*>(last_state->data) : nullptr;
         a.h0 = initial_state ? static_cast<const float*>(initial_state->data) : nullptr;
+        a.lens = (seq_lens && numel(*seq_lens) > 0) ? static_cast<const int32_t*>(seq_lens->data) : nullptr;
         a.Bt = u->shape[0]; a.Dn = u->shape[1]; a.L = u->shape[2];
         a.softplus = softplus_flag ? 1 : 0;
         a.bf16 = u->dtype == MSS_BF16;

@@ -23,6 +23,7 @@ struct ScanLaunch {
     void* out;
     float* last_state;      // nullable
     const float* h0;        // nullable: starting state (Bt, Dn, N), zeros when null
+    const int32_t* lens;    // nullable: per-batch sequence lengths (device), clamped to [0, L]
     int64_t Bt, Dn, L;
     int softplus;
     bool bf16;              // storage type of u / delta / z / out

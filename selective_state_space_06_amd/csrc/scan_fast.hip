@@ -27,7 +27,9 @@
 //     the pairs of the preceding segments with the associative operator
 //     (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2) into its starting state and runs the segment.
 //     A scan continued from a given state h0 starts that fold from h0 instead of zeros (the
-//     aggregates do not depend on it).
+//     aggregates do not depend on it).  With per-batch sequence lengths, the steps at or past a
+//     batch's length get dt = 0 (abar = 1, no input: the state stands still) and zero outputs, so
+//     the aggregates, the fold and the final state need no other change.
 //
 // exp is exp2 of a log2(e)-prescaled argument.  When every row of a wave satisfies
 // A[d, n] == (n + 1) A[d, 0] exactly (the S4D-real A = -(1..N) of the tutorial's init),
@@ -59,11 +61,19 @@ struct RowSetup {
     float A2[kN];     // A[d, n] * log2(e)
     float bias, dskip;
     bool pow_ok;
+    int64_t stop;     // the batch's sequence length (steps at or past it are identity steps)
 };
 
 __device__ __forceinline__ RowSetup row_setup(const float* __restrict__ A, const float* __restrict__ D,
-                                              const float* __restrict__ bias, int64_t Dn) {
+                                              const float* __restrict__ bias, int64_t Dn,
+                                              const int32_t* __restrict__ lens, int64_t L) {
     RowSetup r;
+    if (lens) {
+        const int64_t l = lens[blockIdx.y];
+        r.stop = l < 0 ? 0 : (l > L ? L : l);
+    } else {
+        r.stop = L;
+    }
     const int64_t d = (int64_t)blockIdx.x * 64 + threadIdx.x;
     r.active = d < Dn;
     const int64_t dc = r.active ? d : Dn - 1;
@@ -190,8 +200,9 @@ struct Pair {
     float d[2], x[2], a[2], du[2];
 };
 
-template <class E, bool SOFTPLUS, bool POW, bool WITH_DU>
-__device__ __forceinline__ Pair pair_of(const uint32_t* su, const uint32_t* sd, int j, const RowSetup& rs) {
+template <class E, bool SOFTPLUS, bool POW, bool WITH_DU, bool VARLEN = false>
+__device__ __forceinline__ Pair pair_of(const uint32_t* su, const uint32_t* sd, int j, const RowSetup& rs,
+                                        int64_t t0 = 0) {
     Pair p;
     float u[2], r[2];
     staged2<E>(su, j, u[0], u[1]);
@@ -199,6 +210,7 @@ __device__ __forceinline__ Pair pair_of(const uint32_t* su, const uint32_t* sd, 
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         p.d[i] = delta_of<SOFTPLUS>(r[i], rs.bias);
+        if (VARLEN && t0 + j + i >= rs.stop) p.d[i] = 0.0f;  // past the sequence: an identity step
         p.x[i] = p.d[i] * u[i];
         p.a[i] = POW ? fast_exp2(p.d[i] * rs.A2[0]) : 0.0f;
         p.du[i] = WITH_DU ? rs.dskip * u[i] : 0.0f;
@@ -282,7 +294,7 @@ __device__ __forceinline__ float step_main(float (&h)[kN], const float (&A2)[kN]
     return y0 + y1;
 }
 
-template <class E, bool HAS_Z, bool SOFTPLUS, bool POW>
+template <class E, bool HAS_Z, bool SOFTPLUS, bool POW, bool VARLEN>
 __device__ __forceinline__ void main_body(
     const RowSetup& rs, float (&h)[kN], const typename E::storage* __restrict__ up,
     const typename E::storage* __restrict__ dp, const typename E::storage* __restrict__ zp,
@@ -316,11 +328,11 @@ __device__ __forceinline__ void main_body(
             load_bc<E, true>(bpre, Bb, Cb, L, t0 + TT, t_end);
         }
         const int nsteps = static_cast<int>(t_end - t0 < TT ? t_end - t0 : TT);  // multiple of 4
-        Pair cur = pair_of<E, SOFTPLUS, POW, true>(su, sd, 0, rs);
+        Pair cur = pair_of<E, SOFTPLUS, POW, true, VARLEN>(su, sd, 0, rs, t0);
 #pragma unroll 1
         for (int j = 0; j < nsteps; j += 2) {
             // the last iteration recomputes its own pair (read before put2 overwrites it)
-            const Pair nxt = pair_of<E, SOFTPLUS, POW, true>(su, sd, j + 2 < nsteps ? j + 2 : j, rs);
+            const Pair nxt = pair_of<E, SOFTPLUS, POW, true, VARLEN>(su, sd, j + 2 < nsteps ? j + 2 : j, rs, t0);
             const float y0 = step_main<POW>(h, rs.A2, cur.d[0], cur.x[0], cur.a[0], sbc + j * 36, cur.du[0]);
             const float y1 =
                 step_main<POW>(h, rs.A2, cur.d[1], cur.x[1], cur.a[1], sbc + (j + 1) * 36, cur.du[1]);
@@ -337,6 +349,7 @@ __device__ __forceinline__ void main_body(
             for (int e = 0; e < V; ++e) {
                 o[e] = result_of<E>(srow, v * V + e);
                 if (HAS_Z) o[e] *= silu(vec_elem<E>(zw + 4 * v, e));
+                if (VARLEN && t0 + v * V + e >= rs.stop) o[e] = 0.0f;
             }
             packed[v] = E::pack(o);
         }
@@ -423,17 +436,18 @@ __device__ __forceinline__ void fold_carry(float (&h)[kN], const float (&A2)[kN]
     }
 }
 
-template <class E, bool HAS_Z, bool SOFTPLUS>
+template <class E, bool HAS_Z, bool SOFTPLUS, bool VARLEN>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void scan_main_kernel(
     const typename E::storage* __restrict__ u, const typename E::storage* __restrict__ delta,
     const typename E::storage* __restrict__ z, const float* __restrict__ A,
     const float* __restrict__ B, const float* __restrict__ C, const float* __restrict__ D,
     const float* __restrict__ bias, const float* __restrict__ agg, const float* __restrict__ h0,
-    typename E::storage* __restrict__ out, float* __restrict__ last_state, int64_t Dn, int64_t L, int S) {
+    typename E::storage* __restrict__ out, float* __restrict__ last_state, const int32_t* __restrict__ lens,
+    int64_t Dn, int64_t L, int S) {
     using G = Geo<E>;
     __shared__ uint32_t srow[G::kRowWords];
     __shared__ __align__(16) float sbc[G::TT * 36];
-    const RowSetup rs = row_setup(A, D, bias, Dn);
+    const RowSetup rs = row_setup(A, D, bias, Dn, lens, L);
     const int seg = blockIdx.z;
     const int64_t R = (int64_t)gridDim.y * Dn;
     int64_t t_begin, t_end;
@@ -445,11 +459,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sc
     float h[kN];
     if (__all(rs.pow_ok)) {
         fold_carry<true>(h, rs.A2, agg, h0, seg, R, rs.row);
-        main_body<E, HAS_Z, SOFTPLUS, true>(rs, h, u + base, delta + base, zp, out + base, Bb, Cb, L,
+        main_body<E, HAS_Z, SOFTPLUS, true, VARLEN>(rs, h, u + base, delta + base, zp, out + base, Bb, Cb, L,
                                             srow, sbc, t_begin, t_end);
     } else {
         fold_carry<false>(h, rs.A2, agg, h0, seg, R, rs.row);
-        main_body<E, HAS_Z, SOFTPLUS, false>(rs, h, u + base, delta + base, zp, out + base, Bb, Cb, L,
+        main_body<E, HAS_Z, SOFTPLUS, false, VARLEN>(rs, h, u + base, delta + base, zp, out + base, Bb, Cb, L,
                                              srow, sbc, t_begin, t_end);
     }
     if (last_state && rs.active && seg == S - 1) {
@@ -463,7 +477,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sc
 // Aggregate of one segment: (sum of delta, end state of the segment started from h = 0).
 // POW walks the segment backward (acc_n += x_s B_s R^(n+1), R the product of the later
 // Abar_0); the general path runs the recurrence forward without outputs.
-template <class E, bool SOFTPLUS, bool POW>
+template <class E, bool SOFTPLUS, bool POW, bool VARLEN>
 __device__ __forceinline__ void agg_body(const RowSetup& rs, const typename E::storage* __restrict__ up,
                                          const typename E::storage* __restrict__ dp,
                                          const float* __restrict__ Bb, int64_t L, uint32_t* srow,
@@ -499,12 +513,12 @@ __device__ __forceinline__ void agg_body(const RowSetup& rs, const typename E::s
             // The scalars and the B values of the next pair are read one iteration ahead, so an
             // iteration does not start by waiting for its own LDS reads (unrolled by two so the
             // current / next register sets alternate instead of being copied).
-            Pair cur = pair_of<E, SOFTPLUS, true, false>(su, sd, nsteps - 2, rs);
+            Pair cur = pair_of<E, SOFTPLUS, true, false, VARLEN>(su, sd, nsteps - 2, rs, t0);
             BPair bcur = b_pair(sbc, nsteps - 2);
 #pragma unroll 2
             for (int j = nsteps - 2; j >= 0; j -= 2) {
                 const int jn = j >= 2 ? j - 2 : 0;
-                const Pair nxt = pair_of<E, SOFTPLUS, true, false>(su, sd, jn, rs);
+                const Pair nxt = pair_of<E, SOFTPLUS, true, false, VARLEN>(su, sd, jn, rs, t0);
                 const BPair bnxt = b_pair(sbc, jn);
                 // step j + 1 first (backward), then step j
                 const float R1 = Rp;
@@ -530,8 +544,8 @@ __device__ __forceinline__ void agg_body(const RowSetup& rs, const typename E::s
                 staged2<E>(sd, j, r0, r1);
                 const float4* b0 = reinterpret_cast<const float4*>(sbc + j * 20);
                 const float4* b1 = reinterpret_cast<const float4*>(sbc + (j + 1) * 20);
-                const float d0 = delta_of<SOFTPLUS>(r0, rs.bias);
-                const float d1 = delta_of<SOFTPLUS>(r1, rs.bias);
+                const float d0 = (VARLEN && t0 + j >= rs.stop) ? 0.0f : delta_of<SOFTPLUS>(r0, rs.bias);
+                const float d1 = (VARLEN && t0 + j + 1 >= rs.stop) ? 0.0f : delta_of<SOFTPLUS>(r1, rs.bias);
                 const float x0 = d0 * u0, x1 = d1 * u1;
 #pragma unroll
                 for (int q = 0; q < kN / 4; ++q) {
@@ -552,15 +566,15 @@ __device__ __forceinline__ void agg_body(const RowSetup& rs, const typename E::s
     }
 }
 
-template <class E, bool SOFTPLUS>
+template <class E, bool SOFTPLUS, bool VARLEN>
 __global__ __launch_bounds__(64) void scan_agg_kernel(
     const typename E::storage* __restrict__ u, const typename E::storage* __restrict__ delta,
     const float* __restrict__ A, const float* __restrict__ B, const float* __restrict__ bias,
-    float* __restrict__ agg, int64_t Dn, int64_t L, int S) {
+    float* __restrict__ agg, const int32_t* __restrict__ lens, int64_t Dn, int64_t L, int S) {
     using G = Geo<E>;
     __shared__ uint32_t srow[G::kRowWords];
     __shared__ __align__(16) float sbc[G::TT * 20];
-    const RowSetup rs = row_setup(A, nullptr, bias, Dn);
+    const RowSetup rs = row_setup(A, nullptr, bias, Dn, lens, L);
     const int seg = blockIdx.z;
     const int64_t R = (int64_t)gridDim.y * Dn;
     int64_t t_begin, t_end;
@@ -569,9 +583,9 @@ __global__ __launch_bounds__(64) void scan_agg_kernel(
     const float* Bb = B + (int64_t)blockIdx.y * kN * L;
     float acc[kN], dsum;
     if (__all(rs.pow_ok))
-        agg_body<E, SOFTPLUS, true>(rs, u + base, delta + base, Bb, L, srow, sbc, t_begin, t_end, acc, dsum);
+        agg_body<E, SOFTPLUS, true, VARLEN>(rs, u + base, delta + base, Bb, L, srow, sbc, t_begin, t_end, acc, dsum);
     else
-        agg_body<E, SOFTPLUS, false>(rs, u + base, delta + base, Bb, L, srow, sbc, t_begin, t_end, acc, dsum);
+        agg_body<E, SOFTPLUS, false, VARLEN>(rs, u + base, delta + base, Bb, L, srow, sbc, t_begin, t_end, acc, dsum);
     if (rs.active) {
         float* a = agg + (int64_t)seg * (kN + 1) * R + rs.row;
 #pragma unroll
@@ -580,7 +594,7 @@ __global__ __launch_bounds__(64) void scan_agg_kernel(
     }
 }
 
-template <class E, bool HAS_Z, bool SOFTPLUS>
+template <class E, bool HAS_Z, bool SOFTPLUS, bool VARLEN>
 hipError_t launch_fast_t(const ScanLaunch& a, const ScanPlan& p, float* ws, hipStream_t stream) {
     using S_t = typename E::storage;
     float* agg = ws;
@@ -588,22 +602,28 @@ hipError_t launch_fast_t(const ScanLaunch& a, const ScanPlan& p, float* ws, hipS
     const unsigned gx = static_cast<unsigned>((a.Dn + 63) / 64);
     mark(a, 0, stream);
     if (p.segments > 1)
-        scan_agg_kernel<E, SOFTPLUS><<<dim3(gx, (unsigned)a.Bt, (unsigned)(p.segments - 1)), block, 0, stream>>>(
-            static_cast<const S_t*>(a.u), static_cast<const S_t*>(a.delta), a.A, a.B, a.bias, agg, a.Dn, a.L,
-            p.segments);
+        scan_agg_kernel<E, SOFTPLUS, VARLEN><<<dim3(gx, (unsigned)a.Bt, (unsigned)(p.segments - 1)), block, 0, stream>>>(
+            static_cast<const S_t*>(a.u), static_cast<const S_t*>(a.delta), a.A, a.B, a.bias, agg, a.lens, a.Dn,
+            a.L, p.segments);
     mark(a, 1, stream);
-    scan_main_kernel<E, HAS_Z, SOFTPLUS><<<dim3(gx, (unsigned)a.Bt, (unsigned)p.segments), block, 0, stream>>>(
+    scan_main_kernel<E, HAS_Z, SOFTPLUS, VARLEN><<<dim3(gx, (unsigned)a.Bt, (unsigned)p.segments), block, 0, stream>>>(
         static_cast<const S_t*>(a.u), static_cast<const S_t*>(a.delta), static_cast<const S_t*>(a.z), a.A, a.B,
-        a.C, a.D, a.bias, agg, a.h0, static_cast<S_t*>(a.out), a.last_state, a.Dn, a.L, p.segments);
+        a.C, a.D, a.bias, agg, a.h0, static_cast<S_t*>(a.out), a.last_state, a.lens, a.Dn, a.L, p.segments);
     mark(a, 2, stream);
     return hipGetLastError();
 }
 
+template <class E, bool VARLEN>
+hipError_t launch_fast_v(const ScanLaunch& a, const ScanPlan& p, float* ws, hipStream_t stream) {
+    const bool hz = a.z != nullptr;
+    if (a.softplus)
+        return hz ? launch_fast_t<E, true, true, VARLEN>(a, p, ws, stream) : launch_fast_t<E, false, true, VARLEN>(a, p, ws, stream);
+    return hz ? launch_fast_t<E, true, false, VARLEN>(a, p, ws, stream) : launch_fast_t<E, false, false, VARLEN>(a, p, ws, stream);
+}
+
 template <class E>
 hipError_t launch_fast_e(const ScanLaunch& a, const ScanPlan& p, float* ws, hipStream_t stream) {
-    const bool hz = a.z != nullptr;
-    if (a.softplus) return hz ? launch_fast_t<E, true, true>(a, p, ws, stream) : launch_fast_t<E, false, true>(a, p, ws, stream);
-    return hz ? launch_fast_t<E, true, false>(a, p, ws, stream) : launch_fast_t<E, false, false>(a, p, ws, stream);
+    return a.lens ? launch_fast_v<E, true>(a, p, ws, stream) : launch_fast_v<E, false>(a, p, ws, stream);
 }
 
 }  // namespace

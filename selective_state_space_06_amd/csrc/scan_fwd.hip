@@ -21,7 +21,9 @@
 //     the associative operator (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2) -- the parallel
 //     associative scan the tutorial page and the mamba-jax README describe -- into each
 //     segment's starting state; the main pass then runs every segment from its true start.
-//     A given starting state h0 enters only through segment 0 and the start of that fold.
+//     A given starting state h0 enters only through segment 0 and the start of that fold; with
+//     per-batch sequence lengths, steps at or past a batch's length are identity steps with zero
+//     outputs.
 //
 // exp(delta A) = exp2(delta * A log2e) with A log2e formed once per (d, n).  When a row
 // satisfies A[d, n] == (n + 1) A[d, 0] exactly (the S4D-real initialisation A = -(1..N) the
@@ -49,6 +51,7 @@ struct KArgs {
     void* out;
     float* last_state;
     const float* h0;      // nullable starting state, (rows_total, kN)
+    const int32_t* lens;  // nullable per-batch sequence lengths
     float* ws;            // [S][kN + 1][rows_total] carry workspace
     int64_t Dn, L, seg_len, rows_total;
     int S;
@@ -104,7 +107,7 @@ template <class E, bool VEC, bool HAS_Z, int MODE, bool POW, int TT>
 __device__ __forceinline__ void scan_body(const KArgs& a, Smem<TT>& sm, const int lane, const int b,
                                           const int64_t d0, const int64_t row, const bool active,
                                           const float (&A2)[kN], float (&h)[kN],
-                                          const int64_t t_begin, const int64_t t_end) {
+                                          const int64_t t_begin, const int64_t t_end, const int64_t stop) {
     constexpr int V = E::kPerVec;        // elements per 16-byte vector
     constexpr int CPR = TT / V;          // vectors per row per tile
     constexpr int RPI = kRows / CPR;     // rows covered by one pass of the wave
@@ -156,7 +159,8 @@ __device__ __forceinline__ void scan_body(const KArgs& a, Smem<TT>& sm, const in
             for (int e = 0; e < V; ++e) {
                 const float pre = dv[e] + br;
                 float dlt = a.softplus ? softplus(pre) : pre;
-                dlt = (row_ok && tl + e < tvalid) ? dlt : 0.0f;  // padded steps: identity update
+                // padded steps and steps past the batch's length: identity update
+                dlt = (row_ok && tl + e < tvalid && t0 + tl + e < stop) ? dlt : 0.0f;
                 dl[e] = dlt;
                 xv[e] = dlt * uv[e];
             }
@@ -241,6 +245,7 @@ __device__ __forceinline__ void scan_body(const KArgs& a, Smem<TT>& sm, const in
                 for (int e = 0; e < V; ++e) {
                     const float yy = fmaf(dr, uv[e], sm.dl[r][tl + e]);
                     ov[e] = HAS_Z ? yy * silu(zv[e]) : yy;
+                    if (t0 + tl + e >= stop) ov[e] = 0.0f;  // past the batch's length
                 }
                 if (VEC) {
                     if (row_ok && tl < tvalid)
@@ -317,10 +322,15 @@ __global__ __launch_bounds__(kRows) void scan_kernel(KArgs a) {
 
     const int64_t t_begin = (int64_t)seg * a.seg_len;
     const int64_t t_end = (t_begin + a.seg_len < a.L) ? t_begin + a.seg_len : a.L;
+    int64_t stop = a.L;
+    if (a.lens) {
+        const int64_t l = a.lens[b];
+        stop = l < 0 ? 0 : (l > a.L ? a.L : l);
+    }
     if (__all(pow_ok))
-        scan_body<E, VEC, HAS_Z, MODE, true, TT>(a, sm, lane, b, d0, row, active, A2, h, t_begin, t_end);
+        scan_body<E, VEC, HAS_Z, MODE, true, TT>(a, sm, lane, b, d0, row, active, A2, h, t_begin, t_end, stop);
     else
-        scan_body<E, VEC, HAS_Z, MODE, false, TT>(a, sm, lane, b, d0, row, active, A2, h, t_begin, t_end);
+        scan_body<E, VEC, HAS_Z, MODE, false, TT>(a, sm, lane, b, d0, row, active, A2, h, t_begin, t_end, stop);
 }
 
 // Folds the per-segment pairs (sum delta_s, local end state e_s) into inclusive end states:
@@ -420,7 +430,7 @@ hipError_t launch_scan_fwd(const ScanLaunch& a, const ScanPlan& plan, float* wor
     }
     KArgs k;
     k.u = a.u; k.delta = a.delta; k.z = a.z; k.A = a.A; k.B = a.B; k.C = a.C; k.D = a.D;
-    k.bias = a.bias; k.out = a.out; k.last_state = a.last_state; k.h0 = a.h0; k.ws = workspace;
+    k.bias = a.bias; k.out = a.out; k.last_state = a.last_state; k.h0 = a.h0; k.lens = a.lens; k.ws = workspace;
     k.Dn = a.Dn; k.L = a.L; k.seg_len = plan.seg_len; k.rows_total = rows;
     k.S = plan.segments; k.softplus = a.softplus;
     const bool hz = a.z != nullptr;

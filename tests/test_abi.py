@@ -241,6 +241,29 @@ def test_fwd_state_may_share_inputs(lib):
     assert call_fwd_state(a, h) == OK
 
 
+# ------------------------------------------------------------ sequences of different lengths
+
+def call_varlen(a, lens):
+    return mss.scan_fwd_varlen_raw(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                   a["delta_bias"], None, lens, a["softplus_flag"], a["out"],
+                                   a["last_state"], a["stream"])
+
+
+def test_varlen_validation(lib):
+    lens = Tensor.make(addr(BT * 4), mss.MSS_I32, [BT])
+    bad = Tensor.make(lens.data, mss.MSS_I32, [BT + 1])
+    assert call_varlen(fwd_args(), bad) == SHAPE
+    bad = Tensor.make(lens.data, MSS_F32, [BT])
+    assert call_varlen(fwd_args(), bad) == DTYPE
+    bad = Tensor.make(lens.data + 2, mss.MSS_I32, [BT])
+    assert call_varlen(fwd_args(), bad) == LAYOUT
+    a = fwd_args()
+    assert call_varlen(a, Tensor.make(a["out"].data, mss.MSS_I32, [BT])) == ALIAS
+    a = fwd_args()
+    a["u"].dtype = mss.MSS_I32                             # lengths only: not an activation dtype
+    assert call_varlen(a, lens) == DTYPE
+
+
 # --------------------------------------------------------------------- backward scan
 
 def bwd_args(dtype=MSS_F32, n=N):
