@@ -53,8 +53,8 @@ def _load():
             lib.oracle_selective_scan_bwd.restype = ctypes.c_int
             lib.oracle_selective_scan_bwd.argtypes = [
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i64p,
-                _d, _d, _d, _d, _d, _d, _d, _d, ctypes.c_int, _d,
-                _d, _d, _d, _d, _d, _d, _d, _d, ctypes.c_int, ctypes.c_int]
+                _d, _d, _d, _d, _d, _d, _d, _d, ctypes.c_int, _d, _i64p, _d, _d,
+                _d, _d, _d, _d, _d, _d, _d, _d, _d, ctypes.c_int, ctypes.c_int]
             lib.oracle_causal_conv1d.restype = ctypes.c_int
             lib.oracle_causal_conv1d.argtypes = [
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _d, _d, _d, _d, ctypes.c_int,
@@ -150,7 +150,8 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus_
 
 
 def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus_flag=True,
-                       dout=None, rows=None, nthreads: int = 0, magnitude: bool = False):
+                       dout=None, rows=None, nthreads: int = 0, magnitude: bool = False, h0=None,
+                       seq_lens=None, dlast=None):
     """fp64 gradients of L = sum(dout * out) for the forward scan from h_0 = 0.
 
     Inputs as selective_scan, plus dout (batch, d_inner, L).  Returns a dict:
@@ -160,6 +161,9 @@ def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softp
       dB, dC: (batch, d_state, L), summed over the selected rows.
     dD / ddelta_bias are the gradients at D = 0 / bias = 0 when those are None.
     magnitude=True returns, in the same layout, the sum of |terms| behind each element.
+    h0, seq_lens: as selective_scan; dlast: dL/d last_state (batch, d_inner, d_state), adding
+    sum(dlast * last_state) to the loss.  The dict then also holds dh0 (dL/dh0, same shape as h0,
+    or (len(rows), d_state) with rows).
     """
     u = np.asarray(u)
     Bt, Dn, L = u.shape
@@ -179,22 +183,28 @@ def selective_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softp
     dz = np.empty((R, L)) if z is not None else None
     dA = np.empty((R, N)); dD = np.empty(R); db = np.empty(R)
     dB = np.empty((Bt, N, L)); dC = np.empty((Bt, N, L))
+    dh0 = np.empty((R, N))
+    h0_r = None if h0 is None else _f64(np.asarray(h0).reshape(Bt * Dn, N)[sel])
+    dl_r = None if dlast is None else _f64(np.asarray(dlast).reshape(Bt * Dn, N)[sel])
+    len_r = None if seq_lens is None else np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int64)[rb])
     rc = _load().oracle_selective_scan_bwd(
         R, N, L, Bt, rb.ctypes.data_as(_i64p), _ptr(rows_of(u)), _ptr(rows_of(delta)),
         _ptr(rows_of(z)), _ptr(_f64(np.asarray(A)[ch])), _ptr(_f64(B)), _ptr(_f64(C)),
         _ptr(None if D is None else _f64(np.asarray(D)[ch])),
         _ptr(None if delta_bias is None else _f64(np.asarray(delta_bias)[ch])),
-        int(bool(softplus_flag)), _ptr(rows_of(dout)), _ptr(du), _ptr(dd), _ptr(dz), _ptr(dA),
-        _ptr(dB), _ptr(dC), _ptr(dD), _ptr(db), int(bool(magnitude)), int(nthreads))
+        int(bool(softplus_flag)), _ptr(h0_r), None if len_r is None else len_r.ctypes.data_as(_i64p),
+        _ptr(dl_r), _ptr(rows_of(dout)), _ptr(du), _ptr(dd), _ptr(dz), _ptr(dA),
+        _ptr(dB), _ptr(dC), _ptr(dD), _ptr(db), _ptr(dh0), int(bool(magnitude)), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_selective_scan_bwd rejected its arguments")
     if rows is not None:
-        return dict(du=du, ddelta=dd, dz=dz, dA=dA, dB=dB, dC=dC, dD=dD, ddelta_bias=db)
+        return dict(du=du, ddelta=dd, dz=dz, dA=dA, dB=dB, dC=dC, dD=dD, ddelta_bias=db, dh0=dh0)
     sh = (Bt, Dn, L)
     return dict(du=du.reshape(sh), ddelta=dd.reshape(sh),
                 dz=None if dz is None else dz.reshape(sh),
                 dA=dA.reshape(Bt, Dn, N).sum(0), dB=dB, dC=dC,
-                dD=dD.reshape(Bt, Dn).sum(0), ddelta_bias=db.reshape(Bt, Dn).sum(0))
+                dD=dD.reshape(Bt, Dn).sum(0), ddelta_bias=db.reshape(Bt, Dn).sum(0),
+                dh0=dh0.reshape(Bt, Dn, N))
 
 
 def causal_conv1d(x, weight, bias=None, state=None, silu=True, rows=None, nthreads: int = 0):

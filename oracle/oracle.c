@@ -152,6 +152,10 @@ int oracle_selective_scan(int64_t R, int64_t N, int64_t L, int64_t Bt,
  * magnitude != 0 replaces every term added into an output by its absolute value (G and h
  * themselves stay signed), giving sum |terms| per output element: the scale a rounding-error
  * bound for a re-associated fp32 evaluation of the same sums is proportional to.
+ * The forward may start from h0 (R x N) and stop at row_len[r] (as in the forward above); dlast
+ * (R x N) is dL/d last_state when the loss also depends on the final state (it seeds the adjoint
+ * at the row's last step), and dh0 (R x N, written when not NULL) is dL/dh0.  Steps past a row's
+ * end take no part: their du, ddelta, dz are 0.
  * Not pinned by the pages (they print no gradient); pinned in the tests by central finite
  * differences of the forward above, an L = 1 closed form and linearity in dout.
  */
@@ -160,9 +164,10 @@ int oracle_selective_scan_bwd(int64_t R, int64_t N, int64_t L, int64_t Bt,
                               const double* u, const double* delta, const double* z,
                               const double* A, const double* Bm, const double* Cm,
                               const double* D, const double* bias, int softplus_flag,
+                              const double* h0, const int64_t* row_len, const double* dlast,
                               const double* dout, double* du, double* ddelta, double* dz,
                               double* dA, double* dB, double* dC, double* dD, double* dbias,
-                              int magnitude, int nthreads) {
+                              double* dh0, int magnitude, int nthreads) {
     if (R < 0 || N <= 0 || L < 0 || Bt <= 0) return -1;
     set_threads(nthreads);
     const size_t nbc = (size_t)(Bt * N * L);
@@ -195,9 +200,14 @@ int oracle_selective_scan_bwd(int64_t R, int64_t N, int64_t L, int64_t Bt,
             const double* Cb = Cm + b * N * L;
             const double Dr = D ? D[r] : 0.0;
             const double br = bias ? bias[r] : 0.0;
+            const int64_t Lr = row_len ? (row_len[r] < 0 ? 0 : (row_len[r] > L ? L : row_len[r])) : L;
+            for (int64_t t = Lr; t < L; ++t) {  /* past the row's end */
+                du[r * L + t] = 0.0; ddelta[r * L + t] = 0.0;
+                if (z) dz[r * L + t] = 0.0;
+            }
             /* forward, keeping every h_t and y_t (for magnitude: y's sum of |terms|) */
-            for (int64_t n = 0; n < N; ++n) hs[n] = 0.0;
-            for (int64_t t = 0; t < L; ++t) {
+            for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[r * N + n] : 0.0;
+            for (int64_t t = 0; t < Lr; ++t) {
                 const double ut = u[r * L + t];
                 const double pre = delta[r * L + t] + br;
                 const double dt = softplus_flag ? sp(pre) : pre;
@@ -213,8 +223,11 @@ int oracle_selective_scan_bwd(int64_t R, int64_t N, int64_t L, int64_t Bt,
             }
             /* reverse */
             double dDr = 0.0, dbr = 0.0;
-            for (int64_t n = 0; n < N; ++n) { g[n] = 0.0; dA[r * N + n] = 0.0; }
-            for (int64_t t = L - 1; t >= 0; --t) {
+            for (int64_t n = 0; n < N; ++n) {
+                g[n] = dlast ? dlast[r * N + n] : 0.0;  /* G and h stay signed in either mode */
+                dA[r * N + n] = 0.0;
+            }
+            for (int64_t t = Lr - 1; t >= 0; --t) {
                 const double ut = u[r * L + t];
                 const double pre = delta[r * L + t] + br;
                 const double dt = softplus_flag ? sp(pre) : pre;
@@ -253,6 +266,8 @@ int oracle_selective_scan_bwd(int64_t R, int64_t N, int64_t L, int64_t Bt,
             }
             if (dD) dD[r] = dDr;
             if (dbias) dbias[r] = dbr;
+            if (dh0)
+                for (int64_t n = 0; n < N; ++n) dh0[r * N + n] = magnitude ? fabs(g[n]) : g[n];
         }
 #undef ACC
         free(hs); free(ys); free(g);

@@ -155,3 +155,62 @@ def test_rows_and_threads_agree(oracle_mod):
     np.testing.assert_array_equal(gr["du"], flat(g1["du"])[rows])
     np.testing.assert_array_equal(gr["ddelta"], flat(g1["ddelta"])[rows])
     np.testing.assert_array_equal(gr["dz"], flat(g1["dz"])[rows])
+
+# ---------------------------------------------------------------- starting state, lengths, dL/dh_L
+
+def _loss_ext(orc, a, dout, dlast, h0, lens):
+    out, last = orc.selective_scan(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                   a["delta_bias"], h0=h0, seq_lens=lens)
+    return float(np.sum(out * dout) + np.sum(last * dlast))
+
+
+@pytest.mark.parametrize("lens", [None, [7, 12]])
+def test_state_and_final_state_gradients_by_finite_differences(oracle_mod, lens):
+    """L = sum(dout out) + sum(dlast h_L) from a given h0: every input's gradient and dL/dh0."""
+    s = scan_inputs(2, 3, 5, 12, dtype="f32", seed=90)
+    a = _fields(s)
+    rng = np.random.default_rng(91)
+    dout, dlast = rng.standard_normal(s.u.shape), rng.standard_normal((2, 3, 5))
+    h0 = rng.standard_normal((2, 3, 5))
+    ln = None if lens is None else np.array(lens)
+    g = oracle_mod.selective_scan_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                      a["delta_bias"], dout=dout, h0=h0, seq_lens=ln, dlast=dlast)
+    h = 1e-6
+    targets = dict(GRAD_OF, h0="dh0")
+    for name, gk in targets.items():
+        base = h0 if name == "h0" else a[name]
+        for i in np.ndindex(base.shape):
+            p, m = base.copy(), base.copy()
+            p[i] += h
+            m[i] -= h
+            if name == "h0":
+                fp = _loss_ext(oracle_mod, a, dout, dlast, p, ln)
+                fm = _loss_ext(oracle_mod, a, dout, dlast, m, ln)
+            else:
+                fp = _loss_ext(oracle_mod, {**a, name: p}, dout, dlast, h0, ln)
+                fm = _loss_ext(oracle_mod, {**a, name: m}, dout, dlast, h0, ln)
+            fd = (fp - fm) / (2 * h)
+            assert abs(g[gk][i] - fd) <= 2e-7 + 1e-6 * abs(fd), (name, i, g[gk][i], fd)
+
+
+def test_lengths_equal_truncated_rows(oracle_mod):
+    """With lengths, each batch's gradients are those of its truncated problem; past the end 0."""
+    s = scan_inputs(3, 2, 4, 10, dtype="f32", seed=92)
+    a = _fields(s)
+    rng = np.random.default_rng(93)
+    dout, dlast, h0 = rng.standard_normal(s.u.shape), rng.standard_normal((3, 2, 4)), rng.standard_normal((3, 2, 4))
+    lens = np.array([0, 4, 10])
+    g = oracle_mod.selective_scan_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                      a["delta_bias"], dout=dout, h0=h0, seq_lens=lens, dlast=dlast)
+    for b, lb in enumerate(lens):
+        sl = (slice(b, b + 1), Ellipsis, slice(0, lb))
+        gt = oracle_mod.selective_scan_bwd(a["u"][sl], a["delta"][sl], a["A"], a["B"][sl], a["C"][sl],
+                                           a["D"], a["z"][sl], a["delta_bias"], dout=dout[sl],
+                                           h0=h0[b:b + 1], dlast=dlast[b:b + 1])
+        for k in ("du", "ddelta", "dz"):
+            np.testing.assert_array_equal(g[k][b, :, :lb], gt[k][0])
+            assert not np.any(g[k][b, :, lb:])
+        np.testing.assert_array_equal(g["dh0"][b], gt["dh0"][0])
+        np.testing.assert_array_equal(g["dB"][b, :, :lb], gt["dB"][0])
+        assert not np.any(g["dB"][b, :, lb:]) and not np.any(g["dC"][b, :, lb:])
+    np.testing.assert_array_equal(g["dh0"][0], dlast[0])        # empty sequence: dL/dh0 = dL/dh_L
