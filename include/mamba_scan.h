@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MSS_VERSION 10400 /* major * 10000 + minor * 100 + patch */
+#define MSS_VERSION 10500 /* major * 10000 + minor * 100 + patch */
 
 typedef enum { MSS_F32 = 0, MSS_BF16 = 1, MSS_I32 = 2 } mss_dtype_t;  /* I32: lengths only */
 
@@ -162,6 +162,30 @@ int mss_selective_scan_bwd(const mss_tensor_t* u, const mss_tensor_t* delta,
                            const mss_tensor_t* dB, const mss_tensor_t* dC,
                            const mss_tensor_t* dD, const mss_tensor_t* dz,
                            const mss_tensor_t* ddelta_bias, void* stream);
+
+/*
+ * The backward of mss_selective_scan_fwd_varlen, for chunked training and batches of different
+ * lengths: the forward started from initial_state and stopped at seq_lens (both nullable, as in
+ * the forward), and the loss may also depend on the final state through dlast_state =
+ * dL/d last_state (nullable: 0), which seeds the adjoint at each sequence's last step.
+ * dinitial_state (nullable) receives dL/d initial_state, the adjoint left after step 0 (the
+ * previous chunk's dlast_state).  Steps past a sequence's end take no part: du, ddelta, dz are 0
+ * there.  State tensors (batch, d_inner, d_state) f32, 16-byte aligned; seq_lens (batch,) I32.
+ * Every other argument as for mss_selective_scan_bwd; dinitial_state may not overlap any input
+ * or output.
+ */
+int mss_selective_scan_bwd_varlen(const mss_tensor_t* u, const mss_tensor_t* delta,
+                                  const mss_tensor_t* A, const mss_tensor_t* B,
+                                  const mss_tensor_t* C, const mss_tensor_t* D,
+                                  const mss_tensor_t* z, const mss_tensor_t* delta_bias,
+                                  const mss_tensor_t* initial_state, const mss_tensor_t* seq_lens,
+                                  int softplus_flag, const mss_tensor_t* dout,
+                                  const mss_tensor_t* dlast_state, const mss_tensor_t* du,
+                                  const mss_tensor_t* ddelta, const mss_tensor_t* dA,
+                                  const mss_tensor_t* dB, const mss_tensor_t* dC,
+                                  const mss_tensor_t* dD, const mss_tensor_t* dz,
+                                  const mss_tensor_t* ddelta_bias,
+                                  const mss_tensor_t* dinitial_state, void* stream);
 
 /*
  * One recurrent (decode) step: the same equations for a single token, continuing from

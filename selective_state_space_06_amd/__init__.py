@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     profile_enable,
     profile_fwd,
     scan_bwd_raw,
+    scan_bwd_varlen_raw,
     scan_fwd_raw,
     scan_fwd_varlen_raw,
     scan_fwd_with_state_raw,

@@ -18,7 +18,7 @@ STATUS = {0: "MSS_OK", -1: "MSS_ERR_NULL_ARG", -2: "MSS_ERR_SHAPE", -3: "MSS_ERR
 
 # every symbol include/mamba_scan.h declares
 EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_fwd_with_state",
-           "mss_selective_scan_fwd_varlen", "mss_selective_scan_bwd",
+           "mss_selective_scan_fwd_varlen", "mss_selective_scan_bwd", "mss_selective_scan_bwd_varlen",
            "mss_selective_state_update", "mss_causal_conv1d_fwd", "mss_causal_conv1d_update", "mss_profile_enable", "mss_profile_fwd",
            "mss_status_string", "mss_version")
 
@@ -85,6 +85,10 @@ def load_library(path: str = LIB_PATH):
             lib.mss_causal_conv1d_update.restype = ctypes.c_int
             lib.mss_causal_conv1d_update.argtypes = [_TP, _TP, _TP, _TP, ctypes.c_int, _TP,
                                                      ctypes.c_void_p]
+            lib.mss_selective_scan_bwd_varlen.restype = ctypes.c_int
+            lib.mss_selective_scan_bwd_varlen.argtypes = [
+                _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, ctypes.c_int, _TP, _TP,
+                _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, ctypes.c_void_p]
             lib.mss_selective_state_update.restype = ctypes.c_int
             lib.mss_selective_state_update.argtypes = [_TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP,
                                                        _TP, _TP, ctypes.c_void_p]
@@ -160,6 +164,17 @@ def scan_bwd_raw(u, delta, A, B, C, D, z, delta_bias, softplus_flag, dout, du, d
         _ref(u), _ref(delta), _ref(A), _ref(B), _ref(C), _ref(D), _ref(z), _ref(delta_bias),
         int(softplus_flag), _ref(dout), _ref(du), _ref(ddelta), _ref(dA), _ref(dB), _ref(dC),
         _ref(dD), _ref(dz), _ref(ddelta_bias), stream)
+
+
+def scan_bwd_varlen_raw(u, delta, A, B, C, D, z, delta_bias, initial_state, seq_lens, softplus_flag,
+                        dout, dlast_state, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias,
+                        dinitial_state, stream) -> int:
+    """Direct call of mss_selective_scan_bwd_varlen with Tensor descriptors (or None)."""
+    return load_library().mss_selective_scan_bwd_varlen(
+        _ref(u), _ref(delta), _ref(A), _ref(B), _ref(C), _ref(D), _ref(z), _ref(delta_bias),
+        _ref(initial_state), _ref(seq_lens), int(softplus_flag), _ref(dout), _ref(dlast_state),
+        _ref(du), _ref(ddelta), _ref(dA), _ref(dB), _ref(dC), _ref(dD), _ref(dz),
+        _ref(ddelta_bias), _ref(dinitial_state), stream)
 
 
 def conv1d_fwd_raw(x, weight, bias, initial_state, silu_flag, out, final_state, stream) -> int:
@@ -255,10 +270,13 @@ def causal_conv1d_update(state, x, weight, bias=None, silu=True, out=None):
 
 
 def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
-                       delta_softplus=True):
+                       delta_softplus=True, initial_state=None, seq_lens=None, dlast_state=None,
+                       return_dinitial_state=False):
     """Gradients of selective_scan_fwd (from h = 0) for L = sum(dout * out), on the current
     stream.  Returns a dict: du, ddelta, dz (None without z) in u's dtype; dA, dB, dC, dD,
-    ddelta_bias in float32 (dD / ddelta_bias also when D / delta_bias is None)."""
+    ddelta_bias in float32 (dD / ddelta_bias also when D / delta_bias is None).
+    initial_state / seq_lens describe the forward (as selective_scan_fwd_varlen); dlast_state is
+    dL/d last_state; with return_dinitial_state the dict also holds dinitial_state = dL/dh0."""
     import torch
     dev_ = u.device
     Bt, Dn, L = u.shape
@@ -270,13 +288,17 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
              dA=torch.empty((Dn, N), **f32), dB=torch.empty((Bt, N, L), **f32),
              dC=torch.empty((Bt, N, L), **f32), dD=torch.empty((Dn,), **f32),
              ddelta_bias=torch.empty((Dn,), **f32))
+    if return_dinitial_state:
+        g["dinitial_state"] = torch.empty((Bt, Dn, N), **f32)
     with torch.cuda.device(dev_):
         stream = torch.cuda.current_stream(dev_).cuda_stream
-        st = scan_bwd_raw(_desc(u), _desc(delta), _desc(A), _desc(B), _desc(C), _desc(D),
-                          _desc(z), _desc(delta_bias), 1 if delta_softplus else 0, _desc(dout),
-                          _desc(g["du"]), _desc(g["ddelta"]), _desc(g["dA"]), _desc(g["dB"]),
-                          _desc(g["dC"]), _desc(g["dD"]), _desc(g["dz"]), _desc(g["ddelta_bias"]),
-                          stream)
+        st = scan_bwd_varlen_raw(_desc(u), _desc(delta), _desc(A), _desc(B), _desc(C), _desc(D),
+                                 _desc(z), _desc(delta_bias), _desc(initial_state),
+                                 _desc(seq_lens), 1 if delta_softplus else 0, _desc(dout),
+                                 _desc(dlast_state), _desc(g["du"]), _desc(g["ddelta"]),
+                                 _desc(g["dA"]), _desc(g["dB"]), _desc(g["dC"]), _desc(g["dD"]),
+                                 _desc(g["dz"]), _desc(g["ddelta_bias"]),
+                                 _desc(g.get("dinitial_state")), stream)
     if st != 0:
         raise MssError(st, "mss_selective_scan_bwd")
     return g

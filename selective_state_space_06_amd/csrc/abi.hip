@@ -481,10 +481,52 @@ int mss_selective_scan_bwd(const mss_tensor_t* u, const mss_tensor_t* delta, con
                            const mss_tensor_t* dA, const mss_tensor_t* dB, const mss_tensor_t* dC,
                            const mss_tensor_t* dD, const mss_tensor_t* dz,
                            const mss_tensor_t* ddelta_bias, void* stream) {
+    return mss_selective_scan_bwd_varlen(u, delta, A, B, C, D, z, delta_bias, nullptr, nullptr, softplus_flag,
+                                         dout, nullptr, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, nullptr,
+                                         stream);
+}
+
+int mss_selective_scan_bwd_varlen(const mss_tensor_t* u, const mss_tensor_t* delta, const mss_tensor_t* A,
+                                  const mss_tensor_t* B, const mss_tensor_t* C, const mss_tensor_t* D,
+                                  const mss_tensor_t* z, const mss_tensor_t* delta_bias,
+                                  const mss_tensor_t* initial_state, const mss_tensor_t* seq_lens,
+                                  int softplus_flag, const mss_tensor_t* dout,
+                                  const mss_tensor_t* dlast_state, const mss_tensor_t* du,
+                                  const mss_tensor_t* ddelta, const mss_tensor_t* dA, const mss_tensor_t* dB,
+                                  const mss_tensor_t* dC, const mss_tensor_t* dD, const mss_tensor_t* dz,
+                                  const mss_tensor_t* ddelta_bias, const mss_tensor_t* dinitial_state,
+                                  void* stream) {
     try {
-        const int st = validate_bwd(u, delta, A, B, C, D, z, delta_bias, dout, du, ddelta, dA, dB, dC, dD,
-                                    dz, ddelta_bias);
+        int st = validate_bwd(u, delta, A, B, C, D, z, delta_bias, dout, du, ddelta, dA, dB, dC, dD,
+                              dz, ddelta_bias);
         if (st != MSS_OK) return st;
+        {
+            // the state tensors: (Bt, Dn, N) f32, 16-byte aligned; the lengths: (Bt,) i32
+            const int64_t Bt = u->shape[0], Dn = u->shape[1], N = A->shape[1];
+            for (const mss_tensor_t* t : {initial_state, dlast_state, dinitial_state, seq_lens}) {
+                st = check_desc(t, false);
+                if (st != MSS_OK) return st;
+            }
+            for (const mss_tensor_t* t : {initial_state, dlast_state, dinitial_state}) {
+                if (!t) continue;
+                if (!shape_is(*t, 3, Bt, Dn, N)) return MSS_ERR_SHAPE;
+                if (t->dtype != MSS_F32) return MSS_ERR_DTYPE;
+                if (!dense(*t) || !aligned(*t, 16)) return MSS_ERR_LAYOUT;
+            }
+            if (seq_lens) {
+                if (!shape_is(*seq_lens, 1, Bt)) return MSS_ERR_SHAPE;
+                if (seq_lens->dtype != MSS_I32) return MSS_ERR_DTYPE;
+                if (!dense(*seq_lens) || !aligned(*seq_lens, 4)) return MSS_ERR_LAYOUT;
+            }
+            const mss_tensor_t* outs[] = {du, ddelta, dA, dB, dC, dD, dz, ddelta_bias};
+            for (const mss_tensor_t* o : outs)
+                for (const mss_tensor_t* t : {initial_state, dlast_state, seq_lens, dinitial_state})
+                    if (o && overlap(o, t)) return MSS_ERR_ALIAS;
+            if (dinitial_state)
+                for (const mss_tensor_t* t : {u, delta, A, B, C, D, z, delta_bias, dout, initial_state,
+                                              dlast_state, seq_lens})
+                    if (overlap(dinitial_state, t)) return MSS_ERR_ALIAS;
+        }
         mss::BwdLaunch a;
         a.u = u->data; a.delta = delta->data; a.z = z ? z->data : nullptr; a.dout = dout->data;
         a.A = static_cast<const float*>(A->data);
@@ -498,6 +540,10 @@ int mss_selective_scan_bwd(const mss_tensor_t* u, const mss_tensor_t* delta, con
         a.dC = static_cast<float*>(dC->data);
         a.dD = dD ? static_cast<float*>(dD->data) : nullptr;
         a.dbias = ddelta_bias ? static_cast<float*>(ddelta_bias->data) : nullptr;
+        a.h0 = initial_state ? static_cast<const float*>(initial_state->data) : nullptr;
+        a.lens = (seq_lens && numel(*seq_lens) > 0) ? static_cast<const int32_t*>(seq_lens->data) : nullptr;
+        a.dlast = dlast_state ? static_cast<const float*>(dlast_state->data) : nullptr;
+        a.dh0 = dinitial_state ? static_cast<float*>(dinitial_state->data) : nullptr;
         a.Bt = u->shape[0]; a.Dn = u->shape[1]; a.L = u->shape[2];
         a.softplus = softplus_flag ? 1 : 0;
         a.bf16 = u->dtype == MSS_BF16;
@@ -505,7 +551,7 @@ int mss_selective_scan_bwd(const mss_tensor_t* u, const mss_tensor_t* delta, con
         a.vec_ok = (a.L * static_cast<int64_t>(es)) % 16 == 0 && aligned(*u, 16) && aligned(*delta, 16) &&
                    aligned(*dout, 16) && aligned(*du, 16) && aligned(*ddelta, 16) && (!z || aligned(*z, 16)) &&
                    (!dz || aligned(*dz, 16)) && aligned(*B, 16) && aligned(*C, 16);
-        const int64_t elems = a.Dn * kN + a.Bt * kN * a.L + a.Dn;
+        const int64_t elems = a.Dn * kN + a.Bt * kN * a.L + a.Dn + (a.dh0 ? a.Bt * a.Dn * kN : 0);
         if (elems == 0) return MSS_OK;  // nothing to write
 
         hipStream_t s = static_cast<hipStream_t>(stream);

@@ -71,6 +71,10 @@ struct BwdLaunch {
     float* dC;              // (Bt, N, L)
     float* dD;              // nullable
     float* dbias;           // nullable
+    const float* h0;        // nullable: the forward's starting state (Bt, Dn, N)
+    const int32_t* lens;    // nullable: per-batch sequence lengths (device)
+    const float* dlast;     // nullable: dL/d last_state (Bt, Dn, N)
+    float* dh0;             // nullable: dL/dh0 (Bt, Dn, N), written
     int64_t Bt, Dn, L;
     int softplus;
     bool bf16;

@@ -65,6 +65,8 @@ def _check(mss, orc, s, seed, what, **flags):
     mag = _ref(orc, s, dout, True, **flags)
     worst = {}
     for k, r in ref.items():
+        if k == "dh0":          # the plain backward does not return dL/dh0
+            continue
         if r is None:
             assert g[k] is None, k
             continue
@@ -142,3 +144,75 @@ def test_bwd_empty_sequence(mss):
     torch.cuda.synchronize()
     assert torch.all(g["dA"] == 0) and torch.all(g["dD"] == 0) and torch.all(g["ddelta_bias"] == 0)
     assert g["du"].shape == (2, 64, 0) and g["dB"].shape == (2, 16, 0)
+
+
+# ------------------------------------------------- starting state, lengths, dL/d last_state
+
+def _gpu_ext(mss, s, dout, h0=None, lens=None, dlast=None):
+    import torch
+    z = dev(s.z, s.dtype) if s.z is not None else None
+    return mss.selective_scan_bwd(dev(s.u, s.dtype), dev(s.delta, s.dtype), dev(s.A), dev(s.B),
+                                  dev(s.C), dev(dout, s.dtype), D=dev(s.D), z=z,
+                                  delta_bias=dev(s.delta_bias),
+                                  initial_state=None if h0 is None else dev(h0),
+                                  seq_lens=None if lens is None else torch.from_numpy(lens).to("cuda"),
+                                  dlast_state=None if dlast is None else dev(dlast),
+                                  return_dinitial_state=True)
+
+
+@pytest.mark.parametrize("Bt,Dn,L,dtype", [(4, 64, 256, "bf16"), (4, 70, 100, "f32"), (6, 128, 520, "bf16")])
+def test_bwd_state_lengths_parity(mss, oracle_mod, Bt, Dn, L, dtype):
+    import torch
+    s = scan_inputs(Bt, Dn, 16, L, dtype=dtype, seed=80 + L)
+    rng = np.random.default_rng(81)
+    dout = _dout(s, 81)
+    h0 = (0.5 * rng.standard_normal((Bt, Dn, 16))).astype(np.float32)
+    dlast = rng.standard_normal((Bt, Dn, 16)).astype(np.float32)
+    lens = np.array(([0, 1, L // 2 + 3, L] * 2)[:Bt], dtype=np.int32)
+    g = _gpu_ext(mss, s, dout, h0, lens, dlast)
+    torch.cuda.synchronize()
+    kw = dict(D=s.D, z=s.z, delta_bias=s.delta_bias, dout=dout, h0=h0, seq_lens=lens, dlast=dlast)
+    ref = oracle_mod.selective_scan_bwd(s.u, s.delta, s.A, s.B, s.C, **kw)
+    mag = oracle_mod.selective_scan_bwd(s.u, s.delta, s.A, s.B, s.C, magnitude=True, **kw)
+    for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias"):
+        got = host64(g[k])
+        rtol_out = 2e-2 if (k in ROUNDED and dtype == "bf16") else 0.0
+        lim = rtol_out * np.abs(ref[k]) + RTOL_SUM * mag[k] + ATOL
+        bad = np.abs(got - ref[k]) > lim
+        assert not bad.any(), (k, int(bad.sum()), float((np.abs(got - ref[k]) / lim).max()))
+    for k in ("du", "ddelta", "dz"):   # past each sequence's end: exactly zero
+        got = host64(g[k])
+        for b, lb in enumerate(lens):
+            assert not np.any(got[b, :, lb:]), (k, b)
+    # dL/dh0: a sum along the row; bound by the array's scale
+    got, want = host64(g["dinitial_state"]), ref["dh0"]
+    np.testing.assert_allclose(got, want, rtol=1e-4, atol=1e-5 * np.abs(want).max())
+
+
+def test_chunked_training_equals_whole_sequence(mss):
+    """Forward chunk 1, forward chunk 2 from its state; backward chunk 2 (its dh0 flows back as
+    chunk 1's dlast), backward chunk 1: the gradients of the whole sequence."""
+    import torch
+    Bt, Dn, L, cut = 2, 128, 512, 200
+    s = scan_inputs(Bt, Dn, 16, L, dtype="f32", seed=85)
+    dout = _dout(s, 85)
+    A, D, bias = dev(s.A), dev(s.D), dev(s.delta_bias)
+    full = dict(u=dev(s.u), delta=dev(s.delta), z=dev(s.z), B=dev(s.B), C=dev(s.C), dout=dev(dout))
+    c1 = {k: v[..., :cut].contiguous() for k, v in full.items()}
+    c2 = {k: v[..., cut:].contiguous() for k, v in full.items()}
+    _, h1 = mss.selective_scan_fwd(c1["u"], c1["delta"], A, c1["B"], c1["C"], D=D, z=c1["z"], delta_bias=bias)
+    g2 = mss.selective_scan_bwd(c2["u"], c2["delta"], A, c2["B"], c2["C"], c2["dout"], D=D, z=c2["z"],
+                                delta_bias=bias, initial_state=h1, return_dinitial_state=True)
+    g1 = mss.selective_scan_bwd(c1["u"], c1["delta"], A, c1["B"], c1["C"], c1["dout"], D=D, z=c1["z"],
+                                delta_bias=bias, dlast_state=g2["dinitial_state"])
+    gw = mss.selective_scan_bwd(full["u"], full["delta"], A, full["B"], full["C"], full["dout"], D=D,
+                                z=full["z"], delta_bias=bias)
+    torch.cuda.synchronize()
+    for k in ("du", "ddelta", "dz", "dB", "dC"):
+        cat = torch.cat([g1[k], g2[k]], dim=-1)
+        w = host64(gw[k])
+        np.testing.assert_allclose(host64(cat), w, rtol=1e-4, atol=1e-5 * np.abs(w).max(), err_msg=k)
+    for k in ("dA", "dD", "ddelta_bias"):
+        w = host64(gw[k])
+        np.testing.assert_allclose(host64(g1[k]) + host64(g2[k]), w, rtol=1e-4,
+                                   atol=1e-5 * np.abs(w).max(), err_msg=k)
