@@ -60,11 +60,17 @@ bool overlap(const mss_tensor_t* a, const mss_tensor_t* b) {
 }
 
 // Status of one descriptor before its extents are compared: NULL descriptor or NULL data
-// (for a non-empty tensor) -> NULL_ARG; ndim outside 1..3 -> SHAPE.
+// (for a non-empty tensor) -> NULL_ARG; ndim outside 1..3, a negative extent or an element count
+// beyond 2^48 (so that no later size computation can overflow) -> SHAPE.
 int check_desc(const mss_tensor_t* t, bool required) {
     if (!t) return required ? MSS_ERR_NULL_ARG : MSS_OK;
     if (t->ndim < 1 || t->ndim > 3) return MSS_ERR_SHAPE;
-    if (!t->data && numel(*t) != 0) return MSS_ERR_NULL_ARG;
+    int64_t n = 1;
+    for (int i = 0; i < t->ndim; ++i) {
+        if (t->shape[i] < 0) return MSS_ERR_SHAPE;
+        if (__builtin_mul_overflow(n, t->shape[i], &n) || n > (int64_t{1} << 48)) return MSS_ERR_SHAPE;
+    }
+    if (!t->data && n != 0) return MSS_ERR_NULL_ARG;
     return MSS_OK;
 }
 

@@ -156,6 +156,15 @@ def test_fwd_last_state_alias(lib):
     assert call_fwd(a) == ALIAS
 
 
+def test_fwd_huge_or_negative_extents(lib):
+    a = fwd_args()
+    a["u"] = Tensor.make(a["u"].data, MSS_F32, [1 << 20, 1 << 20, 1 << 20])
+    assert call_fwd(a) == SHAPE
+    a = fwd_args()
+    a["u"].shape[2] = -4
+    assert call_fwd(a) == SHAPE
+
+
 def test_fwd_unsupported_dstate(lib):
     a = fwd_args(n=8)
     assert call_fwd(a) == UNSUPPORTED
