@@ -156,6 +156,17 @@ __device__ __forceinline__ void abar8(float dt, float a0, const float (&A2)[kN],
     }
 }
 
+// v summed over lanes k, k ^ 16, k ^ 32, k ^ 48 (the wave's four 16-lane rows), in every lane:
+// gfx950's row swaps exchange whole rows between two registers in the VALU, without a round
+// trip through LDS.  With both operands v, permlane16_swap leaves rows (0, 0, 2, 2) of v in its
+// first result and rows (1, 1, 3, 3) in its second; permlane32_swap does the same for row pairs.
+__device__ __forceinline__ float rows_sum(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ float sigmoid(float v) { return fast_rcp(1.0f + fast_exp2(-v * kLog2e)); }
 
 // One tile (kBT steps from t0) of the lane's row; steps at or past L read as 0.  VEC: whole
@@ -524,8 +535,7 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
                 const float4 w0 = rr[0], w1 = rr[1], w2 = rr[2], w3 = rr[3];
                 float sum = ((w0.x + w0.y) + (w0.z + w0.w)) + ((w1.x + w1.y) + (w1.z + w1.w)) +
                             (((w2.x + w2.y) + (w2.z + w2.w)) + ((w3.x + w3.y) + (w3.z + w3.w)));
-                sum += __shfl_xor(sum, 16);
-                sum += __shfl_xor(sum, 32);
+                sum = rows_sum(sum);
                 bcs[j] = sum;
                 __syncthreads();
             }
