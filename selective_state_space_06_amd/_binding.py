@@ -300,8 +300,47 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
                                  _desc(g["dz"]), _desc(g["ddelta_bias"]),
                                  _desc(g.get("dinitial_state")), stream)
     if st != 0:
-        raise MssError(st, "mss_selective_scan_bwd")
+        raise MssError(st, "mss_selective_scan_bwd_varlen")
     return g
+
+
+class SelectiveScanFunction:
+    """torch.autograd wrapper: out = selective_scan_fwd(...) with gradients from
+    mss_selective_scan_bwd (the forward states are recomputed there, not kept).  Marshalling only:
+    both passes run in the library's kernels.  Usage: SelectiveScanFunction.apply(u, delta, A, B,
+    C, D, z, delta_bias, delta_softplus); D, z, delta_bias may be None."""
+
+    _fn = None
+
+    @classmethod
+    def apply(cls, u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True):
+        if cls._fn is None:
+            cls._fn = _make_autograd_fn()
+        return cls._fn.apply(u, delta, A, B, C, D, z, delta_bias, delta_softplus)
+
+
+def _make_autograd_fn():
+    import torch
+
+    class _Fn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, u, delta, A, B, C, D, z, delta_bias, delta_softplus):
+            out = selective_scan_fwd(u, delta, A, B, C, D=D, z=z, delta_bias=delta_bias,
+                                     delta_softplus=delta_softplus, return_last_state=False)
+            ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias)
+            ctx.delta_softplus = delta_softplus
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            u, delta, A, B, C, D, z, delta_bias = ctx.saved_tensors
+            g = selective_scan_bwd(u, delta, A, B, C, dout.contiguous(), D=D, z=z,
+                                   delta_bias=delta_bias, delta_softplus=ctx.delta_softplus)
+            return (g["du"], g["ddelta"], g["dA"], g["dB"], g["dC"],
+                    g["dD"] if D is not None else None, g["dz"],
+                    g["ddelta_bias"] if delta_bias is not None else None, None)
+
+    return _Fn
 
 
 def selective_scan_fwd_varlen(u, delta, A, B, C, seq_lens, initial_state=None, D=None, z=None,

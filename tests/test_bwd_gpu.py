@@ -216,3 +216,23 @@ def test_chunked_training_equals_whole_sequence(mss):
         w = host64(gw[k])
         np.testing.assert_allclose(host64(g1[k]) + host64(g2[k]), w, rtol=1e-4,
                                    atol=1e-5 * np.abs(w).max(), err_msg=k)
+
+
+def test_autograd_function_matches_oracle(mss, oracle_mod):
+    """torch.autograd through SelectiveScanFunction: the loss sum(dout * out) gives the oracle's
+    gradients for every input."""
+    import torch
+    s = scan_inputs(2, 96, 16, 200, dtype="f32", seed=86)
+    dout = _dout(s, 86)
+    ts = {k: dev(getattr(s, k)).requires_grad_(True) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
+    out = mss.SelectiveScanFunction.apply(ts["u"], ts["delta"], ts["A"], ts["B"], ts["C"], ts["D"],
+                                          ts["z"], ts["delta_bias"], True)
+    (out * dev(dout)).sum().backward()
+    torch.cuda.synchronize()
+    ref = _ref(oracle_mod, s, dout, False)
+    mag = _ref(oracle_mod, s, dout, True)
+    names = dict(u="du", delta="ddelta", A="dA", B="dB", C="dC", D="dD", z="dz", delta_bias="ddelta_bias")
+    for k, gk in names.items():
+        got = host64(ts[k].grad)
+        lim = RTOL_SUM * mag[gk] + ATOL
+        assert np.all(np.abs(got - ref[gk]) <= lim), (k, float((np.abs(got - ref[gk]) / lim).max()))
