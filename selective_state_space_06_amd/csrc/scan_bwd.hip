@@ -259,6 +259,24 @@ __device__ __forceinline__ void raw_row(const void* base, int64_t off, int64_t t
         w[q] = (t0 + q * V < L) ? *reinterpret_cast<const uint4*>(p + t0 + q * V) : make_uint4(0, 0, 0, 0);
 }
 
+// B or C of one tile: lanes 0..31 load B, 32..63 load C, four steps of one state each.
+template <bool VEC>
+__device__ __forceinline__ void load_bc(const BwdArgs& a, int64_t t0, float (&bc)[4]) {
+    const int lane = threadIdx.x;
+    const int half = lane & 1;
+    const int n = (lane >> 1) & (kN - 1);
+    const float* src = (lane >= 32 ? a.C : a.B) + ((int64_t)blockIdx.y * kN + n) * a.L;
+    const int64_t tb = t0 + 4 * half;
+    if (VEC) {  // always issued (past the end from an in-range address, then zeroed): no branch
+        const bool in = tb < a.L;
+        const float4 v = *reinterpret_cast<const float4*>(src + (in ? tb : a.L - 4));
+        bc[0] = in ? v.x : 0.0f; bc[1] = in ? v.y : 0.0f; bc[2] = in ? v.z : 0.0f; bc[3] = in ? v.w : 0.0f;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bc[e] = (tb + e < a.L) ? src[tb + e] : 0.0f;
+    }
+}
+
 template <class E, bool VEC, bool HAS_Z>
 __device__ __forceinline__ void load_raw(const BwdArgs& a, const Row& r, int64_t t0, Raw<E, VEC>& w) {
     const int64_t off = r.row * a.L;
@@ -273,23 +291,7 @@ __device__ __forceinline__ void load_raw(const BwdArgs& a, const Row& r, int64_t
         load_tile<E, false>(a.dout, off, t0, a.L, w.g);
         if (HAS_Z) load_tile<E, false>(a.z, off, t0, a.L, w.z);
     }
-    // B or C: lanes 0..31 load B, 32..63 load C, four steps of one state each
-    const int lane = threadIdx.x;
-    const int half = lane & 1;
-    const int n = (lane >> 1) & (kN - 1);
-    const float* src = (lane >= 32 ? a.C : a.B) + ((int64_t)blockIdx.y * kN + n) * a.L;
-    const int64_t tb = t0 + 4 * half;
-    if (VEC) {
-        if (tb < a.L) {
-            const float4 v = *reinterpret_cast<const float4*>(src + tb);
-            w.bc[0] = v.x; w.bc[1] = v.y; w.bc[2] = v.z; w.bc[3] = v.w;
-        } else {
-            w.bc[0] = w.bc[1] = w.bc[2] = w.bc[3] = 0.0f;
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w.bc[e] = (tb + e < a.L) ? src[tb + e] : 0.0f;
-    }
+    load_bc<VEC>(a, t0, w.bc);
 }
 
 // The tile's B | C block into LDS, time-major: sbc[t][n] = B, sbc[t][16 + n] = C.
@@ -354,64 +356,220 @@ __device__ __forceinline__ void seg_tiles(int s, int S, int64_t ntiles, int64_t&
 
 // ---------------------------------------------------------------- aggregate kernel
 
+// The workgroup is one wavefront, whose LDS instructions execute in issue order: ordering LDS
+// accesses between its lanes only needs the compiler to keep them in program order.  A
+// workgroup barrier would also wait for the global-to-LDS loads in flight.
+__device__ __forceinline__ void wave_lds_order() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// All of the wave's LDS reads have returned (s_waitcnt lgkmcnt(0), other counters untouched).
+__device__ __forceinline__ void lds_reads_done() {
+    wave_lds_order();
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+}
+
+// The aggregate walk, shared by both ways of fetching the inputs: per tile the checkpoint, then
+// the recurrences of H (the state from h = 0), Rp (the product of abar since the segment start)
+// and Lam (the adjoint carry).
+struct AggState {
+    float H[kN], Lam[kN], Rp[kN];
+    float dsum;
+};
+
+// The tile's start state from h = 0 at the segment start, and sum dt.  ALL: every lane stores
+// (see agg_body_staged), else only the active ones.
+template <bool ALL>
+__device__ __forceinline__ void agg_checkpoint(const BwdArgs& a, const Row& r, int64_t tile, const AggState& st) {
+    if (ALL || r.active) {
+        float* ck = a.ck + tile * kCkW * a.R + r.row;
+#pragma unroll
+        for (int n = 0; n < kN; ++n, ck += a.R) *ck = st.H[n];
+        *ck = st.dsum;
+    }
+}
+
+template <bool POW>
+__device__ __forceinline__ void agg_tile(const BwdArgs& a, const Row& r, int64_t t0, const StepVals& v,
+                                         const float* sbc, AggState& st) {
+#pragma unroll
+    for (int j = 0; j < kBT; ++j) {
+        if (t0 + j >= a.L) break;
+        float bv[kN], cv[kN], p[kN];
+        read_bc(sbc, j, bv, cv);
+        abar16<POW>(v.dt[j], r.A2, p);
+        st.dsum += v.dt[j];
+#pragma unroll
+        for (int n = 0; n < kN; ++n) {
+            st.H[n] = fmaf(p[n], st.H[n], v.x[j] * bv[n]);
+            st.Rp[n] *= p[n];
+            st.Lam[n] = fmaf(st.Rp[n], v.dy[j] * cv[n], st.Lam[n]);
+        }
+    }
+}
+
+template <bool ALL>
+__device__ __forceinline__ void agg_finish(const BwdArgs& a, const Row& r, int s, const AggState& st) {
+    if (ALL || r.active) {
+        float* o = a.agg + (int64_t)s * kAggW * a.R + r.row;
+        o[0] = st.dsum;
+#pragma unroll
+        for (int n = 0; n < kN; ++n) {
+            o[(int64_t)(1 + n) * a.R] = st.H[n];
+            o[(int64_t)(1 + kN + n) * a.R] = st.Lam[n];
+        }
+    }
+}
+
+__device__ __forceinline__ void agg_init(AggState& st) {
+#pragma unroll
+    for (int n = 0; n < kN; ++n) { st.H[n] = 0.0f; st.Lam[n] = 0.0f; st.Rp[n] = 1.0f; }
+    st.dsum = 0.0f;
+}
+
+// Any layout: each tile's inputs come straight into registers, one tile ahead.
 template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z, bool POW>
 __device__ __forceinline__ void agg_body(const BwdArgs& a, const Row& r, float* sbc) {
     const int s = blockIdx.z;
     int64_t tb, te;
     seg_tiles(s, a.S, a.ntiles, tb, te);
-    float H[kN], Lam[kN], Rp[kN];
-#pragma unroll
-    for (int n = 0; n < kN; ++n) { H[n] = 0.0f; Lam[n] = 0.0f; Rp[n] = 1.0f; }
-    float dsum = 0.0f;
+    AggState st;
+    agg_init(st);
     Raw<E, VEC> nx;
     load_raw<E, VEC, HAS_Z>(a, r, tb * kBT, nx);
     for (int64_t tile = tb; tile < te; ++tile) {
         const int64_t t0 = tile * kBT;
-        if (r.active) {  // checkpoint: the tile's start state from h = 0 at the segment start, sum dt
-            float* ck = a.ck + tile * kCkW * a.R + r.row;
-#pragma unroll
-            for (int n = 0; n < kN; ++n) ck[(int64_t)n * a.R] = H[n];
-            ck[(int64_t)kN * a.R] = dsum;
-        }
+        agg_checkpoint<false>(a, r, tile, st);
         const Raw<E, VEC> cur = nx;
         if (tile + 1 < te) load_raw<E, VEC, HAS_Z>(a, r, t0 + kBT, nx);
         StepVals v;
         step_vals<E, VEC, SOFTPLUS, HAS_Z>(a, r, t0, cur, v);
-        __syncthreads();  // readers of the previous tile's B / C are done
+        wave_lds_order();  // after the previous tile's reads of the B / C block
         put_bc(cur.bc, sbc);
-        __syncthreads();
+        wave_lds_order();
+        agg_tile<POW>(a, r, t0, v, sbc, st);
+    }
+    agg_finish<false>(a, r, s, st);
+}
+
+// Rows of whole 16-byte vectors: the inputs are fetched a block at a time, 64 bytes of every row
+// and array (half a 128-byte line), by global-to-LDS loads issued together.  Loading 16 bytes
+// per row per tile instead spreads the reads of one line over eight tiles; with all rows of
+// all wavefronts in flight the line leaves the L2 in between and is fetched again each time.
+// The block sits in LDS as [array][chunk][lane] 16-byte words (a lane reads back only what it
+// loaded: its own row).  The next block is requested once the current block's last tile has been
+// read into registers, so its latency overlaps that tile's arithmetic.
+// 16 bytes per lane from global memory into LDS: lane l's bytes land at dst + 16 l (dst is the
+// same for the whole wave).
+__device__ __forceinline__ void lds_load16(const void* src, uint4* dst) {
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+constexpr int kStageChunks = 4;  // 16-byte chunks per row and array in one block
+
+template <class E>
+struct StageGeo {
+    static constexpr int V = E::kPerVec;              // steps per chunk
+    static constexpr int NV = kBT / V;                // chunks per tile
+    static constexpr int TPB = kStageChunks / NV;     // tiles per block
+};
+
+template <class E, bool HAS_Z>
+__device__ __forceinline__ void stage_block(const BwdArgs& a, const Row& r, int64_t tile, uint4* stage) {
+    using G = StageGeo<E>;
+    using S_t = typename E::storage;
+    const int64_t off = r.row * a.L;
+    const void* src[4] = {a.u, a.delta, a.dout, a.z};
 #pragma unroll
-        for (int j = 0; j < kBT; ++j) {
-            if (t0 + j >= a.L) break;
-            float bv[kN], cv[kN], p[kN];
-            read_bc(sbc, j, bv, cv);
-            abar16<POW>(v.dt[j], r.A2, p);
-            dsum += v.dt[j];
+    for (int c = 0; c < kStageChunks; ++c) {
+        const int64_t t = tile * kBT + c * G::V;
+        const int64_t tc = t < a.L ? t : 0;  // past the row's end: any valid address, those steps are masked
 #pragma unroll
-            for (int n = 0; n < kN; ++n) {
-                H[n] = fmaf(p[n], H[n], v.x[j] * bv[n]);
-                Rp[n] *= p[n];
-                Lam[n] = fmaf(Rp[n], v.dy[j] * cv[n], Lam[n]);
+        for (int q = 0; q < (HAS_Z ? 4 : 3); ++q)
+            lds_load16(static_cast<const S_t*>(src[q]) + off + tc, stage + (q * kStageChunks + c) * 64);
+    }
+}
+
+template <class E, bool HAS_Z>
+__device__ __forceinline__ void staged_tile(const uint4* stage, int k, Raw<E, true>& w) {
+    using G = StageGeo<E>;
+    const int lane = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < G::NV; ++q) {
+        const int c = k * G::NV + q;
+        w.u[q] = stage[(0 * kStageChunks + c) * 64 + lane];
+        w.d[q] = stage[(1 * kStageChunks + c) * 64 + lane];
+        w.g[q] = stage[(2 * kStageChunks + c) * 64 + lane];
+        if (HAS_Z) w.z[q] = stage[(3 * kStageChunks + c) * 64 + lane];
+    }
+}
+
+// Lanes past the last channel (a partial channel group) read the last channel's row (their row
+// index is clamped to it); here they also compute its values, so every lane stores and a
+// duplicate writes the same bits as the owner.  Stores without a branch keep the count of
+// outstanding memory operations exact, so waiting for the next tile's B / C does not also wait
+// for the block in flight.
+template <class E, bool SOFTPLUS, bool HAS_Z, bool POW>
+__device__ __forceinline__ void agg_body_staged(const BwdArgs& a, const Row& r_in, float* sbc, uint4* stage) {
+    using G = StageGeo<E>;
+    Row r = r_in;
+    r.active = true;
+    const int s = blockIdx.z;
+    int64_t tb, te;
+    seg_tiles(s, a.S, a.ntiles, tb, te);
+    AggState st;
+    agg_init(st);
+    float bc_next[4];
+    stage_block<E, HAS_Z>(a, r, tb, stage);
+    load_bc<true>(a, tb * kBT, bc_next);
+    for (int64_t blk = tb; blk < te; blk += G::TPB) {
+        // the block's tiles, unrolled: a tile's LDS words are read one tile ahead, and the
+        // next block is requested before the last tile's arithmetic
+        Raw<E, true> cur;
+        staged_tile<E, HAS_Z>(stage, 0, cur);
+#pragma unroll
+        for (int k = 0; k < G::TPB; ++k) {
+            const int64_t tile = blk + k;
+            if (tile >= te) break;
+            const int64_t t0 = tile * kBT;
+            // B / C of the next tile are requested before this tile's checkpoint stores, so
+            // waiting for them later does not wait for the stores
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cur.bc[e] = bc_next[e];
+            load_bc<true>(a, t0 + kBT, bc_next);
+            agg_checkpoint<true>(a, r, tile, st);
+            Raw<E, true> nx;
+            if (k + 1 < G::TPB) {
+                staged_tile<E, HAS_Z>(stage, k + 1, nx);
+            } else if (tile + 1 < te) {
+                lds_reads_done();  // the block's LDS reads are complete before it is overwritten
+                stage_block<E, HAS_Z>(a, r, tile + 1, stage);
             }
+            StepVals v;
+            step_vals<E, true, SOFTPLUS, HAS_Z>(a, r, t0, cur, v);
+            wave_lds_order();  // after the previous tile's reads of the B / C block
+            put_bc(cur.bc, sbc);
+            wave_lds_order();
+            agg_tile<POW>(a, r, t0, v, sbc, st);
+            if (k + 1 < G::TPB) cur = nx;
         }
     }
-    if (r.active) {
-        float* o = a.agg + (int64_t)s * kAggW * a.R + r.row;
-        o[0] = dsum;
-#pragma unroll
-        for (int n = 0; n < kN; ++n) {
-            o[(int64_t)(1 + n) * a.R] = H[n];
-            o[(int64_t)(1 + kN + n) * a.R] = Lam[n];
-        }
-    }
+    agg_finish<true>(a, r, s, st);
 }
 
 template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z>
 __global__ __launch_bounds__(64) void bwd_agg_kernel(BwdArgs a) {
     __shared__ __align__(16) float sbc[kBT * kBCs];
     const Row r = row_of(a);
-    if (__all(r.pow_ok)) agg_body<E, VEC, SOFTPLUS, HAS_Z, true>(a, r, sbc);
-    else agg_body<E, VEC, SOFTPLUS, HAS_Z, false>(a, r, sbc);
+    if constexpr (VEC) {
+        __shared__ __align__(16) uint4 stage[4 * kStageChunks * 64];
+        if (__all(r.pow_ok)) agg_body_staged<E, SOFTPLUS, HAS_Z, true>(a, r, sbc, stage);
+        else agg_body_staged<E, SOFTPLUS, HAS_Z, false>(a, r, sbc, stage);
+    } else {
+        if (__all(r.pow_ok)) agg_body<E, VEC, SOFTPLUS, HAS_Z, true>(a, r, sbc);
+        else agg_body<E, VEC, SOFTPLUS, HAS_Z, false>(a, r, sbc);
+    }
 }
 
 // ---------------------------------------------------------------- main kernel
@@ -474,9 +632,9 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
         float a0[kBT];  // abar_0 of each step (power path)
 #pragma unroll
         for (int j = 0; j < kBT; ++j) a0[j] = POW ? fast_exp2(v.dt[j] * r.A2[0]) : 0.0f;
-        __syncthreads();
+        wave_lds_order();  // after the previous tile's reads of the B / C block
         put_bc(cur.bc, sbc);
-        __syncthreads();
+        wave_lds_order();
         // The tile's 16 states in two halves of 8 (the states are independent in the recurrence;
         // only the outputs' sums over n combine the halves): recompute the half's states from
         // the checkpoint into LDS (lane-private columns), then consume them in reverse.
@@ -529,7 +687,7 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
                 yacc[j] += y;
                 gbacc[j] += gb;
                 qaacc[j] += qa;
-                __syncthreads();
+                wave_lds_order();
                 // lane (qq, jj) sums term jj over lanes 16 qq .. 16 qq + 15; the quarters then meet
                 const float4* rr = reinterpret_cast<const float4*>(red + (lane & 15) * 64 + 16 * (lane >> 4));
                 const float4 w0 = rr[0], w1 = rr[1], w2 = rr[2], w3 = rr[3];
@@ -537,7 +695,7 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
                             (((w2.x + w2.y) + (w2.z + w2.w)) + ((w3.x + w3.y) + (w3.z + w3.w)));
                 sum = rows_sum(sum);
                 bcs[j] = sum;
-                __syncthreads();
+                wave_lds_order();
             }
             if (lane < 2 * kH) {   // term lane: dB of state kH hf + lane, or dC of state kH hf + lane - kH
                 const int idx = lane < kH ? kH * hf + lane : kN + kH * hf + (lane - kH);
