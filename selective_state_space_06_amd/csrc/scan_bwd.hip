@@ -47,6 +47,11 @@ constexpr int kAggW = 2 * kN + 1; // aggregate words per (segment, row): sum dt 
 constexpr int kParW = kN + 2;     // partial words per (segment, row): dA[16] | dD | dbias
 constexpr int kBCs = 2 * kN + 4;  // LDS words per step of B | C (16-byte pad)
 constexpr int kCkW = kN + 1;      // checkpoint words per (tile, row): local state[16] | sum dt
+// Steps whose recomputed states the main kernel keeps in LDS at once: four for bf16 rows (17.5 KB
+// of LDS: eight wavefronts per CU, as many as the registers allow), the whole tile for fp32 rows
+// (their larger prefetched tiles leave no registers for the re-walk a smaller buffer costs).
+template <class E>
+constexpr int q_steps() { return sizeof(typename E::storage) == 2 ? 4 : kBT; }
 
 struct BwdArgs {
     const void* u;
@@ -641,61 +646,69 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
         float yacc[kBT], gbacc[kBT], qaacc[kBT];
 #pragma unroll
         for (int j = 0; j < kBT; ++j) yacc[j] = gbacc[j] = qaacc[j] = 0.0f;
+        constexpr int kQ = q_steps<E>();
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            float hs[kH], pc[kH];  // tile start: exp(A sum dt) h_in + the local checkpoint
+            float pc[kH];  // tile start: exp(A sum dt) h_in + the local checkpoint
             abar8<POW>(ck0[kN], POW ? fast_exp2(ck0[kN] * r.A2[0]) : 0.0f, r.A2, hf, pc);
-#pragma unroll
-            for (int k = 0; k < kH; ++k) hs[k] = fmaf(pc[k], hin[(kH * hf + k) * 64 + lane], ck0[kH * hf + k]);
-#pragma unroll
-            for (int j = 0; j < kBT; ++j) {
-                if (t0 + j >= a.L) break;
-                float bv[kH], cv[kH], p[kH];
-                read_bc_half(sbc, j, hf, bv, cv);
-                abar8<POW>(v.dt[j], a0[j], r.A2, hf, p);
-#pragma unroll
-                for (int k = 0; k < kH; ++k) {
-                    hs[k] = fmaf(p[k], hs[k], v.x[j] * bv[k]);
-                    hbuf[(j * kH + k) * 64 + lane] = hs[k];
-                }
-            }
             float bcs[kBT];
+            // Steps in chunks of kQ, the latest first: each chunk recomputes the half's states from
+            // the tile start, keeps its own steps' states in LDS and consumes them in reverse (a
+            // later chunk walks the earlier steps too; LDS holds kQ steps, not kBT).
 #pragma unroll
-            for (int j = kBT - 1; j >= 0; --j) {
-                bcs[j] = 0.0f;
-                if (t0 + j >= a.L) continue;
-                float bv[kH], cv[kH], p[kH], hc[kH];
-                read_bc_half(sbc, j, hf, bv, cv);
-                abar8<POW>(v.dt[j], a0[j], r.A2, hf, p);
+            for (int c = kBT / kQ - 1; c >= 0; --c) {
+                float hs[kH];
 #pragma unroll
-                for (int k = 0; k < kH; ++k) hc[k] = hbuf[(j * kH + k) * 64 + lane];
-                float y = 0.0f, gb = 0.0f, qa = 0.0f;
+                for (int k = 0; k < kH; ++k) hs[k] = fmaf(pc[k], hin[(kH * hf + k) * 64 + lane], ck0[kH * hf + k]);
 #pragma unroll
-                for (int k = 0; k < kH; ++k) {
-                    const int n = kH * hf + k;
-                    const float G = fmaf(v.dy[j], cv[k], gc[n]);       // dL/dh_t
-                    y = fmaf(cv[k], hc[k], y);
-                    const float ah = fmaf(-v.x[j], bv[k], hc[k]);      // abar h_{t-1}
-                    const float qn = G * ah;
-                    qa = fmaf(POW ? static_cast<float>(n + 1) : r.An[n], qn, qa);
-                    gb = fmaf(G, bv[k], gb);
-                    dA[n] = fmaf(v.dt[j], qn, dA[n]);
-                    red[k * 64 + lane] = G * v.x[j];                   // dB term
-                    red[(kH + k) * 64 + lane] = v.dy[j] * hc[k];       // dC term
-                    gc[n] = p[k] * G;                                  // toward h_{t-1}
+                for (int j = 0; j < kQ * (c + 1); ++j) {
+                    if (t0 + j >= a.L) break;
+                    float bv[kH], cv[kH], p[kH];
+                    read_bc_half(sbc, j, hf, bv, cv);
+                    abar8<POW>(v.dt[j], a0[j], r.A2, hf, p);
+#pragma unroll
+                    for (int k = 0; k < kH; ++k) {
+                        hs[k] = fmaf(p[k], hs[k], v.x[j] * bv[k]);
+                        if (j >= kQ * c) hbuf[((j - kQ * c) * kH + k) * 64 + lane] = hs[k];
+                    }
                 }
-                yacc[j] += y;
-                gbacc[j] += gb;
-                qaacc[j] += qa;
-                wave_lds_order();
-                // lane (qq, jj) sums term jj over lanes 16 qq .. 16 qq + 15; the quarters then meet
-                const float4* rr = reinterpret_cast<const float4*>(red + (lane & 15) * 64 + 16 * (lane >> 4));
-                const float4 w0 = rr[0], w1 = rr[1], w2 = rr[2], w3 = rr[3];
-                float sum = ((w0.x + w0.y) + (w0.z + w0.w)) + ((w1.x + w1.y) + (w1.z + w1.w)) +
-                            (((w2.x + w2.y) + (w2.z + w2.w)) + ((w3.x + w3.y) + (w3.z + w3.w)));
-                sum = rows_sum(sum);
-                bcs[j] = sum;
-                wave_lds_order();
+#pragma unroll
+                for (int j = kQ * (c + 1) - 1; j >= kQ * c; --j) {
+                    bcs[j] = 0.0f;
+                    if (t0 + j >= a.L) continue;
+                    float bv[kH], cv[kH], p[kH], hc[kH];
+                    read_bc_half(sbc, j, hf, bv, cv);
+                    abar8<POW>(v.dt[j], a0[j], r.A2, hf, p);
+#pragma unroll
+                    for (int k = 0; k < kH; ++k) hc[k] = hbuf[((j - kQ * c) * kH + k) * 64 + lane];
+                    float y = 0.0f, gb = 0.0f, qa = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < kH; ++k) {
+                        const int n = kH * hf + k;
+                        const float G = fmaf(v.dy[j], cv[k], gc[n]);       // dL/dh_t
+                        y = fmaf(cv[k], hc[k], y);
+                        const float ah = fmaf(-v.x[j], bv[k], hc[k]);      // abar h_{t-1}
+                        const float qn = G * ah;
+                        qa = fmaf(POW ? static_cast<float>(n + 1) : r.An[n], qn, qa);
+                        gb = fmaf(G, bv[k], gb);
+                        dA[n] = fmaf(v.dt[j], qn, dA[n]);
+                        red[k * 64 + lane] = G * v.x[j];                   // dB term
+                        red[(kH + k) * 64 + lane] = v.dy[j] * hc[k];       // dC term
+                        gc[n] = p[k] * G;                                  // toward h_{t-1}
+                    }
+                    yacc[j] += y;
+                    gbacc[j] += gb;
+                    qaacc[j] += qa;
+                    wave_lds_order();
+                    // lane (qq, jj) sums term jj over lanes 16 qq .. 16 qq + 15; the quarters then meet
+                    const float4* rr = reinterpret_cast<const float4*>(red + (lane & 15) * 64 + 16 * (lane >> 4));
+                    const float4 w0 = rr[0], w1 = rr[1], w2 = rr[2], w3 = rr[3];
+                    float sum = ((w0.x + w0.y) + (w0.z + w0.w)) + ((w1.x + w1.y) + (w1.z + w1.w)) +
+                                (((w2.x + w2.y) + (w2.z + w2.w)) + ((w3.x + w3.y) + (w3.z + w3.w)));
+                    sum = rows_sum(sum);
+                    bcs[j] = sum;
+                    wave_lds_order();
+                }
             }
             if (lane < 2 * kH) {   // term lane: dB of state kH hf + lane, or dC of state kH hf + lane - kH
                 const int idx = lane < kH ? kH * hf + lane : kN + kH * hf + (lane - kH);
@@ -741,7 +754,7 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
 template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_main_kernel(BwdArgs a) {
     __shared__ __align__(16) float sbc[kBT * kBCs];
-    __shared__ __align__(16) float hbuf[kBT * kH * 64];
+    __shared__ __align__(16) float hbuf[q_steps<E>() * kH * 64];
     __shared__ __align__(16) float red[2 * kH * 64];
     __shared__ __align__(16) float hin[kN * 64];
     const Row r = row_of(a);
@@ -847,12 +860,12 @@ Layout layout_of(const BwdLaunch& a, int S) {
 }  // namespace
 
 // Segments per channel group: as many wavefronts as fit on the chip at once (the main kernel's
-// 26 KB of LDS and 256 VGPRs allow six per CU), at most one per tile.  MSS_BWD_SEGMENTS
-// overrides.
+// LDS and 256 VGPRs allow eight per CU for bf16 rows, six for fp32 rows), at most one per tile.
+// MSS_BWD_SEGMENTS overrides.
 int plan_bwd_segments(const BwdLaunch& a, int num_cus) {
     const int64_t groups = a.Bt * ((a.Dn + 63) / 64);
     const int64_t ntiles = (a.L + kBT - 1) / kBT;
-    const int64_t target = 6LL * (num_cus > 0 ? num_cus : 256);
+    const int64_t target = (a.bf16 ? 8LL : 6LL) * (num_cus > 0 ? num_cus : 256);
     int64_t S = groups > 0 ? target / groups : 1;  // one round: every wavefront resident at once
     const char* env = getenv("MSS_BWD_SEGMENTS");
     if (env && atoi(env) > 0) S = atoi(env);
