@@ -224,6 +224,44 @@ def conv_leg(mss, torch, devc, Bt, Dn, L, K=4, calls=20, warmup=3, copies=3):
                          "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4)}}
 
 
+def shard_leg(mss, torch, devc, s, Bt, Dn, N, L, calls=20, warmup=3):
+    """The forward at the per-GPU shapes of two ways to spread the layer over GPUs without any
+    exchange (rows are independent; B / C are replicated): channel split over 8 GPUs
+    (d_inner / 8 rows each) and batch split over 4 (one sequence each).  One GPU runs one
+    shard; the shapes have 8x / 4x fewer rows, so the segment plan has to fill the chip with
+    longer splits of L."""
+    import numpy as np
+    out = {}
+    for name, (b0, b1, d0, d1) in {"channel_split_8": (0, Bt, 0, Dn // 8),
+                                   "batch_split_4": (0, Bt // 4, 0, Dn)}.items():
+        sb, sd = slice(b0, b1), slice(d0, d1)
+
+        def t(a, bf16=False):
+            x = torch.from_numpy(np.ascontiguousarray(a)).to(devc)
+            return x.to(torch.bfloat16) if bf16 else x
+        u, dl, z = t(s.u[sb, sd], True), t(s.delta[sb, sd], True), t(s.z[sb, sd], True)
+        B, C = t(s.B[sb]), t(s.C[sb])
+        A, D, bias = t(s.A[sd]), t(s.D[sd]), t(s.delta_bias[sd])
+        o = torch.empty_like(u)
+        last = torch.empty((b1 - b0, d1 - d0, N), dtype=torch.float32, device=devc)
+        for _ in range(warmup):
+            mss.selective_scan_fwd(u, dl, A, B, C, D=D, z=z, delta_bias=bias, out=o, last_state=last)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        for k in range(calls):
+            ev[k][0].record(stream)
+            mss.selective_scan_fwd(u, dl, A, B, C, D=D, z=z, delta_bias=bias, out=o, last_state=last)
+            ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(c) for a, c in ev]
+        avg = sum(ms) / len(ms)
+        nb = scan_bytes(b1 - b0, d1 - d0, N, L)
+        out[name] = {"shape": [b1 - b0, d1 - d0, N, L], "avg_ms": round(avg, 4),
+                     "min_ms": round(min(ms), 4), "gbps": round(nb / (avg * 1e-3) / 1e9, 2)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,6 +272,7 @@ def main():
     ap.add_argument("--no-decode-chain", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
+    ap.add_argument("--no-shard", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build runs the scan on a single MI355X "
@@ -351,6 +390,8 @@ def main():
         res["scan_bwd"] = backward_leg(mss, torch, sets, A, D, bias, Bt, Dn, N, L, scan_avg_ms)
     if not args.no_conv:
         res["conv1d"] = conv_leg(mss, torch, devc, Bt, Dn, L)
+    if not args.no_shard:
+        res["shard_fwd"] = shard_leg(mss, torch, devc, s, Bt, Dn, N, L)
     if not args.no_decode_chain:
         res["decode_chain"] = decode_chain(mss, torch, devc)
     if not args.no_cpu_baseline:

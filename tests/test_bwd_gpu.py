@@ -119,6 +119,14 @@ def test_bwd_mamba2p8b_full(mss, oracle_mod):
     _check(mss, oracle_mod, s, 73, "bwd mamba2p8b")
 
 
+@pytest.mark.parametrize("Bt,Dn", [(4, 640), (1, 5120)])
+def test_bwd_mamba2p8b_shard_shapes(mss, oracle_mod, Bt, Dn):
+    """The 2.8B layer as one GPU's share (d_inner split 8 ways, batch split 4 ways): fewer rows,
+    so the plan cuts L into many more segments."""
+    s = scan_inputs(Bt, Dn, 16, CONFIGS["mamba2p8b_bf16"]["L"], dtype="bf16", seed=74 + Bt)
+    _check(mss, oracle_mod, s, 74 + Bt, f"bwd mamba2p8b shard {Bt}x{Dn}")
+
+
 def test_bwd_deterministic_and_linear(mss):
     import torch
     s = scan_inputs(2, 256, 16, 1024, dtype="f32", seed=74)

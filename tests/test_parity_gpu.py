@@ -73,6 +73,13 @@ def test_mamba2p8b_bf16_full(mss, orc):
     _check_scan(mss, orc, _cfg_inputs("mamba2p8b_bf16"), what="mamba2p8b_bf16")
 
 
+@pytest.mark.parametrize("Bt,Dn", [(4, 640), (1, 5120)])
+def test_mamba2p8b_shard_shapes(mss, orc, Bt, Dn):
+    """The 2.8B layer as one GPU's share: d_inner split 8 ways or batch split 4 ways (rows are
+    independent; fewer of them make the plan cut L into many more segments)."""
+    _check_scan(mss, orc, _cfg_inputs("mamba2p8b_bf16", batch=Bt, d_inner=Dn), what=f"mamba2p8b shard {Bt}x{Dn}")
+
+
 def test_long_fp32_sampled(mss, orc):
     s = _cfg_inputs("long_fp32")
     rows = sample_rows(s.u.shape[0] * s.u.shape[1], 64, seed=3)
