@@ -30,8 +30,9 @@
 //     tiles backward.  A tile's true start state is exp(A sum dt) h_in + its checkpoint (the
 //     recurrence is linear); its states are recomputed from there into LDS, 8 at a time, and
 //     consumed in reverse;
-//   * dB and dC sum over channels: per step the wave's 64 x 32 terms go through LDS and are
-//     summed per wave; a reduction kernel adds the per-wave sums of the channel groups.
+//   * dB and dC sum over channels: per step the wave's 64 x 32 terms are summed over its lanes
+//     with cross-lane swaps and DPP (no LDS); a reduction kernel adds the per-wave sums of the
+//     channel groups.
 //     dA / dD / dbias are per-lane sums, added over segments and batches by a second kernel.
 // Every sum is taken in a fixed order, so results do not vary from run to run.
 #include <cstdlib>
@@ -161,15 +162,46 @@ __device__ __forceinline__ void abar8(float dt, float a0, const float (&A2)[kN],
     }
 }
 
-// v summed over lanes k, k ^ 16, k ^ 32, k ^ 48 (the wave's four 16-lane rows), in every lane:
-// gfx950's row swaps exchange whole rows between two registers in the VALU, without a round
-// trip through LDS.  With both operands v, permlane16_swap leaves rows (0, 0, 2, 2) of v in its
-// first result and rows (1, 1, 3, 3) in its second; permlane32_swap does the same for row pairs.
-__device__ __forceinline__ float rows_sum(float v) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+// Sums 16 per-lane terms over the 64 lanes without LDS, halving the number of values per lane
+// at each level: across the wave halves (permlane32 swap), across row pairs (permlane16 swap),
+// then within 16-lane rows by DPP (lane + 8 of the row, the mirrored lane of each half-row,
+// lane ^ 2, lane ^ 1).  Every lane ends with the full sum of term sum16_term(lane); the four
+// lanes of a quad hold the same term.  gfx950's swaps exchange rows between two registers:
+// permlane16_swap(a, b) returns rows (a0, b0, a2, b2) and (a1, b1, a3, b3) of the 16-lane rows,
+// permlane32_swap(a, b) the halves (a_lo, b_lo) and (a_hi, b_hi); the sum of the pair is then
+// b's term summed over the row pair (or halves) in the odd rows (upper half), a's in the others.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ int sum16_term(int lane) {
+    const int b2 = (lane >> 2) & 1, b3 = (lane >> 3) & 1, odd = (lane >> 4) & 1, hi = (lane >> 5) & 1;
+    return b2 + 2 * b3 + 4 * (1 - odd) + 8 * (1 - hi);
+}
+
+__device__ __forceinline__ float lanes_sum16(const float (&t)[16]) {
+    const int lane = threadIdx.x & 63;
+    float u[8], v[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {  // lanes 0..31 keep term i + 8, lanes 32..63 term i
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(t[i + 8]), __float_as_uint(t[i]), false, false);
+        u[i] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // even rows keep u[i + 4], odd rows u[i]
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(u[i + 4]), __float_as_uint(u[i]), false, false);
+        v[i] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    }
+    const bool b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1;
+    // with lane + 8 of the row: bit 3 clear keeps v[0], v[1], set keeps v[2], v[3]
+    const float w0 = (b3 ? v[2] : v[0]) + dpp_f<0x128>(b3 ? v[0] : v[2]);
+    const float w1 = (b3 ? v[3] : v[1]) + dpp_f<0x128>(b3 ? v[1] : v[3]);
+    // with the mirrored lane of the half-row (bit 2 differs): bit 2 clear keeps w0, set keeps w1
+    float x = (b2 ? w1 : w0) + dpp_f<0x141>(b2 ? w0 : w1);
+    x += dpp_f<0x4E>(x);  // lane ^ 2
+    x += dpp_f<0xB1>(x);  // lane ^ 1
+    return x;
 }
 
 __device__ __forceinline__ float sigmoid(float v) { return fast_rcp(1.0f + fast_exp2(-v * kLog2e)); }
@@ -607,7 +639,7 @@ __device__ __forceinline__ void carries(const BwdArgs& a, const Row& r, int s, f
 
 template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z, bool POW>
 __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float* sbc, float* hbuf,
-                                          float* red, float* hin) {
+                                          float* hin) {
     const int s = blockIdx.z;
     const int lane = threadIdx.x;
     const int b = blockIdx.y;
@@ -681,7 +713,7 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
                     abar8<POW>(v.dt[j], a0[j], r.A2, hf, p);
 #pragma unroll
                     for (int k = 0; k < kH; ++k) hc[k] = hbuf[((j - kQ * c) * kH + k) * 64 + lane];
-                    float y = 0.0f, gb = 0.0f, qa = 0.0f;
+                    float y = 0.0f, gb = 0.0f, qa = 0.0f, tm[2 * kH];
 #pragma unroll
                     for (int k = 0; k < kH; ++k) {
                         const int n = kH * hf + k;
@@ -692,26 +724,19 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
                         qa = fmaf(POW ? static_cast<float>(n + 1) : r.An[n], qn, qa);
                         gb = fmaf(G, bv[k], gb);
                         dA[n] = fmaf(v.dt[j], qn, dA[n]);
-                        red[k * 64 + lane] = G * v.x[j];                   // dB term
-                        red[(kH + k) * 64 + lane] = v.dy[j] * hc[k];       // dC term
+                        tm[k] = G * v.x[j];                                // dB term
+                        tm[kH + k] = v.dy[j] * hc[k];                      // dC term
                         gc[n] = p[k] * G;                                  // toward h_{t-1}
                     }
                     yacc[j] += y;
                     gbacc[j] += gb;
                     qaacc[j] += qa;
-                    wave_lds_order();
-                    // lane (qq, jj) sums term jj over lanes 16 qq .. 16 qq + 15; the quarters then meet
-                    const float4* rr = reinterpret_cast<const float4*>(red + (lane & 15) * 64 + 16 * (lane >> 4));
-                    const float4 w0 = rr[0], w1 = rr[1], w2 = rr[2], w3 = rr[3];
-                    float sum = ((w0.x + w0.y) + (w0.z + w0.w)) + ((w1.x + w1.y) + (w1.z + w1.w)) +
-                                (((w2.x + w2.y) + (w2.z + w2.w)) + ((w3.x + w3.y) + (w3.z + w3.w)));
-                    sum = rows_sum(sum);
-                    bcs[j] = sum;
-                    wave_lds_order();
+                    bcs[j] = lanes_sum16(tm);  // over the wave's 64 channels
                 }
             }
-            if (lane < 2 * kH) {   // term lane: dB of state kH hf + lane, or dC of state kH hf + lane - kH
-                const int idx = lane < kH ? kH * hf + lane : kN + kH * hf + (lane - kH);
+            if ((lane & 3) == 0) {  // one lane per term: dB of state kH hf + k, or dC of state kH hf + k - kH
+                const int k = sum16_term(lane);
+                const int idx = k < kH ? kH * hf + k : kN + kH * hf + (k - kH);
                 float4* o = reinterpret_cast<float4*>(
                     a.part + (((int64_t)blockIdx.x * a.Bt + b) * (2 * kN) + idx) * a.tpad + t0);
                 o[0] = make_float4(bcs[0], bcs[1], bcs[2], bcs[3]);
@@ -755,11 +780,10 @@ template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_main_kernel(BwdArgs a) {
     __shared__ __align__(16) float sbc[kBT * kBCs];
     __shared__ __align__(16) float hbuf[q_steps<E>() * kH * 64];
-    __shared__ __align__(16) float red[2 * kH * 64];
     __shared__ __align__(16) float hin[kN * 64];
     const Row r = row_of(a);
-    if (__all(r.pow_ok)) main_body<E, VEC, SOFTPLUS, HAS_Z, true>(a, r, sbc, hbuf, red, hin);
-    else main_body<E, VEC, SOFTPLUS, HAS_Z, false>(a, r, sbc, hbuf, red, hin);
+    if (__all(r.pow_ok)) main_body<E, VEC, SOFTPLUS, HAS_Z, true>(a, r, sbc, hbuf, hin);
+    else main_body<E, VEC, SOFTPLUS, HAS_Z, false>(a, r, sbc, hbuf, hin);
 }
 
 // ---------------------------------------------------------------- reductions
