@@ -48,9 +48,10 @@ constexpr int kAggW = 2 * kN + 1; // aggregate words per (segment, row): sum dt 
 constexpr int kParW = kN + 2;     // partial words per (segment, row): dA[16] | dD | dbias
 constexpr int kBCs = 2 * kN + 4;  // LDS words per step of B | C (16-byte pad)
 constexpr int kCkW = kN + 1;      // checkpoint words per (tile, row): local state[16] | sum dt
-// Steps whose recomputed states the main kernel keeps in LDS at once: four for bf16 rows (17.5 KB
-// of LDS: eight wavefronts per CU, as many as the registers allow), the whole tile for fp32 rows
-// (their larger prefetched tiles leave no registers for the re-walk a smaller buffer costs).
+// Steps whose recomputed states the main kernel keeps in LDS at once: four for bf16 rows (13 KB
+// of LDS in all: eight wavefronts per CU, as many as the registers allow), the whole tile for
+// fp32 rows (21 KB: seven per CU; their larger prefetched tiles leave no registers for the
+// re-walk a smaller buffer costs, which measured slower).
 template <class E>
 constexpr int q_steps() { return sizeof(typename E::storage) == 2 ? 4 : kBT; }
 
@@ -884,12 +885,12 @@ Layout layout_of(const BwdLaunch& a, int S) {
 }  // namespace
 
 // Segments per channel group: as many wavefronts as fit on the chip at once (the main kernel's
-// LDS and 256 VGPRs allow eight per CU for bf16 rows, six for fp32 rows), at most one per tile.
+// LDS and 256 VGPRs allow eight per CU for bf16 rows, seven for fp32 rows), at most one per tile.
 // MSS_BWD_SEGMENTS overrides.
 int plan_bwd_segments(const BwdLaunch& a, int num_cus) {
     const int64_t groups = a.Bt * ((a.Dn + 63) / 64);
     const int64_t ntiles = (a.L + kBT - 1) / kBT;
-    const int64_t target = (a.bf16 ? 8LL : 6LL) * (num_cus > 0 ? num_cus : 256);
+    const int64_t target = (a.bf16 ? 8LL : 7LL) * (num_cus > 0 ? num_cus : 256);
     int64_t S = groups > 0 ? target / groups : 1;  // one round: every wavefront resident at once
     const char* env = getenv("MSS_BWD_SEGMENTS");
     if (env && atoi(env) > 0) S = atoi(env);
