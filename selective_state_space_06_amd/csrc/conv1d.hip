@@ -34,22 +34,24 @@ struct ConvArgs {
     int64_t Dn, L, R;
 };
 
-// Vectorised forward: V = 16 / sizeof(element) steps per thread.
-template <class E, int K, bool SILU>
+// Vectorised forward: V = 16 / sizeof(element) steps per thread.  I: the index type, 32-bit
+// when the vector count allows (its division is far shorter than a 64-bit one).
+template <class E, int K, bool SILU, class I>
 __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(ConvArgs a) {
     constexpr int V = E::kPerVec;
-    const int64_t nv = a.L / V;                 // vectors per row
-    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = a.R * nv;
+    const I nv = static_cast<I>(a.L / V);  // vectors per row
+    const I g = static_cast<I>(blockIdx.x) * static_cast<I>(blockDim.x) + static_cast<I>(threadIdx.x);
+    const I total = static_cast<I>(a.R) * nv;
     if (g >= total) return;
-    const int64_t r = g / nv, q = g % nv;
-    const int64_t d = r % a.Dn;
-    const auto* xs = static_cast<const typename E::storage*>(a.x);
-    // this thread's vector and the one before it in the row (a cache hit: the neighbouring lane
-    // loads it too), both issued before either is used
-    const uint4 raw = *reinterpret_cast<const uint4*>(xs + r * a.L + q * V);
+    const I r = g / nv, q = g % nv;
+    const int64_t d = static_cast<int64_t>(r % static_cast<I>(a.Dn));
+    const int64_t r64 = static_cast<int64_t>(r), q64 = static_cast<int64_t>(q);
+    const auto* xs = static_cast<const typename E::storage*>(a.x) + r64 * a.L;
+    const uint4 raw = *reinterpret_cast<const uint4*>(xs + q64 * V);
+    // the vector before it in the row (a cache hit: the neighbouring lane loads it too), issued
+    // before either is used
     uint4 praw = make_uint4(0, 0, 0, 0);
-    if (q > 0) praw = *reinterpret_cast<const uint4*>(xs + r * a.L + (q - 1) * V);
+    if (q > 0) praw = *reinterpret_cast<const uint4*>(xs + (q64 - 1) * V);
     float v[V], pv[V];
     E::unpack(raw, v);
     E::unpack(praw, pv);
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(ConvArgs a) {
     float halo[kMaxK - 1];
 #pragma unroll
     for (int j = 0; j < K - 1; ++j)
-        halo[j] = q > 0 ? pv[V - (K - 1) + j] : (a.state_in ? E::load1(a.state_in, r * (K - 1) + j) : 0.0f);
+        halo[j] = q > 0 ? pv[V - (K - 1) + j] : (a.state_in ? E::load1(a.state_in, r64 * (K - 1) + j) : 0.0f);
     float wk[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) wk[k] = a.w[d * K + k];
@@ -76,10 +78,10 @@ __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(ConvArgs a) {
         o[e] = SILU ? silu(y) : y;
     }
     auto* os = static_cast<typename E::storage*>(a.out);
-    *reinterpret_cast<uint4*>(os + r * a.L + q * V) = E::pack(o);
+    *reinterpret_cast<uint4*>(os + r64 * a.L + q64 * V) = E::pack(o);
     if (a.state_out && q == nv - 1) {
 #pragma unroll
-        for (int j = 0; j < K - 1; ++j) E::store1(a.state_out, r * (K - 1) + j, v[V - (K - 1) + j]);
+        for (int j = 0; j < K - 1; ++j) E::store1(a.state_out, r64 * (K - 1) + j, v[V - (K - 1) + j]);
     }
 }
 
@@ -152,7 +154,11 @@ hipError_t fwd_t(const ConvArgs& a, bool vec, hipStream_t s) {
     if (a.L > 0) {
         if (vec) {
             const int64_t total = a.R * (a.L / E::kPerVec);
-            conv_fwd_vec_kernel<E, K, SILU><<<dim3(blocks_for(total, INT32_MAX)), dim3(256), 0, s>>>(a);
+            const dim3 grid(blocks_for(total, INT32_MAX));
+            if (total + 256 < (int64_t)UINT32_MAX)
+                conv_fwd_vec_kernel<E, K, SILU, uint32_t><<<grid, dim3(256), 0, s>>>(a);
+            else
+                conv_fwd_vec_kernel<E, K, SILU, int64_t><<<grid, dim3(256), 0, s>>>(a);
         } else {
             conv_fwd_elem_kernel<E, K, SILU><<<dim3(blocks_for(a.R * a.L)), dim3(256), 0, s>>>(a);
         }
