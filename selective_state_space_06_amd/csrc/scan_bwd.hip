@@ -412,7 +412,7 @@ __device__ __forceinline__ void lds_reads_done() {
 // the recurrences of H (the state from h = 0), Rp (the product of abar since the segment start)
 // and Lam (the adjoint carry).
 struct AggState {
-    float H[kN], Lam[kN], Rp[kN];
+    float H[kN], Lam[kN], Rp[kN];  // Rp: the power path keeps only Rp[0]
     float dsum;
 };
 
@@ -439,10 +439,27 @@ __device__ __forceinline__ void agg_tile(const BwdArgs& a, const Row& r, int64_t
         abar16<POW>(v.dt[j], r.A2, p);
         st.dsum += v.dt[j];
 #pragma unroll
-        for (int n = 0; n < kN; ++n) {
-            st.H[n] = fmaf(p[n], st.H[n], v.x[j] * bv[n]);
-            st.Rp[n] *= p[n];
-            st.Lam[n] = fmaf(st.Rp[n], v.dy[j] * cv[n], st.Lam[n]);
+        for (int n = 0; n < kN; ++n) st.H[n] = fmaf(p[n], st.H[n], v.x[j] * bv[n]);
+        if (POW) {
+            // the product of abar_n since the segment start is R^(n+1), R that of abar_0: the
+            // weights dy R^(n+1) come from four interleaved chains stepping by R^4
+            st.Rp[0] *= p[0];
+            const float R = st.Rp[0], R2 = R * R, R4 = R2 * R2;
+            float q[4] = {v.dy[j] * R, v.dy[j] * R2, v.dy[j] * (R2 * R), v.dy[j] * R4};
+#pragma unroll
+            for (int n = 0; n < kN; n += 4) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    st.Lam[n + i] = fmaf(q[i], cv[n + i], st.Lam[n + i]);
+                    if (n + 4 < kN) q[i] *= R4;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < kN; ++n) {
+                st.Rp[n] *= p[n];
+                st.Lam[n] = fmaf(st.Rp[n], v.dy[j] * cv[n], st.Lam[n]);
+            }
         }
     }
 }
