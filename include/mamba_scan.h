@@ -78,7 +78,8 @@ typedef struct {
  * d_state must be 16.  out must not overlap any input or last_state.  A and last_state must
  * be 16-byte aligned (MSS_ERR_LAYOUT otherwise).  When every row of u / delta / z / out spans
  * a multiple of 16 bytes and those tensors and B / C start 16-byte aligned, the vectorised
- * kernels run; any other valid layout takes a slower general path with the same results.
+ * kernels run with aligned 16-byte accesses; any other valid layout runs the same kernels with
+ * element-aligned accesses (about 1.5x the time on the Mamba-2.8B layer shape).
  */
 int mss_selective_scan_fwd(const mss_tensor_t* u, const mss_tensor_t* delta,
                            const mss_tensor_t* A, const mss_tensor_t* B, const mss_tensor_t* C,

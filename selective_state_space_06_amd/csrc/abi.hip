@@ -443,7 +443,9 @@ int mss_selective_scan_fwd_varlen(const mss_tensor_t* u, const mss_tensor_t* del
         int dev = 0, cus = 0;
         if (hipGetDevice(&dev) != hipSuccess) return MSS_ERR_HIP;
         if (device_cus(dev, &cus) != hipSuccess) return MSS_ERR_HIP;
-        const bool fast = a.vec_ok && a.L > 0 && getenv("MSS_SCAN_GENERIC") == nullptr;
+        // the fast path takes every length (rows that are not whole 16-byte vectors run its
+        // element-aligned variant); the generic kernels remain behind MSS_SCAN_GENERIC
+        const bool fast = a.L > 0 && getenv("MSS_SCAN_GENERIC") == nullptr;
         mss::ScanPlan plan;
         if (fast) {
             plan = mss::plan_fast(a, cus);

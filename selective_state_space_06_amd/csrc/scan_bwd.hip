@@ -332,13 +332,14 @@ __device__ __forceinline__ void load_raw(const BwdArgs& a, const Row& r, int64_t
     load_bc<VEC>(a, t0, w.bc);
 }
 
-// The tile's B | C block into LDS, time-major: sbc[t][n] = B, sbc[t][16 + n] = C.
-__device__ __forceinline__ void put_bc(const float (&bc)[4], float* sbc) {
+// The tile's B | C block into LDS, time-major: sbc[t][n] = B, sbc[t][16 + n] = C.  Steps at or
+// past the batch's length stage as zeros: whatever the tensors hold there cannot reach a sum.
+__device__ __forceinline__ void put_bc(const float (&bc)[4], float* sbc, int64_t t0, int64_t stop) {
     const int lane = threadIdx.x;
     const int half = lane & 1;
     const int col = (lane >= 32 ? kN : 0) + ((lane >> 1) & (kN - 1));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sbc[(4 * half + e) * kBCs + col] = bc[e];
+    for (int e = 0; e < 4; ++e) sbc[(4 * half + e) * kBCs + col] = t0 + 4 * half + e < stop ? bc[e] : 0.0f;
 }
 
 // Per-step scalars of one lane.  Inactive lanes and steps past L get dt = x = dy = 0, which
@@ -501,7 +502,7 @@ __device__ __forceinline__ void agg_body(const BwdArgs& a, const Row& r, float* 
         StepVals v;
         step_vals<E, VEC, SOFTPLUS, HAS_Z>(a, r, t0, cur, v);
         wave_lds_order();  // after the previous tile's reads of the B / C block
-        put_bc(cur.bc, sbc);
+        put_bc(cur.bc, sbc, t0, r.stop);
         wave_lds_order();
         agg_tile<POW>(a, r, t0, v, sbc, st);
     }
@@ -604,7 +605,7 @@ __device__ __forceinline__ void agg_body_staged(const BwdArgs& a, const Row& r_i
             StepVals v;
             step_vals<E, true, SOFTPLUS, HAS_Z>(a, r, t0, cur, v);
             wave_lds_order();  // after the previous tile's reads of the B / C block
-            put_bc(cur.bc, sbc);
+            put_bc(cur.bc, sbc, t0, r.stop);
             wave_lds_order();
             agg_tile<POW>(a, r, t0, v, sbc, st);
             if (k + 1 < G::TPB) cur = nx;
@@ -688,7 +689,7 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
 #pragma unroll
         for (int j = 0; j < kBT; ++j) a0[j] = POW ? fast_exp2(v.dt[j] * r.A2[0]) : 0.0f;
         wave_lds_order();  // after the previous tile's reads of the B / C block
-        put_bc(cur.bc, sbc);
+        put_bc(cur.bc, sbc, t0, r.stop);
         wave_lds_order();
         // The tile's 16 states in two halves of 8 (the states are independent in the recurrence;
         // only the outputs' sums over n combine the halves): recompute the half's states from

@@ -102,19 +102,38 @@ struct RawUD {
     uint32_t u[4 * kNV], d[4 * kNV];
 };
 
+// The 16-byte vector of row rp at step t.  RAGGED (rows of any length, so only element-aligned):
+// an unaligned 16-byte load (gfx950 serves it whole), and a vector running past the row's end
+// L is read element by element with zeros after the end, so no load leaves the row's tensor.
+// (t and L are the same for every lane: the choice is uniform.)
+template <class E, bool RAGGED>
+__device__ __forceinline__ uint4 load_vec(const typename E::storage* __restrict__ rp, int64_t t, int64_t L) {
+    constexpr int V = E::kPerVec;
+    if (!RAGGED) return *reinterpret_cast<const uint4*>(rp + t);
+    if (t + V <= L) {
+        uint4 w;
+        __builtin_memcpy(&w, rp + t, 16);
+        return w;
+    }
+    float f[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) f[e] = t + e < L ? E::load1(rp, t + e) : 0.0f;
+    return E::pack(f);  // exact: the values came from this storage type
+}
+
 // Vectors at or past t_end re-read the last valid vector (their steps are never used), so every
-// load is unconditional and in bounds.
-template <class E>
+// load is unconditional and in bounds.  RAGGED: vectors past the row's end read as zeros.
+template <class E, bool RAGGED>
 __device__ __forceinline__ void load_ud(RawUD& r, const typename E::storage* __restrict__ up,
                                         const typename E::storage* __restrict__ dp, int64_t t0,
-                                        int64_t t_end) {
+                                        int64_t t_end, int64_t L) {
     constexpr int V = E::kPerVec;
 #pragma unroll
     for (int v = 0; v < kNV; ++v) {
         int64_t t = t0 + v * V;
-        t = t < t_end ? t : t_end - V;
-        const uint4 a = *reinterpret_cast<const uint4*>(up + t);
-        const uint4 b = *reinterpret_cast<const uint4*>(dp + t);
+        if (!RAGGED) t = t < t_end ? t : t_end - V;
+        const uint4 a = load_vec<E, RAGGED>(up, t, L);
+        const uint4 b = load_vec<E, RAGGED>(dp, t, L);
         r.u[4 * v] = a.x; r.u[4 * v + 1] = a.y; r.u[4 * v + 2] = a.z; r.u[4 * v + 3] = a.w;
         r.d[4 * v] = b.x; r.d[4 * v + 1] = b.y; r.d[4 * v + 2] = b.z; r.d[4 * v + 3] = b.w;
     }
@@ -139,7 +158,7 @@ struct RawBC {
     uint32_t w[4 * Geo<E>::kBCChunks];
 };
 
-template <class E, bool WITH_C>
+template <class E, bool WITH_C, bool RAGGED>
 __device__ __forceinline__ void load_bc(RawBC<E>& r, const float* __restrict__ Bb,
                                         const float* __restrict__ Cb, int64_t L, int64_t t0,
                                         int64_t t_end) {
@@ -150,8 +169,8 @@ __device__ __forceinline__ void load_bc(RawBC<E>& r, const float* __restrict__ B
         const float* src = k < K / 2 ? Bb : Cb;
         const int kk = k % (K / 2);
         int64_t t = t0 + 4 * (4 * kk + (threadIdx.x >> 4));
-        t = t < t_end ? t : t_end - 4;
-        const uint4 v = *reinterpret_cast<const uint4*>(src + n * L + t);
+        if (!RAGGED) t = t < t_end ? t : t_end - 4;
+        const uint4 v = load_vec<F32, RAGGED>(src + n * L, t, L);
         r.w[4 * k] = v.x; r.w[4 * k + 1] = v.y; r.w[4 * k + 2] = v.z; r.w[4 * k + 3] = v.w;
     }
 }
@@ -159,8 +178,10 @@ __device__ __forceinline__ void load_bc(RawBC<E>& r, const float* __restrict__ B
 // Time-major LDS block: step t of the tile at sbc + t * SB, B_t in floats [0, 16), C_t in
 // [16, 32).  SB = 16 (B only) + 4 or 32 + 4: the 4 spare floats per step put the 16 lanes x 4
 // step groups of each scattered 4-byte store in 64 distinct banks.
-template <class E, bool WITH_C>
-__device__ __forceinline__ void stage_bc(float* sbc, const RawBC<E>& r) {
+// VARLEN: B and C at or past the batch's length stage as zeros, so whatever the tensors hold
+// there (padding) cannot reach the state through x B with x = 0.
+template <class E, bool WITH_C, bool VARLEN>
+__device__ __forceinline__ void stage_bc(float* sbc, const RawBC<E>& r, int64_t t0, int64_t stop) {
     constexpr int K = Geo<E>::kBCChunks;
     constexpr int SB = WITH_C ? 36 : 20;
     const int n = threadIdx.x & 15;
@@ -170,7 +191,10 @@ __device__ __forceinline__ void stage_bc(float* sbc, const RawBC<E>& r) {
         const int t = 4 * (4 * kk + (threadIdx.x >> 4));
         float* dst = sbc + t * SB + (k < K / 2 ? 0 : kN) + n;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i * SB] = __uint_as_float(r.w[4 * k + i]);
+        for (int i = 0; i < 4; ++i) {
+            const float v = __uint_as_float(r.w[4 * k + i]);
+            dst[i * SB] = (VARLEN && t0 + t + i >= stop) ? 0.0f : v;
+        }
     }
 }
 
@@ -210,8 +234,8 @@ __device__ __forceinline__ Pair pair_of(const uint32_t* su, const uint32_t* sd, 
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         p.d[i] = delta_of<SOFTPLUS>(r[i], rs.bias);
-        if (VARLEN && t0 + j + i >= rs.stop) p.d[i] = 0.0f;  // past the sequence: an identity step
         p.x[i] = p.d[i] * u[i];
+        if (VARLEN && t0 + j + i >= rs.stop) p.d[i] = p.x[i] = 0.0f;  // past the sequence: an identity step
         p.a[i] = POW ? fast_exp2(p.d[i] * rs.A2[0]) : 0.0f;
         p.du[i] = WITH_DU ? rs.dskip * u[i] : 0.0f;
     }
@@ -294,7 +318,15 @@ __device__ __forceinline__ float step_main(float (&h)[kN], const float (&A2)[kN]
     return y0 + y1;
 }
 
-template <class E, bool HAS_Z, bool SOFTPLUS, bool POW, bool VARLEN>
+// Steps the loops of a tile run: a multiple of 4 (RAGGED: rounded up; the extra steps lie past
+// the row's end and are identity steps).
+template <bool RAGGED, int TT>
+__device__ __forceinline__ int tile_steps(int64_t t0, int64_t t_end) {
+    const int64_t n = t_end - t0 < TT ? t_end - t0 : TT;
+    return static_cast<int>(RAGGED ? ((n + 3) & ~static_cast<int64_t>(3)) : n);
+}
+
+template <class E, bool HAS_Z, bool SOFTPLUS, bool POW, bool VARLEN, bool RAGGED>
 __device__ __forceinline__ void main_body(
     const RowSetup& rs, float (&h)[kN], const typename E::storage* __restrict__ up,
     const typename E::storage* __restrict__ dp, const typename E::storage* __restrict__ zp,
@@ -306,28 +338,28 @@ __device__ __forceinline__ void main_body(
     const uint32_t* sd = srow + W * 64;
     RawUD pre;
     RawBC<E> bpre;
-    load_ud<E>(pre, up, dp, t_begin, t_end);
-    load_bc<E, true>(bpre, Bb, Cb, L, t_begin, t_end);
+    load_ud<E, RAGGED>(pre, up, dp, t_begin, t_end, L);
+    load_bc<E, true, RAGGED>(bpre, Bb, Cb, L, t_begin, t_end);
     for (int64_t t0 = t_begin; t0 < t_end; t0 += TT) {
         __syncthreads();  // the previous tile's reads of the shared B|C block are done
         stage_ud<E>(srow, pre);
-        stage_bc<E, true>(sbc, bpre);
+        stage_bc<E, true, VARLEN>(sbc, bpre, t0, rs.stop);
         __syncthreads();
         uint32_t zw[4 * kNV];  // z of this tile, consumed by the epilogue
         if (HAS_Z) {
 #pragma unroll
             for (int v = 0; v < kNV; ++v) {
                 int64_t t = t0 + v * V;
-                t = t < t_end ? t : t_end - V;
-                const uint4 a = *reinterpret_cast<const uint4*>(zp + t);
+                if (!RAGGED) t = t < t_end ? t : t_end - V;
+                const uint4 a = load_vec<E, RAGGED>(zp, t, L);
                 zw[4 * v] = a.x; zw[4 * v + 1] = a.y; zw[4 * v + 2] = a.z; zw[4 * v + 3] = a.w;
             }
         }
         if (t0 + TT < t_end) {
-            load_ud<E>(pre, up, dp, t0 + TT, t_end);
-            load_bc<E, true>(bpre, Bb, Cb, L, t0 + TT, t_end);
+            load_ud<E, RAGGED>(pre, up, dp, t0 + TT, t_end, L);
+            load_bc<E, true, RAGGED>(bpre, Bb, Cb, L, t0 + TT, t_end);
         }
-        const int nsteps = static_cast<int>(t_end - t0 < TT ? t_end - t0 : TT);  // multiple of 4
+        const int nsteps = tile_steps<RAGGED, TT>(t0, t_end);  // multiple of 4
         Pair cur = pair_of<E, SOFTPLUS, POW, true, VARLEN>(su, sd, 0, rs, t0);
 #pragma unroll 1
         for (int j = 0; j < nsteps; j += 2) {
@@ -355,8 +387,18 @@ __device__ __forceinline__ void main_body(
         }
         if (rs.active) {
 #pragma unroll
-            for (int v = 0; v < kNV; ++v)
-                if (t0 + v * V < t_end) *reinterpret_cast<uint4*>(op + t0 + v * V) = packed[v];
+            for (int v = 0; v < kNV; ++v) {
+                const int64_t t = t0 + v * V;
+                if (!RAGGED) {
+                    if (t < t_end) *reinterpret_cast<uint4*>(op + t) = packed[v];
+                } else if (t + V <= t_end) {
+                    __builtin_memcpy(op + t, &packed[v], 16);  // element-aligned 16-byte store
+                } else if (t < t_end) {  // the row's last, partial vector: only its own elements
+#pragma unroll
+                    for (int e = 0; e < V; ++e)
+                        if (t + e < t_end) E::store1(op, t + e, vec_elem<E>(&packed[v].x, e));
+                }
+            }
         }
     }
 }
@@ -436,7 +478,7 @@ __device__ __forceinline__ void fold_carry(float (&h)[kN], const float (&A2)[kN]
     }
 }
 
-template <class E, bool HAS_Z, bool SOFTPLUS, bool VARLEN>
+template <class E, bool HAS_Z, bool SOFTPLUS, bool VARLEN, bool RAGGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void scan_main_kernel(
     const typename E::storage* __restrict__ u, const typename E::storage* __restrict__ delta,
     const typename E::storage* __restrict__ z, const float* __restrict__ A,
@@ -459,12 +501,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sc
     float h[kN];
     if (__all(rs.pow_ok)) {
         fold_carry<true>(h, rs.A2, agg, h0, seg, R, rs.row);
-        main_body<E, HAS_Z, SOFTPLUS, true, VARLEN>(rs, h, u + base, delta + base, zp, out + base, Bb, Cb, L,
-                                            srow, sbc, t_begin, t_end);
+        main_body<E, HAS_Z, SOFTPLUS, true, VARLEN, RAGGED>(rs, h, u + base, delta + base, zp, out + base, Bb, Cb,
+                                                    L, srow, sbc, t_begin, t_end);
     } else {
         fold_carry<false>(h, rs.A2, agg, h0, seg, R, rs.row);
-        main_body<E, HAS_Z, SOFTPLUS, false, VARLEN>(rs, h, u + base, delta + base, zp, out + base, Bb, Cb, L,
-                                             srow, sbc, t_begin, t_end);
+        main_body<E, HAS_Z, SOFTPLUS, false, VARLEN, RAGGED>(rs, h, u + base, delta + base, zp, out + base, Bb, Cb,
+                                                     L, srow, sbc, t_begin, t_end);
     }
     if (last_state && rs.active && seg == S - 1) {
         float4* dst = reinterpret_cast<float4*>(last_state + rs.row * kN);
@@ -477,7 +519,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sc
 // Aggregate of one segment: (sum of delta, end state of the segment started from h = 0).
 // POW walks the segment backward (acc_n += x_s B_s R^(n+1), R the product of the later
 // Abar_0); the general path runs the recurrence forward without outputs.
-template <class E, bool SOFTPLUS, bool POW, bool VARLEN>
+template <class E, bool SOFTPLUS, bool POW, bool VARLEN, bool RAGGED>
 __device__ __forceinline__ void agg_body(const RowSetup& rs, const typename E::storage* __restrict__ up,
                                          const typename E::storage* __restrict__ dp,
                                          const float* __restrict__ Bb, int64_t L, uint32_t* srow,
@@ -496,19 +538,19 @@ __device__ __forceinline__ void agg_body(const RowSetup& rs, const typename E::s
     const int64_t ntiles = (t_end - t_begin + TT - 1) / TT;
     // tiles in visiting order (POW: from the last tile of the segment back to the first)
     int64_t t0 = POW ? t_begin + (ntiles - 1) * TT : t_begin;
-    load_ud<E>(pre, up, dp, t0, t_end);
-    load_bc<E, false>(bpre, Bb, nullptr, L, t0, t_end);
+    load_ud<E, RAGGED>(pre, up, dp, t0, t_end, L);
+    load_bc<E, false, RAGGED>(bpre, Bb, nullptr, L, t0, t_end);
     for (int64_t k = 0; k < ntiles; ++k) {
         __syncthreads();
         stage_ud<E>(srow, pre);
-        stage_bc<E, false>(sbc, bpre);
+        stage_bc<E, false, VARLEN>(sbc, bpre, t0, rs.stop);
         __syncthreads();
         const int64_t tnext = POW ? t0 - TT : t0 + TT;
         if (k + 1 < ntiles) {
-            load_ud<E>(pre, up, dp, tnext, t_end);
-            load_bc<E, false>(bpre, Bb, nullptr, L, tnext, t_end);
+            load_ud<E, RAGGED>(pre, up, dp, tnext, t_end, L);
+            load_bc<E, false, RAGGED>(bpre, Bb, nullptr, L, tnext, t_end);
         }
-        const int nsteps = static_cast<int>(t_end - t0 < TT ? t_end - t0 : TT);
+        const int nsteps = tile_steps<RAGGED, TT>(t0, t_end);
         if (POW) {
             // The scalars and the B values of the next pair are read one iteration ahead, so an
             // iteration does not start by waiting for its own LDS reads (unrolled by two so the
@@ -546,7 +588,8 @@ __device__ __forceinline__ void agg_body(const RowSetup& rs, const typename E::s
                 const float4* b1 = reinterpret_cast<const float4*>(sbc + (j + 1) * 20);
                 const float d0 = (VARLEN && t0 + j >= rs.stop) ? 0.0f : delta_of<SOFTPLUS>(r0, rs.bias);
                 const float d1 = (VARLEN && t0 + j + 1 >= rs.stop) ? 0.0f : delta_of<SOFTPLUS>(r1, rs.bias);
-                const float x0 = d0 * u0, x1 = d1 * u1;
+                const float x0 = (VARLEN && t0 + j >= rs.stop) ? 0.0f : d0 * u0;
+                const float x1 = (VARLEN && t0 + j + 1 >= rs.stop) ? 0.0f : d1 * u1;
 #pragma unroll
                 for (int q = 0; q < kN / 4; ++q) {
                     const float4 y0 = b0[q], y1 = b1[q];
@@ -566,7 +609,7 @@ __device__ __forceinline__ void agg_body(const RowSetup& rs, const typename E::s
     }
 }
 
-template <class E, bool SOFTPLUS, bool VARLEN>
+template <class E, bool SOFTPLUS, bool VARLEN, bool RAGGED>
 __global__ __launch_bounds__(64) void scan_agg_kernel(
     const typename E::storage* __restrict__ u, const typename E::storage* __restrict__ delta,
     const float* __restrict__ A, const float* __restrict__ B, const float* __restrict__ bias,
@@ -583,9 +626,11 @@ __global__ __launch_bounds__(64) void scan_agg_kernel(
     const float* Bb = B + (int64_t)blockIdx.y * kN * L;
     float acc[kN], dsum;
     if (__all(rs.pow_ok))
-        agg_body<E, SOFTPLUS, true, VARLEN>(rs, u + base, delta + base, Bb, L, srow, sbc, t_begin, t_end, acc, dsum);
+        agg_body<E, SOFTPLUS, true, VARLEN, RAGGED>(rs, u + base, delta + base, Bb, L, srow, sbc, t_begin, t_end, acc,
+                                                    dsum);
     else
-        agg_body<E, SOFTPLUS, false, VARLEN>(rs, u + base, delta + base, Bb, L, srow, sbc, t_begin, t_end, acc, dsum);
+        agg_body<E, SOFTPLUS, false, VARLEN, RAGGED>(rs, u + base, delta + base, Bb, L, srow, sbc, t_begin, t_end, acc,
+                                                     dsum);
     if (rs.active) {
         float* a = agg + (int64_t)seg * (kN + 1) * R + rs.row;
 #pragma unroll
@@ -594,7 +639,7 @@ __global__ __launch_bounds__(64) void scan_agg_kernel(
     }
 }
 
-template <class E, bool HAS_Z, bool SOFTPLUS, bool VARLEN>
+template <class E, bool HAS_Z, bool SOFTPLUS, bool VARLEN, bool RAGGED>
 hipError_t launch_fast_t(const ScanLaunch& a, const ScanPlan& p, float* ws, hipStream_t stream) {
     using S_t = typename E::storage;
     float* agg = ws;
@@ -602,28 +647,33 @@ hipError_t launch_fast_t(const ScanLaunch& a, const ScanPlan& p, float* ws, hipS
     const unsigned gx = static_cast<unsigned>((a.Dn + 63) / 64);
     mark(a, 0, stream);
     if (p.segments > 1)
-        scan_agg_kernel<E, SOFTPLUS, VARLEN><<<dim3(gx, (unsigned)a.Bt, (unsigned)(p.segments - 1)), block, 0, stream>>>(
+        scan_agg_kernel<E, SOFTPLUS, VARLEN, RAGGED><<<dim3(gx, (unsigned)a.Bt, (unsigned)(p.segments - 1)), block, 0, stream>>>(
             static_cast<const S_t*>(a.u), static_cast<const S_t*>(a.delta), a.A, a.B, a.bias, agg, a.lens, a.Dn,
             a.L, p.segments);
     mark(a, 1, stream);
-    scan_main_kernel<E, HAS_Z, SOFTPLUS, VARLEN><<<dim3(gx, (unsigned)a.Bt, (unsigned)p.segments), block, 0, stream>>>(
+    scan_main_kernel<E, HAS_Z, SOFTPLUS, VARLEN, RAGGED><<<dim3(gx, (unsigned)a.Bt, (unsigned)p.segments), block, 0, stream>>>(
         static_cast<const S_t*>(a.u), static_cast<const S_t*>(a.delta), static_cast<const S_t*>(a.z), a.A, a.B,
         a.C, a.D, a.bias, agg, a.h0, static_cast<S_t*>(a.out), a.last_state, a.lens, a.Dn, a.L, p.segments);
     mark(a, 2, stream);
     return hipGetLastError();
 }
 
-template <class E, bool VARLEN>
+template <class E, bool VARLEN, bool RAGGED>
 hipError_t launch_fast_v(const ScanLaunch& a, const ScanPlan& p, float* ws, hipStream_t stream) {
     const bool hz = a.z != nullptr;
     if (a.softplus)
-        return hz ? launch_fast_t<E, true, true, VARLEN>(a, p, ws, stream) : launch_fast_t<E, false, true, VARLEN>(a, p, ws, stream);
-    return hz ? launch_fast_t<E, true, false, VARLEN>(a, p, ws, stream) : launch_fast_t<E, false, false, VARLEN>(a, p, ws, stream);
+        return hz ? launch_fast_t<E, true, true, VARLEN, RAGGED>(a, p, ws, stream)
+                  : launch_fast_t<E, false, true, VARLEN, RAGGED>(a, p, ws, stream);
+    return hz ? launch_fast_t<E, true, false, VARLEN, RAGGED>(a, p, ws, stream)
+              : launch_fast_t<E, false, false, VARLEN, RAGGED>(a, p, ws, stream);
 }
 
+// Rows of any length (not whole 16-byte vectors) run the same kernels with element-aligned
+// loads and stores and the steps past L masked as with per-batch lengths.
 template <class E>
 hipError_t launch_fast_e(const ScanLaunch& a, const ScanPlan& p, float* ws, hipStream_t stream) {
-    return a.lens ? launch_fast_v<E, true>(a, p, ws, stream) : launch_fast_v<E, false>(a, p, ws, stream);
+    if (!a.vec_ok) return launch_fast_v<E, true, true>(a, p, ws, stream);
+    return a.lens ? launch_fast_v<E, true, false>(a, p, ws, stream) : launch_fast_v<E, false, false>(a, p, ws, stream);
 }
 
 }  // namespace

@@ -160,9 +160,9 @@ __device__ __forceinline__ void scan_body(const KArgs& a, Smem<TT>& sm, const in
                 const float pre = dv[e] + br;
                 float dlt = a.softplus ? softplus(pre) : pre;
                 // padded steps and steps past the batch's length: identity update
-                dlt = (row_ok && tl + e < tvalid && t0 + tl + e < stop) ? dlt : 0.0f;
-                dl[e] = dlt;
-                xv[e] = dlt * uv[e];
+                const bool live = row_ok && tl + e < tvalid && t0 + tl + e < stop;
+                dl[e] = live ? dlt : 0.0f;
+                xv[e] = live ? dlt * uv[e] : 0.0f;
             }
 #pragma unroll
             for (int q = 0; q < V / 4; ++q) {
@@ -182,8 +182,8 @@ __device__ __forceinline__ void scan_body(const KArgs& a, Smem<TT>& sm, const in
                 const int tl = (lane % BCHUNK) * 4;
                 const float* src = (rr < kN ? a.B : a.C) + ((int64_t)b * kN + (rr % kN)) * L + t0 + tl;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sm.bc[tl + e][rr] = (tl + e < tvalid) ? src[e] : 0.0f;
+                for (int e = 0; e < 4; ++e)  // past the batch's length: zeros, whatever the padding holds
+                    sm.bc[tl + e][rr] = (tl + e < tvalid && t0 + tl + e < stop) ? src[e] : 0.0f;
             }
         }
         // prefetch z for phase C while the recurrence runs

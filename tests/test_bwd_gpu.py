@@ -168,8 +168,12 @@ def _gpu_ext(mss, s, dout, h0=None, lens=None, dlast=None):
                                   return_dinitial_state=True)
 
 
-@pytest.mark.parametrize("Bt,Dn,L,dtype", [(4, 64, 256, "bf16"), (4, 70, 100, "f32"), (6, 128, 520, "bf16")])
-def test_bwd_state_lengths_parity(mss, oracle_mod, Bt, Dn, L, dtype):
+@pytest.mark.parametrize("Bt,Dn,L,dtype,nan_pad", [
+    (4, 64, 256, "bf16", False), (4, 70, 100, "f32", False), (6, 128, 520, "bf16", False),
+    (4, 64, 256, "bf16", True), (4, 70, 101, "f32", True)])
+def test_bwd_state_lengths_parity(mss, oracle_mod, Bt, Dn, L, dtype, nan_pad):
+    """nan_pad: past each sequence's end u, delta, z, B, C and dout hold NaN / inf, which the
+    oracle never reads; no gradient may pick them up."""
     import torch
     s = scan_inputs(Bt, Dn, 16, L, dtype=dtype, seed=80 + L)
     rng = np.random.default_rng(81)
@@ -177,6 +181,14 @@ def test_bwd_state_lengths_parity(mss, oracle_mod, Bt, Dn, L, dtype):
     h0 = (0.5 * rng.standard_normal((Bt, Dn, 16))).astype(np.float32)
     dlast = rng.standard_normal((Bt, Dn, 16)).astype(np.float32)
     lens = np.array(([0, 1, L // 2 + 3, L] * 2)[:Bt], dtype=np.int32)
+    if nan_pad:
+        for b, n in enumerate(lens):
+            s.u[b, :, n:] = np.nan
+            s.delta[b, :, n:] = np.inf
+            s.z[b, :, n:] = np.nan
+            s.B[b, :, n:] = np.inf
+            s.C[b, :, n:] = np.nan
+            dout[b, :, n:] = np.nan
     g = _gpu_ext(mss, s, dout, h0, lens, dlast)
     torch.cuda.synchronize()
     kw = dict(D=s.D, z=s.z, delta_bias=s.delta_bias, dout=dout, h0=h0, seq_lens=lens, dlast=dlast)

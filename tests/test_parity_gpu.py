@@ -80,6 +80,26 @@ def test_mamba2p8b_shard_shapes(mss, orc, Bt, Dn):
     _check_scan(mss, orc, _cfg_inputs("mamba2p8b_bf16", batch=Bt, d_inner=Dn), what=f"mamba2p8b shard {Bt}x{Dn}")
 
 
+@pytest.mark.parametrize("name,L", [("mamba2p8b_bf16", 2047), ("mamba2p8b_bf16", 2044), ("mamba130m_fp32", 2047),
+                                    ("mamba130m_fp32", 2046)])
+def test_ragged_length_full_size(mss, orc, name, L):
+    """L that is not a whole number of 16-byte vectors: rows start at element offsets that are
+    not 16-byte aligned and end in a partial vector (the fast path's element-aligned variant)."""
+    _check_scan(mss, orc, _cfg_inputs(name, L=L), what=f"{name} L={L}")
+
+
+def test_ragged_rows_match_generic_path(mss, monkeypatch):
+    """The element-aligned fast path and the generic kernels agree to rounding on ragged rows."""
+    import torch
+    s = scan_inputs(3, 200, 16, 777, dtype="bf16", seed=24)
+    out_f, last_f = run_scan(mss, s)
+    monkeypatch.setenv("MSS_SCAN_GENERIC", "1")
+    out_g, last_g = run_scan(mss, s)
+    torch.cuda.synchronize()
+    assert_close(host64(out_f), host64(out_g), what="fast vs generic out", **TOL_BF16)
+    assert_close(host64(last_f), host64(last_g), what="fast vs generic last_state", **TOL_F32)
+
+
 def test_long_fp32_sampled(mss, orc):
     s = _cfg_inputs("long_fp32")
     rows = sample_rows(s.u.shape[0] * s.u.shape[1], 64, seed=3)

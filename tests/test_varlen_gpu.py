@@ -87,6 +87,35 @@ def test_varlen_generic_path(mss, oracle_mod, dtype, monkeypatch):
     _check(mss, oracle_mod, s, _lens(6, 300, 63), what=f"varlen generic {dtype}")
 
 
+@pytest.mark.parametrize("dtype,generic", [("bf16", False), ("f32", False), ("bf16", True), ("f32", True)])
+def test_varlen_padding_never_reaches_results(mss, oracle_mod, dtype, generic, monkeypatch):
+    """Past each sequence's end the tensors hold NaN / inf (u, delta, z and B, C of that batch):
+    the oracle never reads there, so outputs and final states must match it exactly as with finite
+    padding -- masked steps may not multiply padding by zero."""
+    if generic:
+        monkeypatch.setenv("MSS_SCAN_GENERIC", "1")
+    Bt, Dn, L = 6, 96, 300
+    s = scan_inputs(Bt, Dn, 16, L, dtype=dtype, seed=66)
+    lens = _lens(Bt, L, 66)
+    for b, n in enumerate(lens):
+        s.u[b, :, n:] = np.nan
+        s.delta[b, :, n:] = np.inf
+        s.z[b, :, n:] = np.nan
+        s.B[b, :, n:] = np.inf
+        s.C[b, :, n:] = np.nan
+    _check(mss, oracle_mod, s, lens, what=f"varlen nan padding {dtype} generic={generic}")
+
+
+@pytest.mark.parametrize("L", [2047, 2041, 1001])
+def test_varlen_ragged_length_mamba2p8b_sampled(mss, oracle_mod, L):
+    """Lengths and L that are not whole 16-byte vectors (rows start at odd element offsets)."""
+    c = CONFIGS["mamba2p8b_bf16"]
+    s = scan_inputs(c["batch"], c["d_inner"], 16, L, dtype="bf16", seed=67)
+    lens = np.array([L, 1, L - 8, 1000], dtype=np.int32)
+    rows = sample_rows(c["batch"] * c["d_inner"], 64, seed=67)
+    _check(mss, oracle_mod, s, lens, rows=rows, what=f"varlen mamba2p8b L={L}")
+
+
 def test_varlen_mamba2p8b_sampled(mss, oracle_mod):
     c = CONFIGS["mamba2p8b_bf16"]
     s = scan_inputs(c["batch"], c["d_inner"], 16, c["L"], dtype="bf16", seed=64)
