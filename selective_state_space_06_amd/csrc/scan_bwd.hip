@@ -207,46 +207,28 @@ __device__ __forceinline__ float lanes_sum16(const float (&t)[16]) {
 
 __device__ __forceinline__ float sigmoid(float v) { return fast_rcp(1.0f + fast_exp2(-v * kLog2e)); }
 
-// One tile (kBT steps from t0) of the lane's row; steps at or past L read as 0.  VEC: whole
-// 16-byte vectors (L is then a multiple of the vector length, so a vector is entirely valid or
-// entirely past the end).
-template <class E, bool VEC>
-__device__ __forceinline__ void load_tile(const void* base, int64_t off, int64_t t0, int64_t L,
-                                          float (&v)[kBT]) {
-    const typename E::storage* p = static_cast<const typename E::storage*>(base) + off;
-    if (VEC) {
-        constexpr int V = E::kPerVec;
-#pragma unroll
-        for (int q = 0; q < kBT / V; ++q) {
-            float w[V];
-            if (t0 + q * V < L) {
-                E::unpack(*reinterpret_cast<const uint4*>(p + t0 + q * V), w);
-            } else {
-#pragma unroll
-                for (int e = 0; e < V; ++e) w[e] = 0.0f;
-            }
-#pragma unroll
-            for (int e = 0; e < V; ++e) v[q * V + e] = w[e];
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < kBT; ++i) v[i] = (t0 + i < L) ? E::load1(p, t0 + i) : 0.0f;
-    }
-}
-
+// One tile (kBT steps from t0) of the lane's row into the output.  VEC: whole aligned 16-byte
+// vectors (L is then a multiple of the vector length, so a vector is entirely valid or entirely
+// past the end).  Otherwise (rows of any length, element-aligned): element-aligned 16-byte
+// stores, and the vector that crosses the row's end element by element.
 template <class E, bool VEC>
 __device__ __forceinline__ void store_tile(void* base, int64_t off, int64_t t0, int64_t L,
                                            const float (&v)[kBT]) {
     typename E::storage* p = static_cast<typename E::storage*>(base) + off;
-    if (VEC) {
-        constexpr int V = E::kPerVec;
+    constexpr int V = E::kPerVec;
 #pragma unroll
-        for (int q = 0; q < kBT / V; ++q)
-            if (t0 + q * V < L) *reinterpret_cast<uint4*>(p + t0 + q * V) = E::pack(&v[q * V]);
-    } else {
+    for (int q = 0; q < kBT / V; ++q) {
+        const int64_t t = t0 + q * V;
+        if (VEC) {
+            if (t < L) *reinterpret_cast<uint4*>(p + t) = E::pack(&v[q * V]);
+        } else if (t + V <= L) {
+            const uint4 w = E::pack(&v[q * V]);
+            __builtin_memcpy(p + t, &w, 16);
+        } else {
 #pragma unroll
-        for (int i = 0; i < kBT; ++i)
-            if (t0 + i < L) E::store1(p, t0 + i, v[i]);
+            for (int e = 0; e < V; ++e)
+                if (t + e < L) E::store1(p, t + e, v[q * V + e]);
+        }
     }
 }
 
@@ -272,7 +254,7 @@ __device__ __forceinline__ void read_bc_half(const float* sbc, int j, int hf, fl
     }
 }
 
-// One tile of the lane's inputs as loaded (VEC: the 16-byte vectors, converted when used, so the
+// One tile of the lane's inputs as loaded (the 16-byte vectors, converted when used, so the
 // loads of the next tile can be in flight while this one is computed), plus the lane's four
 // B or C values for the tile's LDS block.
 template <class E, bool VEC>
@@ -281,20 +263,30 @@ struct Raw {
     uint4 u[NV], d[NV], g[NV], z[NV];
     float bc[4];
 };
-template <class E>
-struct Raw<E, false> {
-    float u[kBT], d[kBT], g[kBT], z[kBT];
-    float bc[4];
-};
 
+// The tile's vectors of one array; past the row's end they read as zeros.  VEC: aligned 16-byte
+// loads.  Otherwise (rows of any length): element-aligned 16-byte loads, and the vector that
+// crosses the row's end element by element, so no load leaves the row's tensor.  (t0 and L are
+// the same for every lane: the choice is uniform.)
 template <class E, bool VEC>
 __device__ __forceinline__ void raw_row(const void* base, int64_t off, int64_t t0, int64_t L,
                                         uint4 (&w)[Raw<E, true>::NV]) {
     const typename E::storage* p = static_cast<const typename E::storage*>(base) + off;
     constexpr int V = E::kPerVec;
 #pragma unroll
-    for (int q = 0; q < Raw<E, true>::NV; ++q)
-        w[q] = (t0 + q * V < L) ? *reinterpret_cast<const uint4*>(p + t0 + q * V) : make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < Raw<E, true>::NV; ++q) {
+        const int64_t t = t0 + q * V;
+        if (VEC) {
+            w[q] = t < L ? *reinterpret_cast<const uint4*>(p + t) : make_uint4(0, 0, 0, 0);
+        } else if (t + V <= L) {
+            __builtin_memcpy(&w[q], p + t, 16);
+        } else {
+            float f[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) f[e] = t + e < L ? E::load1(p, t + e) : 0.0f;
+            w[q] = E::pack(f);  // exact: the values came from this storage type
+        }
+    }
 }
 
 // B or C of one tile: lanes 0..31 load B, 32..63 load C, four steps of one state each.
@@ -309,6 +301,8 @@ __device__ __forceinline__ void load_bc(const BwdArgs& a, int64_t t0, float (&bc
         const bool in = tb < a.L;
         const float4 v = *reinterpret_cast<const float4*>(src + (in ? tb : a.L - 4));
         bc[0] = in ? v.x : 0.0f; bc[1] = in ? v.y : 0.0f; bc[2] = in ? v.z : 0.0f; bc[3] = in ? v.w : 0.0f;
+    } else if (tb + 4 <= a.L) {  // rows of any length: an element-aligned 16-byte load
+        __builtin_memcpy(bc, src + tb, 16);
     } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) bc[e] = (tb + e < a.L) ? src[tb + e] : 0.0f;
@@ -318,17 +312,10 @@ __device__ __forceinline__ void load_bc(const BwdArgs& a, int64_t t0, float (&bc
 template <class E, bool VEC, bool HAS_Z>
 __device__ __forceinline__ void load_raw(const BwdArgs& a, const Row& r, int64_t t0, Raw<E, VEC>& w) {
     const int64_t off = r.row * a.L;
-    if constexpr (VEC) {
-        raw_row<E, VEC>(a.u, off, t0, a.L, w.u);
-        raw_row<E, VEC>(a.delta, off, t0, a.L, w.d);
-        raw_row<E, VEC>(a.dout, off, t0, a.L, w.g);
-        if (HAS_Z) raw_row<E, VEC>(a.z, off, t0, a.L, w.z);
-    } else {
-        load_tile<E, false>(a.u, off, t0, a.L, w.u);
-        load_tile<E, false>(a.delta, off, t0, a.L, w.d);
-        load_tile<E, false>(a.dout, off, t0, a.L, w.g);
-        if (HAS_Z) load_tile<E, false>(a.z, off, t0, a.L, w.z);
-    }
+    raw_row<E, VEC>(a.u, off, t0, a.L, w.u);
+    raw_row<E, VEC>(a.delta, off, t0, a.L, w.d);
+    raw_row<E, VEC>(a.dout, off, t0, a.L, w.g);
+    if (HAS_Z) raw_row<E, VEC>(a.z, off, t0, a.L, w.z);
     load_bc<VEC>(a, t0, w.bc);
 }
 
@@ -352,20 +339,13 @@ template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z>
 __device__ __forceinline__ void step_vals(const BwdArgs& a, const Row& r, int64_t t0, const Raw<E, VEC>& w,
                                           StepVals& s) {
     float dv[kBT], gv[kBT], zv[kBT];
-    if constexpr (VEC) {
-        constexpr int V = E::kPerVec;
+    constexpr int V = E::kPerVec;
 #pragma unroll
-        for (int q = 0; q < Raw<E, true>::NV; ++q) {
-            E::unpack(w.u[q], &s.u[q * V]);
-            E::unpack(w.d[q], &dv[q * V]);
-            E::unpack(w.g[q], &gv[q * V]);
-            if (HAS_Z) E::unpack(w.z[q], &zv[q * V]);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < kBT; ++j) {
-            s.u[j] = w.u[j]; dv[j] = w.d[j]; gv[j] = w.g[j]; zv[j] = HAS_Z ? w.z[j] : 0.0f;
-        }
+    for (int q = 0; q < Raw<E, true>::NV; ++q) {
+        E::unpack(w.u[q], &s.u[q * V]);
+        E::unpack(w.d[q], &dv[q * V]);
+        E::unpack(w.g[q], &gv[q * V]);
+        if (HAS_Z) E::unpack(w.z[q], &zv[q * V]);
     }
 #pragma unroll
     for (int j = 0; j < kBT; ++j) {

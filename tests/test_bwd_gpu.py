@@ -113,10 +113,13 @@ def test_bwd_segment_splits(mss, oracle_mod, segments, monkeypatch):
     _check(mss, oracle_mod, s, 72, f"bwd segments={segments}")
 
 
-def test_bwd_mamba2p8b_full(mss, oracle_mod):
+@pytest.mark.parametrize("L", [2048, 2047])
+def test_bwd_mamba2p8b_full(mss, oracle_mod, L):
+    """The 2.8B layer; at L = 2047 the rows are not whole 16-byte vectors (element-aligned
+    accesses, a partial vector at each row's end)."""
     c = CONFIGS["mamba2p8b_bf16"]
-    s = scan_inputs(c["batch"], c["d_inner"], 16, c["L"], dtype="bf16", seed=73)
-    _check(mss, oracle_mod, s, 73, "bwd mamba2p8b")
+    s = scan_inputs(c["batch"], c["d_inner"], 16, L, dtype="bf16", seed=73)
+    _check(mss, oracle_mod, s, 73, f"bwd mamba2p8b L={L}")
 
 
 @pytest.mark.parametrize("Bt,Dn", [(4, 640), (1, 5120)])
