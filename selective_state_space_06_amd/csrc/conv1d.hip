@@ -35,11 +35,14 @@ struct ConvArgs {
 };
 
 // Vectorised forward: V = 16 / sizeof(element) steps per thread.  I: the index type, 32-bit
-// when the vector count allows (its division is far shorter than a 64-bit one).
-template <class E, int K, bool SILU, class I>
+// when the vector count allows (its division is far shorter than a 64-bit one).  RAGGED: rows
+// of any length (element-aligned, not whole vectors): element-aligned 16-byte loads and stores,
+// the row's last, partial vector element by element (no access leaves the row), and the final
+// state left to conv_state_kernel.
+template <class E, int K, bool SILU, class I, bool RAGGED>
 __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(ConvArgs a) {
     constexpr int V = E::kPerVec;
-    const I nv = static_cast<I>(a.L / V);  // vectors per row
+    const I nv = static_cast<I>(RAGGED ? (a.L + V - 1) / V : a.L / V);  // vectors per row
     const I g = static_cast<I>(blockIdx.x) * static_cast<I>(blockDim.x) + static_cast<I>(threadIdx.x);
     const I total = static_cast<I>(a.R) * nv;
     if (g >= total) return;
@@ -47,11 +50,25 @@ __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(ConvArgs a) {
     const int64_t d = static_cast<int64_t>(r % static_cast<I>(a.Dn));
     const int64_t r64 = static_cast<int64_t>(r), q64 = static_cast<int64_t>(q);
     const auto* xs = static_cast<const typename E::storage*>(a.x) + r64 * a.L;
-    const uint4 raw = *reinterpret_cast<const uint4*>(xs + q64 * V);
-    // the vector before it in the row (a cache hit: the neighbouring lane loads it too), issued
-    // before either is used
+    const bool whole = !RAGGED || q64 * V + V <= a.L;  // this vector lies inside the row
+    uint4 raw;
+    if (!RAGGED) {
+        raw = *reinterpret_cast<const uint4*>(xs + q64 * V);
+    } else if (whole) {
+        __builtin_memcpy(&raw, xs + q64 * V, 16);
+    } else {
+        float f[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) f[e] = q64 * V + e < a.L ? E::load1(xs, q64 * V + e) : 0.0f;
+        raw = E::pack(f);  // exact: the values came from this storage type
+    }
+    // the vector before it in the row (a cache hit: the neighbouring lane loads it too; always
+    // whole), issued before either is used
     uint4 praw = make_uint4(0, 0, 0, 0);
-    if (q > 0) praw = *reinterpret_cast<const uint4*>(xs + (q64 - 1) * V);
+    if (q > 0) {
+        if (RAGGED) __builtin_memcpy(&praw, xs + (q64 - 1) * V, 16);
+        else praw = *reinterpret_cast<const uint4*>(xs + (q64 - 1) * V);
+    }
     float v[V], pv[V];
     E::unpack(raw, v);
     E::unpack(praw, pv);
@@ -77,35 +94,24 @@ __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(ConvArgs a) {
         }
         o[e] = SILU ? silu(y) : y;
     }
-    auto* os = static_cast<typename E::storage*>(a.out);
-    *reinterpret_cast<uint4*>(os + r64 * a.L + q64 * V) = E::pack(o);
-    if (a.state_out && q == nv - 1) {
+    auto* os = static_cast<typename E::storage*>(a.out) + r64 * a.L;
+    const uint4 packed = E::pack(o);
+    if (!RAGGED) {
+        *reinterpret_cast<uint4*>(os + q64 * V) = packed;
+    } else if (whole) {
+        __builtin_memcpy(os + q64 * V, &packed, 16);
+    } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+            if (q64 * V + e < a.L) E::store1(os, q64 * V + e, o[e]);
+    }
+    if (!RAGGED && a.state_out && q == nv - 1) {
 #pragma unroll
         for (int j = 0; j < K - 1; ++j) E::store1(a.state_out, r64 * (K - 1) + j, v[V - (K - 1) + j]);
     }
 }
 
-// Any layout: one thread per output element.
-template <class E, int K, bool SILU>
-__global__ __launch_bounds__(256) void conv_fwd_elem_kernel(ConvArgs a) {
-    const int64_t total = a.R * a.L;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = i / a.L, t = i % a.L, d = r % a.Dn;
-        float y = a.bias ? a.bias[d] : 0.0f;
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int64_t s = t - (K - 1) + k;
-            float xv;
-            if (s >= 0) xv = E::load1(a.x, r * a.L + s);
-            else xv = a.state_in ? E::load1(a.state_in, r * (K - 1) + (s + K - 1)) : 0.0f;
-            y = fmaf(a.w[d * K + k], xv, y);
-        }
-        E::store1(a.out, i, SILU ? silu(y) : y);
-    }
-}
-
-// final state for the element path (and for L < K - 1 on any path): the last K - 1 inputs,
+// final state for rows of any length (and for L = 0): the last K - 1 inputs,
 // taken from the carried state where the sequence is shorter than that.
 template <class E, int K>
 __global__ __launch_bounds__(256) void conv_state_kernel(ConvArgs a) {
@@ -149,21 +155,25 @@ unsigned blocks_for(int64_t n, int64_t cap = 1 << 20) {
     return static_cast<unsigned>(b);
 }
 
+template <class E, int K, bool SILU, bool RAGGED>
+void fwd_vec(const ConvArgs& a, hipStream_t s) {
+    constexpr int V = E::kPerVec;
+    const int64_t total = a.R * ((a.L + V - 1) / V);
+    const dim3 grid(blocks_for(total, INT32_MAX));
+    if (total + 256 < (int64_t)UINT32_MAX)
+        conv_fwd_vec_kernel<E, K, SILU, uint32_t, RAGGED><<<grid, dim3(256), 0, s>>>(a);
+    else
+        conv_fwd_vec_kernel<E, K, SILU, int64_t, RAGGED><<<grid, dim3(256), 0, s>>>(a);
+}
+
+// vec: rows are whole aligned 16-byte vectors; otherwise the element-aligned variant.
 template <class E, int K, bool SILU>
 hipError_t fwd_t(const ConvArgs& a, bool vec, hipStream_t s) {
     if (a.L > 0) {
-        if (vec) {
-            const int64_t total = a.R * (a.L / E::kPerVec);
-            const dim3 grid(blocks_for(total, INT32_MAX));
-            if (total + 256 < (int64_t)UINT32_MAX)
-                conv_fwd_vec_kernel<E, K, SILU, uint32_t><<<grid, dim3(256), 0, s>>>(a);
-            else
-                conv_fwd_vec_kernel<E, K, SILU, int64_t><<<grid, dim3(256), 0, s>>>(a);
-        } else {
-            conv_fwd_elem_kernel<E, K, SILU><<<dim3(blocks_for(a.R * a.L)), dim3(256), 0, s>>>(a);
-        }
+        if (vec) fwd_vec<E, K, SILU, false>(a, s);
+        else fwd_vec<E, K, SILU, true>(a, s);
     }
-    // the vector path writes the final state itself (L >= V >= K - 1 there)
+    // the aligned vector path writes the final state itself (L >= V >= K - 1 there)
     if (K > 1 && a.state_out && (!vec || a.L == 0))
         conv_state_kernel<E, K><<<dim3(blocks_for(a.R * (K - 1))), dim3(256), 0, s>>>(a);
     return hipGetLastError();

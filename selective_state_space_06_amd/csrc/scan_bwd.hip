@@ -464,7 +464,8 @@ __device__ __forceinline__ void agg_init(AggState& st) {
     st.dsum = 0.0f;
 }
 
-// Any layout: each tile's inputs come straight into registers, one tile ahead.
+// Each tile's inputs come straight into registers, one tile ahead (any layout; rows of whole
+// 16-byte vectors use the staged variant below).
 template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z, bool POW>
 __device__ __forceinline__ void agg_body(const BwdArgs& a, const Row& r, float* sbc) {
     const int s = blockIdx.z;

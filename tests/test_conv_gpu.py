@@ -61,12 +61,15 @@ def test_conv_no_bias(mss, oracle_mod):
     assert_close(host64(out), ref, what="conv no bias", **TOL_F32)
 
 
-def test_conv_mamba2p8b_full(mss, oracle_mod):
+@pytest.mark.parametrize("L", [2048, 2047, 2042])
+def test_conv_mamba2p8b_full(mss, oracle_mod, L):
+    """The 2.8B layer shape; L not a multiple of 8 runs the element-aligned variant."""
     c = CONFIGS["mamba2p8b_bf16"]
-    x, w, b, st = _inputs(c["batch"], c["d_inner"], c["L"], 4, "bf16", 2)
-    out, fin = mss.causal_conv1d_fwd(dev(x, "bf16"), dev(w), dev(b), return_final_state=True)
-    ref, rfin = oracle_mod.causal_conv1d(x, w, b)
-    assert_close(host64(out), ref, what="conv mamba2p8b", **TOL_BF16)
+    x, w, b, st = _inputs(c["batch"], c["d_inner"], L, 4, "bf16", 2)
+    out, fin = mss.causal_conv1d_fwd(dev(x, "bf16"), dev(w), dev(b), initial_state=dev(st, "bf16"),
+                                     return_final_state=True)
+    ref, rfin = oracle_mod.causal_conv1d(x, w, b, state=st)
+    assert_close(host64(out), ref, what=f"conv mamba2p8b L={L}", **TOL_BF16)
     np.testing.assert_array_equal(host64(fin), rfin)
 
 
