@@ -36,8 +36,30 @@ def compile_flags() -> list[str]:
             "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 
 
+EXAMPLE_SRC = os.path.join(PKG_DIR, "examples", "scan_from_c.c")
+EXAMPLE_BIN = os.path.join(PKG_DIR, "examples", "scan_from_c")
+
+
+def build_example(verbose: bool = False) -> str:
+    """Compile the plain-C example against the built library (host code only: gcc and the HIP
+    runtime's C API). Returns the executable's path."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = [os.environ.get("CC", "gcc"), "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", INCLUDE, EXAMPLE_SRC, "-L", PKG_DIR, "-lmamba_scan",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath,$ORIGIN/..",
+           "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", EXAMPLE_BIN]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        sys.stderr.write(proc.stdout + proc.stderr)
+        raise RuntimeError(f"compiling the C example failed with exit code {proc.returncode}")
+    return EXAMPLE_BIN
+
+
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    """Compile every source into LIB_PATH (atomically replaced). Returns the path."""
+    """Compile every source into LIB_PATH (atomically replaced), then the C example against it.
+    Returns the library's path."""
     tmp = LIB_PATH + f".tmp{os.getpid()}"
     cmd = [hipcc(), *compile_flags(), *(extra or []), "-shared",
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
@@ -48,6 +70,7 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
         sys.stderr.write(proc.stdout + proc.stderr)
         raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
     os.replace(tmp, LIB_PATH)
+    build_example(verbose)
     return LIB_PATH
 
 
