@@ -189,6 +189,51 @@ int mss_selective_scan_bwd_varlen(const mss_tensor_t* u, const mss_tensor_t* del
                                   const mss_tensor_t* dinitial_state, void* stream);
 
 /*
+ * mss_selective_scan_fwd_varlen that also keeps the states its backward needs, so that
+ * mss_selective_scan_bwd_saved need not recompute them: saved_states[k] receives h entering step
+ * 8k (h_{8k-1} of the recurrence; initial_state, or 0, for k = 0) for every 8k < L.  Past a
+ * sequence's end (seq_lens) the state is held, so the entries there repeat the final state.
+ *   saved_states  (ceil(L / 8), d_state / 4, batch * d_inner * 4) f32, written: state n of row
+ *                 r = b * d_inner + d entering step 8k is at [k][n / 4][4 r + n % 4] (planes of
+ *                 four states, so that 64 rows' float4s are one contiguous 1 KiB run); dense,
+ *                 16-byte aligned; may not overlap any input or output (MSS_ERR_ALIAS).
+ *                 NULL: exactly mss_selective_scan_fwd_varlen.
+ * Costs 64 / 8 = 8 bytes of extra writes per (batch, d_inner, step).  Every other argument as
+ * for mss_selective_scan_fwd_varlen; out and last_state are bit-identical to it.
+ */
+int mss_selective_scan_fwd_save(const mss_tensor_t* u, const mss_tensor_t* delta,
+                                const mss_tensor_t* A, const mss_tensor_t* B,
+                                const mss_tensor_t* C, const mss_tensor_t* D,
+                                const mss_tensor_t* z, const mss_tensor_t* delta_bias,
+                                const mss_tensor_t* initial_state, const mss_tensor_t* seq_lens,
+                                int softplus_flag, const mss_tensor_t* out,
+                                const mss_tensor_t* last_state, const mss_tensor_t* saved_states,
+                                void* stream);
+
+/*
+ * mss_selective_scan_bwd_varlen from the states saved by mss_selective_scan_fwd_save (the same
+ * inputs; the forward's initial_state is carried inside saved_states, so it is not passed):
+ * the backward then skips its forward recomputation.  Results agree with
+ * mss_selective_scan_bwd_varlen to rounding (the states come from the forward's own order of
+ * operations), and need a smaller workspace (no checkpoints).
+ *   saved_states  as written by mss_selective_scan_fwd_save for these inputs, read only; NULL
+ *                 gives MSS_ERR_NULL_ARG; no output may overlap it (MSS_ERR_ALIAS).
+ * Every other argument as for mss_selective_scan_bwd_varlen.
+ */
+int mss_selective_scan_bwd_saved(const mss_tensor_t* u, const mss_tensor_t* delta,
+                                 const mss_tensor_t* A, const mss_tensor_t* B,
+                                 const mss_tensor_t* C, const mss_tensor_t* D,
+                                 const mss_tensor_t* z, const mss_tensor_t* delta_bias,
+                                 const mss_tensor_t* seq_lens, int softplus_flag,
+                                 const mss_tensor_t* saved_states, const mss_tensor_t* dout,
+                                 const mss_tensor_t* dlast_state, const mss_tensor_t* du,
+                                 const mss_tensor_t* ddelta, const mss_tensor_t* dA,
+                                 const mss_tensor_t* dB, const mss_tensor_t* dC,
+                                 const mss_tensor_t* dD, const mss_tensor_t* dz,
+                                 const mss_tensor_t* ddelta_bias,
+                                 const mss_tensor_t* dinitial_state, void* stream);
+
+/*
  * One recurrent (decode) step: the same equations for a single token, continuing from
  * `state`, which is updated in place (the recurrent mode the mamba-jax README's `--scan`
  * generation loop and the upstream README's generation benchmark run token by token).

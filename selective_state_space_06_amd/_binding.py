@@ -19,6 +19,7 @@ STATUS = {0: "MSS_OK", -1: "MSS_ERR_NULL_ARG", -2: "MSS_ERR_SHAPE", -3: "MSS_ERR
 # every symbol include/mamba_scan.h declares
 EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_fwd_with_state",
            "mss_selective_scan_fwd_varlen", "mss_selective_scan_bwd", "mss_selective_scan_bwd_varlen",
+           "mss_selective_scan_fwd_save", "mss_selective_scan_bwd_saved",
            "mss_selective_state_update", "mss_causal_conv1d_fwd", "mss_causal_conv1d_update", "mss_profile_enable", "mss_profile_fwd",
            "mss_status_string", "mss_version")
 
@@ -88,6 +89,14 @@ def load_library(path: str = LIB_PATH):
             lib.mss_selective_scan_bwd_varlen.restype = ctypes.c_int
             lib.mss_selective_scan_bwd_varlen.argtypes = [
                 _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, ctypes.c_int, _TP, _TP,
+                _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, ctypes.c_void_p]
+            lib.mss_selective_scan_fwd_save.restype = ctypes.c_int
+            lib.mss_selective_scan_fwd_save.argtypes = [
+                _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, ctypes.c_int, _TP, _TP, _TP,
+                ctypes.c_void_p]
+            lib.mss_selective_scan_bwd_saved.restype = ctypes.c_int
+            lib.mss_selective_scan_bwd_saved.argtypes = [
+                _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, ctypes.c_int, _TP, _TP, _TP,
                 _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, ctypes.c_void_p]
             lib.mss_selective_state_update.restype = ctypes.c_int
             lib.mss_selective_state_update.argtypes = [_TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP,
@@ -173,6 +182,26 @@ def scan_bwd_varlen_raw(u, delta, A, B, C, D, z, delta_bias, initial_state, seq_
     return load_library().mss_selective_scan_bwd_varlen(
         _ref(u), _ref(delta), _ref(A), _ref(B), _ref(C), _ref(D), _ref(z), _ref(delta_bias),
         _ref(initial_state), _ref(seq_lens), int(softplus_flag), _ref(dout), _ref(dlast_state),
+        _ref(du), _ref(ddelta), _ref(dA), _ref(dB), _ref(dC), _ref(dD), _ref(dz),
+        _ref(ddelta_bias), _ref(dinitial_state), stream)
+
+
+def scan_fwd_save_raw(u, delta, A, B, C, D, z, delta_bias, initial_state, seq_lens, softplus_flag,
+                      out, last_state, saved_states, stream) -> int:
+    """Direct call of mss_selective_scan_fwd_save with Tensor descriptors (or None)."""
+    return load_library().mss_selective_scan_fwd_save(
+        _ref(u), _ref(delta), _ref(A), _ref(B), _ref(C), _ref(D), _ref(z), _ref(delta_bias),
+        _ref(initial_state), _ref(seq_lens), int(softplus_flag), _ref(out), _ref(last_state),
+        _ref(saved_states), stream)
+
+
+def scan_bwd_saved_raw(u, delta, A, B, C, D, z, delta_bias, seq_lens, softplus_flag, saved_states,
+                       dout, dlast_state, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias,
+                       dinitial_state, stream) -> int:
+    """Direct call of mss_selective_scan_bwd_saved with Tensor descriptors (or None)."""
+    return load_library().mss_selective_scan_bwd_saved(
+        _ref(u), _ref(delta), _ref(A), _ref(B), _ref(C), _ref(D), _ref(z), _ref(delta_bias),
+        _ref(seq_lens), int(softplus_flag), _ref(saved_states), _ref(dout), _ref(dlast_state),
         _ref(du), _ref(ddelta), _ref(dA), _ref(dB), _ref(dC), _ref(dD), _ref(dz),
         _ref(ddelta_bias), _ref(dinitial_state), stream)
 
@@ -271,12 +300,14 @@ def causal_conv1d_update(state, x, weight, bias=None, silu=True, out=None):
 
 def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
                        delta_softplus=True, initial_state=None, seq_lens=None, dlast_state=None,
-                       return_dinitial_state=False):
+                       return_dinitial_state=False, saved_states=None):
     """Gradients of selective_scan_fwd (from h = 0) for L = sum(dout * out), on the current
     stream.  Returns a dict: du, ddelta, dz (None without z) in u's dtype; dA, dB, dC, dD,
     ddelta_bias in float32 (dD / ddelta_bias also when D / delta_bias is None).
     initial_state / seq_lens describe the forward (as selective_scan_fwd_varlen); dlast_state is
-    dL/d last_state; with return_dinitial_state the dict also holds dinitial_state = dL/dh0."""
+    dL/d last_state; with return_dinitial_state the dict also holds dinitial_state = dL/dh0.
+    saved_states: the states selective_scan_fwd_save wrote for this forward (it carries the
+    forward's initial_state); the backward then reads them instead of recomputing them."""
     import torch
     dev_ = u.device
     Bt, Dn, L = u.shape
@@ -292,6 +323,17 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
         g["dinitial_state"] = torch.empty((Bt, Dn, N), **f32)
     with torch.cuda.device(dev_):
         stream = torch.cuda.current_stream(dev_).cuda_stream
+        if saved_states is not None:
+            st = scan_bwd_saved_raw(_desc(u), _desc(delta), _desc(A), _desc(B), _desc(C), _desc(D),
+                                    _desc(z), _desc(delta_bias), _desc(seq_lens),
+                                    1 if delta_softplus else 0, _desc(saved_states), _desc(dout),
+                                    _desc(dlast_state), _desc(g["du"]), _desc(g["ddelta"]),
+                                    _desc(g["dA"]), _desc(g["dB"]), _desc(g["dC"]), _desc(g["dD"]),
+                                    _desc(g["dz"]), _desc(g["ddelta_bias"]),
+                                    _desc(g.get("dinitial_state")), stream)
+            if st != 0:
+                raise MssError(st, "mss_selective_scan_bwd_saved")
+            return g
         st = scan_bwd_varlen_raw(_desc(u), _desc(delta), _desc(A), _desc(B), _desc(C), _desc(D),
                                  _desc(z), _desc(delta_bias), _desc(initial_state),
                                  _desc(seq_lens), 1 if delta_softplus else 0, _desc(dout),
@@ -305,18 +347,20 @@ def selective_scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
 
 
 class SelectiveScanFunction:
-    """torch.autograd wrapper: out = selective_scan_fwd(...) with gradients from
-    mss_selective_scan_bwd (the forward states are recomputed there, not kept).  Marshalling only:
+    """torch.autograd wrapper: out = selective_scan_fwd(...) with gradients from the library's
+    backward.  save_states=True keeps the forward's states at every eighth step (8 bytes per
+    (batch, d_inner, step)) for the backward; False recomputes them there.  Marshalling only:
     both passes run in the library's kernels.  Usage: SelectiveScanFunction.apply(u, delta, A, B,
-    C, D, z, delta_bias, delta_softplus); D, z, delta_bias may be None."""
+    C, D, z, delta_bias, delta_softplus, save_states); D, z, delta_bias may be None."""
 
     _fn = None
 
     @classmethod
-    def apply(cls, u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True):
+    def apply(cls, u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+              save_states=False):
         if cls._fn is None:
             cls._fn = _make_autograd_fn()
-        return cls._fn.apply(u, delta, A, B, C, D, z, delta_bias, delta_softplus)
+        return cls._fn.apply(u, delta, A, B, C, D, z, delta_bias, delta_softplus, save_states)
 
 
 def _make_autograd_fn():
@@ -324,21 +368,28 @@ def _make_autograd_fn():
 
     class _Fn(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, u, delta, A, B, C, D, z, delta_bias, delta_softplus):
-            out = selective_scan_fwd(u, delta, A, B, C, D=D, z=z, delta_bias=delta_bias,
-                                     delta_softplus=delta_softplus, return_last_state=False)
-            ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias)
+        def forward(ctx, u, delta, A, B, C, D, z, delta_bias, delta_softplus, save_states):
+            saved = None
+            if save_states:
+                out, _, saved = selective_scan_fwd_save(u, delta, A, B, C, D=D, z=z,
+                                                        delta_bias=delta_bias,
+                                                        delta_softplus=delta_softplus)
+            else:
+                out = selective_scan_fwd(u, delta, A, B, C, D=D, z=z, delta_bias=delta_bias,
+                                         delta_softplus=delta_softplus, return_last_state=False)
+            ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias, saved)
             ctx.delta_softplus = delta_softplus
             return out
 
         @staticmethod
         def backward(ctx, dout):
-            u, delta, A, B, C, D, z, delta_bias = ctx.saved_tensors
+            u, delta, A, B, C, D, z, delta_bias, saved = ctx.saved_tensors
             g = selective_scan_bwd(u, delta, A, B, C, dout.contiguous(), D=D, z=z,
-                                   delta_bias=delta_bias, delta_softplus=ctx.delta_softplus)
+                                   delta_bias=delta_bias, delta_softplus=ctx.delta_softplus,
+                                   saved_states=saved)
             return (g["du"], g["ddelta"], g["dA"], g["dB"], g["dC"],
                     g["dD"] if D is not None else None, g["dz"],
-                    g["ddelta_bias"] if delta_bias is not None else None, None)
+                    g["ddelta_bias"] if delta_bias is not None else None, None, None)
 
     return _Fn
 
@@ -362,6 +413,41 @@ def selective_scan_fwd_varlen(u, delta, A, B, C, seq_lens, initial_state=None, D
     if st != 0:
         raise MssError(st, "mss_selective_scan_fwd_varlen")
     return out, last_state
+
+
+def selective_scan_fwd_save(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                            initial_state=None, seq_lens=None, out=None, last_state=None,
+                            saved_states=None):
+    """Forward scan (as selective_scan_fwd_varlen; seq_lens and initial_state may be None) that
+    also writes the states its backward reads: saved_states (ceil(L / 8), 4, batch * d_inner * 4)
+    float32, the state entering every eighth step (state n of row r entering step 8k at
+    [k, n // 4, 4 r + n % 4]; saved_state_blocks() gives (ceil(L / 8), batch * d_inner, 16)).
+    Returns (out, last_state, saved_states)."""
+    import torch
+    Bt, Dn, L = u.shape
+    if out is None:
+        out = torch.empty_like(u, memory_format=torch.contiguous_format)
+    if last_state is None:
+        last_state = torch.empty((Bt, Dn, A.shape[1]), dtype=torch.float32, device=u.device)
+    if saved_states is None:
+        saved_states = torch.empty(((L + 7) // 8, A.shape[1] // 4, Bt * Dn * 4),
+                                   dtype=torch.float32, device=u.device)
+    with torch.cuda.device(u.device):
+        stream = torch.cuda.current_stream(u.device).cuda_stream
+        st = scan_fwd_save_raw(_desc(u), _desc(delta), _desc(A), _desc(B), _desc(C), _desc(D),
+                               _desc(z), _desc(delta_bias), _desc(initial_state), _desc(seq_lens),
+                               1 if delta_softplus else 0, _desc(out), _desc(last_state),
+                               _desc(saved_states), stream)
+    if st != 0:
+        raise MssError(st, "mss_selective_scan_fwd_save")
+    return out, last_state, saved_states
+
+
+def saved_state_blocks(saved_states):
+    """View of selective_scan_fwd_save's saved_states as (ceil(L / 8), batch * d_inner, 16): block
+    k is the state entering step 8k, laid out like last_state (a copy; for inspection)."""
+    K, Q, R4 = saved_states.shape
+    return saved_states.reshape(K, Q, R4 // 4, 4).permute(0, 2, 1, 3).reshape(K, R4 // 4, 4 * Q)
 
 
 def selective_scan_fwd_with_state(u, delta, A, B, C, initial_state, D=None, z=None,

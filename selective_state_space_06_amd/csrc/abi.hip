@@ -408,9 +408,42 @@ int mss_selective_scan_fwd_varlen(const mss_tensor_t* u, const mss_tensor_t* del
                                   const mss_tensor_t* initial_state, const mss_tensor_t* seq_lens,
                                   int softplus_flag, const mss_tensor_t* out,
                                   const mss_tensor_t* last_state, void* stream) {
+    return mss_selective_scan_fwd_save(u, delta, A, B, C, D, z, delta_bias, initial_state, seq_lens,
+                                       softplus_flag, out, last_state, nullptr, stream);
+}
+
+namespace {
+// The states saved for the backward: (ceil(L / 8), d_state / 4, batch * d_inner * 4) f32, planes
+// of float4 (states 4q..4q+3 of each row).
+int check_saved(const mss_tensor_t* saved, const mss_tensor_t* u, int64_t N) {
+    const int st = check_desc(saved, true);
+    if (st != MSS_OK) return st;
+    const int64_t Bt = u->shape[0], Dn = u->shape[1], L = u->shape[2];
+    if (!shape_is(*saved, 3, (L + 7) / 8, N / 4, Bt * Dn * 4)) return MSS_ERR_SHAPE;
+    if (saved->dtype != MSS_F32) return MSS_ERR_DTYPE;
+    if (!dense(*saved) || !aligned(*saved, 16)) return MSS_ERR_LAYOUT;
+    return MSS_OK;
+}
+}  // namespace
+
+int mss_selective_scan_fwd_save(const mss_tensor_t* u, const mss_tensor_t* delta,
+                                const mss_tensor_t* A, const mss_tensor_t* B,
+                                const mss_tensor_t* C, const mss_tensor_t* D,
+                                const mss_tensor_t* z, const mss_tensor_t* delta_bias,
+                                const mss_tensor_t* initial_state, const mss_tensor_t* seq_lens,
+                                int softplus_flag, const mss_tensor_t* out,
+                                const mss_tensor_t* last_state, const mss_tensor_t* saved_states,
+                                void* stream) {
     try {
         int st = validate_fwd(u, delta, A, B, C, D, z, delta_bias, initial_state, out, last_state);
         if (st != MSS_OK) return st;
+        if (saved_states) {
+            st = check_saved(saved_states, u, A->shape[1]);
+            if (st != MSS_OK) return st;
+            for (const mss_tensor_t* t : {u, delta, A, B, C, D, z, delta_bias, initial_state, seq_lens, out,
+                                          last_state})
+                if (t && overlap(saved_states, t)) return MSS_ERR_ALIAS;
+        }
         if (seq_lens) {
             st = check_desc(seq_lens, false);
             if (st != MSS_OK) return st;
@@ -430,6 +463,7 @@ int mss_selective_scan_fwd_varlen(const mss_tensor_t* u, const mss_tensor_t* del
         a.last_state = last_state ? static_cast<float*>(last_state->data) : nullptr;
         a.h0 = initial_state ? static_cast<const float*>(initial_state->data) : nullptr;
         a.lens = (seq_lens && numel(*seq_lens) > 0) ? static_cast<const int32_t*>(seq_lens->data) : nullptr;
+        a.saved = (saved_states && numel(*saved_states) > 0) ? static_cast<float*>(saved_states->data) : nullptr;
         a.Bt = u->shape[0]; a.Dn = u->shape[1]; a.L = u->shape[2];
         a.softplus = softplus_flag ? 1 : 0;
         a.bf16 = u->dtype == MSS_BF16;
@@ -445,7 +479,7 @@ int mss_selective_scan_fwd_varlen(const mss_tensor_t* u, const mss_tensor_t* del
         if (device_cus(dev, &cus) != hipSuccess) return MSS_ERR_HIP;
         // the fast path takes every length (rows that are not whole 16-byte vectors run its
         // element-aligned variant); the generic kernels remain behind MSS_SCAN_GENERIC
-        const bool fast = a.L > 0 && getenv("MSS_SCAN_GENERIC") == nullptr;
+        const bool fast = a.L > 0 && (a.saved || getenv("MSS_SCAN_GENERIC") == nullptr);
         mss::ScanPlan plan;
         if (fast) {
             plan = mss::plan_fast(a, cus);
@@ -494,20 +528,24 @@ int mss_selective_scan_bwd(const mss_tensor_t* u, const mss_tensor_t* delta, con
                                          stream);
 }
 
-int mss_selective_scan_bwd_varlen(const mss_tensor_t* u, const mss_tensor_t* delta, const mss_tensor_t* A,
-                                  const mss_tensor_t* B, const mss_tensor_t* C, const mss_tensor_t* D,
-                                  const mss_tensor_t* z, const mss_tensor_t* delta_bias,
-                                  const mss_tensor_t* initial_state, const mss_tensor_t* seq_lens,
-                                  int softplus_flag, const mss_tensor_t* dout,
-                                  const mss_tensor_t* dlast_state, const mss_tensor_t* du,
-                                  const mss_tensor_t* ddelta, const mss_tensor_t* dA, const mss_tensor_t* dB,
-                                  const mss_tensor_t* dC, const mss_tensor_t* dD, const mss_tensor_t* dz,
-                                  const mss_tensor_t* ddelta_bias, const mss_tensor_t* dinitial_state,
-                                  void* stream) {
+namespace {
+int bwd_impl(const mss_tensor_t* u, const mss_tensor_t* delta, const mss_tensor_t* A, const mss_tensor_t* B,
+             const mss_tensor_t* C, const mss_tensor_t* D, const mss_tensor_t* z, const mss_tensor_t* delta_bias,
+             const mss_tensor_t* initial_state, const mss_tensor_t* seq_lens, const mss_tensor_t* saved,
+             int softplus_flag, const mss_tensor_t* dout, const mss_tensor_t* dlast_state, const mss_tensor_t* du,
+             const mss_tensor_t* ddelta, const mss_tensor_t* dA, const mss_tensor_t* dB, const mss_tensor_t* dC,
+             const mss_tensor_t* dD, const mss_tensor_t* dz, const mss_tensor_t* ddelta_bias,
+             const mss_tensor_t* dinitial_state, void* stream) {
     try {
         int st = validate_bwd(u, delta, A, B, C, D, z, delta_bias, dout, du, ddelta, dA, dB, dC, dD,
                               dz, ddelta_bias);
         if (st != MSS_OK) return st;
+        if (saved) {
+            st = check_saved(saved, u, A->shape[1]);
+            if (st != MSS_OK) return st;
+            for (const mss_tensor_t* o : {du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state})
+                if (o && overlap(o, saved)) return MSS_ERR_ALIAS;
+        }
         {
             // the state tensors: (Bt, Dn, N) f32, 16-byte aligned; the lengths: (Bt,) i32
             const int64_t Bt = u->shape[0], Dn = u->shape[1], N = A->shape[1];
@@ -552,6 +590,7 @@ int mss_selective_scan_bwd_varlen(const mss_tensor_t* u, const mss_tensor_t* del
         a.lens = (seq_lens && numel(*seq_lens) > 0) ? static_cast<const int32_t*>(seq_lens->data) : nullptr;
         a.dlast = dlast_state ? static_cast<const float*>(dlast_state->data) : nullptr;
         a.dh0 = dinitial_state ? static_cast<float*>(dinitial_state->data) : nullptr;
+        a.saved = (saved && numel(*saved) > 0) ? static_cast<const float*>(saved->data) : nullptr;
         a.Bt = u->shape[0]; a.Dn = u->shape[1]; a.L = u->shape[2];
         a.softplus = softplus_flag ? 1 : 0;
         a.bf16 = u->dtype == MSS_BF16;
@@ -574,6 +613,36 @@ int mss_selective_scan_bwd_varlen(const mss_tensor_t* u, const mss_tensor_t* del
     } catch (...) {
         return MSS_ERR_HIP;
     }
+}
+}  // namespace
+
+int mss_selective_scan_bwd_varlen(const mss_tensor_t* u, const mss_tensor_t* delta, const mss_tensor_t* A,
+                                  const mss_tensor_t* B, const mss_tensor_t* C, const mss_tensor_t* D,
+                                  const mss_tensor_t* z, const mss_tensor_t* delta_bias,
+                                  const mss_tensor_t* initial_state, const mss_tensor_t* seq_lens,
+                                  int softplus_flag, const mss_tensor_t* dout,
+                                  const mss_tensor_t* dlast_state, const mss_tensor_t* du,
+                                  const mss_tensor_t* ddelta, const mss_tensor_t* dA, const mss_tensor_t* dB,
+                                  const mss_tensor_t* dC, const mss_tensor_t* dD, const mss_tensor_t* dz,
+                                  const mss_tensor_t* ddelta_bias, const mss_tensor_t* dinitial_state,
+                                  void* stream) {
+    return bwd_impl(u, delta, A, B, C, D, z, delta_bias, initial_state, seq_lens, nullptr, softplus_flag, dout,
+                    dlast_state, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, stream);
+}
+
+int mss_selective_scan_bwd_saved(const mss_tensor_t* u, const mss_tensor_t* delta, const mss_tensor_t* A,
+                                 const mss_tensor_t* B, const mss_tensor_t* C, const mss_tensor_t* D,
+                                 const mss_tensor_t* z, const mss_tensor_t* delta_bias,
+                                 const mss_tensor_t* seq_lens, int softplus_flag,
+                                 const mss_tensor_t* saved_states, const mss_tensor_t* dout,
+                                 const mss_tensor_t* dlast_state, const mss_tensor_t* du,
+                                 const mss_tensor_t* ddelta, const mss_tensor_t* dA, const mss_tensor_t* dB,
+                                 const mss_tensor_t* dC, const mss_tensor_t* dD, const mss_tensor_t* dz,
+                                 const mss_tensor_t* ddelta_bias, const mss_tensor_t* dinitial_state,
+                                 void* stream) {
+    if (!saved_states) return MSS_ERR_NULL_ARG;
+    return bwd_impl(u, delta, A, B, C, D, z, delta_bias, nullptr, seq_lens, saved_states, softplus_flag, dout,
+                    dlast_state, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, stream);
 }
 
 int mss_causal_conv1d_fwd(const mss_tensor_t* x, const mss_tensor_t* weight, const mss_tensor_t* bias,

@@ -10,6 +10,9 @@
 
 namespace mss {
 
+// A native 4 x f32 vector (what the nontemporal builtins take; HIP's float4 is a struct).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -24,6 +24,7 @@ struct ScanLaunch {
     float* last_state;      // nullable
     const float* h0;        // nullable: starting state (Bt, Dn, N), zeros when null
     const int32_t* lens;    // nullable: per-batch sequence lengths (device), clamped to [0, L]
+    float* saved;           // nullable: the state entering every 8-step tile, [ceil(L/8)][N][Bt*Dn]
     int64_t Bt, Dn, L;
     int softplus;
     bool bf16;              // storage type of u / delta / z / out
@@ -75,6 +76,8 @@ struct BwdLaunch {
     const int32_t* lens;    // nullable: per-batch sequence lengths (device)
     const float* dlast;     // nullable: dL/d last_state (Bt, Dn, N)
     float* dh0;             // nullable: dL/dh0 (Bt, Dn, N), written
+    const float* saved;     // nullable: the forward's states entering every 8-step tile
+                            // ([ceil(L/8)][N][Bt*Dn]); when given they replace the recomputation
     int64_t Bt, Dn, L;
     int softplus;
     bool bf16;

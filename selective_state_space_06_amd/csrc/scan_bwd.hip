@@ -72,6 +72,7 @@ struct BwdArgs {
     const int32_t* lens; // nullable per-batch lengths
     const float* dlast;  // nullable dL/d last_state (R, kN)
     float* dh0;          // nullable dL/dh0 (R, kN), written by segment 0
+    const float* saved;  // nullable: the forward's state entering each tile, [ntiles][kN / 4][R][4]
     float* agg;   // [S][kAggW][R]
     float* ck;    // [ntiles][kCkW][R]
     float* part;  // [G][Bt][2 kN][tpad]
@@ -409,7 +410,8 @@ __device__ __forceinline__ void agg_checkpoint(const BwdArgs& a, const Row& r, i
     }
 }
 
-template <bool POW>
+// SAVED: the forward saved the states, so only the adjoint carry (and sum dt) is walked.
+template <bool POW, bool SAVED>
 __device__ __forceinline__ void agg_tile(const BwdArgs& a, const Row& r, int64_t t0, const StepVals& v,
                                          const float* sbc, AggState& st) {
 #pragma unroll
@@ -420,7 +422,8 @@ __device__ __forceinline__ void agg_tile(const BwdArgs& a, const Row& r, int64_t
         abar16<POW>(v.dt[j], r.A2, p);
         st.dsum += v.dt[j];
 #pragma unroll
-        for (int n = 0; n < kN; ++n) st.H[n] = fmaf(p[n], st.H[n], v.x[j] * bv[n]);
+        for (int n = 0; n < kN; ++n)
+            if (!SAVED) st.H[n] = fmaf(p[n], st.H[n], v.x[j] * bv[n]);
         if (POW) {
             // the product of abar_n since the segment start is R^(n+1), R that of abar_0: the
             // weights dy R^(n+1) come from four interleaved chains stepping by R^4
@@ -466,7 +469,7 @@ __device__ __forceinline__ void agg_init(AggState& st) {
 
 // Each tile's inputs come straight into registers, one tile ahead (any layout; rows of whole
 // 16-byte vectors use the staged variant below).
-template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z, bool POW>
+template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z, bool POW, bool SAVED>
 __device__ __forceinline__ void agg_body(const BwdArgs& a, const Row& r, float* sbc) {
     const int s = blockIdx.z;
     int64_t tb, te;
@@ -477,7 +480,7 @@ __device__ __forceinline__ void agg_body(const BwdArgs& a, const Row& r, float* 
     load_raw<E, VEC, HAS_Z>(a, r, tb * kBT, nx);
     for (int64_t tile = tb; tile < te; ++tile) {
         const int64_t t0 = tile * kBT;
-        agg_checkpoint<false>(a, r, tile, st);
+        if (!SAVED) agg_checkpoint<false>(a, r, tile, st);
         const Raw<E, VEC> cur = nx;
         if (tile + 1 < te) load_raw<E, VEC, HAS_Z>(a, r, t0 + kBT, nx);
         StepVals v;
@@ -485,7 +488,7 @@ __device__ __forceinline__ void agg_body(const BwdArgs& a, const Row& r, float* 
         wave_lds_order();  // after the previous tile's reads of the B / C block
         put_bc(cur.bc, sbc, t0, r.stop);
         wave_lds_order();
-        agg_tile<POW>(a, r, t0, v, sbc, st);
+        agg_tile<POW, SAVED>(a, r, t0, v, sbc, st);
     }
     agg_finish<false>(a, r, s, st);
 }
@@ -512,7 +515,8 @@ struct StageGeo {
     static constexpr int TPB = kStageChunks / NV;     // tiles per block
 };
 
-template <class E, bool HAS_Z>
+// SAVED: u is not read (it only feeds the forward state, which the forward saved).
+template <class E, bool HAS_Z, bool SAVED>
 __device__ __forceinline__ void stage_block(const BwdArgs& a, const Row& r, int64_t tile, uint4* stage) {
     using G = StageGeo<E>;
     using S_t = typename E::storage;
@@ -523,7 +527,7 @@ __device__ __forceinline__ void stage_block(const BwdArgs& a, const Row& r, int6
         const int64_t t = tile * kBT + c * G::V;
         const int64_t tc = t < a.L ? t : 0;  // past the row's end: any valid address, those steps are masked
 #pragma unroll
-        for (int q = 0; q < (HAS_Z ? 4 : 3); ++q)
+        for (int q = SAVED ? 1 : 0; q < (HAS_Z ? 4 : 3); ++q)
             lds_load16(static_cast<const S_t*>(src[q]) + off + tc, stage + (q * kStageChunks + c) * 64);
     }
 }
@@ -547,7 +551,7 @@ __device__ __forceinline__ void staged_tile(const uint4* stage, int k, Raw<E, tr
 // duplicate writes the same bits as the owner.  Stores without a branch keep the count of
 // outstanding memory operations exact, so waiting for the next tile's B / C does not also wait
 // for the block in flight.
-template <class E, bool SOFTPLUS, bool HAS_Z, bool POW>
+template <class E, bool SOFTPLUS, bool HAS_Z, bool POW, bool SAVED>
 __device__ __forceinline__ void agg_body_staged(const BwdArgs& a, const Row& r_in, float* sbc, uint4* stage) {
     using G = StageGeo<E>;
     Row r = r_in;
@@ -558,7 +562,7 @@ __device__ __forceinline__ void agg_body_staged(const BwdArgs& a, const Row& r_i
     AggState st;
     agg_init(st);
     float bc_next[4];
-    stage_block<E, HAS_Z>(a, r, tb, stage);
+    stage_block<E, HAS_Z, SAVED>(a, r, tb, stage);
     load_bc<true>(a, tb * kBT, bc_next);
     for (int64_t blk = tb; blk < te; blk += G::TPB) {
         // the block's tiles, unrolled: a tile's LDS words are read one tile ahead, and the
@@ -575,37 +579,37 @@ __device__ __forceinline__ void agg_body_staged(const BwdArgs& a, const Row& r_i
 #pragma unroll
             for (int e = 0; e < 4; ++e) cur.bc[e] = bc_next[e];
             load_bc<true>(a, t0 + kBT, bc_next);
-            agg_checkpoint<true>(a, r, tile, st);
+            if (!SAVED) agg_checkpoint<true>(a, r, tile, st);
             Raw<E, true> nx;
             if (k + 1 < G::TPB) {
                 staged_tile<E, HAS_Z>(stage, k + 1, nx);
             } else if (tile + 1 < te) {
                 lds_reads_done();  // the block's LDS reads are complete before it is overwritten
-                stage_block<E, HAS_Z>(a, r, tile + 1, stage);
+                stage_block<E, HAS_Z, SAVED>(a, r, tile + 1, stage);
             }
             StepVals v;
             step_vals<E, true, SOFTPLUS, HAS_Z>(a, r, t0, cur, v);
             wave_lds_order();  // after the previous tile's reads of the B / C block
             put_bc(cur.bc, sbc, t0, r.stop);
             wave_lds_order();
-            agg_tile<POW>(a, r, t0, v, sbc, st);
+            agg_tile<POW, SAVED>(a, r, t0, v, sbc, st);
             if (k + 1 < G::TPB) cur = nx;
         }
     }
     agg_finish<true>(a, r, s, st);
 }
 
-template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z>
+template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z, bool SAVED>
 __global__ __launch_bounds__(64) void bwd_agg_kernel(BwdArgs a) {
     __shared__ __align__(16) float sbc[kBT * kBCs];
     const Row r = row_of(a);
     if constexpr (VEC) {
         __shared__ __align__(16) uint4 stage[4 * kStageChunks * 64];
-        if (__all(r.pow_ok)) agg_body_staged<E, SOFTPLUS, HAS_Z, true>(a, r, sbc, stage);
-        else agg_body_staged<E, SOFTPLUS, HAS_Z, false>(a, r, sbc, stage);
+        if (__all(r.pow_ok)) agg_body_staged<E, SOFTPLUS, HAS_Z, true, SAVED>(a, r, sbc, stage);
+        else agg_body_staged<E, SOFTPLUS, HAS_Z, false, SAVED>(a, r, sbc, stage);
     } else {
-        if (__all(r.pow_ok)) agg_body<E, VEC, SOFTPLUS, HAS_Z, true>(a, r, sbc);
-        else agg_body<E, VEC, SOFTPLUS, HAS_Z, false>(a, r, sbc);
+        if (__all(r.pow_ok)) agg_body<E, VEC, SOFTPLUS, HAS_Z, true, SAVED>(a, r, sbc);
+        else agg_body<E, VEC, SOFTPLUS, HAS_Z, false, SAVED>(a, r, sbc);
     }
 }
 
@@ -613,7 +617,8 @@ __global__ __launch_bounds__(64) void bwd_agg_kernel(BwdArgs a) {
 
 // Segment carries: the forward state entering segment s (fold of segments 0..s-1) and the
 // adjoint entering its last step from the later segments (fold of S-1 down to s+1).
-template <bool POW>
+// WITH_H: also the forward state (not needed when the forward saved its states).
+template <bool POW, bool WITH_H>
 __device__ __forceinline__ void carries(const BwdArgs& a, const Row& r, int s, float (&h)[kN],
                                         float (&gc)[kN]) {
 #pragma unroll
@@ -621,7 +626,7 @@ __device__ __forceinline__ void carries(const BwdArgs& a, const Row& r, int s, f
         h[n] = a.h0 ? a.h0[r.row * kN + n] : 0.0f;        // the forward's starting state
         gc[n] = a.dlast ? a.dlast[r.row * kN + n] : 0.0f; // dL/dh at the last step, if any
     }
-    for (int k = 0; k < s; ++k) {
+    for (int k = 0; k < (WITH_H ? s : 0); ++k) {
         const float* g = a.agg + (int64_t)k * kAggW * a.R + r.row;
         float p[kN];
         abar16<POW>(g[0], r.A2, p);
@@ -637,7 +642,7 @@ __device__ __forceinline__ void carries(const BwdArgs& a, const Row& r, int s, f
     }
 }
 
-template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z, bool POW>
+template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z, bool POW, bool SAVED>
 __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float* sbc, float* hbuf,
                                           float* hin) {
     const int s = blockIdx.z;
@@ -646,7 +651,7 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
     int64_t tb, te;
     seg_tiles(s, a.S, a.ntiles, tb, te);
     float h[kN], gc[kN];  // state entering the segment; adjoint entering its last step
-    carries<POW>(a, r, s, h, gc);
+    carries<POW, !SAVED>(a, r, s, h, gc);
 
     // backward walk
     float dA[kN];
@@ -655,14 +660,25 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
     float dDacc = 0.0f, dbacc = 0.0f;
     Raw<E, VEC> nx;
     load_raw<E, VEC, HAS_Z>(a, r, (te - 1) * kBT, nx);
+    if (!SAVED) {
 #pragma unroll
-    for (int n = 0; n < kN; ++n) hin[n * 64 + lane] = h[n];  // h_in waits in LDS: fewer live VGPRs
+        for (int n = 0; n < kN; ++n) hin[n * 64 + lane] = h[n];  // h_in waits in LDS: fewer live VGPRs
+    }
     for (int64_t tile = te - 1; tile >= tb; --tile) {
         const int64_t t0 = tile * kBT;
         const Raw<E, VEC> cur = nx;
-        float ck0[kCkW];  // loaded here, used after the tile's set-up
+        float ck0[kCkW];  // loaded here, used after the tile's set-up (SAVED: the true start state)
+        if (SAVED) {
+            const float4* sp = reinterpret_cast<const float4*>(a.saved + tile * kN * a.R + r.row * 4);
 #pragma unroll
-        for (int n = 0; n < kCkW; ++n) ck0[n] = r.active ? a.ck[(tile * kCkW + n) * a.R + r.row] : 0.0f;
+            for (int q = 0; q < kN / 4; ++q) {
+                const float4 v = r.active ? sp[q * a.R] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                ck0[4 * q] = v.x; ck0[4 * q + 1] = v.y; ck0[4 * q + 2] = v.z; ck0[4 * q + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < kCkW; ++n) ck0[n] = r.active ? a.ck[(tile * kCkW + n) * a.R + r.row] : 0.0f;
+        }
         if (tile > tb) load_raw<E, VEC, HAS_Z>(a, r, t0 - kBT, nx);
         StepVals v;
         step_vals<E, VEC, SOFTPLUS, HAS_Z>(a, r, t0, cur, v);
@@ -681,8 +697,8 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
         constexpr int kQ = q_steps<E>();
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            float pc[kH];  // tile start: exp(A sum dt) h_in + the local checkpoint
-            abar8<POW>(ck0[kN], POW ? fast_exp2(ck0[kN] * r.A2[0]) : 0.0f, r.A2, hf, pc);
+            float pc[kH];  // tile start: exp(A sum dt) h_in + the local checkpoint (SAVED: given)
+            if (!SAVED) abar8<POW>(ck0[kN], POW ? fast_exp2(ck0[kN] * r.A2[0]) : 0.0f, r.A2, hf, pc);
             float bcs[kBT];
             // Steps in chunks of kQ, the latest first: each chunk recomputes the half's states from
             // the tile start, keeps its own steps' states in LDS and consumes them in reverse (a
@@ -691,7 +707,8 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
             for (int c = kBT / kQ - 1; c >= 0; --c) {
                 float hs[kH];
 #pragma unroll
-                for (int k = 0; k < kH; ++k) hs[k] = fmaf(pc[k], hin[(kH * hf + k) * 64 + lane], ck0[kH * hf + k]);
+                for (int k = 0; k < kH; ++k)
+                    hs[k] = SAVED ? ck0[kH * hf + k] : fmaf(pc[k], hin[(kH * hf + k) * 64 + lane], ck0[kH * hf + k]);
 #pragma unroll
                 for (int j = 0; j < kQ * (c + 1); ++j) {
                     if (t0 + j >= a.L) break;
@@ -776,14 +793,14 @@ __device__ __forceinline__ void main_body(const BwdArgs& a, const Row& r, float*
     }
 }
 
-template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z>
+template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z, bool SAVED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_main_kernel(BwdArgs a) {
     __shared__ __align__(16) float sbc[kBT * kBCs];
     __shared__ __align__(16) float hbuf[q_steps<E>() * kH * 64];
     __shared__ __align__(16) float hin[kN * 64];
     const Row r = row_of(a);
-    if (__all(r.pow_ok)) main_body<E, VEC, SOFTPLUS, HAS_Z, true>(a, r, sbc, hbuf, hin);
-    else main_body<E, VEC, SOFTPLUS, HAS_Z, false>(a, r, sbc, hbuf, hin);
+    if (__all(r.pow_ok)) main_body<E, VEC, SOFTPLUS, HAS_Z, true, SAVED>(a, r, sbc, hbuf, hin);
+    else main_body<E, VEC, SOFTPLUS, HAS_Z, false, SAVED>(a, r, sbc, hbuf, hin);
 }
 
 // ---------------------------------------------------------------- reductions
@@ -846,8 +863,13 @@ hipError_t zero(float* p, int64_t n, hipStream_t s) {
 template <class E, bool VEC, bool SOFTPLUS, bool HAS_Z>
 hipError_t launch_t(const BwdArgs& k, const BwdLaunch& a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(k.G), static_cast<unsigned>(k.Bt), static_cast<unsigned>(k.S));
-    bwd_agg_kernel<E, VEC, SOFTPLUS, HAS_Z><<<grid, dim3(64), 0, stream>>>(k);
-    bwd_main_kernel<E, VEC, SOFTPLUS, HAS_Z><<<grid, dim3(64), 0, stream>>>(k);
+    if (k.saved) {
+        bwd_agg_kernel<E, VEC, SOFTPLUS, HAS_Z, true><<<grid, dim3(64), 0, stream>>>(k);
+        bwd_main_kernel<E, VEC, SOFTPLUS, HAS_Z, true><<<grid, dim3(64), 0, stream>>>(k);
+    } else {
+        bwd_agg_kernel<E, VEC, SOFTPLUS, HAS_Z, false><<<grid, dim3(64), 0, stream>>>(k);
+        bwd_main_kernel<E, VEC, SOFTPLUS, HAS_Z, false><<<grid, dim3(64), 0, stream>>>(k);
+    }
     const int64_t nbc = (int64_t)k.Bt * 2 * kN * k.L;
     bwd_reduce_bc_kernel<<<dim3(grid_for(nbc)), dim3(256), 0, stream>>>(k.part, a.dB, a.dC, k.G, k.Bt, k.L, k.tpad);
     bwd_reduce_par_kernel<<<dim3(grid_for((int64_t)kParW * k.Dn)), dim3(256), 0, stream>>>(
@@ -868,14 +890,14 @@ struct Layout {
     size_t agg, ck, part, par, total;
 };
 
-Layout layout_of(const BwdLaunch& a, int S) {
+Layout layout_of(const BwdLaunch& a, int S) {  // no checkpoints when the forward saved its states
     const int64_t R = a.Bt * a.Dn;
     const int64_t ntiles = (a.L + kBT - 1) / kBT;
     const int64_t G = (a.Dn + 63) / 64;
     Layout l;
     l.agg = 0;
     l.ck = l.agg + align256(static_cast<size_t>(S) * kAggW * R * sizeof(float));
-    l.part = l.ck + align256(static_cast<size_t>(ntiles) * kCkW * R * sizeof(float));
+    l.part = l.ck + (a.saved ? 0 : align256(static_cast<size_t>(ntiles) * kCkW * R * sizeof(float)));
     l.par = l.part + align256(static_cast<size_t>(G) * a.Bt * 2 * kN * ntiles * kBT * sizeof(float));
     l.total = l.par + align256(static_cast<size_t>(S) * kParW * R * sizeof(float));
     return l;
@@ -926,7 +948,7 @@ hipError_t launch_scan_bwd(const BwdLaunch& a, int segments, void* workspace, hi
     k.u = a.u; k.delta = a.delta; k.z = a.z; k.dout = a.dout;
     k.A = a.A; k.B = a.B; k.C = a.C; k.D = a.D; k.bias = a.bias;
     k.du = a.du; k.ddelta = a.ddelta; k.dz = a.dz;
-    k.h0 = a.h0; k.lens = a.lens; k.dlast = a.dlast; k.dh0 = a.dh0;
+    k.h0 = a.h0; k.lens = a.lens; k.dlast = a.dlast; k.dh0 = a.dh0; k.saved = a.saved;
     k.agg = reinterpret_cast<float*>(ws + l.agg);
     k.ck = reinterpret_cast<float*>(ws + l.ck);
     k.part = reinterpret_cast<float*>(ws + l.part);

@@ -326,16 +326,17 @@ __device__ __forceinline__ int tile_steps(int64_t t0, int64_t t_end) {
     return static_cast<int>(RAGGED ? ((n + 3) & ~static_cast<int64_t>(3)) : n);
 }
 
-template <class E, bool HAS_Z, bool SOFTPLUS, bool POW, bool VARLEN, bool RAGGED>
+template <class E, bool HAS_Z, bool SOFTPLUS, bool POW, bool VARLEN, bool RAGGED, bool SAVE>
 __device__ __forceinline__ void main_body(
     const RowSetup& rs, float (&h)[kN], const typename E::storage* __restrict__ up,
     const typename E::storage* __restrict__ dp, const typename E::storage* __restrict__ zp,
     typename E::storage* __restrict__ op, const float* __restrict__ Bb, const float* __restrict__ Cb,
-    int64_t L, uint32_t* srow, float* sbc, int64_t t_begin, int64_t t_end) {
+    int64_t L, uint32_t* srow, float* sbc, int64_t t_begin, int64_t t_end, float* saved, int64_t R) {
     using G = Geo<E>;
     constexpr int V = G::V, TT = G::TT, W = G::W;
     const uint32_t* su = srow;
     const uint32_t* sd = srow + W * 64;
+    float* const srow_saved = SAVE ? saved + rs.row * 4 : nullptr;  // this lane's float4 in each plane
     RawUD pre;
     RawBC<E> bpre;
     load_ud<E, RAGGED>(pre, up, dp, t_begin, t_end, L);
@@ -363,6 +364,17 @@ __device__ __forceinline__ void main_body(
         Pair cur = pair_of<E, SOFTPLUS, POW, true, VARLEN>(su, sd, 0, rs, t0);
 #pragma unroll 1
         for (int j = 0; j < nsteps; j += 2) {
+            // for the backward: the state entering each 8-step tile (tiles start on multiples of 8)
+            if (SAVE && (j & 7) == 0 && t0 + j < L && rs.active) {
+                // planes of float4 (states 4q..4q+3 of every row): a wave writes 1 KiB runs,
+                // streamed past the caches (read back only by the backward)
+                f32x4* sp = reinterpret_cast<f32x4*>(srow_saved + ((t0 + j) >> 3) * kN * R);
+#pragma unroll
+                for (int q = 0; q < kN / 4; ++q) {
+                    const f32x4 v = {h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]};
+                    __builtin_nontemporal_store(v, sp + q * R);
+                }
+            }
             // the last iteration recomputes its own pair (read before put2 overwrites it)
             const Pair nxt = pair_of<E, SOFTPLUS, POW, true, VARLEN>(su, sd, j + 2 < nsteps ? j + 2 : j, rs, t0);
             const float y0 = step_main<POW>(h, rs.A2, cur.d[0], cur.x[0], cur.a[0], sbc + j * 36, cur.du[0]);
@@ -478,14 +490,14 @@ __device__ __forceinline__ void fold_carry(float (&h)[kN], const float (&A2)[kN]
     }
 }
 
-template <class E, bool HAS_Z, bool SOFTPLUS, bool VARLEN, bool RAGGED>
+template <class E, bool HAS_Z, bool SOFTPLUS, bool VARLEN, bool RAGGED, bool SAVE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void scan_main_kernel(
     const typename E::storage* __restrict__ u, const typename E::storage* __restrict__ delta,
     const typename E::storage* __restrict__ z, const float* __restrict__ A,
     const float* __restrict__ B, const float* __restrict__ C, const float* __restrict__ D,
     const float* __restrict__ bias, const float* __restrict__ agg, const float* __restrict__ h0,
     typename E::storage* __restrict__ out, float* __restrict__ last_state, const int32_t* __restrict__ lens,
-    int64_t Dn, int64_t L, int S) {
+    float* __restrict__ saved, int64_t Dn, int64_t L, int S) {
     using G = Geo<E>;
     __shared__ uint32_t srow[G::kRowWords];
     __shared__ __align__(16) float sbc[G::TT * 36];
@@ -501,12 +513,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sc
     float h[kN];
     if (__all(rs.pow_ok)) {
         fold_carry<true>(h, rs.A2, agg, h0, seg, R, rs.row);
-        main_body<E, HAS_Z, SOFTPLUS, true, VARLEN, RAGGED>(rs, h, u + base, delta + base, zp, out + base, Bb, Cb,
-                                                    L, srow, sbc, t_begin, t_end);
+        main_body<E, HAS_Z, SOFTPLUS, true, VARLEN, RAGGED, SAVE>(rs, h, u + base, delta + base, zp, out + base, Bb, Cb,
+                                                    L, srow, sbc, t_begin, t_end, saved, R);
     } else {
         fold_carry<false>(h, rs.A2, agg, h0, seg, R, rs.row);
-        main_body<E, HAS_Z, SOFTPLUS, false, VARLEN, RAGGED>(rs, h, u + base, delta + base, zp, out + base, Bb, Cb,
-                                                     L, srow, sbc, t_begin, t_end);
+        main_body<E, HAS_Z, SOFTPLUS, false, VARLEN, RAGGED, SAVE>(rs, h, u + base, delta + base, zp, out + base, Bb, Cb,
+                                                     L, srow, sbc, t_begin, t_end, saved, R);
     }
     if (last_state && rs.active && seg == S - 1) {
         float4* dst = reinterpret_cast<float4*>(last_state + rs.row * kN);
@@ -651,9 +663,17 @@ hipError_t launch_fast_t(const ScanLaunch& a, const ScanPlan& p, float* ws, hipS
             static_cast<const S_t*>(a.u), static_cast<const S_t*>(a.delta), a.A, a.B, a.bias, agg, a.lens, a.Dn,
             a.L, p.segments);
     mark(a, 1, stream);
-    scan_main_kernel<E, HAS_Z, SOFTPLUS, VARLEN, RAGGED><<<dim3(gx, (unsigned)a.Bt, (unsigned)p.segments), block, 0, stream>>>(
-        static_cast<const S_t*>(a.u), static_cast<const S_t*>(a.delta), static_cast<const S_t*>(a.z), a.A, a.B,
-        a.C, a.D, a.bias, agg, a.h0, static_cast<S_t*>(a.out), a.last_state, a.lens, a.Dn, a.L, p.segments);
+    const dim3 grid(gx, (unsigned)a.Bt, (unsigned)p.segments);
+    if (a.saved)
+        scan_main_kernel<E, HAS_Z, SOFTPLUS, VARLEN, RAGGED, true><<<grid, block, 0, stream>>>(
+            static_cast<const S_t*>(a.u), static_cast<const S_t*>(a.delta), static_cast<const S_t*>(a.z), a.A, a.B,
+            a.C, a.D, a.bias, agg, a.h0, static_cast<S_t*>(a.out), a.last_state, a.lens, a.saved, a.Dn, a.L,
+            p.segments);
+    else
+        scan_main_kernel<E, HAS_Z, SOFTPLUS, VARLEN, RAGGED, false><<<grid, block, 0, stream>>>(
+            static_cast<const S_t*>(a.u), static_cast<const S_t*>(a.delta), static_cast<const S_t*>(a.z), a.A, a.B,
+            a.C, a.D, a.bias, agg, a.h0, static_cast<S_t*>(a.out), a.last_state, a.lens, nullptr, a.Dn, a.L,
+            p.segments);
     mark(a, 2, stream);
     return hipGetLastError();
 }

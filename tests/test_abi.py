@@ -370,6 +370,64 @@ def test_bwd_nothing_to_write_is_ok(lib):
     assert call_bwd(a) == OK
 
 
+# ------------------------------------------------ forward that saves states / backward from them
+
+def saved_desc(dtype=MSS_F32, n=N, steps=(L + 7) // 8):
+    return Tensor.make(addr(steps * n * BT * DN * 4), dtype, [steps, n // 4, BT * DN * 4])
+
+
+def call_fwd_save(a, saved):
+    return mss.scan_fwd_save_raw(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                 a["delta_bias"], None, None, a["softplus_flag"], a["out"],
+                                 a["last_state"], saved, a["stream"])
+
+
+def call_bwd_saved(a, saved):
+    return mss.scan_bwd_saved_raw(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                  a["delta_bias"], None, a["softplus_flag"], saved, a["dout"], None,
+                                  a["du"], a["ddelta"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"],
+                                  a["ddelta_bias"], None, a["stream"])
+
+
+def test_fwd_save_validation(lib):
+    a = fwd_args()
+    a["A"].data += 4                           # the forward's own checks come first
+    assert call_fwd_save(a, saved_desc()) == LAYOUT
+    for shape in ([(L + 7) // 8 + 1, 4, BT * DN * 4], [L // 8 - 1, 4, BT * DN * 4],
+                  [(L + 7) // 8, 4, DN * 4], [(L + 7) // 8, 2, BT * DN * 4],
+                  [(L + 7) // 8, BT * DN, N], [(L + 7) // 8, N, BT * DN]):
+        t = saved_desc()
+        assert call_fwd_save(fwd_args(), Tensor.make(t.data, MSS_F32, shape)) == SHAPE, shape
+    assert call_fwd_save(fwd_args(), saved_desc(MSS_BF16)) == DTYPE
+    t = saved_desc()
+    t.stride[1] = BT * DN * 4 + 4               # not dense
+    assert call_fwd_save(fwd_args(), t) == LAYOUT
+    t = saved_desc()
+    t.data += 4                                 # records must be 16-byte aligned
+    assert call_fwd_save(fwd_args(), t) == LAYOUT
+    t = saved_desc()
+    t.data = None
+    assert call_fwd_save(fwd_args(), t) == NULL_ARG
+    for victim in ("u", "out", "last_state", "B"):
+        a = fwd_args()
+        assert call_fwd_save(a, Tensor.make(a[victim].data, MSS_F32,
+                                            [(L + 7) // 8, 4, BT * DN * 4])) == ALIAS, victim
+
+
+def test_bwd_saved_validation(lib):
+    assert call_bwd_saved(bwd_args(), None) == NULL_ARG
+    t = saved_desc()
+    assert call_bwd_saved(bwd_args(), Tensor.make(t.data, MSS_F32, [L // 8, 4, BT * DN * 4 + 4])) == SHAPE
+    assert call_bwd_saved(bwd_args(), saved_desc(MSS_BF16)) == DTYPE
+    a = bwd_args()
+    a["dB"].stride[0], a["dB"].stride[1] = L, BT * L   # the backward's own checks still apply
+    assert call_bwd_saved(a, saved_desc()) == LAYOUT
+    for out in ("du", "dA", "dB", "ddelta_bias"):
+        a = bwd_args()
+        assert call_bwd_saved(a, Tensor.make(a[out].data, MSS_F32,
+                                             [(L + 7) // 8, 4, BT * DN * 4])) == ALIAS, out
+
+
 # --------------------------------------------------------------------- causal conv1d
 
 def conv_args(dtype=MSS_BF16, K=4):
@@ -528,3 +586,16 @@ def test_profile_fwd_null_outputs(lib):
     assert lib.mss_profile_fwd(None, ctypes.byref(c), ctypes.byref(c)) == NULL_ARG
     assert lib.mss_profile_fwd(ctypes.byref(n), None, ctypes.byref(c)) == NULL_ARG
     assert lib.mss_profile_fwd(ctypes.byref(n), ctypes.byref(c), None) == NULL_ARG
+
+
+def test_saved_state_blocks_follows_the_documented_index():
+    """saved_state_blocks: state n of row r entering step 8k sits at [k][n // 4][4 r + n % 4]."""
+    import torch
+    K, R = 3, 5
+    flat = torch.arange(K * 4 * R * 4, dtype=torch.float32).reshape(K, 4, R * 4)
+    blocks = mss.saved_state_blocks(flat)
+    assert blocks.shape == (K, R, 16)
+    for k in range(K):
+        for r in range(R):
+            for n in range(16):
+                assert blocks[k, r, n] == flat[k, n // 4, 4 * r + n % 4]
