@@ -45,7 +45,7 @@ FLOPS_PER_ROW_STEP = 12
 # each scaled by what the counter reads for a plain 1 GiB device copy (FETCH_SIZE x2.0,
 # WRITE_SIZE x1.0).  Valid only for the kernel source with this SHA-256 prefix; otherwise
 # traffic is reported as null.
-MAIN_TRAFFIC = {"src_sha256": "d8b9d958143d1707", "fetch_bytes": 505476212, "write_bytes": 99428008}
+MAIN_TRAFFIC = {"src_sha256": "e281d96109a5fd61", "fetch_bytes": 507552885, "write_bytes": 99434954}
 
 
 def kernel_source_digest():
@@ -184,10 +184,41 @@ def backward_leg(mss, torch, sets, A, D, bias, Bt, Dn, N, L, fwd_ms, calls=10, w
     ms = [a.elapsed_time(b) for a, b in ev]
     avg = sum(ms) / len(ms)
     nb = bwd_bytes(Bt, Dn, N, L)
+
+    # forward + backward per training step: recomputing the states vs keeping them
+    saved = torch.empty(((L + 7) // 8, N // 4, Bt * Dn * 4), dtype=torch.float32, device="cuda:0")
+    out = torch.empty_like(sets[0]["u"])
+    last = torch.empty((Bt, Dn, N), dtype=torch.float32, device="cuda:0")
+
+    def pair(k, keep):
+        p = sets[k % len(sets)]
+        if keep:
+            mss.selective_scan_fwd_save(p["u"], p["delta"], A, p["B"], p["C"], D=D, z=p["z"],
+                                        delta_bias=bias, out=out, last_state=last, saved_states=saved)
+        else:
+            mss.selective_scan_fwd(p["u"], p["delta"], A, p["B"], p["C"], D=D, z=p["z"],
+                                   delta_bias=bias, out=out, last_state=last)
+        return mss.selective_scan_bwd(p["u"], p["delta"], A, p["B"], p["C"], douts[k % len(sets)], D=D,
+                                      z=p["z"], delta_bias=bias, saved_states=saved if keep else None)
+
+    pairs = {}
+    for keep in (False, True):
+        for k in range(warmup):
+            pair(k, keep)
+        torch.cuda.synchronize()
+        evp = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        for k in range(calls):
+            evp[k][0].record(stream)
+            pair(k, keep)
+            evp[k][1].record(stream)
+        torch.cuda.synchronize()
+        pairs[keep] = sum(a.elapsed_time(b) for a, b in evp) / calls
     return {"avg_ms": round(avg, 4), "min_ms": round(min(ms), 4), "calls": calls,
             "gbps": round(nb / (avg * 1e-3) / 1e9, 2), "algorithmic_bytes": nb,
             "ratio_to_fwd": round(avg / fwd_ms, 2),
-            "outputs": "du, ddelta, dz (bf16); dA, dB, dC, dD, ddelta_bias (fp32)"}
+            "outputs": "du, ddelta, dz (bf16); dA, dB, dC, dD, ddelta_bias (fp32)",
+            "fwd_bwd_recompute_ms": round(pairs[False], 4), "fwd_bwd_saved_states_ms": round(pairs[True], 4),
+            "saved_state_bytes": saved.numel() * 4}
 
 
 def conv_leg(mss, torch, devc, Bt, Dn, L, K=4, calls=20, warmup=3, copies=3):
