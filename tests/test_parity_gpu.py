@@ -132,6 +132,33 @@ def test_decode_bf16_1024_steps(mss, orc):
     assert_close(gs, ref_state, what="decode state", **TOL_F32)
 
 
+@pytest.mark.parametrize("Bt,Dn,dtype,with_z,a_kind", [
+    (1, 1, "f32", True, "s4d"), (1, 3, "bf16", True, "s4d"), (5, 7, "f32", False, "random"),
+    (3, 130, "bf16", True, "s4d"), (7, 333, "f32", True, "random"), (2, 5120, "bf16", False, "s4d"),
+    (129, 64, "bf16", True, "s4d")])
+def test_decode_row_counts(mss, orc, Bt, Dn, dtype, with_z, a_kind):
+    """Row counts that leave partial groups of rows and partial wavefronts: every row of three
+    chained steps, state and out, against the oracle."""
+    import torch
+    steps = 3
+    di = decode_inputs(Bt, Dn, 16, steps, dtype=dtype, with_z=with_z, seed=Bt * 1000 + Dn, a_kind=a_kind)
+    state0 = (0.5 * np.random.default_rng(Bt + Dn).standard_normal((Bt, Dn, 16))).astype(np.float32)
+    state = dev(state0)
+    A, D, bias = dev(di.A), dev(di.D), dev(di.dt_bias)
+    ref_state = state0.astype(np.float64).reshape(Bt * Dn, 16).copy()
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    for s in range(steps):
+        z = dev(di.z[s], dtype) if with_z else None
+        out = mss.selective_state_update(state, dev(di.x[s], dtype), dev(di.dt[s], dtype), A,
+                                         dev(di.B[s]), dev(di.C[s]), D=D, z=z, dt_bias=bias)
+        torch.cuda.synchronize()
+        ref = orc.selective_state_update(ref_state, di.x[s], di.dt[s], di.A, di.B[s], di.C[s], D=di.D,
+                                         z=di.z[s] if with_z else None, dt_bias=di.dt_bias,
+                                         rows=np.arange(Bt * Dn))
+        assert_close(host64(out).reshape(-1), ref.reshape(-1), what=f"decode out step {s}", **tol)
+        assert_close(host64(state).reshape(Bt * Dn, 16), ref_state, what=f"decode state step {s}", **TOL_F32)
+
+
 # ------------------------------------------------------------------ shapes and flags
 
 @pytest.mark.parametrize("Bt,Dn,L,dtype", [
