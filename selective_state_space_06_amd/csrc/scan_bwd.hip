@@ -806,22 +806,36 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
 // ---------------------------------------------------------------- reductions
 
 // dB[b][n][t] = sum_g part[g][b][n][t], dC[b][n][t] = sum_g part[g][b][16 + n][t].
+// Each lane sums kRedV consecutive steps of one (b, k) over the G groups, in group order (the
+// same order for every call), with kRedU groups' loads in flight; the partial rows are padded to
+// a multiple of kBT steps, so the vector loads stay inside them.
+constexpr int kRedV = 4, kRedU = 8;
 __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ part, float* __restrict__ dB,
                                                             float* __restrict__ dC, int G, int Bt, int64_t L,
                                                             int64_t tpad) {
-    const int64_t total = (int64_t)Bt * 2 * kN * L;
-    const int64_t gstride = (int64_t)Bt * 2 * kN * tpad;
+    const int64_t nv = tpad / kRedV;                 // vectors per padded row
+    const int64_t total = (int64_t)Bt * 2 * kN * nv;
+    const int64_t gstride = (int64_t)Bt * 2 * kN * tpad / kRedV;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t t = i % L;
-        const int64_t bk = i / L;           // b * 32 + k
+        const int64_t v = i % nv;
+        const int64_t bk = i / nv;           // b * 32 + k
+        const int64_t t = v * kRedV;
+        if (t >= L) continue;                // padding only
         const int k = static_cast<int>(bk % (2 * kN));
         const int64_t b = bk / (2 * kN);
-        const float* p = part + bk * tpad + t;
-        float s = 0.0f;
-        for (int g = 0; g < G; ++g) s += p[(int64_t)g * gstride];
-        if (k < kN) dB[(b * kN + k) * L + t] = s;
-        else dC[(b * kN + (k - kN)) * L + t] = s;
+        const float4* p = reinterpret_cast<const float4*>(part) + bk * nv + v;
+        float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll kRedU
+        for (int g = 0; g < G; ++g) {
+            const float4 q = p[(int64_t)g * gstride];
+            s.x += q.x; s.y += q.y; s.z += q.z; s.w += q.w;
+        }
+        float* dst = k < kN ? dB + (b * kN + k) * L : dC + (b * kN + (k - kN)) * L;
+        const float o[kRedV] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+        for (int e = 0; e < kRedV; ++e)
+            if (t + e < L) dst[t + e] = o[e];
     }
 }
 
@@ -834,9 +848,13 @@ __global__ __launch_bounds__(256) void bwd_reduce_par_kernel(const float* __rest
          i += (int64_t)gridDim.x * blockDim.x) {
         const int k = static_cast<int>(i / Dn);
         const int64_t d = i % Dn;
-        float s = 0.0f;
-        for (int sg = 0; sg < S; ++sg)
-            for (int b = 0; b < Bt; ++b) s += par[((int64_t)sg * kParW + k) * R + (int64_t)b * Dn + d];
+        float s = 0.0f;  // segment-major, batch-minor order, kRedU loads in flight
+        const int n = S * Bt;
+#pragma unroll kRedU
+        for (int j = 0; j < n; ++j) {
+            const int sg = j / Bt, b = j - sg * Bt;
+            s += par[((int64_t)sg * kParW + k) * R + (int64_t)b * Dn + d];
+        }
         if (k < kN) dA[d * kN + k] = s;
         else if (k == kN) { if (dD) dD[d] = s; }
         else if (dbias) dbias[d] = s;
@@ -870,7 +888,7 @@ hipError_t launch_t(const BwdArgs& k, const BwdLaunch& a, hipStream_t stream) {
         bwd_agg_kernel<E, VEC, SOFTPLUS, HAS_Z, false><<<grid, dim3(64), 0, stream>>>(k);
         bwd_main_kernel<E, VEC, SOFTPLUS, HAS_Z, false><<<grid, dim3(64), 0, stream>>>(k);
     }
-    const int64_t nbc = (int64_t)k.Bt * 2 * kN * k.L;
+    const int64_t nbc = (int64_t)k.Bt * 2 * kN * (k.tpad / kRedV);
     bwd_reduce_bc_kernel<<<dim3(grid_for(nbc)), dim3(256), 0, stream>>>(k.part, a.dB, a.dC, k.G, k.Bt, k.L, k.tpad);
     bwd_reduce_par_kernel<<<dim3(grid_for((int64_t)kParW * k.Dn)), dim3(256), 0, stream>>>(
         k.par, a.dA, a.dD, a.dbias, k.S, k.Bt, k.Dn, k.R);
