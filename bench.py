@@ -255,6 +255,49 @@ def conv_leg(mss, torch, devc, Bt, Dn, L, K=4, calls=20, warmup=3, copies=3):
                          "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4)}}
 
 
+def configs_leg(mss, torch, devc, warmup=3):
+    """The forward on the other scan workloads (fp32 u / delta / z / out): tiny (2 x 64 x 16 x 256),
+    Mamba-130M (8 x 1536 x 16 x 2048) and long context (1 x 1536 x 16 x 131072, no gate), each
+    from the seeded generators, with last_state, timed with events on the stream it runs on."""
+    import numpy as np
+    from synth import CONFIGS, scan_inputs
+    out = {}
+    for name, calls in (("tiny_fp32", 50), ("mamba130m_fp32", 20), ("long_fp32", 10)):
+        c = CONFIGS[name]
+        Bt, Dn, N, L = c["batch"], c["d_inner"], c["d_state"], c["L"]
+        s = scan_inputs(Bt, Dn, N, L, dtype="f32", with_z=c["with_z"], seed=0)
+        t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(devc)
+        u, dl, z, B, C = t(s.u), t(s.delta), t(s.z), t(s.B), t(s.C)
+        A, D, bias = t(s.A), t(s.D), t(s.delta_bias)
+        del s
+        o = torch.empty_like(u)
+        last = torch.empty((Bt, Dn, N), dtype=torch.float32, device=devc)
+
+        def call():
+            mss.selective_scan_fwd(u, dl, A, B, C, D=D, z=z, delta_bias=bias, out=o, last_state=last)
+
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        for k in range(calls):
+            ev[k][0].record(stream)
+            call()
+            ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in ev]
+        avg = sum(ms) / len(ms)
+        nb = scan_bytes(Bt, Dn, N, L, es_io=4, with_z=c["with_z"])
+        out[name] = {"shape": [Bt, Dn, N, L], "gate": bool(c["with_z"]), "avg_ms": round(avg, 4),
+                     "min_ms": round(min(ms), 4), "calls": calls, "gbps": round(nb / (avg * 1e-3) / 1e9, 2),
+                     "frac_hbm_peak": round(nb / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "state_updates_per_s": Bt * Dn * L * N / (avg * 1e-3)}
+        del u, dl, z, B, C, A, D, bias, o, last
+        torch.cuda.empty_cache()
+    return out
+
+
 def shard_leg(mss, torch, devc, s, Bt, Dn, N, L, calls=20, warmup=3):
     """The forward at the per-GPU shapes of two ways to spread the layer over GPUs without any
     exchange (rows are independent; B / C are replicated): channel split over 8 GPUs
@@ -304,6 +347,7 @@ def main():
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-shard", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the tiny / 130M / long-context fp32 forward")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build runs the scan on a single MI355X "
@@ -425,6 +469,8 @@ def main():
         res["shard_fwd"] = shard_leg(mss, torch, devc, s, Bt, Dn, N, L)
     if not args.no_decode_chain:
         res["decode_chain"] = decode_chain(mss, torch, devc)
+    if not args.no_configs:
+        res["other_configs"] = configs_leg(mss, torch, devc)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(s, Bt, Dn, N, L)
     print(json.dumps(res), flush=True)
