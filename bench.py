@@ -90,7 +90,33 @@ def cpu_baseline(s, Bt, Dn, N, L, min_cpu_s=12.0, max_reps=8):
     nbytes = scan_bytes(Bt, Dn, N, L) + decode_bytes(Bt, Dn, N)
     return {"value": nbytes * reps / total / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{reps} full steps (all {Bt * Dn} rows x {L} steps of the scan + 1 decode token "
-                      f"each), fp64, {total:.2f} s wall on {threads} threads"}
+                      f"each), fp64, {total:.2f} s wall on {threads} threads",
+            "cpu_model": cpu_model(), "single_thread_130m": single_thread_130m()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def single_thread_130m(rows=1536):
+    """The oracle on one host thread over one batch row block (1536 of the 12288 rows) of the
+    Mamba-130M fp32 workload (8 x 1536 x 16 x 2048): state updates per second."""
+    import oracle
+    from synth import CONFIGS, scan_inputs
+    c = CONFIGS["mamba130m_fp32"]
+    s = scan_inputs(1, c["d_inner"], c["d_state"], c["L"], dtype="f32", with_z=True, seed=0)
+    t = time.perf_counter()
+    oracle.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.D, s.z, s.delta_bias, nthreads=1)
+    wall = time.perf_counter() - t
+    n = rows * c["L"] * c["d_state"]
+    return {"state_updates_per_s": n / wall, "rows": rows, "L": c["L"], "wall_s": round(wall, 3)}
 
 
 def decode_chain(mss, torch, devc, steps=1024, pool=64):
