@@ -29,7 +29,10 @@
  *   - The forward scan may split long sequences across workgroups; it then uses a
  *     library-owned device workspace per (device, stream), grown on demand with hipMalloc
  *     and kept until the process ends.  Calls on one stream are ordered, so they never
- *     share that workspace concurrently.
+ *     share that workspace concurrently.  Under stream capture (a HIP graph) nothing can be
+ *     allocated: make one call of at least the same size on the capturing stream first.
+ *     The graph then holds that workspace's address, so its replays must not overlap other
+ *     calls on that stream.  No entry point records a memset: scratch is cleared by kernels.
  */
 #ifndef MAMBA_SCAN_H
 #define MAMBA_SCAN_H
@@ -40,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MSS_VERSION 10500 /* major * 10000 + minor * 100 + patch */
+#define MSS_VERSION 10600 /* major * 10000 + minor * 100 + patch */
 
 typedef enum { MSS_F32 = 0, MSS_BF16 = 1, MSS_I32 = 2 } mss_dtype_t;  /* I32: lengths only */
 

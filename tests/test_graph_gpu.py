@@ -1,0 +1,95 @@
+"""The scan forward, the forward that saves states and both backwards captured in a HIP graph
+(torch.cuda.graph) and replayed: every replay, with new inputs copied in between and eager
+library calls interleaved, must give exactly the eager results for those inputs.  The library's
+workspace belongs to a (device, stream) pair, so one warm-up call on the capture stream comes
+first (it allocates the workspace outside the capture); the kernels clear their scratch with
+kernels, not memset nodes.
+"""
+import numpy as np
+import pytest
+
+from synth import scan_inputs
+from tests.gpu_helpers import dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mss():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_06_amd as m
+    m.load_library()
+    return m
+
+
+def _inputs(dtype, seed, Bt=2, Dn=192, L=520):
+    s = scan_inputs(Bt, Dn, 16, L, dtype=dtype, seed=seed)
+    g = np.random.default_rng(700 + seed).standard_normal(s.u.shape).astype(np.float32)
+    return dict(u=dev(s.u, dtype), delta=dev(s.delta, dtype), z=dev(s.z, dtype), B=dev(s.B), C=dev(s.C),
+                dout=dev(g, dtype)), dict(A=dev(s.A), D=dev(s.D), bias=dev(s.delta_bias))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_graph_replays_match_eager(mss, dtype):
+    import torch
+    x, p = _inputs(dtype, 1)
+    Bt, Dn, L = x["u"].shape
+    out = torch.empty_like(x["u"])
+    last = torch.empty((Bt, Dn, 16), dtype=torch.float32, device="cuda")
+    out_s = torch.empty_like(x["u"])
+    last_s = torch.empty_like(last)
+    saved = torch.empty(((L + 7) // 8, 4, Bt * Dn * 4), dtype=torch.float32, device="cuda")
+
+    def body():
+        mss.selective_scan_fwd(x["u"], x["delta"], p["A"], x["B"], x["C"], D=p["D"], z=x["z"],
+                               delta_bias=p["bias"], out=out, last_state=last)
+        mss.selective_scan_fwd_save(x["u"], x["delta"], p["A"], x["B"], x["C"], D=p["D"], z=x["z"],
+                                    delta_bias=p["bias"], out=out_s, last_state=last_s, saved_states=saved)
+        g1 = mss.selective_scan_bwd(x["u"], x["delta"], p["A"], x["B"], x["C"], x["dout"], D=p["D"],
+                                    z=x["z"], delta_bias=p["bias"])
+        g2 = mss.selective_scan_bwd(x["u"], x["delta"], p["A"], x["B"], x["C"], x["dout"], D=p["D"],
+                                    z=x["z"], delta_bias=p["bias"], saved_states=saved)
+        return g1, g2
+
+    def snapshot(g1, g2):
+        r = {"out": out.clone(), "last": last.clone(), "out_s": out_s.clone(), "last_s": last_s.clone(),
+             "saved": saved.clone()}
+        for k, v in g1.items():
+            if v is not None:
+                r["g1_" + k] = v.clone()
+        for k, v in g2.items():
+            if v is not None:
+                r["g2_" + k] = v.clone()
+        return r
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        body()  # warm-up on the capture stream: the workspace is allocated here
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        gg1, gg2 = body()
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        nx, _ = _inputs(dtype, 10 + rep)
+        for k in x:
+            x[k].copy_(nx[k])
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):  # eager on the same inputs (and the same workspace)
+            e1, e2 = body()
+        torch.cuda.synchronize()
+        eager = snapshot(e1, e2)
+        graph.replay()
+        torch.cuda.synchronize()
+        replayed = snapshot(gg1, gg2)
+        assert set(eager) == set(replayed)
+        for k in eager:
+            assert torch.equal(eager[k], replayed[k]), (dtype, rep, k)
+        # the results changed with the inputs (the replay did run)
+        if rep > 0:
+            assert not torch.equal(replayed["out"], prev_out)
+        prev_out = replayed["out"].clone()
