@@ -120,3 +120,34 @@ def test_conv1d_past_2_31_elements(mss, oracle_mod, layer):
         assert np.array_equal(_row(fin, r), ref_fin[0, 0]), r   # the last K - 1 inputs, exactly
     del out, fin
     torch.cuda.empty_cache()
+
+
+def test_saved_states_past_2_31_elements(mss, oracle_mod, layer):
+    """The forward that saves states and the backward that reads them (saved states of 4.3 GB,
+    offsets past 2^31 floats): sampled saved blocks and du / ddelta / dz rows against the oracle."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(2027)
+    dout = torch.randn((BT, DN, L), generator=g, device="cuda", dtype=torch.bfloat16)
+    _, _, saved = mss.selective_scan_fwd_save(layer["u"], layer["delta"], layer["A"], layer["B"], layer["C"],
+                                              D=layer["D"], z=layer["z"], delta_bias=layer["delta_bias"])
+    grads = mss.selective_scan_bwd(layer["u"], layer["delta"], layer["A"], layer["B"], layer["C"], dout,
+                                   D=layer["D"], z=layer["z"], delta_bias=layer["delta_bias"],
+                                   saved_states=saved)
+    torch.cuda.synchronize()
+    for r in ROWS[-2:]:
+        q = _one_row_problem(layer, r)
+        for k8 in (1, L // 8 - 1):   # state entering step 8 k8: the row's scan stopped there
+            _, want = oracle_mod.selective_scan(q["u"], q["delta"], q["A"], q["B"], q["C"], D=q["D"], z=q["z"],
+                                                delta_bias=q["delta_bias"], seq_lens=np.array([8 * k8]))
+            got = host64(saved[k8].reshape(4, BT * DN, 4)[:, r, :].reshape(-1))
+            assert_close(got, want[0, 0], what=f"saved[{k8}] row {r}", **TOL_F32)
+        kw = dict(D=q["D"], z=q["z"], delta_bias=q["delta_bias"], dout=_row(dout, r)[None, None])
+        ref = oracle_mod.selective_scan_bwd(q["u"], q["delta"], q["A"], q["B"], q["C"], **kw)
+        mag = oracle_mod.selective_scan_bwd(q["u"], q["delta"], q["A"], q["B"], q["C"], magnitude=True, **kw)
+        for k in ("du", "ddelta", "dz"):
+            got = _row(grads[k], r)
+            lim = 2e-2 * np.abs(ref[k][0, 0]) + 1e-4 * mag[k][0, 0] + 1e-6
+            ratio = np.abs(got - ref[k][0, 0]) / lim
+            assert ratio.max() <= 1.0, (k, r, float(ratio.max()), int((ratio > 1).sum()))
+    del grads, dout, saved
+    torch.cuda.empty_cache()
