@@ -151,3 +151,33 @@ def test_saved_states_past_2_31_elements(mss, oracle_mod, layer):
             assert ratio.max() <= 1.0, (k, r, float(ratio.max()), int((ratio > 1).sum()))
     del grads, dout, saved
     torch.cuda.empty_cache()
+
+
+def test_decode_past_2_31_state_elements(mss, oracle_mod):
+    """One decode step on a (2100, 65600, 16) state (2.2e9 floats, 8.8 GB): sampled rows past
+    element 2^31 against the oracle."""
+    import torch
+    Bt = 2100
+    rows = [0, 65599, 137_000_000, Bt * DN - 1]
+    assert Bt * DN * N > 2**31
+    g = torch.Generator(device="cuda").manual_seed(2028)
+    state = torch.randn((Bt, DN, N), generator=g, device="cuda") * 0.5
+    x, dt, z = (torch.randn((Bt, DN), generator=g, device="cuda", dtype=torch.bfloat16) for _ in range(3))
+    B = torch.randn((Bt, N), generator=g, device="cuda")
+    C = torch.randn((Bt, N), generator=g, device="cuda")
+    small = scan_inputs(1, DN, N, 1, dtype="f32", seed=8)
+    A, D, bias = (torch.from_numpy(getattr(small, k)).to("cuda") for k in ("A", "D", "delta_bias"))
+    before = [np.ascontiguousarray(host64(state.reshape(-1, N)[r]).reshape(1, 1, N)) for r in rows]
+    out = mss.selective_state_update(state, x, dt, A, B, C, D=D, z=z, dt_bias=bias)
+    torch.cuda.synchronize()
+    for r, ref_state in zip(rows, before):   # each row as a (1, 1, N) problem of its own
+        b, d = divmod(r, DN)
+        one = lambda t: host64(t[b, d]).reshape(1, 1)
+        ref_out = oracle_mod.selective_state_update(ref_state, one(x), one(dt), host64(A[d]).reshape(1, N),
+                                                    host64(B[b]).reshape(1, N), host64(C[b]).reshape(1, N),
+                                                    D=host64(D[d : d + 1]), z=one(z),
+                                                    dt_bias=host64(bias[d : d + 1]))
+        assert_close(host64(out[b, d]).reshape(1, 1), ref_out, what=f"decode out row {r}", **TOL_BF16)
+        assert_close(host64(state[b, d]).reshape(1, 1, N), ref_state, what=f"decode state row {r}", **TOL_F32)
+    del state, x, dt, z, B, C, out
+    torch.cuda.empty_cache()
