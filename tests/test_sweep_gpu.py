@@ -123,6 +123,62 @@ def test_backward_sweep(mss, oracle_mod, monkeypatch, i):
         assert np.all(np.isfinite(got)) and ratio.max() <= 1.0, (i, k, float(ratio.max()))
 
 
+@pytest.mark.parametrize("i", range(1, N_CASES, 2))
+def test_saved_states_sweep(mss, oracle_mod, monkeypatch, i):
+    """The forward that saves states, then the backward from them (the cases the backward sweep
+    above skips): out, last_state, the first and last saved blocks and every gradient."""
+    import torch
+    c = _case(i)
+    print(f"[sweep saved {i}] {c}", flush=True)
+    if c["segments"]:
+        monkeypatch.setenv("MSS_SCAN_SEGMENTS", str(c["segments"]))
+        monkeypatch.setenv("MSS_BWD_SEGMENTS", str(c["segments"]))
+    s = scan_inputs(c["Bt"], c["Dn"], 16, c["L"], dtype=c["dtype"], seed=c["seed"] % 100000,
+                    a_kind=c["a_kind"], with_z=c["use_z"])
+    rng = np.random.default_rng(c["seed"] + 2)
+    dout = rng.standard_normal(s.u.shape).astype(np.float32)
+    if c["dtype"] == "bf16":
+        from synth import round_to_bf16
+        dout = round_to_bf16(dout)
+    h0 = (0.5 * rng.standard_normal((c["Bt"], c["Dn"], 16))).astype(np.float32) if c["with_h0"] else None
+    dlast = rng.standard_normal((c["Bt"], c["Dn"], 16)).astype(np.float32) if c["with_h0"] else None
+    lens = rng.integers(0, c["L"] + 1, c["Bt"]).astype(np.int32) if c["with_lens"] else None
+    dt = c["dtype"]
+    u, delta = _to_dev(s.u, dt, c["offset"]), _to_dev(s.delta, dt, c["offset"])
+    z = _to_dev(s.z, dt, c["offset"]) if c["use_z"] else None
+    D = dev(s.D) if c["use_D"] else None
+    bias = dev(s.delta_bias) if c["use_bias"] else None
+    lens_d = None if lens is None else torch.from_numpy(lens).to("cuda")
+    out, last, saved = mss.selective_scan_fwd_save(u, delta, dev(s.A), dev(s.B), dev(s.C), D=D, z=z,
+                                                   delta_bias=bias, initial_state=None if h0 is None else dev(h0),
+                                                   seq_lens=lens_d)
+    g = mss.selective_scan_bwd(u, delta, dev(s.A), dev(s.B), dev(s.C), _to_dev(dout, dt, c["offset"]), D=D, z=z,
+                               delta_bias=bias, seq_lens=lens_d, dlast_state=None if dlast is None else dev(dlast),
+                               saved_states=saved)
+    torch.cuda.synchronize()
+    okw = dict(D=s.D if c["use_D"] else None, z=s.z if c["use_z"] else None,
+               delta_bias=s.delta_bias if c["use_bias"] else None, h0=h0)
+    ref_out, ref_last = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, seq_lens=lens, **okw)
+    assert_close(host64(out), ref_out, what=f"sweep saved {i} out", **(TOL_BF16 if dt == "bf16" else TOL_F32))
+    assert_close(host64(last), ref_last, what=f"sweep saved {i} last_state", **TOL_F32)
+    blocks = host64(mss.saved_state_blocks(saved))
+    full = lens if lens is not None else np.full(c["Bt"], c["L"], np.int32)
+    for k in sorted({0, blocks.shape[0] - 1}):
+        _, want = oracle_mod.selective_scan(s.u, s.delta, s.A, s.B, s.C, seq_lens=np.minimum(full, 8 * k), **okw)
+        assert_close(blocks[k], want.reshape(-1, 16), what=f"sweep saved {i} block {k}", **TOL_F32)
+    kw = dict(D=okw["D"], z=okw["z"], delta_bias=okw["delta_bias"], dout=dout, h0=h0, seq_lens=lens, dlast=dlast)
+    ref = oracle_mod.selective_scan_bwd(s.u, s.delta, s.A, s.B, s.C, **kw)
+    mag = oracle_mod.selective_scan_bwd(s.u, s.delta, s.A, s.B, s.C, magnitude=True, **kw)
+    for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias"):
+        if ref[k] is None:
+            continue
+        got = host64(g[k])
+        rtol_out = 2e-2 if (k in ("du", "ddelta", "dz") and dt == "bf16") else 0.0
+        lim = rtol_out * np.abs(ref[k]) + 1e-4 * mag[k] + 1e-6
+        ratio = np.abs(got - ref[k]) / lim
+        assert np.all(np.isfinite(got)) and ratio.max() <= 1.0, (i, k, float(ratio.max()))
+
+
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_conv_sweep(mss, oracle_mod, i):
     import torch
