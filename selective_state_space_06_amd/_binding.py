@@ -6,6 +6,7 @@ There is no fallback: if the shared library has not been built, loading raises.
 from __future__ import annotations
 
 import ctypes
+import struct
 import os
 import threading
 
@@ -228,14 +229,37 @@ def state_update_raw(state, x, dt, A, B, C, D, z, dt_bias, out, stream) -> int:
 
 # ----------------------------------------------------------------------- torch front end
 
+_DESC = struct.Struct("<Qii3q3q")   # the bytes of one Tensor (mss_tensor_t)
+_DTYPES = None
+
+
 def _desc(t):
-    import torch
+    """torch tensor (or None) -> Tensor descriptor, packed in one step (this runs for every
+    argument of every call, so it is kept to a few attribute reads)."""
+    global _DTYPES
     if t is None:
         return None
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError("libmamba_scan takes device tensors")
-    dt = {torch.float32: MSS_F32, torch.bfloat16: MSS_BF16, torch.int32: MSS_I32}.get(t.dtype, -1)
-    return Tensor.make(t.data_ptr(), dt, list(t.shape), list(t.stride()))
+    if _DTYPES is None:
+        import torch
+        _DTYPES = {torch.float32: MSS_F32, torch.bfloat16: MSS_BF16, torch.int32: MSS_I32}
+    shape, stride = tuple(t.shape), t.stride()
+    n = len(shape)
+    if n > 3:
+        return Tensor.make(t.data_ptr(), _DTYPES.get(t.dtype, -1), list(shape), list(stride))  # rejected by the ABI
+    pad = (0,) * (3 - n)
+    return Tensor.from_buffer_copy(_DESC.pack(t.data_ptr(), _DTYPES.get(t.dtype, -1), n, *shape, *pad,
+                                              *stride, *pad))
+
+
+def _stream_of(dev_):
+    """The current HIP stream of dev_ (an int) when dev_ is the current device, else None (the
+    caller then switches devices for the call)."""
+    import torch
+    if dev_.index is None or dev_.index == torch.cuda.current_device():
+        return torch.cuda.current_stream().cuda_stream
+    return None
 
 
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
@@ -289,10 +313,15 @@ def causal_conv1d_update(state, x, weight, bias=None, silu=True, out=None):
     import torch
     if out is None:
         out = torch.empty_like(x, memory_format=torch.contiguous_format)
-    with torch.cuda.device(x.device):
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-        st = conv1d_update_raw(_desc(state), _desc(x), _desc(weight), _desc(bias),
-                               1 if silu else 0, _desc(out), stream)
+    stream = _stream_of(x.device)
+    if stream is not None:
+        st = conv1d_update_raw(_desc(state), _desc(x), _desc(weight), _desc(bias), 1 if silu else 0,
+                               _desc(out), stream)
+    else:
+        with torch.cuda.device(x.device):
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+            st = conv1d_update_raw(_desc(state), _desc(x), _desc(weight), _desc(bias),
+                                   1 if silu else 0, _desc(out), stream)
     if st != 0:
         raise MssError(st, "mss_causal_conv1d_update")
     return out
@@ -479,10 +508,15 @@ def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, 
     import torch
     if out is None:
         out = torch.empty_like(x, memory_format=torch.contiguous_format)
-    with torch.cuda.device(x.device):
-        stream = torch.cuda.current_stream(x.device).cuda_stream
+    stream = _stream_of(x.device)
+    if stream is not None:
         st = state_update_raw(_desc(state), _desc(x), _desc(dt), _desc(A), _desc(B), _desc(C),
                               _desc(D), _desc(z), _desc(dt_bias), _desc(out), stream)
+    else:
+        with torch.cuda.device(x.device):
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+            st = state_update_raw(_desc(state), _desc(x), _desc(dt), _desc(A), _desc(B), _desc(C),
+                                  _desc(D), _desc(z), _desc(dt_bias), _desc(out), stream)
     if st != 0:
         raise MssError(st, "mss_selective_state_update")
     return out
