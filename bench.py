@@ -376,7 +376,7 @@ def main():
     ap.add_argument("--no-configs", action="store_true", help="skip the tiny / 130M / long-context fp32 forward")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build runs the scan on a single MI355X "
+        print("bench.py measures one GPU only: the library runs the scan on a single MI355X "
               "(no multi-GPU path); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
