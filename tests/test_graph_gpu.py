@@ -93,3 +93,42 @@ def test_graph_replays_match_eager(mss, dtype):
         if rep > 0:
             assert not torch.equal(replayed["out"], prev_out)
         prev_out = replayed["out"].clone()
+
+
+def test_concurrent_streams_have_separate_workspaces(mss):
+    """Forward + backward (and the saved-state pair) on two streams at once, each on its own inputs:
+    the workspace belongs to the (device, stream) pair, so the overlapping calls must give
+    exactly what each gives alone."""
+    import torch
+    xs, ps = zip(*[_inputs("bf16", 40 + k, Bt=2, Dn=320, L=1536) for k in range(2)])
+    torch.cuda.synchronize()  # the inputs were made on the default stream
+
+    def work(x, p):
+        out, last = mss.selective_scan_fwd(x["u"], x["delta"], p["A"], x["B"], x["C"], D=p["D"], z=x["z"],
+                                           delta_bias=p["bias"])
+        _, _, saved = mss.selective_scan_fwd_save(x["u"], x["delta"], p["A"], x["B"], x["C"], D=p["D"],
+                                                  z=x["z"], delta_bias=p["bias"])
+        g = mss.selective_scan_bwd(x["u"], x["delta"], p["A"], x["B"], x["C"], x["dout"], D=p["D"], z=x["z"],
+                                   delta_bias=p["bias"])
+        gs = mss.selective_scan_bwd(x["u"], x["delta"], p["A"], x["B"], x["C"], x["dout"], D=p["D"],
+                                    z=x["z"], delta_bias=p["bias"], saved_states=saved)
+        r = {"out": out, "last": last, "saved": saved}
+        r.update({"g_" + k: v for k, v in g.items() if v is not None})
+        r.update({"gs_" + k: v for k, v in gs.items() if v is not None})
+        return r
+
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    alone = []
+    for k in range(2):  # one at a time (also allocates each stream's workspace)
+        with torch.cuda.stream(streams[k]):
+            alone.append({n: v.clone() for n, v in work(xs[k], ps[k]).items()})
+        torch.cuda.synchronize()
+    for rep in range(3):  # both queued before either is waited for
+        res = []
+        for k in range(2):
+            with torch.cuda.stream(streams[k]):
+                res.append(work(xs[k], ps[k]))
+        torch.cuda.synchronize()
+        for k in range(2):
+            for n, v in alone[k].items():
+                assert torch.equal(res[k][n], v), (rep, k, n)
