@@ -26,13 +26,19 @@
  *     invalid call never touches the device.
  *   - Return value: MSS_OK (0) or a negative mss_status_t; mss_status_string() names it.
  *     No C++ exception crosses the ABI.
- *   - The forward scan may split long sequences across workgroups; it then uses a
- *     library-owned device workspace per (device, stream), grown on demand with hipMalloc
- *     and kept until the process ends.  Calls on one stream are ordered, so they never
- *     share that workspace concurrently.  Under stream capture (a HIP graph) nothing can be
- *     allocated: make one call of at least the same size on the capturing stream first.
- *     The graph then holds that workspace's address, so its replays must not overlap other
- *     calls on that stream.  No entry point records a memset: scratch is cleared by kernels.
+ *   - The forward and backward scans split their work across wavefronts and carry state
+ *     between the parts through a library-owned device workspace per (device, stream; for
+ *     hipStreamPerThread also per host thread), allocated with hipMalloc on first need.  Calls
+ *     on one stream are ordered, so they never share it concurrently.  When a later call needs
+ *     more room, a larger buffer replaces it; the old one is kept (not freed) until
+ *     mss_release_workspaces(), because a HIP graph captured earlier may still hold its address.
+ *     Under stream capture nothing can be allocated: if the stream's workspace is too small the
+ *     call returns MSS_ERR_UNSUPPORTED, so make one call of at least the same size on the
+ *     capturing stream first.  A captured graph holds the workspace's address, so its replays
+ *     must not overlap other calls on that stream.  No entry point records a memset: scratch is
+ *     cleared by kernels.  (The forward's workspace does not depend on the problem size: 17
+ *     floats per row of a 64-row wavefront, 4352 bytes per wavefront of one round of
+ *     wavefronts, 13.4 MB on a 256-CU device.)
  */
 #ifndef MAMBA_SCAN_H
 #define MAMBA_SCAN_H
@@ -43,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MSS_VERSION 10600 /* major * 10000 + minor * 100 + patch */
+#define MSS_VERSION 10700 /* major * 10000 + minor * 100 + patch */
 
 typedef enum { MSS_F32 = 0, MSS_BF16 = 1, MSS_I32 = 2 } mss_dtype_t;  /* I32: lengths only */
 
@@ -311,6 +317,28 @@ int mss_causal_conv1d_update(const mss_tensor_t* state, const mss_tensor_t* x,
  */
 int mss_profile_enable(int on);
 int mss_profile_fwd(int* calls, double* carry_ms, double* main_ms);
+
+/*
+ * Frees every workspace buffer the library holds, on every device (current ones and those
+ * replaced by larger ones), after waiting for each device to finish its work.  HIP graphs that
+ * captured library calls must not be replayed afterwards (their workspace is gone); later calls
+ * allocate again.  Returns MSS_OK or MSS_ERR_HIP.
+ */
+int mss_release_workspaces(void);
+
+/*
+ * Test and tuning hook, not for production use: fixes choices the library otherwise makes by
+ * itself, for every later call in the process (results agree to rounding with any setting).
+ *   force_generic     nonzero: the forward runs the generic kernels (any layout; slower)
+ *   generic_segments  > 0: segments per channel group of the generic forward
+ *   fast_waves        > 0: wavefronts the fast forward spreads a call over (each takes an equal
+ *                     share of the (64-channel group, time tile) work; more than the groups
+ *                     splits sequences, fewer makes one wavefront scan several groups)
+ *   bwd_segments      > 0: segments per channel group of the backward
+ * Zeros restore the automatic plans.  Returns MSS_OK, or MSS_ERR_SHAPE for a negative count.
+ */
+int mss_set_plan_overrides(int force_generic, int generic_segments, int64_t fast_waves,
+                           int bwd_segments);
 
 /* Static, NUL-terminated name of a status code ("MSS_OK", "MSS_ERR_SHAPE", ...). */
 const char* mss_status_string(int status);

@@ -22,7 +22,7 @@ EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_fwd_with_state",
            "mss_selective_scan_fwd_varlen", "mss_selective_scan_bwd", "mss_selective_scan_bwd_varlen",
            "mss_selective_scan_fwd_save", "mss_selective_scan_bwd_saved",
            "mss_selective_state_update", "mss_causal_conv1d_fwd", "mss_causal_conv1d_update", "mss_profile_enable", "mss_profile_fwd",
-           "mss_status_string", "mss_version")
+           "mss_release_workspaces", "mss_set_plan_overrides", "mss_status_string", "mss_version")
 
 
 class Tensor(ctypes.Structure):
@@ -106,6 +106,10 @@ def load_library(path: str = LIB_PATH):
             lib.mss_status_string.argtypes = [ctypes.c_int]
             lib.mss_version.restype = ctypes.c_int
             lib.mss_version.argtypes = []
+            lib.mss_release_workspaces.restype = ctypes.c_int
+            lib.mss_release_workspaces.argtypes = []
+            lib.mss_set_plan_overrides.restype = ctypes.c_int
+            lib.mss_set_plan_overrides.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int]
             lib.mss_profile_enable.restype = ctypes.c_int
             lib.mss_profile_enable.argtypes = [ctypes.c_int]
             lib.mss_profile_fwd.restype = ctypes.c_int
@@ -122,6 +126,23 @@ def status_string(status: int) -> str:
 
 def version() -> int:
     return int(load_library().mss_version())
+
+
+def release_workspaces() -> None:
+    """mss_release_workspaces: free the library's workspace buffers (after the device is idle)."""
+    st = load_library().mss_release_workspaces()
+    if st != 0:
+        raise MssError(st, "mss_release_workspaces")
+
+
+def set_plan_overrides(force_generic: bool = False, generic_segments: int = 0, fast_waves: int = 0,
+                       bwd_segments: int = 0) -> None:
+    """mss_set_plan_overrides (tests and tuning only): fix the forward's path and split and the
+    backward's segment count for later calls; all defaults restore the automatic plans."""
+    st = load_library().mss_set_plan_overrides(1 if force_generic else 0, int(generic_segments),
+                                                int(fast_waves), int(bwd_segments))
+    if st != 0:
+        raise MssError(st, "mss_set_plan_overrides")
 
 
 def profile_enable(on: bool = True) -> None:

@@ -58,17 +58,35 @@ def build_example(verbose: bool = False) -> str:
 
 
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    """Compile every source into LIB_PATH (atomically replaced), then the C example against it.
-    Returns the library's path."""
+    """Compile every source (in parallel, one object each) and link them into LIB_PATH
+    (atomically replaced), then the C example against it. Returns the library's path."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(PKG_DIR, "_build")
+    os.makedirs(objdir, exist_ok=True)
+
+    def compile_one(src: str) -> str:
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc(), *compile_flags(), *(extra or []), "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        proc = subprocess.run(cmd, capture_output=True, text=True)
+        if proc.returncode != 0:
+            sys.stderr.write(proc.stdout + proc.stderr)
+            raise RuntimeError(f"hipcc failed on {src} with exit code {proc.returncode}")
+        return obj
+
+    jobs = max(1, min(len(SOURCES), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB_PATH + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *compile_flags(), *(extra or []), "-shared",
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         sys.stderr.write(proc.stdout + proc.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
+        raise RuntimeError(f"linking failed with exit code {proc.returncode}")
     os.replace(tmp, LIB_PATH)
     build_example(verbose)
     return LIB_PATH

@@ -1,10 +1,11 @@
 // abi.hip -- the extern "C" boundary of libmamba_scan: argument validation, the carry
 // workspace, and dispatch to the gfx950 kernels.  Every check runs before the first HIP call,
 // so invalid arguments never reach the device.
-#include <cstdlib>
+#include <atomic>
 #include <vector>
 #include <initializer_list>
 #include <mutex>
+#include <thread>
 #include <unordered_map>
 #include <utility>
 
@@ -90,23 +91,37 @@ int check_descs(const mss_tensor_t* const (&req)[K], std::initializer_list<const
 }
 
 // ---- per-device facts and the per-(device, stream) carry workspace
+// hipStreamPerThread is one handle value standing for a different stream in every host thread, so
+// its workspaces are also keyed by the calling thread.
 struct WsKey {
     int dev;
     void* stream;
-    bool operator==(const WsKey& o) const { return dev == o.dev && stream == o.stream; }
+    size_t thread;
+    bool operator==(const WsKey& o) const { return dev == o.dev && stream == o.stream && thread == o.thread; }
 };
 struct WsHash {
     size_t operator()(const WsKey& k) const {
-        return std::hash<void*>()(k.stream) * 31u + static_cast<size_t>(k.dev);
+        return (std::hash<void*>()(k.stream) * 31u + static_cast<size_t>(k.dev)) * 31u + k.thread;
     }
 };
 struct WsEntry {
     void* ptr = nullptr;
     size_t bytes = 0;
+    int dev = 0;
 };
 std::mutex g_mu;
 std::unordered_map<WsKey, WsEntry, WsHash> g_ws;
+// Buffers replaced by larger ones.  They are not freed when replaced: a HIP graph captured
+// earlier may hold their address and replay later, and another host thread may have been handed
+// the pointer and not yet queued its kernels.  mss_release_workspaces() frees them.
+std::vector<std::pair<int, void*>> g_retired;
 std::unordered_map<int, int> g_cus;
+
+// Test and tuning overrides (mss_set_plan_overrides); zero = automatic plan.
+std::atomic<int> g_force_generic{0};
+std::atomic<int> g_generic_segments{0};
+std::atomic<int64_t> g_fast_waves{0};
+std::atomic<int> g_bwd_segments{0};
 
 hipError_t device_cus(int dev, int* cus) {
     std::lock_guard<std::mutex> lk(g_mu);
@@ -123,26 +138,29 @@ hipError_t device_cus(int dev, int* cus) {
     return hipSuccess;
 }
 
-hipError_t workspace(int dev, void* stream, size_t bytes, float** out) {
+// The workspace of (dev, stream) with at least `bytes`, in *out.  Returns MSS_OK, MSS_ERR_HIP, or
+// MSS_ERR_UNSUPPORTED when the buffer would have to grow while `stream` is being captured into a
+// graph (nothing can be allocated then: a call of at least the same size on that stream must come
+// first).
+int workspace(int dev, void* stream, size_t bytes, float** out) {
     std::lock_guard<std::mutex> lk(g_mu);
-    WsEntry& w = g_ws[WsKey{dev, stream}];
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const size_t tid = hs == hipStreamPerThread ? std::hash<std::thread::id>()(std::this_thread::get_id()) : 0;
+    WsEntry& w = g_ws[WsKey{dev, stream, tid}];
     if (w.bytes < bytes) {
-        if (w.ptr) {
-            hipError_t e = hipFree(w.ptr);  // synchronises the device: no kernel still uses it
-            w.ptr = nullptr;
-            w.bytes = 0;
-            if (e != hipSuccess) return e;
-        }
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(hs, &cs) != hipSuccess) return MSS_ERR_HIP;
+        if (cs != hipStreamCaptureStatusNone) return MSS_ERR_UNSUPPORTED;
         const size_t grown = bytes + bytes / 4;
-        hipError_t e = hipMalloc(&w.ptr, grown);
-        if (e != hipSuccess) {
-            w.ptr = nullptr;
-            return e;
-        }
+        void* p = nullptr;
+        if (hipMalloc(&p, grown) != hipSuccess) return MSS_ERR_HIP;
+        if (w.ptr) g_retired.emplace_back(w.dev, w.ptr);
+        w.ptr = p;
         w.bytes = grown;
+        w.dev = dev;
     }
     *out = static_cast<float*>(w.ptr);
-    return hipSuccess;
+    return MSS_OK;
 }
 
 // Launch timing (mss_profile_enable / mss_profile_fwd): one event triple per recorded call.
@@ -246,7 +264,6 @@ int validate_decode(const mss_tensor_t* state, const mss_tensor_t* x, const mss_
     if (overlap(out, state)) return MSS_ERR_ALIAS;
 
     if (N != kN) return MSS_ERR_UNSUPPORTED;
-    if (Bt * Dn * 4 > (int64_t)0x7fffffff * 256) return MSS_ERR_UNSUPPORTED;
     return MSS_OK;
 }
 
@@ -478,18 +495,27 @@ int mss_selective_scan_fwd_save(const mss_tensor_t* u, const mss_tensor_t* delta
         if (hipGetDevice(&dev) != hipSuccess) return MSS_ERR_HIP;
         if (device_cus(dev, &cus) != hipSuccess) return MSS_ERR_HIP;
         // the fast path takes every length (rows that are not whole 16-byte vectors run its
-        // element-aligned variant); the generic kernels remain behind MSS_SCAN_GENERIC
-        const bool fast = a.L > 0 && (a.saved || getenv("MSS_SCAN_GENERIC") == nullptr);
+        // element-aligned variant); the generic kernels run for L = 0 and when a test forces them
+        bool fast = a.L > 0 && (a.saved || g_force_generic.load() == 0);
         mss::ScanPlan plan;
         if (fast) {
-            plan = mss::plan_fast(a, cus);
-        } else {
-            plan = mss::plan_scan(a, cus, mss::generic_tile());
+            plan = mss::plan_fast(a, cus, g_fast_waves.load());
+            // 2^32 (64-channel group, 16- or 32-step tile) pairs and more: the generic kernels
+            // (only the state-saving variant has no generic form)
+            if (!plan.fits) {
+                if (a.saved) return MSS_ERR_UNSUPPORTED;
+                fast = false;
+            }
+        }
+        if (!fast) {
+            plan = mss::plan_scan(a, cus, mss::generic_tile(), g_generic_segments.load());
             plan.workspace_bytes = mss::generic_workspace_bytes(a, plan.segments);
         }
         float* ws = nullptr;
-        if (plan.workspace_bytes > 0 && workspace(dev, stream, plan.workspace_bytes, &ws) != hipSuccess)
-            return MSS_ERR_HIP;
+        if (plan.workspace_bytes > 0) {
+            const int wst = workspace(dev, stream, plan.workspace_bytes, &ws);
+            if (wst != MSS_OK) return wst;
+        }
         std::unique_lock<std::mutex> plk(g_mu, std::defer_lock);
         int slot = -1;
         if (g_prof.on) {
@@ -605,10 +631,13 @@ int bwd_impl(const mss_tensor_t* u, const mss_tensor_t* delta, const mss_tensor_
         int dev = 0, cus = 0;
         if (hipGetDevice(&dev) != hipSuccess) return MSS_ERR_HIP;
         if (device_cus(dev, &cus) != hipSuccess) return MSS_ERR_HIP;
-        const int segments = mss::plan_bwd_segments(a, cus);
+        const int segments = mss::plan_bwd_segments(a, cus, g_bwd_segments.load());
         const size_t bytes = mss::bwd_workspace_bytes(a, segments);
         float* ws = nullptr;
-        if (bytes > 0 && workspace(dev, stream, bytes, &ws) != hipSuccess) return MSS_ERR_HIP;
+        if (bytes > 0) {
+            const int wst = workspace(dev, stream, bytes, &ws);
+            if (wst != MSS_OK) return wst;
+        }
         return mss::launch_scan_bwd(a, segments, ws, s) == hipSuccess ? MSS_OK : MSS_ERR_HIP;
     } catch (...) {
         return MSS_ERR_HIP;
@@ -725,6 +754,37 @@ int mss_profile_fwd(int* calls, double* carry_ms, double* main_ms) {
     } catch (...) {
         return MSS_ERR_HIP;
     }
+}
+
+int mss_release_workspaces(void) {
+    try {
+        std::lock_guard<std::mutex> lk(g_mu);
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return MSS_ERR_HIP;
+        std::vector<std::pair<int, void*>> all(g_retired);
+        for (const auto& kv : g_ws)
+            if (kv.second.ptr) all.emplace_back(kv.second.dev, kv.second.ptr);
+        int st = MSS_OK;
+        for (const auto& b : all) {
+            if (hipSetDevice(b.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess || hipFree(b.second) != hipSuccess)
+                st = MSS_ERR_HIP;
+        }
+        g_retired.clear();
+        g_ws.clear();
+        if (hipSetDevice(cur) != hipSuccess) st = MSS_ERR_HIP;
+        return st;
+    } catch (...) {
+        return MSS_ERR_HIP;
+    }
+}
+
+int mss_set_plan_overrides(int force_generic, int generic_segments, int64_t fast_waves, int bwd_segments) {
+    if (generic_segments < 0 || fast_waves < 0 || bwd_segments < 0) return MSS_ERR_SHAPE;
+    g_force_generic.store(force_generic != 0 ? 1 : 0);
+    g_generic_segments.store(generic_segments);
+    g_fast_waves.store(fast_waves);
+    g_bwd_segments.store(bwd_segments);
+    return MSS_OK;
 }
 
 int mss_selective_state_update(const mss_tensor_t* state, const mss_tensor_t* x, const mss_tensor_t* dt,

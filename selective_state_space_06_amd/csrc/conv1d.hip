@@ -14,8 +14,6 @@
 // input read once from memory, each output written once.  A thread's K - 1 left neighbours are
 // the tail of the previous vector, which the thread loads as well (its neighbour's line, already
 // on its way); a row's first vector takes them from the carried state.
-#include <cstdlib>
-
 #include "device_math.hpp"
 #include "mss_internal.hpp"
 
@@ -40,12 +38,8 @@ struct ConvArgs {
 // the row's last, partial vector element by element (no access leaves the row), and the final
 // state left to conv_state_kernel.
 template <class E, int K, bool SILU, class I, bool RAGGED>
-__global__ __launch_bounds__(256) void conv_fwd_vec_kernel(ConvArgs a) {
+__device__ __forceinline__ void conv_vec(const ConvArgs& a, I g, I nv) {
     constexpr int V = E::kPerVec;
-    const I nv = static_cast<I>(RAGGED ? (a.L + V - 1) / V : a.L / V);  // vectors per row
-    const I g = static_cast<I>(blockIdx.x) * static_cast<I>(blockDim.x) + static_cast<I>(threadIdx.x);
-    const I total = static_cast<I>(a.R) * nv;
-    if (g >= total) return;
     const I r = g / nv, q = g % nv;
     const int64_t d = static_cast<int64_t>(r % static_cast<I>(a.Dn));
     const int64_t r64 = static_cast<int64_t>(r), q64 = static_cast<int64_t>(q);
@@ -111,6 +105,19 @@ __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(ConvArgs a) {
     }
 }
 
+// The grid is capped (a dispatch holds at most 2^32 - 1 work-items per dimension): threads
+// stride over the vectors; at the usual sizes each thread takes exactly one.
+template <class E, int K, bool SILU, class I, bool RAGGED>
+__global__ __launch_bounds__(256) void conv_fwd_vec_kernel(ConvArgs a) {
+    constexpr int V = E::kPerVec;
+    const I nv = static_cast<I>(RAGGED ? (a.L + V - 1) / V : a.L / V);  // vectors per row
+    const I total = static_cast<I>(a.R) * nv;
+    const I stride = static_cast<I>(gridDim.x) * static_cast<I>(blockDim.x);
+    for (I g = static_cast<I>(blockIdx.x) * static_cast<I>(blockDim.x) + static_cast<I>(threadIdx.x); g < total;
+         g += stride)
+        conv_vec<E, K, SILU, I, RAGGED>(a, g, nv);
+}
+
 // final state for rows of any length (and for L = 0): the last K - 1 inputs,
 // taken from the carried state where the sequence is shorter than that.
 template <class E, int K>
@@ -159,8 +166,8 @@ template <class E, int K, bool SILU, bool RAGGED>
 void fwd_vec(const ConvArgs& a, hipStream_t s) {
     constexpr int V = E::kPerVec;
     const int64_t total = a.R * ((a.L + V - 1) / V);
-    const dim3 grid(blocks_for(total, INT32_MAX));
-    if (total + 256 < (int64_t)UINT32_MAX)
+    const dim3 grid(blocks_for(total, 1 << 22));
+    if (total + (int64_t{1} << 30) < (int64_t)UINT32_MAX)
         conv_fwd_vec_kernel<E, K, SILU, uint32_t, RAGGED><<<grid, dim3(256), 0, s>>>(a);
     else
         conv_fwd_vec_kernel<E, K, SILU, int64_t, RAGGED><<<grid, dim3(256), 0, s>>>(a);

@@ -108,25 +108,29 @@ struct ConvUpdateLaunch {
     bool silu, bf16;
 };
 
-// How the forward scan is decomposed along L: `segments` workgroup-rows per channel
-// group, each covering `seg_len` steps (a multiple of the time tile).
+// How the forward scan is decomposed.  Generic path: `segments` workgroup-rows per channel
+// group, each covering `seg_len` steps.  Fast path: `waves` wavefronts, each taking an equal
+// contiguous range of the (channel group, tile) work; `segments` > 1 when some range ends
+// inside a group (the aggregate kernel then has work).
 struct ScanPlan {
     int segments;
     int64_t seg_len;
-    size_t workspace_bytes;  // carry workspace needed (0 when segments == 1)
+    int64_t waves;
+    int64_t xcds;            // fast path: XCDs the wavefronts are dealt over
+    bool fits = true;        // fast path: the (group, tile) count fits the kernels' 32-bit counts
+    size_t workspace_bytes;  // carry workspace needed (0 when nothing is carried)
 };
 
 // Segment plan for a time tile of `tile` steps (segments are whole tiles).
-ScanPlan plan_scan(const ScanLaunch& a, int num_cus, int tile);
+ScanPlan plan_scan(const ScanLaunch& a, int num_cus, int tile, int segments_override);
 // Generic path (any alignment): scan_fwd.hip.
 hipError_t launch_scan_fwd(const ScanLaunch& a, const ScanPlan& plan, float* workspace,
                            hipStream_t stream);
 int generic_tile();
 size_t generic_workspace_bytes(const ScanLaunch& a, int segments);
-// Fast path (rows 16-byte aligned): scan_fast.hip.  Its plan splits the tiles of L evenly
-// over the segments (seg_len is not used).
-ScanPlan plan_fast(const ScanLaunch& a, int num_cus);
-size_t fast_workspace_bytes(const ScanLaunch& a, int segments);
+// Fast path: scan_fast.hip.  `waves_override` > 0 replaces the automatic wavefront count.
+ScanPlan plan_fast(const ScanLaunch& a, int num_cus, int64_t waves_override);
+size_t fast_workspace_bytes(const ScanLaunch& a, const ScanPlan& plan);
 hipError_t launch_scan_fast(const ScanLaunch& a, const ScanPlan& plan, float* workspace,
                             hipStream_t stream);
 hipError_t launch_state_update(const DecodeLaunch& a, hipStream_t stream);
@@ -134,7 +138,7 @@ hipError_t launch_state_update(const DecodeLaunch& a, hipStream_t stream);
 hipError_t launch_conv1d_fwd(const ConvLaunch& a, hipStream_t stream);
 hipError_t launch_conv1d_update(const ConvUpdateLaunch& a, hipStream_t stream);
 // Backward scan: scan_bwd.hip.
-int plan_bwd_segments(const BwdLaunch& a, int num_cus);
+int plan_bwd_segments(const BwdLaunch& a, int num_cus, int segments_override);
 size_t bwd_workspace_bytes(const BwdLaunch& a, int segments);
 hipError_t launch_scan_bwd(const BwdLaunch& a, int segments, void* workspace, hipStream_t stream);
 

@@ -925,14 +925,13 @@ Layout layout_of(const BwdLaunch& a, int S) {  // no checkpoints when the forwar
 
 // Segments per channel group: as many wavefronts as fit on the chip at once (the main kernel's
 // LDS and 256 VGPRs allow eight per CU for bf16 rows, seven for fp32 rows), at most one per tile.
-// MSS_BWD_SEGMENTS overrides.
-int plan_bwd_segments(const BwdLaunch& a, int num_cus) {
+// `segments_override` > 0 replaces the count (tests force many or few segments with it).
+int plan_bwd_segments(const BwdLaunch& a, int num_cus, int segments_override) {
     const int64_t groups = a.Bt * ((a.Dn + 63) / 64);
     const int64_t ntiles = (a.L + kBT - 1) / kBT;
     const int64_t target = (a.bf16 ? 8LL : 7LL) * (num_cus > 0 ? num_cus : 256);
     int64_t S = groups > 0 ? target / groups : 1;  // one round: every wavefront resident at once
-    const char* env = getenv("MSS_BWD_SEGMENTS");
-    if (env && atoi(env) > 0) S = atoi(env);
+    if (segments_override > 0) S = segments_override;
     if (S > ntiles) S = ntiles;
     if (S > 65535) S = 65535;
     if (S < 1) S = 1;

@@ -21,11 +21,13 @@
 //   * the per-step result y + D u stays fp32 in the LDS words the step has consumed; an
 //     epilogue per tile applies the gate silu(z) (z of the tile is loaded into VGPRs when the
 //     tile starts), rounds to the storage type and writes 16-byte vectors;
-//   * long sequences are split into S segments of whole tiles per channel group (segment k
-//     takes tiles [k T / S, (k + 1) T / S) of the T tiles).  A first kernel computes,
-//     per segment, the pair (sum of delta, local end state from h = 0); the main kernel folds
-//     the pairs of the preceding segments with the associative operator
-//     (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2) into its starting state and runs the segment.
+//   * the work is spread over one round of wavefronts for the whole chip: the (64-channel group,
+//     tile) pairs of the call are numbered group-major and each wavefront takes an equal
+//     contiguous range of them, so no SIMD holds more work than another.  A range that starts
+//     inside a group needs the state reached there: a first kernel computes, for every range
+//     that ends inside a group, the pair (sum of delta, end state from h = 0) of that last piece;
+//     the main kernel folds the pairs of the group's earlier pieces with the associative operator
+//     (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2) into its starting state and runs its piece.
 //     A scan continued from a given state h0 starts that fold from h0 instead of zeros (the
 //     aggregates do not depend on it).  With per-batch sequence lengths, the steps at or past a
 //     batch's length get dt = 0 (abar = 1, no input: the state stands still) and zero outputs, so
@@ -36,8 +38,6 @@
 // Abar_n = Abar_0^(n+1) is formed by multiplications (one exp2 per (b, d, t)); the aggregate
 // pass then uses the backward form sum_s x_s B_s R_s^(n+1), R_s the product of the later
 // Abar_0, which costs two VALU operations per state update.
-#include <cstdlib>
-
 #include "device_math.hpp"
 #include "mss_internal.hpp"
 
@@ -66,18 +66,19 @@ struct RowSetup {
 
 __device__ __forceinline__ RowSetup row_setup(const float* __restrict__ A, const float* __restrict__ D,
                                               const float* __restrict__ bias, int64_t Dn,
-                                              const int32_t* __restrict__ lens, int64_t L) {
+                                              const int32_t* __restrict__ lens, int64_t L, int64_t cb,
+                                              int64_t b) {
     RowSetup r;
     if (lens) {
-        const int64_t l = lens[blockIdx.y];
+        const int64_t l = lens[b];
         r.stop = l < 0 ? 0 : (l > L ? L : l);
     } else {
         r.stop = L;
     }
-    const int64_t d = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    const int64_t d = cb * 64 + threadIdx.x;
     r.active = d < Dn;
     const int64_t dc = r.active ? d : Dn - 1;
-    r.row = (int64_t)blockIdx.y * Dn + dc;
+    r.row = b * Dn + dc;
     const float4* Ar = reinterpret_cast<const float4*>(A + dc * kN);
     float Av[kN];
 #pragma unroll
@@ -415,15 +416,54 @@ __device__ __forceinline__ void main_body(
     }
 }
 
-// Segment seg of S: tiles [seg T / S, (seg + 1) T / S) of the T = ceil(L / TT) tiles.  (Whole
-// tiles keep every tile on a 64-byte boundary of its rows; finer splits were measured slower.)
-template <class E>
-__device__ __forceinline__ void seg_bounds(int seg, int S, int64_t L, int64_t& t_begin, int64_t& t_end) {
-    constexpr int TT = Geo<E>::TT;
-    const int64_t T = (L + TT - 1) / TT;
-    t_begin = (seg * T / S) * TT;
-    const int64_t e = ((seg + 1) * T / S) * TT;
-    t_end = e < L ? e : L;
+// The work of a call is the grid of (channel group, tile) pairs: G groups of 64 rows (a group is
+// one batch's channel block cb, g = b * gx + cb) times T = ceil(L / TT) tiles each, numbered
+// group-major.  With GT = q W + rem, wavefront w of W takes the contiguous range starting at
+// w q + min(w, rem), q + 1 tiles for the first rem wavefronts and q for the others, so every
+// wavefront gets the same number of tiles to within one.  A range can start
+// in the middle of a group (its first piece then needs the state reached at that tile) and can
+// run on into the next group (whose first tile starts from h0 / zeros).  W is one full round of
+// wavefronts for the chip, so no SIMD ends up with more wavefronts than another.
+//
+// Wavefront numbers are dealt to the XCDs in contiguous blocks.  The hardware hands consecutive
+// workgroups to the XCDs in turn (workgroup i to XCD i mod X), so workgroup i takes number
+// xcd * q + min(xcd, r) + i / X, with W = q X + r: XCD k then scans one contiguous stretch of
+// groups, and its L2 and address translation see 1/X of the rows instead of all of them
+// (measured: 12-24% faster than numbering the wavefronts in workgroup order).
+// Every count below the tile count is held in 32 bits (the host refuses a plan whose counts do
+// not fit), so the divisions of the per-piece set-up stay short.
+struct Part {
+    uint32_t T;    // tiles per group
+    uint32_t W;    // wavefronts, 1 <= W <= G T
+    uint32_t q;    // G T / W
+    uint32_t rem;  // G T mod W
+    uint32_t gx;   // channel groups per batch
+    uint32_t xq, xr;  // W = xq X + xr: wavefronts per XCD (the first xr XCDs take one more)
+    uint32_t X;    // XCDs the workgroups are dealt over
+};
+
+__device__ __forceinline__ uint32_t part_begin(const Part& p, uint32_t w) {
+    return w * p.q + (w < p.rem ? w : p.rem);
+}
+
+// This workgroup's wavefront number (a bijection of [0, W)).
+__device__ __forceinline__ uint32_t wave_of(const Part& p) {
+    const uint32_t i = blockIdx.x, x = i % p.X;
+    return x * p.xq + (x < p.xr ? x : p.xr) + i / p.X;
+}
+
+// The wavefront whose range holds tile t of the numbering.  For t = g T, the start of group g,
+// its range and those of the wavefronts up to the one holding tile r cover group g's tiles
+// before r.
+__device__ __forceinline__ uint32_t wave_holding(const Part& p, uint32_t t) {
+    const uint32_t big = p.rem * (p.q + 1);  // tiles of the wavefronts that take q + 1
+    return t < big ? t / (p.q + 1) : p.rem + (t - big) / p.q;
+}
+
+// Where wavefront w's aggregate lives: one slot per wavefront, [slot][n (16 states, then the sum of
+// delta)][lane], so a wave's loads of one word are 256 contiguous bytes.
+__device__ __forceinline__ const float* agg_slot(const float* agg, uint32_t w) {
+    return agg + static_cast<size_t>(w) * (kN + 1) * 64 + threadIdx.x;
 }
 
 // B at steps j, j + 1 from the aggregate kernel's B block (stride 20 floats per step).
@@ -445,13 +485,14 @@ __device__ __forceinline__ BPair b_pair(const float* sbc, int j) {
     return r;
 }
 
-// Folds the aggregates of segments [0, seg) into the starting state of segment seg, four
-// segments per round: the 68 loads of a round are issued together, so a round costs one memory
-// round trip.  The fold starts from the row's h0 when one is given, else from zeros.
+// Folds the aggregates of slots [s_begin, s_end) (the pieces of this group before the current
+// one, in order) into the starting state, four slots per round: the 68 loads of a round are
+// issued together, so a round costs one memory round trip.  The fold starts from the row's h0
+// when one is given, else from zeros.
 template <bool POW>
 __device__ __forceinline__ void fold_carry(float (&h)[kN], const float (&A2)[kN],
                                            const float* __restrict__ agg, const float* __restrict__ h0,
-                                           int seg, int64_t R, int64_t row) {
+                                           uint32_t s_begin, uint32_t s_end, int64_t row) {
     constexpr int kRound = 4;
     if (h0) {
         const float4* src = reinterpret_cast<const float4*>(h0 + row * kN);
@@ -464,18 +505,18 @@ __device__ __forceinline__ void fold_carry(float (&h)[kN], const float (&A2)[kN]
 #pragma unroll
         for (int n = 0; n < kN; ++n) h[n] = 0.0f;
     }
-    for (int s0 = 0; s0 < seg; s0 += kRound) {
+    for (uint32_t s0 = s_begin; s0 < s_end; s0 += kRound) {
         float v[kRound][kN + 1];
 #pragma unroll
         for (int i = 0; i < kRound; ++i) {
-            const int s = s0 + i < seg ? s0 + i : seg - 1;  // past the end: reload the last one
-            const float* a = agg + (int64_t)s * (kN + 1) * R + row;
+            const uint32_t s = s0 + i < s_end ? s0 + i : s_end - 1;  // past the end: reload the last one
+            const float* a = agg_slot(agg, s);
 #pragma unroll
-            for (int n = 0; n <= kN; ++n) v[i][n] = a[(int64_t)n * R];
+            for (int n = 0; n <= kN; ++n) v[i][n] = a[n * 64];
         }
 #pragma unroll
         for (int i = 0; i < kRound; ++i) {
-            if (s0 + i < seg) {
+            if (s0 + i < s_end) {
                 if (POW) {
                     float p[kN];
                     powers16(fast_exp2(v[i][kN] * A2[0]), p);
@@ -497,34 +538,44 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void sc
     const float* __restrict__ B, const float* __restrict__ C, const float* __restrict__ D,
     const float* __restrict__ bias, const float* __restrict__ agg, const float* __restrict__ h0,
     typename E::storage* __restrict__ out, float* __restrict__ last_state, const int32_t* __restrict__ lens,
-    float* __restrict__ saved, int64_t Dn, int64_t L, int S) {
+    float* __restrict__ saved, int64_t Dn, int64_t L, int64_t R, Part p) {
     using G = Geo<E>;
     __shared__ uint32_t srow[G::kRowWords];
     __shared__ __align__(16) float sbc[G::TT * 36];
-    const RowSetup rs = row_setup(A, D, bias, Dn, lens, L);
-    const int seg = blockIdx.z;
-    const int64_t R = (int64_t)gridDim.y * Dn;
-    int64_t t_begin, t_end;
-    seg_bounds<E>(seg, S, L, t_begin, t_end);
-    const int64_t base = rs.row * L;
-    const float* Bb = B + (int64_t)blockIdx.y * kN * L;
-    const float* Cb = C + (int64_t)blockIdx.y * kN * L;
-    const typename E::storage* zp = z ? z + base : nullptr;
-    float h[kN];
-    if (__all(rs.pow_ok)) {
-        fold_carry<true>(h, rs.A2, agg, h0, seg, R, rs.row);
-        main_body<E, HAS_Z, SOFTPLUS, true, VARLEN, RAGGED, SAVE>(rs, h, u + base, delta + base, zp, out + base, Bb, Cb,
-                                                    L, srow, sbc, t_begin, t_end, saved, R);
-    } else {
-        fold_carry<false>(h, rs.A2, agg, h0, seg, R, rs.row);
-        main_body<E, HAS_Z, SOFTPLUS, false, VARLEN, RAGGED, SAVE>(rs, h, u + base, delta + base, zp, out + base, Bb, Cb,
-                                                     L, srow, sbc, t_begin, t_end, saved, R);
-    }
-    if (last_state && rs.active && seg == S - 1) {
-        float4* dst = reinterpret_cast<float4*>(last_state + rs.row * kN);
+    const uint32_t w = wave_of(p);
+    const uint32_t r1 = part_begin(p, w + 1);
+    for (uint32_t r = part_begin(p, w); r < r1;) {
+        // the piece of group g this range holds: tiles [ta, te)
+        const uint32_t g = r / p.T;
+        const uint32_t gs = g * p.T;
+        const uint32_t te = (r1 < gs + p.T ? r1 : gs + p.T) - gs;
+        const uint32_t ta = r - gs;
+        const uint32_t b = g / p.gx;
+        const RowSetup rs = row_setup(A, D, bias, Dn, lens, L, g - b * p.gx, b);
+        const int64_t t_begin = static_cast<int64_t>(ta) * G::TT;
+        const int64_t t_end = static_cast<int64_t>(te) * G::TT < L ? static_cast<int64_t>(te) * G::TT : L;
+        const uint32_t s_begin = ta > 0 ? wave_holding(p, gs) : w;  // earlier pieces of this group
+        const int64_t base = rs.row * L;
+        const float* Bb = B + static_cast<int64_t>(b) * kN * L;
+        const float* Cb = C + static_cast<int64_t>(b) * kN * L;
+        const typename E::storage* zp = z ? z + base : nullptr;
+        float h[kN];
+        if (__all(rs.pow_ok)) {
+            fold_carry<true>(h, rs.A2, agg, h0, s_begin, w, rs.row);
+            main_body<E, HAS_Z, SOFTPLUS, true, VARLEN, RAGGED, SAVE>(rs, h, u + base, delta + base, zp, out + base,
+                                                                    Bb, Cb, L, srow, sbc, t_begin, t_end, saved, R);
+        } else {
+            fold_carry<false>(h, rs.A2, agg, h0, s_begin, w, rs.row);
+            main_body<E, HAS_Z, SOFTPLUS, false, VARLEN, RAGGED, SAVE>(rs, h, u + base, delta + base, zp, out + base,
+                                                                     Bb, Cb, L, srow, sbc, t_begin, t_end, saved, R);
+        }
+        if (last_state && rs.active && te == p.T) {
+            float4* dst = reinterpret_cast<float4*>(last_state + rs.row * kN);
 #pragma unroll
-        for (int q = 0; q < kN / 4; ++q)
-            dst[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+            for (int q = 0; q < kN / 4; ++q)
+                dst[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+        }
+        r = gs + te;
     }
 }
 
@@ -621,21 +672,29 @@ __device__ __forceinline__ void agg_body(const RowSetup& rs, const typename E::s
     }
 }
 
+// Wavefront w's aggregate: the last piece of its range, unless that piece ends its group (then
+// nothing later in the group needs it and the wavefront has no aggregate to compute).
 template <class E, bool SOFTPLUS, bool VARLEN, bool RAGGED>
 __global__ __launch_bounds__(64) void scan_agg_kernel(
     const typename E::storage* __restrict__ u, const typename E::storage* __restrict__ delta,
     const float* __restrict__ A, const float* __restrict__ B, const float* __restrict__ bias,
-    float* __restrict__ agg, const int32_t* __restrict__ lens, int64_t Dn, int64_t L, int S) {
+    float* __restrict__ agg, const int32_t* __restrict__ lens, int64_t Dn, int64_t L, Part p) {
     using G = Geo<E>;
     __shared__ uint32_t srow[G::kRowWords];
     __shared__ __align__(16) float sbc[G::TT * 20];
-    const RowSetup rs = row_setup(A, nullptr, bias, Dn, lens, L);
-    const int seg = blockIdx.z;
-    const int64_t R = (int64_t)gridDim.y * Dn;
-    int64_t t_begin, t_end;
-    seg_bounds<E>(seg, S, L, t_begin, t_end);
+    const uint32_t w = wave_of(p);
+    const uint32_t r0 = part_begin(p, w), r1 = part_begin(p, w + 1);
+    const uint32_t g = (r1 - 1) / p.T;
+    const uint32_t gs = g * p.T;
+    const uint32_t te = r1 - gs;
+    if (r1 <= r0 || te == p.T) return;  // uniform over the wavefront
+    const uint32_t ta = (r0 > gs ? r0 : gs) - gs;
+    const uint32_t b = g / p.gx;
+    const RowSetup rs = row_setup(A, nullptr, bias, Dn, lens, L, g - b * p.gx, b);
+    const int64_t t_begin = static_cast<int64_t>(ta) * G::TT;
+    const int64_t t_end = static_cast<int64_t>(te) * G::TT;  // < L: the piece does not end the group
     const int64_t base = rs.row * L;
-    const float* Bb = B + (int64_t)blockIdx.y * kN * L;
+    const float* Bb = B + static_cast<int64_t>(b) * kN * L;
     float acc[kN], dsum;
     if (__all(rs.pow_ok))
         agg_body<E, SOFTPLUS, true, VARLEN, RAGGED>(rs, u + base, delta + base, Bb, L, srow, sbc, t_begin, t_end, acc,
@@ -643,37 +702,47 @@ __global__ __launch_bounds__(64) void scan_agg_kernel(
     else
         agg_body<E, SOFTPLUS, false, VARLEN, RAGGED>(rs, u + base, delta + base, Bb, L, srow, sbc, t_begin, t_end, acc,
                                                      dsum);
-    if (rs.active) {
-        float* a = agg + (int64_t)seg * (kN + 1) * R + rs.row;
+    // every lane stores (inactive lanes hold a copy of the group's last channel, never read for
+    // an output): the slot is dense
+    float* a = agg + static_cast<size_t>(w) * (kN + 1) * 64 + threadIdx.x;
 #pragma unroll
-        for (int n = 0; n < kN; ++n) a[(int64_t)n * R] = acc[n];
-        a[(int64_t)kN * R] = dsum;
-    }
+    for (int n = 0; n < kN; ++n) a[n * 64] = acc[n];
+    a[kN * 64] = dsum;
 }
 
 template <class E, bool HAS_Z, bool SOFTPLUS, bool VARLEN, bool RAGGED>
-hipError_t launch_fast_t(const ScanLaunch& a, const ScanPlan& p, float* ws, hipStream_t stream) {
+hipError_t launch_fast_t(const ScanLaunch& a, const ScanPlan& pl, float* ws, hipStream_t stream) {
     using S_t = typename E::storage;
     float* agg = ws;
     const dim3 block(64);
-    const unsigned gx = static_cast<unsigned>((a.Dn + 63) / 64);
+    const int64_t gx = (a.Dn + 63) / 64;
+    const int64_t T = (a.L + Geo<E>::TT - 1) / Geo<E>::TT;
+    const int64_t GT = a.Bt * gx * T;  // < 2^32 (plan_fast refuses larger)
+    Part p;
+    p.T = static_cast<uint32_t>(T);
+    p.W = static_cast<uint32_t>(pl.waves);
+    p.q = static_cast<uint32_t>(GT / pl.waves);
+    p.rem = static_cast<uint32_t>(GT % pl.waves);
+    p.gx = static_cast<uint32_t>(gx);
+    p.X = static_cast<uint32_t>(pl.xcds);
+    p.xq = p.W / p.X;
+    p.xr = p.W % p.X;
+    const int64_t R = a.Bt * a.Dn;
+    const dim3 grid(static_cast<unsigned>(p.W));
     mark(a, 0, stream);
-    if (p.segments > 1)
-        scan_agg_kernel<E, SOFTPLUS, VARLEN, RAGGED><<<dim3(gx, (unsigned)a.Bt, (unsigned)(p.segments - 1)), block, 0, stream>>>(
+    if (pl.segments > 1)
+        scan_agg_kernel<E, SOFTPLUS, VARLEN, RAGGED><<<grid, block, 0, stream>>>(
             static_cast<const S_t*>(a.u), static_cast<const S_t*>(a.delta), a.A, a.B, a.bias, agg, a.lens, a.Dn,
-            a.L, p.segments);
+            a.L, p);
     mark(a, 1, stream);
-    const dim3 grid(gx, (unsigned)a.Bt, (unsigned)p.segments);
     if (a.saved)
         scan_main_kernel<E, HAS_Z, SOFTPLUS, VARLEN, RAGGED, true><<<grid, block, 0, stream>>>(
             static_cast<const S_t*>(a.u), static_cast<const S_t*>(a.delta), static_cast<const S_t*>(a.z), a.A, a.B,
-            a.C, a.D, a.bias, agg, a.h0, static_cast<S_t*>(a.out), a.last_state, a.lens, a.saved, a.Dn, a.L,
-            p.segments);
+            a.C, a.D, a.bias, agg, a.h0, static_cast<S_t*>(a.out), a.last_state, a.lens, a.saved, a.Dn, a.L, R, p);
     else
         scan_main_kernel<E, HAS_Z, SOFTPLUS, VARLEN, RAGGED, false><<<grid, block, 0, stream>>>(
             static_cast<const S_t*>(a.u), static_cast<const S_t*>(a.delta), static_cast<const S_t*>(a.z), a.A, a.B,
-            a.C, a.D, a.bias, agg, a.h0, static_cast<S_t*>(a.out), a.last_state, a.lens, nullptr, a.Dn, a.L,
-            p.segments);
+            a.C, a.D, a.bias, agg, a.h0, static_cast<S_t*>(a.out), a.last_state, a.lens, nullptr, a.Dn, a.L, R, p);
     mark(a, 2, stream);
     return hipGetLastError();
 }
@@ -698,32 +767,39 @@ hipError_t launch_fast_e(const ScanLaunch& a, const ScanPlan& p, float* ws, hipS
 
 }  // namespace
 
-// Segments per channel group: about ten wavefronts per CU for bf16 rows and six for fp32 rows
-// (the main kernel holds 12), which measured best on the Mamba-2.8B (bf16) and Mamba-130M (fp32)
-// layer shapes; at least two tiles per segment (one-tile segments spend more on the aggregate
-// fold than they gain: 69 vs 66 us on a 4 x 640 x 2048 shard).  MSS_SCAN_SEGMENTS overrides.
-ScanPlan plan_fast(const ScanLaunch& a, int num_cus) {
+// Wavefronts: two per SIMD for bf16 rows and one and a half for fp32 rows, all resident at once
+// (the main kernel could hold three per SIMD, but that was slower: Mamba-2.8B layer 226 us at two
+// per SIMD, 259 us at three, 239 / 250 us at 1.9 / 2.25; Mamba-130M fp32 layer 216 us at 1.5,
+// 232 us at 2 -- more streams in flight evict more of each other's lines), and at least two tiles
+// each (a shorter piece spends more on folding the aggregates before it than it saves).  `waves_override` > 0 replaces the count (tests use it to force many or few
+// pieces per group, and ranges that cross groups).  `segments` reports whether some range ends
+// inside a group, i.e. whether the aggregate kernel has work.
+ScanPlan plan_fast(const ScanLaunch& a, int num_cus, int64_t waves_override) {
     ScanPlan p;
     const int TT = kFastTileBytes / (a.bf16 ? 2 : 4);
     const int64_t groups = a.Bt * ((a.Dn + 63) / 64);
     const int64_t tiles = (a.L + TT - 1) / TT;
-    const int64_t target = (a.bf16 ? 10LL : 6LL) * (num_cus > 0 ? num_cus : 256);
-    int64_t S = (target + groups / 2) / groups;
-    if (S > tiles / 2) S = tiles / 2;
-    const char* env = getenv("MSS_SCAN_SEGMENTS");
-    if (env && atoi(env) > 0) S = atoi(env);
-    if (S > tiles) S = tiles;
-    if (S > 65535) S = 65535;
-    if (S < 1) S = 1;
-    p.segments = static_cast<int>(S);
+    const int64_t GT = groups * tiles;
+    int64_t W = (a.bf16 ? 8LL : 6LL) * (num_cus > 0 ? num_cus : 256);
+    if (W > GT / 2) W = GT / 2;
+    if (waves_override > 0) W = waves_override;
+    if (W > GT) W = GT;
+    if (W > 0x7fffffffLL) W = 0x7fffffffLL;
+    if (W < 1) W = 1;
+    p.fits = GT < (int64_t{1} << 32);  // the kernels count tiles in 32 bits
+    p.waves = W;
+    p.xcds = num_cus >= 64 && num_cus % 32 == 0 ? num_cus / 32 : 1;  // 32 CUs per XCD on gfx950
+    // every range ends on a group boundary exactly when each wavefront takes whole groups
+    const bool whole = W <= groups && groups % W == 0;
+    p.segments = whole ? 1 : 2;
     p.seg_len = 0;
-    p.workspace_bytes = fast_workspace_bytes(a, p.segments);
+    p.workspace_bytes = fast_workspace_bytes(a, p);
     return p;
 }
 
-size_t fast_workspace_bytes(const ScanLaunch& a, int segments) {
-    return static_cast<size_t>(segments > 1 ? segments - 1 : 0) * (kN + 1) * static_cast<size_t>(a.Bt * a.Dn) *
-           sizeof(float);
+size_t fast_workspace_bytes(const ScanLaunch& a, const ScanPlan& p) {
+    (void)a;
+    return p.segments > 1 ? static_cast<size_t>(p.waves) * (kN + 1) * 64 * sizeof(float) : 0;
 }
 
 hipError_t launch_scan_fast(const ScanLaunch& a, const ScanPlan& p, float* ws, hipStream_t stream) {

@@ -386,15 +386,14 @@ hipError_t launch_typed(const KArgs& k, const ScanLaunch& a, hipStream_t stream)
 
 }  // namespace
 
-ScanPlan plan_scan(const ScanLaunch& a, int num_cus, int tile) {
+ScanPlan plan_scan(const ScanLaunch& a, int num_cus, int tile, int segments_override) {
     ScanPlan p;
     const int64_t groups = a.Bt * ((a.Dn + kRows - 1) / kRows);
     const int64_t tiles = (a.L + tile - 1) / tile;
     // aim for ~2 wavefronts per SIMD (4 SIMDs per CU) across the whole launch
     const int64_t target = 8LL * (num_cus > 0 ? num_cus : 256);
     int64_t S = (target + groups - 1) / groups;
-    const char* env = getenv("MSS_SCAN_SEGMENTS");
-    if (env && atoi(env) > 0) S = atoi(env);
+    if (segments_override > 0) S = segments_override;
     if (S < 1) S = 1;
     if (S > tiles) S = tiles > 0 ? tiles : 1;
     if (S > 65535) S = 65535;
@@ -402,6 +401,8 @@ ScanPlan plan_scan(const ScanLaunch& a, int num_cus, int tile) {
     if (seg_tiles < 1) seg_tiles = 1;
     p.seg_len = seg_tiles * tile;
     p.segments = static_cast<int>(tiles > 0 ? (tiles + seg_tiles - 1) / seg_tiles : 1);
+    p.waves = 0;
+    p.xcds = 1;
     p.workspace_bytes = 0;
     return p;
 }

@@ -39,18 +39,19 @@ __device__ __forceinline__ float quad_sum(float v) {
     return v;
 }
 
+// Threads stride over the rows' quads (the grid is capped: a dispatch holds at most 2^32 - 1
+// work-items per dimension).  The stride is a multiple of four, so the four lanes of a row stay
+// together in every iteration and the quad's DPP sum sees only its own row.
 template <class E, bool HAS_Z>
 __global__ __launch_bounds__(256) void state_update_kernel(DArgs a) {
-    const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t row = gt >> 2;   // flat (b, d)
-    const int q = static_cast<int>(gt & 3);  // this lane holds states 4q .. 4q + 3
-    const bool active = row < a.rows;
-    float y = 0.0f, xv = 0.0f;
-    int64_t d = 0;
-    if (active) {
-        d = row % a.Dn;
+    const int64_t total = a.rows * 4;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gt < total; gt += stride) {
+        const int64_t row = gt >> 2;   // flat (b, d)
+        const int q = static_cast<int>(gt & 3);  // this lane holds states 4q .. 4q + 3
+        const int64_t d = row % a.Dn;
         const int64_t b = row / a.Dn;
-        xv = E::load1(a.x, row);
+        const float xv = E::load1(a.x, row);
         const float dl = softplus(E::load1(a.dt, row) + (a.bias ? a.bias[d] : 0.0f));
         float4* sp = reinterpret_cast<float4*>(a.state) + row * 4 + q;
         const float4 s = *sp;
@@ -64,20 +65,21 @@ __global__ __launch_bounds__(256) void state_update_kernel(DArgs a) {
         hn.z = fmaf(fast_exp2(dl * (A4.z * kLog2e)), s.z, dx * B4.z);
         hn.w = fmaf(fast_exp2(dl * (A4.w * kLog2e)), s.w, dx * B4.w);
         *sp = hn;
-        y = fmaf(C4.w, hn.w, fmaf(C4.z, hn.z, fmaf(C4.y, hn.y, C4.x * hn.x)));
-    }
-    y = quad_sum(y);  // executed by every lane: all four lanes of a row are active together
-    if (active && q == 0) {
-        float o = fmaf(a.D ? a.D[d] : 0.0f, xv, y);
-        if (HAS_Z) o *= silu(E::load1(a.z, row));
-        E::store1(a.out, row, o);
+        float y = fmaf(C4.w, hn.w, fmaf(C4.z, hn.z, fmaf(C4.y, hn.y, C4.x * hn.x)));
+        y = quad_sum(y);
+        if (q == 0) {
+            float o = fmaf(a.D ? a.D[d] : 0.0f, xv, y);
+            if (HAS_Z) o *= silu(E::load1(a.z, row));
+            E::store1(a.out, row, o);
+        }
     }
 }
 
 template <class E, bool HAS_Z>
 hipError_t launch_t(const DArgs& k, hipStream_t stream) {
     const int64_t threads = k.rows * 4;
-    const int64_t blocks = (threads + 255) / 256;
+    int64_t blocks = (threads + 255) / 256;
+    if (blocks > (1 << 22)) blocks = 1 << 22;
     state_update_kernel<E, HAS_Z><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(k);
     return hipGetLastError();
 }

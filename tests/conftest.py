@@ -17,3 +17,12 @@ def oracle_mod():
     import oracle
     oracle.build(force=False)
     return oracle
+
+
+@pytest.fixture
+def plan():
+    """Fixes the library's plans (mss_set_plan_overrides) for one test and restores the automatic
+    plans afterwards, also when the test fails."""
+    import selective_state_space_06_amd as mss
+    yield lambda **kw: mss.set_plan_overrides(**kw)
+    mss.set_plan_overrides()

@@ -9,6 +9,12 @@ TOL_F32 = dict(rtol=1e-4, atol=1e-5)    # fp32 inputs
 TOL_BF16 = dict(rtol=2e-2, atol=1e-5)   # bf16 u / delta / z / out, fp32 state
 
 
+def waves_for(Bt, Dn, pieces):
+    """Wavefront count that gives the fast forward `pieces` equal pieces of each 64-channel group
+    (the plan spreads the (group, tile) work evenly over the wavefronts)."""
+    return int(pieces) * Bt * ((Dn + 63) // 64)
+
+
 def torch_dev():
     import torch
     return torch.device("cuda:0")

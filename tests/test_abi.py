@@ -599,3 +599,15 @@ def test_saved_state_blocks_follows_the_documented_index():
         for r in range(R):
             for n in range(16):
                 assert blocks[k, r, n] == flat[k, n // 4, 4 * r + n % 4]
+
+
+# --------------------------------------------------------------------- plan overrides
+
+def test_plan_overrides_reject_negative_counts_and_reset(lib):
+    """mss_set_plan_overrides: negative counts are refused (nothing changes); zeros restore the
+    automatic plans.  No HIP call is made."""
+    assert lib.mss_set_plan_overrides(0, -1, 0, 0) == SHAPE
+    assert lib.mss_set_plan_overrides(0, 0, -5, 0) == SHAPE
+    assert lib.mss_set_plan_overrides(0, 0, 0, -2) == SHAPE
+    assert lib.mss_set_plan_overrides(1, 3, 17, 4) == OK
+    assert lib.mss_set_plan_overrides(0, 0, 0, 0) == OK

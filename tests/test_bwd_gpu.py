@@ -107,8 +107,8 @@ def test_bwd_optional_arguments(mss, oracle_mod, flags):
 
 
 @pytest.mark.parametrize("segments", ["1", "2", "7", "40"])
-def test_bwd_segment_splits(mss, oracle_mod, segments, monkeypatch):
-    monkeypatch.setenv("MSS_BWD_SEGMENTS", segments)
+def test_bwd_segment_splits(mss, oracle_mod, segments, plan):
+    plan(bwd_segments=int(segments))
     s = scan_inputs(1, 128, 16, 320, dtype="f32", seed=72)
     _check(mss, oracle_mod, s, 72, f"bwd segments={segments}")
 

@@ -95,6 +95,76 @@ def test_graph_replays_match_eager(mss, dtype):
         prev_out = replayed["out"].clone()
 
 
+def test_graph_replays_after_the_workspace_grew(mss):
+    """A graph captured while its stream's workspace was small keeps replaying correctly after a
+    larger call on the same stream replaced that workspace (the library keeps the old buffer)."""
+    import torch
+    x, p = _inputs("bf16", 2, Bt=1, Dn=64, L=256)
+    out = torch.empty_like(x["u"])
+    last = torch.empty((1, 64, 16), dtype=torch.float32, device="cuda")
+
+    def small():
+        mss.selective_scan_fwd(x["u"], x["delta"], p["A"], x["B"], x["C"], D=p["D"], z=x["z"],
+                               delta_bias=p["bias"], out=out, last_state=last)
+        return mss.selective_scan_bwd(x["u"], x["delta"], p["A"], x["B"], x["C"], x["dout"], D=p["D"],
+                                      z=x["z"], delta_bias=p["bias"])
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        small()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        gg = small()
+    torch.cuda.synchronize()
+    big_x, big_p = _inputs("bf16", 3, Bt=2, Dn=1024, L=2048)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):  # needs far more workspace: the stream's buffer is replaced
+        mss.selective_scan_fwd(big_x["u"], big_x["delta"], big_p["A"], big_x["B"], big_x["C"], D=big_p["D"],
+                               z=big_x["z"], delta_bias=big_p["bias"])
+        mss.selective_scan_bwd(big_x["u"], big_x["delta"], big_p["A"], big_x["B"], big_x["C"], big_x["dout"],
+                               D=big_p["D"], z=big_x["z"], delta_bias=big_p["bias"])
+    torch.cuda.synchronize()
+    for rep in range(2):
+        nx, _ = _inputs("bf16", 20 + rep, Bt=1, Dn=64, L=256)
+        for k in x:
+            x[k].copy_(nx[k])
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            e = small()
+            eager = {"out": out.clone(), "last": last.clone(), **{k: v.clone() for k, v in e.items() if v is not None}}
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        replayed = {"out": out, "last": last, **{k: v for k, v in gg.items() if v is not None}}
+        for k in eager:
+            assert torch.equal(eager[k], replayed[k]), (rep, k)
+
+
+def test_capture_that_needs_a_larger_workspace_is_refused(mss):
+    """Under stream capture nothing can be allocated: a call whose stream has no workspace yet is
+    refused with MSS_ERR_UNSUPPORTED (before any HIP call), and the capture can still end."""
+    import torch
+    x, p = _inputs("bf16", 4, Bt=1, Dn=64, L=256)
+    stream = torch.cuda.Stream()  # never used by the library: no workspace
+    stream.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with pytest.raises(mss.MssError) as ei:
+        with torch.cuda.graph(graph, stream=stream):
+            x["u"].mul_(1.0)  # the graph is not empty
+            mss.selective_scan_fwd(x["u"], x["delta"], p["A"], x["B"], x["C"], D=p["D"], z=x["z"],
+                                   delta_bias=p["bias"])
+    assert ei.value.status == -6  # MSS_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):  # outside the capture the same call runs
+        out, _ = mss.selective_scan_fwd(x["u"], x["delta"], p["A"], x["B"], x["C"], D=p["D"], z=x["z"],
+                                        delta_bias=p["bias"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+
+
 def test_concurrent_streams_have_separate_workspaces(mss):
     """Forward + backward (and the saved-state pair) on two streams at once, each on its own inputs:
     the workspace belongs to the (device, stream) pair, so the overlapping calls must give

@@ -12,7 +12,7 @@ import pytest
 
 from synth import CONFIGS, decode_inputs, sample_rows, scan_inputs
 from tests.gpu_helpers import (TOL_BF16, TOL_F32, assert_close, dev, host64, oracle_scan,
-                               run_scan)
+                               run_scan, waves_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -88,12 +88,12 @@ def test_ragged_length_full_size(mss, orc, name, L):
     _check_scan(mss, orc, _cfg_inputs(name, L=L), what=f"{name} L={L}")
 
 
-def test_ragged_rows_match_generic_path(mss, monkeypatch):
+def test_ragged_rows_match_generic_path(mss, plan):
     """The element-aligned fast path and the generic kernels agree to rounding on ragged rows."""
     import torch
     s = scan_inputs(3, 200, 16, 777, dtype="bf16", seed=24)
     out_f, last_f = run_scan(mss, s)
-    monkeypatch.setenv("MSS_SCAN_GENERIC", "1")
+    plan(force_generic=True)
     out_g, last_g = run_scan(mss, s)
     torch.cuda.synchronize()
     assert_close(host64(out_f), host64(out_g), what="fast vs generic out", **TOL_BF16)
@@ -187,10 +187,22 @@ def test_random_A_general_path(mss, orc, dtype):
 
 
 @pytest.mark.parametrize("segments", ["1", "2", "5", "64"])
-def test_segment_split_counts(mss, orc, segments, monkeypatch):
-    monkeypatch.setenv("MSS_SCAN_SEGMENTS", segments)
+def test_segment_split_counts(mss, orc, segments, plan):
+    plan(fast_waves=waves_for(1, 128, segments))
     s = scan_inputs(1, 128, 16, 1000, dtype="f32", seed=23)
     _check_scan(mss, orc, s, what=f"segments={segments}")
+
+
+@pytest.mark.parametrize("waves,dtype,a_kind", [
+    (1, "bf16", "s4d"), (5, "f32", "random"), (7, "bf16", "random"), (13, "f32", "s4d"),
+    (50, "bf16", "s4d"), (299, "f32", "s4d"), (1000, "bf16", "random")])
+def test_wavefront_ranges_cross_groups(mss, orc, waves, dtype, a_kind, plan):
+    """The fast forward's work split at any wavefront count: one wavefront scanning all twelve
+    channel groups in turn, ranges that start and end inside groups and run on into the next
+    group, and one-tile pieces (the count is capped at the 300 (group, tile) pairs)."""
+    plan(fast_waves=waves)
+    s = scan_inputs(3, 200, 16, 777 if dtype == "bf16" else 400, dtype=dtype, seed=25, a_kind=a_kind)
+    _check_scan(mss, orc, s, what=f"waves={waves} {dtype} {a_kind}")
 
 
 def test_empty_sequence_zeroes_state(mss):

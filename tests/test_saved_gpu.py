@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from synth import CONFIGS, scan_inputs
-from tests.gpu_helpers import TOL_F32, assert_close, dev, host64
+from tests.gpu_helpers import TOL_F32, assert_close, dev, host64, waves_for
 
 pytestmark = pytest.mark.gpu
 
@@ -85,10 +85,10 @@ def test_saved_states_match_oracle(mss, oracle_mod, Bt, Dn, L, dtype, with_h0, w
 
 
 @pytest.mark.parametrize("segments", ["1", "2", "5", "40"])
-def test_saved_states_segment_splits(mss, oracle_mod, segments, monkeypatch):
+def test_saved_states_segment_splits(mss, oracle_mod, segments, plan):
     """The forward split along L into segments (each starts from the carried state)."""
     import torch
-    monkeypatch.setenv("MSS_SCAN_SEGMENTS", segments)
+    plan(fast_waves=waves_for(2, 64, segments))
     s = scan_inputs(2, 64, 16, 520, dtype="bf16", seed=93)
     h0, lens, _, _ = _extras(s, 93, True, True)
     _, last, saved = _fwd_save(mss, s, h0, lens)
@@ -164,9 +164,9 @@ def test_bwd_saved_parity(mss, oracle_mod, Bt, Dn, L, dtype, with_h0, with_lens,
 
 
 @pytest.mark.parametrize("segments", ["1", "3", "40"])
-def test_bwd_saved_segment_splits(mss, oracle_mod, segments, monkeypatch):
+def test_bwd_saved_segment_splits(mss, oracle_mod, segments, plan):
     import torch
-    monkeypatch.setenv("MSS_BWD_SEGMENTS", segments)
+    plan(bwd_segments=int(segments))
     s = scan_inputs(1, 128, 16, 320, dtype="f32", seed=96)
     h0, lens, dout, dlast = _extras(s, 96, True, False)
     _, _, saved = _fwd_save(mss, s, h0, lens)

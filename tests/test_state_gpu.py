@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 from synth import CONFIGS, sample_rows, scan_inputs
-from tests.gpu_helpers import TOL_BF16, TOL_F32, assert_close, dev, host64, run_scan
+from tests.gpu_helpers import TOL_BF16, TOL_F32, assert_close, dev, host64, run_scan, waves_for
 
 pytestmark = pytest.mark.gpu
 
@@ -64,15 +64,15 @@ def test_with_state_parity(mss, oracle_mod, Bt, Dn, L, dtype, a_kind):
 
 
 @pytest.mark.parametrize("segments", ["1", "2", "5", "64"])
-def test_with_state_segment_splits(mss, oracle_mod, segments, monkeypatch):
-    monkeypatch.setenv("MSS_SCAN_SEGMENTS", segments)
+def test_with_state_segment_splits(mss, oracle_mod, segments, plan):
+    plan(fast_waves=waves_for(1, 128, segments))
     s = scan_inputs(1, 128, 16, 1000, dtype="f32", seed=41)
     _check(mss, oracle_mod, s, _h0(1, 128, 41), what=f"h0 segments={segments}")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_with_state_generic_path(mss, oracle_mod, dtype, monkeypatch):
-    monkeypatch.setenv("MSS_SCAN_GENERIC", "1")
+def test_with_state_generic_path(mss, oracle_mod, dtype, plan):
+    plan(force_generic=True)
     s = scan_inputs(2, 96, 16, 300, dtype=dtype, seed=42)
     _check(mss, oracle_mod, s, _h0(2, 96, 42), what=f"h0 generic {dtype}")
 

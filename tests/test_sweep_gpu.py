@@ -39,6 +39,12 @@ def _case(i):
         segments=int(rng.choice([0, 0, 1, 3, 9])), seed=int(rng.integers(0, 1 << 30)))
 
 
+def _sweep_waves(c):
+    """Wavefronts for a forced split: `segments` pieces per 64-channel group plus one, so that
+    wavefront ranges start and end inside groups and cross from one group into the next."""
+    return c["segments"] * c["Bt"] * ((c["Dn"] + 63) // 64) + 1
+
+
 def _to_dev(a, dtype, offset):
     """Device copy; with offset, a view one element into a larger buffer (rows lose alignment)."""
     import torch
@@ -52,12 +58,12 @@ def _to_dev(a, dtype, offset):
 
 
 @pytest.mark.parametrize("i", range(N_CASES))
-def test_forward_sweep(mss, oracle_mod, monkeypatch, i):
+def test_forward_sweep(mss, oracle_mod, plan, i):
     import torch
     c = _case(i)
     print(f"[sweep fwd {i}] {c}", flush=True)
     if c["segments"]:
-        monkeypatch.setenv("MSS_SCAN_SEGMENTS", str(c["segments"]))
+        plan(fast_waves=_sweep_waves(c))
     s = scan_inputs(c["Bt"], c["Dn"], 16, c["L"], dtype=c["dtype"], seed=c["seed"] % 100000,
                     a_kind=c["a_kind"], with_z=c["use_z"])
     rng = np.random.default_rng(c["seed"])
@@ -82,12 +88,12 @@ def test_forward_sweep(mss, oracle_mod, monkeypatch, i):
 
 
 @pytest.mark.parametrize("i", range(0, N_CASES, 2))
-def test_backward_sweep(mss, oracle_mod, monkeypatch, i):
+def test_backward_sweep(mss, oracle_mod, plan, i):
     import torch
     c = _case(i)
     print(f"[sweep bwd {i}] {c}", flush=True)
     if c["segments"]:
-        monkeypatch.setenv("MSS_BWD_SEGMENTS", str(c["segments"]))
+        plan(bwd_segments=c["segments"])
     s = scan_inputs(c["Bt"], c["Dn"], 16, c["L"], dtype=c["dtype"], seed=c["seed"] % 100000,
                     a_kind=c["a_kind"], with_z=c["use_z"])
     rng = np.random.default_rng(c["seed"] + 1)
@@ -124,15 +130,14 @@ def test_backward_sweep(mss, oracle_mod, monkeypatch, i):
 
 
 @pytest.mark.parametrize("i", range(1, N_CASES, 2))
-def test_saved_states_sweep(mss, oracle_mod, monkeypatch, i):
+def test_saved_states_sweep(mss, oracle_mod, plan, i):
     """The forward that saves states, then the backward from them (the cases the backward sweep
     above skips): out, last_state, the first and last saved blocks and every gradient."""
     import torch
     c = _case(i)
     print(f"[sweep saved {i}] {c}", flush=True)
     if c["segments"]:
-        monkeypatch.setenv("MSS_SCAN_SEGMENTS", str(c["segments"]))
-        monkeypatch.setenv("MSS_BWD_SEGMENTS", str(c["segments"]))
+        plan(fast_waves=_sweep_waves(c), bwd_segments=c["segments"])
     s = scan_inputs(c["Bt"], c["Dn"], 16, c["L"], dtype=c["dtype"], seed=c["seed"] % 100000,
                     a_kind=c["a_kind"], with_z=c["use_z"])
     rng = np.random.default_rng(c["seed"] + 2)

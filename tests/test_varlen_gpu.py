@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from synth import CONFIGS, sample_rows, scan_inputs
-from tests.gpu_helpers import TOL_BF16, TOL_F32, assert_close, dev, host64, run_scan
+from tests.gpu_helpers import TOL_BF16, TOL_F32, assert_close, dev, host64, run_scan, waves_for
 
 pytestmark = pytest.mark.gpu
 
@@ -74,26 +74,26 @@ def test_varlen_parity(mss, oracle_mod, Bt, Dn, L, dtype, a_kind, with_h0):
 
 
 @pytest.mark.parametrize("segments", ["1", "3", "16"])
-def test_varlen_segment_splits(mss, oracle_mod, segments, monkeypatch):
-    monkeypatch.setenv("MSS_SCAN_SEGMENTS", segments)
+def test_varlen_segment_splits(mss, oracle_mod, segments, plan):
+    plan(fast_waves=waves_for(6, 128, segments))
     s = scan_inputs(6, 128, 16, 1000, dtype="bf16", seed=62)
     _check(mss, oracle_mod, s, _lens(6, 1000, 62), what=f"varlen segments={segments}")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_varlen_generic_path(mss, oracle_mod, dtype, monkeypatch):
-    monkeypatch.setenv("MSS_SCAN_GENERIC", "1")
+def test_varlen_generic_path(mss, oracle_mod, dtype, plan):
+    plan(force_generic=True)
     s = scan_inputs(6, 96, 16, 300, dtype=dtype, seed=63)
     _check(mss, oracle_mod, s, _lens(6, 300, 63), what=f"varlen generic {dtype}")
 
 
 @pytest.mark.parametrize("dtype,generic", [("bf16", False), ("f32", False), ("bf16", True), ("f32", True)])
-def test_varlen_padding_never_reaches_results(mss, oracle_mod, dtype, generic, monkeypatch):
+def test_varlen_padding_never_reaches_results(mss, oracle_mod, dtype, generic, plan):
     """Past each sequence's end the tensors hold NaN / inf (u, delta, z and B, C of that batch):
     the oracle never reads there, so outputs and final states must match it exactly as with finite
     padding -- masked steps may not multiply padding by zero."""
     if generic:
-        monkeypatch.setenv("MSS_SCAN_GENERIC", "1")
+        plan(force_generic=True)
     Bt, Dn, L = 6, 96, 300
     s = scan_inputs(Bt, Dn, 16, L, dtype=dtype, seed=66)
     lens = _lens(Bt, L, 66)
