@@ -142,6 +142,31 @@ int mss_selective_scan_fwd_varlen(const mss_tensor_t* u, const mss_tensor_t* del
                                   const mss_tensor_t* last_state, void* stream);
 
 /*
+ * mss_selective_scan_fwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments, checks and
+ * results (bit-identical to mss_selective_scan_fwd whenever that call would split the work the
+ * same way, which it does on devices of up to 320 CUs), but the carried segment aggregates live in
+ * a fixed 16 MiB array of device memory that the library holds on each GPU for the life of the
+ * process, so the call allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *   - Limit: the aggregates take 4352 bytes per wavefront of the split, so at most 3855
+ *     wavefronts; the automatic split is capped there, and a wavefront count forced through
+ *     mss_set_plan_overrides beyond it returns MSS_ERR_UNSUPPORTED before any HIP call.  So do
+ *     problems of 2^32 or more (64-channel group, time tile) pairs, which the other forward
+ *     entry points hand to kernels that need row-sized scratch.
+ *   - Every call on one GPU shares that GPU's array (nothing in it needs to start at zero; a
+ *     call leaves its own aggregates behind): calls that overlap in time on one GPU (on two
+ *     streams, or two host threads) race and may give wrong results.  Order them on one stream.
+ *   - The first call on a device looks up that device's array (hipGetSymbolAddress); make it
+ *     once outside graph capture if the capture mode forbids that lookup.
+ */
+int mss_selective_scan_fwd_noalloc(const mss_tensor_t* u, const mss_tensor_t* delta,
+                                   const mss_tensor_t* A, const mss_tensor_t* B,
+                                   const mss_tensor_t* C, const mss_tensor_t* D,
+                                   const mss_tensor_t* z, const mss_tensor_t* delta_bias,
+                                   int softplus_flag, const mss_tensor_t* out,
+                                   const mss_tensor_t* last_state, void* stream);
+
+/*
  * Gradients of mss_selective_scan_fwd (h_0 = 0) for training: given dout = dL/dout of a scalar
  * loss L, writes dL/d(every input).  The pages define only the forward; these are its exact
  * derivatives by the chain rule (reverse mode through the recurrence: with dy = dout silu(z),

@@ -22,7 +22,8 @@ EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_fwd_with_state",
            "mss_selective_scan_fwd_varlen", "mss_selective_scan_bwd", "mss_selective_scan_bwd_varlen",
            "mss_selective_scan_fwd_save", "mss_selective_scan_bwd_saved",
            "mss_selective_state_update", "mss_causal_conv1d_fwd", "mss_causal_conv1d_update", "mss_profile_enable", "mss_profile_fwd",
-           "mss_release_workspaces", "mss_set_plan_overrides", "mss_status_string", "mss_version")
+           "mss_release_workspaces", "mss_set_plan_overrides", "mss_selective_scan_fwd_noalloc",
+           "mss_status_string", "mss_version")
 
 
 class Tensor(ctypes.Structure):
@@ -106,6 +107,9 @@ def load_library(path: str = LIB_PATH):
             lib.mss_status_string.argtypes = [ctypes.c_int]
             lib.mss_version.restype = ctypes.c_int
             lib.mss_version.argtypes = []
+            lib.mss_selective_scan_fwd_noalloc.restype = ctypes.c_int
+            lib.mss_selective_scan_fwd_noalloc.argtypes = [_TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP,
+                                                           ctypes.c_int, _TP, _TP, ctypes.c_void_p]
             lib.mss_release_workspaces.restype = ctypes.c_int
             lib.mss_release_workspaces.argtypes = []
             lib.mss_set_plan_overrides.restype = ctypes.c_int
@@ -170,6 +174,12 @@ def scan_fwd_raw(u, delta, A, B, C, D, z, delta_bias, softplus_flag, out, last_s
     return load_library().mss_selective_scan_fwd(
         _ref(u), _ref(delta), _ref(A), _ref(B), _ref(C), _ref(D), _ref(z), _ref(delta_bias),
         int(softplus_flag), _ref(out), _ref(last_state), stream)
+
+
+def scan_fwd_noalloc_raw(u, delta, A, B, C, D, z, delta_bias, softplus_flag, out, last_state, stream) -> int:
+    return load_library().mss_selective_scan_fwd_noalloc(_ref(u), _ref(delta), _ref(A), _ref(B), _ref(C), _ref(D),
+                                                         _ref(z), _ref(delta_bias), int(softplus_flag), _ref(out),
+                                                         _ref(last_state), stream)
 
 
 def scan_fwd_with_state_raw(u, delta, A, B, C, D, z, delta_bias, initial_state, softplus_flag,
@@ -306,6 +316,22 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
         raise MssError(st, "mss_selective_scan_fwd")
     return (out, last_state) if return_last_state else out
 
+
+
+def selective_scan_fwd_noalloc(u, delta, A, B, C, out, D=None, z=None, delta_bias=None,
+                               delta_softplus=True, last_state=None):
+    """mss_selective_scan_fwd_noalloc on the current stream of u's device: the forward scan with
+    the library's fixed per-GPU scratch (no device allocation by the library).  The caller passes
+    `out` (and `last_state`, or None): this wrapper allocates nothing either."""
+    import torch
+    with torch.cuda.device(u.device):
+        stream = torch.cuda.current_stream(u.device).cuda_stream
+        st = scan_fwd_noalloc_raw(_desc(u), _desc(delta), _desc(A), _desc(B), _desc(C), _desc(D), _desc(z),
+                                  _desc(delta_bias), 1 if delta_softplus else 0, _desc(out), _desc(last_state),
+                                  stream)
+    if st != 0:
+        raise MssError(st, "mss_selective_scan_fwd_noalloc")
+    return out
 
 def causal_conv1d_fwd(x, weight, bias=None, initial_state=None, silu=True, out=None,
                       return_final_state=False, final_state=None):

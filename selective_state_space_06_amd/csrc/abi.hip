@@ -163,6 +163,30 @@ int workspace(int dev, void* stream, size_t bytes, float** out) {
     return MSS_OK;
 }
 
+// ---- the scratch of mss_selective_scan_fwd_noalloc: a fixed array in device memory, one copy per
+// GPU, owned by the loaded library for the life of the process.  Host code never uses the name
+// `scratch` as an address (on the host it is only a stand-in for the symbol): each device's
+// address comes from hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = size_t{16} << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::unordered_map<int, void*> g_scratch_ptr;
+
+// This device's scratch address in *out (g_mu is taken here).
+hipError_t scratch_of(int dev, void** out) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_scratch_ptr.find(dev);
+    if (it != g_scratch_ptr.end()) {
+        *out = it->second;
+        return hipSuccess;
+    }
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+    *out = ptr;
+    return hipSuccess;
+}
+
 // Launch timing (mss_profile_enable / mss_profile_fwd): one event triple per recorded call.
 constexpr int kProfMaxCalls = 1024;
 struct Prof {
@@ -537,6 +561,61 @@ int mss_selective_scan_fwd_save(const mss_tensor_t* u, const mss_tensor_t* delta
         const hipError_t e = fast ? mss::launch_scan_fast(a, plan, ws, s) : mss::launch_scan_fwd(a, plan, ws, s);
         if (slot >= 0 && e == hipSuccess) g_prof.calls = slot + 1;
         return e == hipSuccess ? MSS_OK : MSS_ERR_HIP;
+    } catch (...) {
+        return MSS_ERR_HIP;
+    }
+}
+
+int mss_selective_scan_fwd_noalloc(const mss_tensor_t* u, const mss_tensor_t* delta, const mss_tensor_t* A,
+                                   const mss_tensor_t* B, const mss_tensor_t* C, const mss_tensor_t* D,
+                                   const mss_tensor_t* z, const mss_tensor_t* delta_bias, int softplus_flag,
+                                   const mss_tensor_t* out, const mss_tensor_t* last_state, void* stream) {
+    try {
+        const int st = validate_fwd(u, delta, A, B, C, D, z, delta_bias, nullptr, out, last_state);
+        if (st != MSS_OK) return st;
+        // a forced wavefront count whose aggregates cannot fit: refused before any HIP call
+        const int64_t forced = g_fast_waves.load();
+        const size_t slot_bytes = (kN + 1) * 64 * sizeof(float);
+        if (forced > 0 && static_cast<size_t>(forced) > kScratchBytes / slot_bytes) return MSS_ERR_UNSUPPORTED;
+        mss::ScanLaunch a;
+        a.u = u->data; a.delta = delta->data; a.z = z ? z->data : nullptr;
+        a.A = static_cast<const float*>(A->data);
+        a.B = static_cast<const float*>(B->data);
+        a.C = static_cast<const float*>(C->data);
+        a.D = D ? static_cast<const float*>(D->data) : nullptr;
+        a.bias = delta_bias ? static_cast<const float*>(delta_bias->data) : nullptr;
+        a.out = out->data;
+        a.last_state = last_state ? static_cast<float*>(last_state->data) : nullptr;
+        a.h0 = nullptr;
+        a.lens = nullptr;
+        a.saved = nullptr;
+        a.Bt = u->shape[0]; a.Dn = u->shape[1]; a.L = u->shape[2];
+        a.softplus = softplus_flag ? 1 : 0;
+        a.bf16 = u->dtype == MSS_BF16;
+        const size_t es = elem_size(u->dtype);
+        a.vec_ok = (a.L * static_cast<int64_t>(es)) % 16 == 0 && aligned(*u, 16) &&
+                   aligned(*delta, 16) && aligned(*out, 16) && (!z || aligned(*z, 16)) &&
+                   aligned(*B, 16) && aligned(*C, 16);
+        if (a.Bt * a.Dn == 0) return MSS_OK;
+
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return MSS_ERR_HIP;
+        if (device_cus(dev, &cus) != hipSuccess) return MSS_ERR_HIP;
+        void* base = nullptr;
+        if (scratch_of(dev, &base) != hipSuccess) return MSS_ERR_HIP;
+        if (a.L == 0) {  // no scan steps: last_state <- zeros (no scratch)
+            mss::ScanPlan none{};
+            return mss::launch_scan_fwd(a, none, nullptr, s) == hipSuccess ? MSS_OK : MSS_ERR_HIP;
+        }
+        // the fast kernels only (the generic ones need scratch in proportion to the rows); the
+        // automatic wavefront count is capped so that its aggregates fit the scratch
+        mss::ScanPlan plan = mss::plan_fast(a, cus, forced);
+        const int64_t cap = static_cast<int64_t>(kScratchBytes / slot_bytes);
+        if (forced == 0 && plan.waves > cap) plan = mss::plan_fast(a, cus, cap);
+        if (!plan.fits || plan.workspace_bytes > kScratchBytes) return MSS_ERR_UNSUPPORTED;
+        float* ws = plan.workspace_bytes > 0 ? static_cast<float*>(base) : nullptr;
+        return mss::launch_scan_fast(a, plan, ws, s) == hipSuccess ? MSS_OK : MSS_ERR_HIP;
     } catch (...) {
         return MSS_ERR_HIP;
     }
