@@ -15,13 +15,15 @@ every output written once) over the K timed steps; the scan alone is also timed 
 events on the stream it runs on, and the library's launch-timing hook (mss_profile_enable /
 mss_profile_fwd) times its two kernels separately over the same timed steps.
 
-`roofline` describes the scan's dominant kernel, the main scan kernel: it is bound by VALU and
-transcendental issue, so it is priced in algorithmic fp32 work against the MI355X fp32 vector
-peak.  Algorithmic work of the recurrence per (b, d, t): per state n, exp(delta A) (a multiply
-and an exp), Abar h + (delta u) B (a multiply and an FMA) and C h accumulated into y (an FMA):
-7 flops with an exp counted as one; per (b, d, t) besides, softplus(delta + bias) (4),
-delta u (1), y + D u (2) and the silu(z) gate (5): 12.  The main kernel's share of HBM
-traffic, from rocprofv3 counters taken on this exact kernel source, is `traffic`.
+`roofline` prices the scan's dominant kernel, the main scan kernel, against HBM: achieved =
+the call's algorithmic bytes (every input read once, every output written once: 338,272,256
+bytes on this layer) / the main kernel's average duration (HIP events the library records on
+the stream it launches on), against the 8 TB/s MI355X peak; `call_frac` is the same bytes over
+the whole call (aggregate kernel + main kernel).  `traffic` is the main kernel's HBM bytes per
+launch from rocprofv3 counters taken on this exact kernel source (null otherwise).  The scan is
+in fact limited by VALU issue: `valu` gives the main kernel's counted instructions per
+(b, d, t) and the issue rate they imply, against the one-instruction-per-4-cycles rate of a
+wave64 fp32 VALU instruction on a 16-lane SIMD (1024 SIMDs at 2.4 GHz).
 """
 from __future__ import annotations
 
@@ -35,17 +37,18 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, AMD published peak
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, AMD published peak
 WORKLOAD = "mamba2p8b_bf16"
-FLOPS_PER_STATE_UPDATE = 7
-FLOPS_PER_ROW_STEP = 12
+# VALU issue ceiling: 256 CUs x 4 SIMDs, one wave64 fp32 instruction per 4 cycles each (16 lanes),
+# 2.4 GHz: 614.4e9 wave-instructions per second.  (Transcendentals take 2-3 such slots: measured
+# v_exp_f32 ~8.4 cycles, v_log_f32 / v_rcp_f32 ~12.5 cycles per wave instruction.)
+VALU_WAVE_INSTR_PER_S = 256 * 4 * 2.4e9 / 4
 
 # HBM bytes per launch of the main scan kernel on this workload, from two rocprofv3 --pmc runs
 # of `python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline` (FETCH_SIZE, then WRITE_SIZE),
 # each scaled by what the counter reads for a plain 1 GiB device copy (FETCH_SIZE x2.0,
-# WRITE_SIZE x1.0).  Valid only for the kernel source with this SHA-256 prefix; otherwise
-# traffic is reported as null.
-MAIN_TRAFFIC = {"src_sha256": "e281d96109a5fd61", "fetch_bytes": 507552885, "write_bytes": 99434954}
+# WRITE_SIZE x1.0), and its VALU instructions per (b, d, t) (SQ_INSTS_VALU x 64 / B D L).
+# Valid only for the kernel source with this SHA-256 prefix; otherwise reported as null.
+MAIN_COUNTERS = {"src_sha256": None, "fetch_bytes": None, "write_bytes": None, "valu_per_bdt": None}
 
 
 def kernel_source_digest():
@@ -117,6 +120,103 @@ def single_thread_130m(rows=1536):
     wall = time.perf_counter() - t
     n = rows * c["L"] * c["d_state"]
     return {"state_updates_per_s": n / wall, "rows": rows, "L": c["L"], "wall_s": round(wall, 3)}
+
+
+def decode_hbm_chain(mss, torch, devc, steps=1024, states=16, pool=64):
+    """Chained one-token updates of `states` distinct (64, 5120, 16) fp32 states in turn (one per
+    layer of a model, as generation steps a whole stack), 16 x 21 MB = 336 MB: more than the 256 MB
+    Infinity Cache, so every step reads and writes its state in HBM.  Timed as replays of a
+    captured HIP graph of `pool` steps (inputs cycle through `pool` resident sets)."""
+    import numpy as np
+    from synth import CONFIGS, decode_inputs
+    c = CONFIGS["decode_bf16"]
+    Bt, Dn, N = c["batch"], c["d_inner"], c["d_state"]
+    d = decode_inputs(Bt, Dn, N, pool, dtype="bf16", with_z=True, seed=0)
+    up = lambda a, bf=False: (torch.from_numpy(np.ascontiguousarray(a)).to(devc).to(torch.bfloat16)
+                              if bf else torch.from_numpy(np.ascontiguousarray(a)).to(devc))
+    X, DT, Z = up(d.x, True), up(d.dt, True), up(d.z, True)
+    Bs, Cs = up(d.B), up(d.C)
+    A, D, bias = up(d.A), up(d.D), up(d.dt_bias)
+    st = [torch.zeros((Bt, Dn, N), dtype=torch.float32, device=devc) for _ in range(states)]
+    outs = torch.empty((pool, Bt, Dn), dtype=torch.bfloat16, device=devc)
+
+    def run(k):
+        j = k % pool
+        mss.selective_state_update(st[k % states], X[j], DT[j], A, Bs[j], Cs[j], D=D, z=Z[j], dt_bias=bias,
+                                   out=outs[j])
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for k in range(pool):
+            run(k)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for k in range(pool):
+            run(k)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // pool)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * pool)
+    nbytes = decode_bytes(Bt, Dn, N)
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"shape": [Bt, Dn, N], "distinct_states": states, "state_bytes_total": states * Bt * Dn * N * 4,
+            "steps": reps * pool, "graph_us_per_step": round(us, 3), "graph_gbps": round(gbps, 1),
+            "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "note": "each step's state is one of 16 (336 MB in all, above the 256 MB Infinity Cache): HBM-resident"}
+
+
+def general_a_leg(mss, torch, devc, Bt, Dn, N, L, calls=20, warmup=3, copies=2):
+    """The forward on the same layer shape with an unstructured negative A (synth a_kind="random":
+    what a trained layer holds), so every state update takes its own exp: the path the
+    power-chain shortcut for A = -(n+1) does not cover.  Rotated input copies, events on the
+    stream, and the library's kernel split."""
+    import numpy as np
+    from synth import scan_inputs
+    s = scan_inputs(Bt, Dn, N, L, dtype="bf16", with_z=True, seed=0, a_kind="random")
+    up = lambda a, bf=False: (torch.from_numpy(np.ascontiguousarray(a)).to(devc).to(torch.bfloat16)
+                              if bf else torch.from_numpy(np.ascontiguousarray(a)).to(devc))
+    A, D, bias = up(s.A), up(s.D), up(s.delta_bias)
+    sets = [dict(u=up(s.u, True), d=up(s.delta, True), z=up(s.z, True), B=up(s.B), C=up(s.C)) for _ in range(copies)]
+    del s
+    out = torch.empty_like(sets[0]["u"])
+    last = torch.empty((Bt, Dn, N), dtype=torch.float32, device=devc)
+
+    def call(k):
+        p = sets[k % copies]
+        mss.selective_scan_fwd(p["u"], p["d"], A, p["B"], p["C"], D=D, z=p["z"], delta_bias=bias, out=out,
+                               last_state=last)
+
+    for k in range(warmup):
+        call(k)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    mss.profile_enable(True)
+    for k in range(calls):
+        ev[k][0].record(stream)
+        call(k)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    mss.profile_enable(False)
+    n, carry, main = mss.profile_fwd()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    avg = sum(ms) / len(ms)
+    nb = scan_bytes(Bt, Dn, N, L)
+    main_ms = main / max(n, 1)
+    return {"shape": [Bt, Dn, N, L], "a": "random negative (synth a_kind=random)", "avg_ms": round(avg, 4),
+            "min_ms": round(min(ms), 4), "gbps": round(nb / (avg * 1e-3) / 1e9, 2),
+            "frac_hbm_peak": round(nb / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "carry_stage_avg_ms": round(carry / max(n, 1), 4), "main_avg_ms": round(main_ms, 4),
+            "main_frac_hbm_peak": round(nb / (main_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
 def decode_chain(mss, torch, devc, steps=1024, pool=64):
@@ -370,6 +470,7 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="input sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-chain", action="store_true")
+    ap.add_argument("--no-general-a", action="store_true", help="skip the random-A forward leg")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-shard", action="store_true")
@@ -446,12 +547,16 @@ def main():
     updates = Bt * Dn * L * N + Bt * Dn * N
     main_ms = main_ms_tot / max(n_calls, 1)
     carry_ms = carry_ms_tot / max(n_calls, 1)
-    flops = Bt * Dn * L * (N * FLOPS_PER_STATE_UPDATE + FLOPS_PER_ROW_STEP)
-    achieved = flops / (main_ms * 1e-3) / 1e12
-    traffic = None
-    if MAIN_TRAFFIC["src_sha256"] == kernel_source_digest():
-        traffic = MAIN_TRAFFIC["fetch_bytes"] + MAIN_TRAFFIC["write_bytes"]
-    main_bytes = Bt * Dn * L * 2 * 4 + 2 * Bt * N * L * 4  # u, delta, z in, out; B, C
+    achieved = sb / (main_ms * 1e-3) / 1e9
+    counted = MAIN_COUNTERS["src_sha256"] == kernel_source_digest()
+    traffic = (MAIN_COUNTERS["fetch_bytes"] + MAIN_COUNTERS["write_bytes"]) if counted else None
+    valu = None
+    if counted:
+        per = MAIN_COUNTERS["valu_per_bdt"]
+        need_s = per * Bt * Dn * L / 64 / VALU_WAVE_INSTR_PER_S
+        valu = {"instr_per_bdt": per, "issue_time_ms_at_peak": round(need_s * 1e3, 4),
+                "issue_frac": round(need_s / (main_ms * 1e-3), 4),
+                "peak": "1 wave64 fp32 VALU instruction per 4 cycles per SIMD, 1024 SIMDs, 2.4 GHz"}
 
     res = {
         "metric": "selective-scan fwd GB/s + state-updates/s (B*D*L*N/s), % of MI355X HBM peak",
@@ -478,14 +583,14 @@ def main():
         "decode_token": {"avg_us": round(float(np.mean(dec_ms)) * 1e3, 2)},
         "kernels": {"calls_timed": n_calls, "carry_stage_avg_ms": round(carry_ms, 4),
                     "main_avg_ms": round(main_ms, 4),
-                    "main_hbm_gbps": round(main_bytes / (main_ms * 1e-3) / 1e9, 2),
-                    "main_frac_hbm_peak": round(main_bytes / (main_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
-        "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": FP32_VECTOR_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / FP32_VECTOR_PEAK_TFLOPS, 4),
-                     "traffic": traffic,
+                    "carry_share_of_call": round(carry_ms / scan_avg_ms, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "scan_main_kernel (the main kernel of mss_selective_scan_fwd), "
                                "timed by the library's HIP events on its stream",
-                     "algorithmic_flops": flops},
+                     "algorithmic_bytes": sb,
+                     "call_achieved": round(scan_gbps, 1), "call_frac": round(scan_gbps / HBM_PEAK_GBPS, 4)},
+        "valu": valu,
     }
     if not args.no_bwd:
         res["scan_bwd"] = backward_leg(mss, torch, sets, A, D, bias, Bt, Dn, N, L, scan_avg_ms)
@@ -493,8 +598,11 @@ def main():
         res["conv1d"] = conv_leg(mss, torch, devc, Bt, Dn, L)
     if not args.no_shard:
         res["shard_fwd"] = shard_leg(mss, torch, devc, s, Bt, Dn, N, L)
+    if not args.no_general_a:
+        res["scan_fwd_general_A"] = general_a_leg(mss, torch, devc, Bt, Dn, N, L)
     if not args.no_decode_chain:
         res["decode_chain"] = decode_chain(mss, torch, devc)
+        res["decode_chain_hbm"] = decode_hbm_chain(mss, torch, devc)
     if not args.no_configs:
         res["other_configs"] = configs_leg(mss, torch, devc)
     if not args.no_cpu_baseline:

@@ -8,6 +8,21 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+def pytest_sessionfinish(session, exitstatus):
+    """With MSS_PARITY_MARGINS=<file>, write the recorded worst error / limit ratios (JSON)."""
+    path = os.environ.get("MSS_PARITY_MARGINS")
+    if not path:
+        return
+    try:
+        from tests.gpu_helpers import MARGINS
+    except ImportError:
+        return
+    if MARGINS:
+        import json
+        with open(path, "w") as f:
+            json.dump(dict(sorted(MARGINS.items())), f, indent=1)
+
+
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 

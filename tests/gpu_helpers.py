@@ -34,6 +34,16 @@ def host64(t):
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
+# worst |gpu - ref| / (atol + rtol |ref|) of every named comparison in this session (tests that
+# record margins add to it; conftest writes it out when MSS_PARITY_MARGINS names a file)
+MARGINS = {}
+
+
+def record_margin(what, ratio):
+    MARGINS[what] = max(float(ratio), MARGINS.get(what, 0.0))
+    return ratio
+
+
 def assert_close(gpu, ref, rtol, atol, what=""):
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
