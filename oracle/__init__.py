@@ -63,6 +63,11 @@ def _load():
             lib.oracle_state_update.argtypes = [
                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i64p,
                 _d, _d, _d, _d, _d, _d, _d, _d, _d, _d, ctypes.c_int]
+            lib.oracle_ssd_scan.restype = ctypes.c_int
+            lib.oracle_ssd_scan.argtypes = [
+                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                _d, _d, _d, _d, _d, _d, _d, _d, ctypes.c_int, _d, _i64p, ctypes.c_int64, _d, _d, ctypes.c_int,
+                ctypes.c_int]
             lib.oracle_softplus.restype = None
             lib.oracle_softplus.argtypes = [_d, _d, ctypes.c_int64]
             lib.oracle_silu.restype = None
@@ -273,3 +278,40 @@ def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
     if rc != 0:
         raise ValueError("oracle_state_update rejected its arguments")
     return out.reshape(Bt, Dn) if rows is None else out
+
+
+def ssd_scan(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus_flag=True, h0=None,
+             pairs=None, magnitude=False, nthreads=0):
+    """Mamba-2 SSD layer in fp64 (oracle_ssd_scan: the selective recurrence with one A per head,
+    one delta per (batch, time, head) and B / C per (batch, time, group); heads in contiguous
+    blocks of H / G per group).
+
+    x, z: (Bt, L, H, P); dt: (Bt, L, H); B, C: (Bt, L, G, N); A, D, dt_bias: (H,);
+    h0: (Bt, H, P, N) or None.  pairs: flat b * H + h indices to compute (default all).
+    Returns (out (Bt, L, H, P), last_state (Bt, H, P, N)); entries of pairs not computed are NaN.
+    With magnitude=True, every term in absolute value: the per-element error scale M.
+    """
+    x, dt, A, B, C = _f64(x), _f64(dt), _f64(A), _f64(B), _f64(C)
+    Bt, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if dt.shape != (Bt, L, H) or B.shape != (Bt, L, G, N) or C.shape != B.shape or A.shape != (H,):
+        raise ValueError("ssd_scan: inconsistent shapes")
+    D = None if D is None else _f64(D)
+    z = None if z is None else _f64(z)
+    dt_bias = None if dt_bias is None else _f64(dt_bias)
+    h0 = None if h0 is None else _f64(h0)
+    out = np.full((Bt, L, H, P), np.nan)
+    last = np.full((Bt, H, P, N), np.nan)
+    if pairs is not None:
+        pairs = np.ascontiguousarray(np.asarray(pairs, dtype=np.int64))
+        pp = pairs.ctypes.data_as(_i64p)
+        npairs = pairs.size
+    else:
+        pp = ctypes.cast(None, _i64p)
+        npairs = 0
+    rc = _load().oracle_ssd_scan(Bt, L, H, P, G, N, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                 _ptr(z), _ptr(dt_bias), 1 if softplus_flag else 0, _ptr(h0), pp, npairs,
+                                 _ptr(out), _ptr(last), 1 if magnitude else 0, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_ssd_scan: bad arguments")
+    return out, last

@@ -352,3 +352,77 @@ int oracle_state_update(int64_t R, int64_t N, int64_t Bt, const int64_t* row_bat
     }
     return bad ? -1 : 0;
 }
+
+/*
+ * Mamba-2's SSD layer (the upstream README's Mamba-2 block: d_state "typically 64 or 128", and
+ * its pointer to a minimal SSD module; the pages give no equations for it).  Reading: the same
+ * selective recurrence as oracle_selective_scan with Mamba-2's tied parameters --
+ *   - heads h of P channels each; the head's A is one scalar A[h], the same for every channel p
+ *     and every state n;
+ *   - one delta per (batch, time, head), shared by the head's P channels:
+ *     delta = softplus(dt + dt_bias[h]) (or dt + dt_bias with the flag off);
+ *   - B and C per (batch, time, group), G groups, heads taken in contiguous blocks of H / G
+ *     (head h reads group h / (H / G));
+ *   - Euler input term delta B x, inclusive h_t, y = C.h_t + D[h] x, out = y silu(z).
+ * Layouts: x, z, out (Bt, L, H, P); dt (Bt, L, H); B, C (Bt, L, G, N); A, D, dt_bias (H);
+ * h0, last_state (Bt, H, P, N).  Only the (batch, head) pairs listed in `pairs` (flat
+ * b * H + h, n_pairs of them) are computed (NULL: all); out and last_state are written in the
+ * full layouts at those pairs only.  With magnitude != 0 every term is added in absolute value
+ * (|x|, |B|, |C|, |D|, |h0|, |silu(z)|; the decays are positive already): the per-element scale
+ * M that bounds the rounding error of any other summation order.
+ */
+int oracle_ssd_scan(int64_t Bt, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                    const double* x, const double* dt, const double* A, const double* Bm,
+                    const double* Cm, const double* D, const double* z, const double* dt_bias,
+                    int softplus_flag, const double* h0, const int64_t* pairs, int64_t n_pairs,
+                    double* out, double* last_state, int magnitude, int nthreads) {
+    if (Bt < 0 || L < 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || H % G != 0) return -1;
+    set_threads(nthreads);
+    const int64_t hpg = H / G;  /* heads per group */
+    const int64_t total = pairs ? n_pairs : Bt * H;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t k = 0; k < total; ++k) {
+        const int64_t bh = pairs ? pairs[k] : k;
+        if (bh < 0 || bh >= Bt * H) { bad = 1; continue; }
+        const int64_t b = bh / H, h = bh % H, g = h / hpg;
+        double* st = (double*)malloc((size_t)(P * N) * sizeof(double));
+        if (!st) { bad = 1; continue; }
+        for (int64_t i = 0; i < P * N; ++i) {
+            const double v = h0 ? h0[(b * H + h) * P * N + i] : 0.0;
+            st[i] = magnitude ? fabs(v) : v;
+        }
+        const double a = A[h];
+        const double Dh = D ? D[h] : 0.0;
+        const double bias = dt_bias ? dt_bias[h] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            const double pre = dt[(b * L + t) * H + h] + bias;
+            const double delta = softplus_flag ? sp(pre) : pre;
+            const double abar = exp(delta * a);                      /* A_bar = exp(delta A[h]) */
+            const double* Bt_ = Bm + ((b * L + t) * G + g) * N;
+            const double* Ct_ = Cm + ((b * L + t) * G + g) * N;
+            for (int64_t p = 0; p < P; ++p) {
+                const int64_t xi = ((b * L + t) * H + h) * P + p;
+                const double xv = magnitude ? fabs(x[xi]) : x[xi];
+                double* hp = st + p * N;
+                double y = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double Bn = magnitude ? fabs(Bt_[n]) : Bt_[n];
+                    const double Cn = magnitude ? fabs(Ct_[n]) : Ct_[n];
+                    hp[n] = abar * hp[n] + delta * Bn * xv;              /* + delta B x */
+                    y += Cn * hp[n];                                    /* C . h_t     */
+                }
+                y += (magnitude ? fabs(Dh) : Dh) * xv;                 /* D skip      */
+                if (z) {
+                    const double s = silu(z[xi]);
+                    y *= magnitude ? fabs(s) : s;                       /* gate after skip */
+                }
+                out[xi] = y;
+            }
+        }
+        if (last_state)
+            for (int64_t i = 0; i < P * N; ++i) last_state[(b * H + h) * P * N + i] = st[i];
+        free(st);
+    }
+    return bad ? -1 : 0;
+}

@@ -12,4 +12,7 @@ from .inputs import (  # noqa: F401
     scan_inputs,
     decode_inputs,
     sample_rows,
+    SSD_CONFIGS,
+    SSDInputs,
+    ssd_inputs,
 )

@@ -167,6 +167,51 @@ def decode_inputs(batch: int, d_inner: int, d_state: int, steps: int, dtype: str
     return DecodeInputs(x=xs, dt=dts, z=zs, B=Bs, C=Cs, A=A, D=D, dt_bias=bias, dtype=dtype)
 
 
+# Mamba-2 SSD layer workloads (the upstream README's Mamba-2 block: d_state 64, "typically 64 or
+# 128"; d_model 2560 with expand 2 as for the 2.8B / 2.7B models gives d_inner 5120, here as 80 heads
+# of 64 channels; one group of B / C).  Layout (batch, L, heads, headdim).
+SSD_CONFIGS = {
+    "ssd_tiny": dict(batch=2, L=256, heads=4, headdim=64, groups=1, d_state=64, dtype="bf16", with_z=True),
+    "ssd_2p7b_n64": dict(batch=4, L=2048, heads=80, headdim=64, groups=1, d_state=64, dtype="bf16",
+                         with_z=True),
+    "ssd_2p7b_n128": dict(batch=4, L=2048, heads=80, headdim=64, groups=1, d_state=128, dtype="bf16",
+                          with_z=True),
+}
+
+
+@dataclass
+class SSDInputs:
+    x: np.ndarray            # (batch, L, heads, headdim) float32, bf16-exact when dtype == "bf16"
+    dt: np.ndarray           # (batch, L, heads) raw dt, before bias and softplus
+    z: Optional[np.ndarray]  # (batch, L, heads, headdim) or None
+    A: np.ndarray            # (heads,) float32, negative
+    B: np.ndarray            # (batch, L, groups, d_state), bf16-exact when dtype == "bf16"
+    C: np.ndarray            # (batch, L, groups, d_state)
+    D: np.ndarray            # (heads,) float32
+    dt_bias: np.ndarray      # (heads,) float32
+    dtype: str
+
+
+def ssd_inputs(batch: int, L: int, heads: int, headdim: int, groups: int, d_state: int,
+               dtype: str = "bf16", with_z: bool = True, seed: int = 0) -> SSDInputs:
+    """One seeded input set for the SSD layer.  Draw order from Generator(PCG64(seed)): x, dt, z
+    (skipped without a gate), B, C, the dt bias (as for the S6 layer, per head), then A: one value
+    per head, -U(1, 16) (the span of the tutorial's S4D-real values 1..16, one scalar per head as
+    Mamba-2 ties them).  D = 1.  x, dt, z, B, C are drawn in fp32 and rounded to bf16 for bf16."""
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = _draw_normal(rng, (batch, L, heads, headdim), dtype)
+    dt = _draw_normal(rng, (batch, L, heads), dtype)
+    z = _draw_normal(rng, (batch, L, heads, headdim), dtype) if with_z else None
+    B = _draw_normal(rng, (batch, L, groups, d_state), dtype)
+    C = _draw_normal(rng, (batch, L, groups, d_state), dtype)
+    bias = _draw_dt_bias(rng, heads)
+    A = (-rng.uniform(1.0, 16.0, size=heads)).astype(np.float32)
+    D = np.ones(heads, dtype=np.float32)
+    return SSDInputs(x=x, dt=dt, z=z, A=A, B=B, C=C, D=D, dt_bias=bias, dtype=dtype)
+
+
 def sample_rows(n_rows: int, k: int, seed: int = 1) -> np.ndarray:
     """k distinct flat row indices in [0, n_rows): the first and last rows plus seeded picks."""
     k = min(k, n_rows)
