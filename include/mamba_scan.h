@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MSS_VERSION 10700 /* major * 10000 + minor * 100 + patch */
+#define MSS_VERSION 20000 /* major * 10000 + minor * 100 + patch */
 
 typedef enum { MSS_F32 = 0, MSS_BF16 = 1, MSS_I32 = 2 } mss_dtype_t;  /* I32: lengths only */
 
@@ -68,9 +68,9 @@ typedef enum {
 typedef struct {
     void* data;        /* device pointer                                   */
     int32_t dtype;     /* mss_dtype_t                                      */
-    int32_t ndim;      /* 1, 2 or 3                                        */
-    int64_t shape[3];
-    int64_t stride[3]; /* in elements                                      */
+    int32_t ndim;      /* 1 to 4                                           */
+    int64_t shape[4];
+    int64_t stride[4]; /* in elements                                      */
 } mss_tensor_t;
 
 /*
@@ -342,6 +342,33 @@ int mss_causal_conv1d_update(const mss_tensor_t* state, const mss_tensor_t* x,
  */
 int mss_profile_enable(int on);
 int mss_profile_fwd(int* calls, double* carry_ms, double* main_ms);
+
+/*
+ * Mamba-2's SSD layer (the upstream README's Mamba-2 block, d_state "typically 64 or 128"): the
+ * selective recurrence above with Mamba-2's tied parameters, for every batch b, head h (P
+ * channels p) and state n:
+ *     delta_t   = softplus(dt[b, t, h] + dt_bias[h])               (or without softplus)
+ *     h_t[p, n] = exp(delta_t A[h]) h_{t-1}[p, n] + delta_t B[b, t, g, n] x[b, t, h, p]   (h_0 = 0)
+ *     y_t[p]    = sum_n C[b, t, g, n] h_t[p, n] + D[h] x[b, t, h, p]
+ *     out       = y silu(z[b, t, h, p])                            (when z is given)
+ * with one scalar A per head, one delta per (batch, time, head) shared by its channels, and B, C per
+ * (batch, time, group), heads in contiguous blocks of H / G per group (head h reads g = h / (H/G)).
+ * Computed as a chunked scan (64-step chunks, dense products on the matrix cores); results agree
+ * with the step-by-step recurrence to rounding.
+ *   x, z, out   (batch, L, heads, headdim)    bf16 (z nullable: no gate)
+ *   dt          (batch, L, heads)             bf16, raw (before bias and softplus)
+ *   A           (heads,)                      f32, negative
+ *   B, C        (batch, L, groups, d_state)   bf16; heads % groups == 0 (MSS_ERR_SHAPE otherwise)
+ *   D, dt_bias  (heads,)                      f32, nullable
+ *   last_state  (batch, heads, headdim, d_state) f32, nullable; written with h_L
+ * headdim must be 64 and d_state 64 or 128; fp32 activations are not implemented (both
+ * MSS_ERR_UNSUPPORTED).  x, z, out, B and C must be 16-byte aligned (MSS_ERR_LAYOUT).  out and
+ * last_state may not overlap an input or each other.  No workspace.
+ */
+int mss_ssd_scan_fwd(const mss_tensor_t* x, const mss_tensor_t* dt, const mss_tensor_t* A,
+                     const mss_tensor_t* B, const mss_tensor_t* C, const mss_tensor_t* D,
+                     const mss_tensor_t* z, const mss_tensor_t* dt_bias, int softplus_flag,
+                     const mss_tensor_t* out, const mss_tensor_t* last_state, void* stream);
 
 /*
  * Frees every workspace buffer the library holds, on every device (current ones and those

@@ -23,13 +23,14 @@ EXPORTS = ("mss_selective_scan_fwd", "mss_selective_scan_fwd_with_state",
            "mss_selective_scan_fwd_save", "mss_selective_scan_bwd_saved",
            "mss_selective_state_update", "mss_causal_conv1d_fwd", "mss_causal_conv1d_update", "mss_profile_enable", "mss_profile_fwd",
            "mss_release_workspaces", "mss_set_plan_overrides", "mss_selective_scan_fwd_noalloc",
+           "mss_ssd_scan_fwd",
            "mss_status_string", "mss_version")
 
 
 class Tensor(ctypes.Structure):
     """mss_tensor_t"""
     _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
-                ("shape", ctypes.c_int64 * 3), ("stride", ctypes.c_int64 * 3)]
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
 
     @classmethod
     def make(cls, data: int, dtype: int, shape, stride=None) -> "Tensor":
@@ -42,7 +43,7 @@ class Tensor(ctypes.Structure):
             for s in reversed(shape):
                 stride.insert(0, acc)
                 acc *= s
-        for i, (s, st) in enumerate(zip(shape, stride)):
+        for i, (s, st) in enumerate(zip(shape[:4], stride[:4])):  # ndim > 4: rejected by the ABI
             t.shape[i] = s
             t.stride[i] = st
         return t
@@ -110,6 +111,9 @@ def load_library(path: str = LIB_PATH):
             lib.mss_selective_scan_fwd_noalloc.restype = ctypes.c_int
             lib.mss_selective_scan_fwd_noalloc.argtypes = [_TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP,
                                                            ctypes.c_int, _TP, _TP, ctypes.c_void_p]
+            lib.mss_ssd_scan_fwd.restype = ctypes.c_int
+            lib.mss_ssd_scan_fwd.argtypes = [_TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP, ctypes.c_int, _TP, _TP,
+                                             ctypes.c_void_p]
             lib.mss_release_workspaces.restype = ctypes.c_int
             lib.mss_release_workspaces.argtypes = []
             lib.mss_set_plan_overrides.restype = ctypes.c_int
@@ -180,6 +184,11 @@ def scan_fwd_noalloc_raw(u, delta, A, B, C, D, z, delta_bias, softplus_flag, out
     return load_library().mss_selective_scan_fwd_noalloc(_ref(u), _ref(delta), _ref(A), _ref(B), _ref(C), _ref(D),
                                                          _ref(z), _ref(delta_bias), int(softplus_flag), _ref(out),
                                                          _ref(last_state), stream)
+
+
+def ssd_scan_fwd_raw(x, dt, A, B, C, D, z, dt_bias, softplus_flag, out, last_state, stream) -> int:
+    return load_library().mss_ssd_scan_fwd(_ref(x), _ref(dt), _ref(A), _ref(B), _ref(C), _ref(D), _ref(z),
+                                           _ref(dt_bias), int(softplus_flag), _ref(out), _ref(last_state), stream)
 
 
 def scan_fwd_with_state_raw(u, delta, A, B, C, D, z, delta_bias, initial_state, softplus_flag,
@@ -260,7 +269,7 @@ def state_update_raw(state, x, dt, A, B, C, D, z, dt_bias, out, stream) -> int:
 
 # ----------------------------------------------------------------------- torch front end
 
-_DESC = struct.Struct("<Qii3q3q")   # the bytes of one Tensor (mss_tensor_t)
+_DESC = struct.Struct("<Qii4q4q")   # the bytes of one Tensor (mss_tensor_t)
 _DTYPES = None
 
 
@@ -277,9 +286,9 @@ def _desc(t):
         _DTYPES = {torch.float32: MSS_F32, torch.bfloat16: MSS_BF16, torch.int32: MSS_I32}
     shape, stride = tuple(t.shape), t.stride()
     n = len(shape)
-    if n > 3:
+    if n > 4:
         return Tensor.make(t.data_ptr(), _DTYPES.get(t.dtype, -1), list(shape), list(stride))  # rejected by the ABI
-    pad = (0,) * (3 - n)
+    pad = (0,) * (4 - n)
     return Tensor.from_buffer_copy(_DESC.pack(t.data_ptr(), _DTYPES.get(t.dtype, -1), n, *shape, *pad,
                                               *stride, *pad))
 
@@ -567,3 +576,27 @@ def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, 
     if st != 0:
         raise MssError(st, "mss_selective_state_update")
     return out
+
+
+def ssd_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True, return_last_state=True,
+                 out=None, last_state=None):
+    """Mamba-2 SSD layer (mss_ssd_scan_fwd) on the current stream of x's device.
+
+    x, z: (batch, L, heads, 64) bfloat16; dt: (batch, L, heads) bfloat16; A, D, dt_bias: (heads,)
+    float32; B, C: (batch, L, groups, d_state) bfloat16 with d_state 64 or 128.
+    Returns out, or (out, last_state) with last_state (batch, heads, 64, d_state) float32.
+    """
+    import torch
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    if return_last_state and last_state is None:
+        last_state = torch.empty((x.shape[0], x.shape[2], x.shape[3], B.shape[3]), dtype=torch.float32,
+                                 device=x.device)
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        st = ssd_scan_fwd_raw(_desc(x), _desc(dt), _desc(A), _desc(B), _desc(C), _desc(D), _desc(z),
+                              _desc(dt_bias), 1 if dt_softplus else 0, _desc(out),
+                              _desc(last_state) if return_last_state else None, stream)
+    if st != 0:
+        raise MssError(st, "mss_ssd_scan_fwd")
+    return (out, last_state) if return_last_state else out

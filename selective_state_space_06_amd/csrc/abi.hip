@@ -24,9 +24,9 @@ int64_t numel(const mss_tensor_t& t) {
 
 size_t elem_size(int32_t dtype) { return dtype == MSS_BF16 ? 2 : 4; }
 
-bool shape_is(const mss_tensor_t& t, int ndim, int64_t s0, int64_t s1 = 0, int64_t s2 = 0) {
+bool shape_is(const mss_tensor_t& t, int ndim, int64_t s0, int64_t s1 = 0, int64_t s2 = 0, int64_t s3 = 0) {
     if (t.ndim != ndim) return false;
-    const int64_t s[3] = {s0, s1, s2};
+    const int64_t s[4] = {s0, s1, s2, s3};
     for (int i = 0; i < ndim; ++i)
         if (t.shape[i] != s[i]) return false;
     return true;
@@ -61,11 +61,11 @@ bool overlap(const mss_tensor_t* a, const mss_tensor_t* b) {
 }
 
 // Status of one descriptor before its extents are compared: NULL descriptor or NULL data
-// (for a non-empty tensor) -> NULL_ARG; ndim outside 1..3, a negative extent or an element count
+// (for a non-empty tensor) -> NULL_ARG; ndim outside 1..4, a negative extent or an element count
 // beyond 2^48 (so that no later size computation can overflow) -> SHAPE.
 int check_desc(const mss_tensor_t* t, bool required) {
     if (!t) return required ? MSS_ERR_NULL_ARG : MSS_OK;
-    if (t->ndim < 1 || t->ndim > 3) return MSS_ERR_SHAPE;
+    if (t->ndim < 1 || t->ndim > 4) return MSS_ERR_SHAPE;
     int64_t n = 1;
     for (int i = 0; i < t->ndim; ++i) {
         if (t->shape[i] < 0) return MSS_ERR_SHAPE;
@@ -830,6 +830,63 @@ int mss_profile_fwd(int* calls, double* carry_ms, double* main_ms) {
         *carry_ms = c;
         *main_ms = m;
         return MSS_OK;
+    } catch (...) {
+        return MSS_ERR_HIP;
+    }
+}
+
+int mss_ssd_scan_fwd(const mss_tensor_t* x, const mss_tensor_t* dt, const mss_tensor_t* A,
+                     const mss_tensor_t* B, const mss_tensor_t* C, const mss_tensor_t* D,
+                     const mss_tensor_t* z, const mss_tensor_t* dt_bias, int softplus_flag,
+                     const mss_tensor_t* out, const mss_tensor_t* last_state, void* stream) {
+    try {
+        {
+            const mss_tensor_t* const req[] = {x, dt, A, B, C, out};
+            const int s = check_descs(req, {D, z, dt_bias, last_state});
+            if (s != MSS_OK) return s;
+        }
+        if (x->ndim != 4 || B->ndim != 4) return MSS_ERR_SHAPE;
+        const int64_t Bt = x->shape[0], L = x->shape[1], H = x->shape[2], P = x->shape[3];
+        const int64_t G = B->shape[2], N = B->shape[3];
+        if (!shape_is(*dt, 3, Bt, L, H) || !shape_is(*A, 1, H) || !shape_is(*out, 4, Bt, L, H, P)) return MSS_ERR_SHAPE;
+        if (!shape_is(*B, 4, Bt, L, G, N) || !shape_is(*C, 4, Bt, L, G, N)) return MSS_ERR_SHAPE;
+        if (z && !shape_is(*z, 4, Bt, L, H, P)) return MSS_ERR_SHAPE;
+        if ((D && !shape_is(*D, 1, H)) || (dt_bias && !shape_is(*dt_bias, 1, H))) return MSS_ERR_SHAPE;
+        if (last_state && !shape_is(*last_state, 4, Bt, H, P, N)) return MSS_ERR_SHAPE;
+        if (G < 1 || H % G != 0) return MSS_ERR_SHAPE;  // heads come in whole blocks per group
+
+        if (x->dtype != MSS_BF16 && x->dtype != MSS_F32) return MSS_ERR_DTYPE;
+        for (const mss_tensor_t* t : {dt, B, C, out, z})
+            if (t && t->dtype != x->dtype) return MSS_ERR_DTYPE;
+        for (const mss_tensor_t* t : {A, D, dt_bias, last_state})
+            if (t && t->dtype != MSS_F32) return MSS_ERR_DTYPE;
+        for (const mss_tensor_t* t : {x, dt, A, B, C, D, z, dt_bias, out, last_state}) {
+            if (!t) continue;
+            if (!dense(*t) || !aligned(*t, elem_size(t->dtype))) return MSS_ERR_LAYOUT;
+        }
+        for (const mss_tensor_t* t : {x, B, C, z, out})  // 16-byte vector accesses
+            if (t && !aligned(*t, 16)) return MSS_ERR_LAYOUT;
+        for (const mss_tensor_t* t : {x, dt, A, B, C, D, z, dt_bias}) {
+            if (overlap(out, t)) return MSS_ERR_ALIAS;
+            if (last_state && overlap(last_state, t)) return MSS_ERR_ALIAS;
+        }
+        if (last_state && overlap(out, last_state)) return MSS_ERR_ALIAS;
+        if (x->dtype != MSS_BF16) return MSS_ERR_UNSUPPORTED;        // fp32 inputs: not built
+        if (P != 64 || (N != 64 && N != 128)) return MSS_ERR_UNSUPPORTED;
+        if (Bt > 65535 || H > 65535) return MSS_ERR_UNSUPPORTED;
+
+        mss::SsdLaunch a;
+        a.x = x->data; a.dt = dt->data; a.A = static_cast<const float*>(A->data);
+        a.B = B->data; a.C = C->data;
+        a.D = D ? static_cast<const float*>(D->data) : nullptr;
+        a.z = z ? z->data : nullptr;
+        a.bias = dt_bias ? static_cast<const float*>(dt_bias->data) : nullptr;
+        a.out = out->data;
+        a.last_state = last_state ? static_cast<float*>(last_state->data) : nullptr;
+        a.Bt = Bt; a.L = L; a.H = H; a.P = P; a.G = G; a.N = N;
+        a.softplus = softplus_flag ? 1 : 0;
+        if (Bt * H == 0) return MSS_OK;
+        return mss::launch_ssd_scan(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MSS_OK : MSS_ERR_HIP;
     } catch (...) {
         return MSS_ERR_HIP;
     }

@@ -108,6 +108,24 @@ struct ConvUpdateLaunch {
     bool silu, bf16;
 };
 
+// Mamba-2 SSD layer (ssd_scan.hip): x, z, out (Bt, L, H, P); dt (Bt, L, H); B, C (Bt, L, G, N), all
+// bf16; A, D, bias (H) fp32; last_state (Bt, H, P, N) fp32.  P = 64, N = 64 or 128.
+struct SsdLaunch {
+    const void* x;
+    const void* dt;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;         // nullable
+    const void* z;          // nullable
+    const float* bias;      // nullable
+    void* out;
+    float* last_state;      // nullable
+    int64_t Bt, L, H, P, G, N;
+    int softplus;
+};
+hipError_t launch_ssd_scan(const SsdLaunch& a, hipStream_t stream);
+
 // How the forward scan is decomposed.  Generic path: `segments` workgroup-rows per channel
 // group, each covering `seg_len` steps.  Fast path: `waves` wavefronts, each taking an equal
 // contiguous range of the (channel group, tile) work; `segments` > 1 when some range ends

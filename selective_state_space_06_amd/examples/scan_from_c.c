@@ -33,14 +33,14 @@ static float uniform(float lo, float hi) {
 
 static mss_tensor_t desc(void* data, int ndim, int64_t s0, int64_t s1, int64_t s2) {
     mss_tensor_t t;
-    int64_t shape[3] = {s0, s1, s2};
+    int64_t shape[4] = {s0, s1, s2, 1};
     t.data = data;
     t.dtype = MSS_F32;
     t.ndim = ndim;
-    for (int i = 0; i < 3; ++i) t.shape[i] = i < ndim ? shape[i] : 1;
+    for (int i = 0; i < 4; ++i) t.shape[i] = i < ndim ? shape[i] : 1;
     t.stride[ndim - 1] = 1;
     for (int i = ndim - 2; i >= 0; --i) t.stride[i] = t.stride[i + 1] * t.shape[i + 1];
-    for (int i = ndim; i < 3; ++i) t.stride[i] = 1;
+    for (int i = ndim; i < 4; ++i) t.stride[i] = 1;
     return t;
 }
 

@@ -611,3 +611,81 @@ def test_plan_overrides_reject_negative_counts_and_reset(lib):
     assert lib.mss_set_plan_overrides(0, 0, 0, -2) == SHAPE
     assert lib.mss_set_plan_overrides(1, 3, 17, 4) == OK
     assert lib.mss_set_plan_overrides(0, 0, 0, 0) == OK
+
+
+# --------------------------------------------------------------------- SSD (Mamba-2) validation
+
+def ssd_args(dtype=MSS_BF16, P=64, N=64, H=4, G=2, Ls=70):
+    es = 2 if dtype == MSS_BF16 else 4
+    big = BT * Ls * H * P
+    return dict(
+        x=Tensor.make(addr(big * es), dtype, [BT, Ls, H, P]),
+        dt=Tensor.make(addr(BT * Ls * H * es), dtype, [BT, Ls, H]),
+        A=Tensor.make(addr(H * 4), MSS_F32, [H]),
+        B=Tensor.make(addr(BT * Ls * G * N * es), dtype, [BT, Ls, G, N]),
+        C=Tensor.make(addr(BT * Ls * G * N * es), dtype, [BT, Ls, G, N]),
+        D=Tensor.make(addr(H * 4), MSS_F32, [H]),
+        z=Tensor.make(addr(big * es), dtype, [BT, Ls, H, P]),
+        dt_bias=Tensor.make(addr(H * 4), MSS_F32, [H]),
+        softplus_flag=1,
+        out=Tensor.make(addr(big * es), dtype, [BT, Ls, H, P]),
+        last_state=Tensor.make(addr(BT * H * P * N * 4), MSS_F32, [BT, H, P, N]),
+        stream=None)
+
+
+def call_ssd(a):
+    return mss.ssd_scan_fwd_raw(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["dt_bias"],
+                                a["softplus_flag"], a["out"], a["last_state"], a["stream"])
+
+
+@pytest.mark.parametrize("name", ["x", "dt", "A", "B", "C", "out"])
+def test_ssd_null_required(lib, name):
+    a = ssd_args()
+    a[name] = None
+    assert call_ssd(a) == NULL_ARG
+
+
+@pytest.mark.parametrize("name,shape", [
+    ("dt", [BT, 70, 5]), ("A", [5]), ("B", [BT, 71, 2, 64]), ("C", [BT, 70, 2, 32]), ("z", [BT, 70, 4, 32]),
+    ("out", [BT + 1, 70, 4, 64]), ("D", [3]), ("dt_bias", [8]), ("last_state", [BT, 4, 64, 32])])
+def test_ssd_shape_mismatch(lib, name, shape):
+    a = ssd_args()
+    t = a[name]
+    a[name] = Tensor.make(t.data, t.dtype, shape)
+    assert call_ssd(a) == SHAPE
+
+
+def test_ssd_heads_not_divisible_by_groups(lib):
+    assert call_ssd(ssd_args(H=6, G=4)) == SHAPE
+
+
+def test_ssd_dtype_layout_alias_unsupported(lib):
+    a = ssd_args()
+    a["A"].dtype = MSS_BF16
+    assert call_ssd(a) == DTYPE
+    a = ssd_args()
+    a["z"].dtype = MSS_F32
+    assert call_ssd(a) == DTYPE
+    a = ssd_args()
+    a["x"].data += 2  # element-aligned but not 16-byte aligned
+    assert call_ssd(a) == LAYOUT
+    a = ssd_args()
+    a["out"].data = a["z"].data
+    assert call_ssd(a) == ALIAS
+    assert call_ssd(ssd_args(dtype=MSS_F32)) == UNSUPPORTED
+    assert call_ssd(ssd_args(P=32)) == UNSUPPORTED
+    assert call_ssd(ssd_args(N=96)) == UNSUPPORTED
+    a = ssd_args()
+    a["x"].ndim = 3
+    assert call_ssd(a) == SHAPE
+    a = ssd_args()
+    a["x"].ndim = 5
+    assert call_ssd(a) == SHAPE
+
+
+def test_ssd_empty_batch_is_ok(lib):
+    a = ssd_args()
+    for k in ("x", "dt", "B", "C", "z", "out", "last_state"):
+        t = a[k]
+        a[k] = Tensor.make(t.data, t.dtype, [0] + [t.shape[i] for i in range(1, t.ndim)])
+    assert call_ssd(a) == OK
