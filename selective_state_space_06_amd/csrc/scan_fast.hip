@@ -532,7 +532,7 @@ __device__ __forceinline__ void fold_carry(float (&h)[kN], const float (&A2)[kN]
 }
 
 template <class E, bool HAS_Z, bool SOFTPLUS, bool VARLEN, bool RAGGED, bool SAVE>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void scan_main_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void scan_main_kernel(
     const typename E::storage* __restrict__ u, const typename E::storage* __restrict__ delta,
     const typename E::storage* __restrict__ z, const float* __restrict__ A,
     const float* __restrict__ B, const float* __restrict__ C, const float* __restrict__ D,
@@ -767,10 +767,11 @@ hipError_t launch_fast_e(const ScanLaunch& a, const ScanPlan& p, float* ws, hipS
 
 }  // namespace
 
-// Wavefronts: two per SIMD for bf16 rows and one and a half for fp32 rows, all resident at once
-// (the main kernel could hold three per SIMD, but that was slower: Mamba-2.8B layer 226 us at two
-// per SIMD, 259 us at three, 239 / 250 us at 1.9 / 2.25; Mamba-130M fp32 layer 216 us at 1.5,
-// 232 us at 2 -- more streams in flight evict more of each other's lines), and at least two tiles
+// Wavefronts: two per SIMD for bf16 rows and one for fp32 rows, all resident at once (the main
+// kernel is built for two per SIMD: 256 VGPRs, no spills).  More were slower: Mamba-2.8B layer
+// 226 us at two per SIMD, 259 us at three, 239 / 250 us at 1.9 / 2.25 (uneven SIMD loads);
+// Mamba-130M fp32 layer 203 us at one per SIMD, 218 us at 1.5, 233 us at 2; long context 1341 us at
+// one, 1359 at 1.5 -- more streams in flight evict more of each other's lines.  At least two tiles
 // each (a shorter piece spends more on folding the aggregates before it than it saves).  `waves_override` > 0 replaces the count (tests use it to force many or few
 // pieces per group, and ranges that cross groups).  `segments` reports whether some range ends
 // inside a group, i.e. whether the aggregate kernel has work.
@@ -780,7 +781,7 @@ ScanPlan plan_fast(const ScanLaunch& a, int num_cus, int64_t waves_override) {
     const int64_t groups = a.Bt * ((a.Dn + 63) / 64);
     const int64_t tiles = (a.L + TT - 1) / TT;
     const int64_t GT = groups * tiles;
-    int64_t W = (a.bf16 ? 8LL : 6LL) * (num_cus > 0 ? num_cus : 256);
+    int64_t W = (a.bf16 ? 8LL : 4LL) * (num_cus > 0 ? num_cus : 256);
     if (W > GT / 2) W = GT / 2;
     if (waves_override > 0) W = waves_override;
     if (W > GT) W = GT;
