@@ -363,7 +363,9 @@ int mss_profile_fwd(int* calls, double* carry_ms, double* main_ms);
  *   last_state  (batch, heads, headdim, d_state) f32, nullable; written with h_L
  * headdim must be 64 and d_state 64 or 128; fp32 activations are not implemented (both
  * MSS_ERR_UNSUPPORTED).  x, z, out, B and C must be 16-byte aligned (MSS_ERR_LAYOUT).  out and
- * last_state may not overlap an input or each other.  No workspace.
+ * last_state may not overlap an input or each other.  Long sequences are cut into segments whose
+ * local end states pass through the library workspace (headdim * d_state + 1 floats per batch,
+ * head and segment but the last).
  */
 int mss_ssd_scan_fwd(const mss_tensor_t* x, const mss_tensor_t* dt, const mss_tensor_t* A,
                      const mss_tensor_t* B, const mss_tensor_t* C, const mss_tensor_t* D,
@@ -387,10 +389,11 @@ int mss_release_workspaces(void);
  *                     share of the (64-channel group, time tile) work; more than the groups
  *                     splits sequences, fewer makes one wavefront scan several groups)
  *   bwd_segments      > 0: segments per channel group of the backward
+ *   ssd_segments      > 0: segments each (batch, head) of mss_ssd_scan_fwd is cut into
  * Zeros restore the automatic plans.  Returns MSS_OK, or MSS_ERR_SHAPE for a negative count.
  */
 int mss_set_plan_overrides(int force_generic, int generic_segments, int64_t fast_waves,
-                           int bwd_segments);
+                           int bwd_segments, int ssd_segments);
 
 /* Static, NUL-terminated name of a status code ("MSS_OK", "MSS_ERR_SHAPE", ...). */
 const char* mss_status_string(int status);

@@ -117,7 +117,8 @@ def load_library(path: str = LIB_PATH):
             lib.mss_release_workspaces.restype = ctypes.c_int
             lib.mss_release_workspaces.argtypes = []
             lib.mss_set_plan_overrides.restype = ctypes.c_int
-            lib.mss_set_plan_overrides.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int]
+            lib.mss_set_plan_overrides.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                                   ctypes.c_int]
             lib.mss_profile_enable.restype = ctypes.c_int
             lib.mss_profile_enable.argtypes = [ctypes.c_int]
             lib.mss_profile_fwd.restype = ctypes.c_int
@@ -144,11 +145,12 @@ def release_workspaces() -> None:
 
 
 def set_plan_overrides(force_generic: bool = False, generic_segments: int = 0, fast_waves: int = 0,
-                       bwd_segments: int = 0) -> None:
-    """mss_set_plan_overrides (tests and tuning only): fix the forward's path and split and the
-    backward's segment count for later calls; all defaults restore the automatic plans."""
+                       bwd_segments: int = 0, ssd_segments: int = 0) -> None:
+    """mss_set_plan_overrides (tests and tuning only): fix the forward's path and split, the
+    backward's and the SSD scan's segment counts for later calls; all defaults restore the
+    automatic plans."""
     st = load_library().mss_set_plan_overrides(1 if force_generic else 0, int(generic_segments),
-                                                int(fast_waves), int(bwd_segments))
+                                                int(fast_waves), int(bwd_segments), int(ssd_segments))
     if st != 0:
         raise MssError(st, "mss_set_plan_overrides")
 

@@ -122,6 +122,7 @@ std::atomic<int> g_force_generic{0};
 std::atomic<int> g_generic_segments{0};
 std::atomic<int64_t> g_fast_waves{0};
 std::atomic<int> g_bwd_segments{0};
+std::atomic<int> g_ssd_segments{0};
 
 hipError_t device_cus(int dev, int* cus) {
     std::lock_guard<std::mutex> lk(g_mu);
@@ -886,7 +887,18 @@ int mss_ssd_scan_fwd(const mss_tensor_t* x, const mss_tensor_t* dt, const mss_te
         a.Bt = Bt; a.L = L; a.H = H; a.P = P; a.G = G; a.N = N;
         a.softplus = softplus_flag ? 1 : 0;
         if (Bt * H == 0) return MSS_OK;
-        return mss::launch_ssd_scan(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MSS_OK : MSS_ERR_HIP;
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return MSS_ERR_HIP;
+        if (device_cus(dev, &cus) != hipSuccess) return MSS_ERR_HIP;
+        const int segments = mss::plan_ssd_segments(a, cus, g_ssd_segments.load());
+        const size_t bytes = mss::ssd_workspace_bytes(a, segments);
+        float* ws = nullptr;
+        if (bytes > 0) {
+            const int wst = workspace(dev, stream, bytes, &ws);
+            if (wst != MSS_OK) return wst;
+        }
+        return mss::launch_ssd_scan(a, segments, ws, static_cast<hipStream_t>(stream)) == hipSuccess ? MSS_OK
+                                                                                                    : MSS_ERR_HIP;
     } catch (...) {
         return MSS_ERR_HIP;
     }
@@ -914,8 +926,10 @@ int mss_release_workspaces(void) {
     }
 }
 
-int mss_set_plan_overrides(int force_generic, int generic_segments, int64_t fast_waves, int bwd_segments) {
-    if (generic_segments < 0 || fast_waves < 0 || bwd_segments < 0) return MSS_ERR_SHAPE;
+int mss_set_plan_overrides(int force_generic, int generic_segments, int64_t fast_waves, int bwd_segments,
+                           int ssd_segments) {
+    if (generic_segments < 0 || fast_waves < 0 || bwd_segments < 0 || ssd_segments < 0) return MSS_ERR_SHAPE;
+    g_ssd_segments.store(ssd_segments);
     g_force_generic.store(force_generic != 0 ? 1 : 0);
     g_generic_segments.store(generic_segments);
     g_fast_waves.store(fast_waves);

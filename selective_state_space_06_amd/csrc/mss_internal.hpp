@@ -124,7 +124,11 @@ struct SsdLaunch {
     int64_t Bt, L, H, P, G, N;
     int softplus;
 };
-hipError_t launch_ssd_scan(const SsdLaunch& a, hipStream_t stream);
+// Segments per (batch, head) (segments_override > 0 replaces the count), the workspace they need,
+// and the launch.
+int plan_ssd_segments(const SsdLaunch& a, int num_cus, int segments_override);
+size_t ssd_workspace_bytes(const SsdLaunch& a, int segments);
+hipError_t launch_ssd_scan(const SsdLaunch& a, int segments, float* workspace, hipStream_t stream);
 
 // How the forward scan is decomposed.  Generic path: `segments` workgroup-rows per channel
 // group, each covering `seg_len` steps.  Fast path: `waves` wavefronts, each taking an equal

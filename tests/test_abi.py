@@ -606,11 +606,12 @@ def test_saved_state_blocks_follows_the_documented_index():
 def test_plan_overrides_reject_negative_counts_and_reset(lib):
     """mss_set_plan_overrides: negative counts are refused (nothing changes); zeros restore the
     automatic plans.  No HIP call is made."""
-    assert lib.mss_set_plan_overrides(0, -1, 0, 0) == SHAPE
-    assert lib.mss_set_plan_overrides(0, 0, -5, 0) == SHAPE
-    assert lib.mss_set_plan_overrides(0, 0, 0, -2) == SHAPE
-    assert lib.mss_set_plan_overrides(1, 3, 17, 4) == OK
-    assert lib.mss_set_plan_overrides(0, 0, 0, 0) == OK
+    assert lib.mss_set_plan_overrides(0, -1, 0, 0, 0) == SHAPE
+    assert lib.mss_set_plan_overrides(0, 0, -5, 0, 0) == SHAPE
+    assert lib.mss_set_plan_overrides(0, 0, 0, -2, 0) == SHAPE
+    assert lib.mss_set_plan_overrides(0, 0, 0, 0, -3) == SHAPE
+    assert lib.mss_set_plan_overrides(1, 3, 17, 4, 5) == OK
+    assert lib.mss_set_plan_overrides(0, 0, 0, 0, 0) == OK
 
 
 # --------------------------------------------------------------------- SSD (Mamba-2) validation

@@ -117,6 +117,16 @@ def test_ssd_full_layer_sampled_heads(mss, oracle_mod, name):
     _check(mss, oracle_mod, s, name, pairs=pairs)
 
 
+@pytest.mark.parametrize("segments", [1, 2, 3, 7, 16])
+def test_ssd_segment_splits(mss, oracle_mod, segments, plan):
+    """The chunks of each (batch, head) cut into segments (local end states folded into the state
+    entering each segment), up to one chunk per segment; a ragged last chunk."""
+    plan(ssd_segments=segments)
+    s = ssd_inputs(2, 16 * 64 - 20, 4, 64, 2, 128 if segments % 2 else 64, dtype="bf16", with_z=True,
+                   seed=60 + segments)
+    _check(mss, oracle_mod, s, f"ssd segments={segments}")
+
+
 def test_ssd_empty_sequence_zeroes_state(mss):
     import torch
     x = torch.empty((2, 0, 4, 64), dtype=torch.bfloat16, device="cuda")
