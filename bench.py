@@ -24,6 +24,11 @@ launch from rocprofv3 counters taken on this exact kernel source (null otherwise
 in fact limited by VALU issue: `valu` gives the main kernel's counted instructions per
 (b, d, t) and the issue rate they imply, against the one-instruction-per-4-cycles rate of a
 wave64 fp32 VALU instruction on a 16-lane SIMD (1024 SIMDs at 2.4 GHz).
+
+Beside the headline the line carries legs for the rest of the path: the backward, the causal
+conv, the forward at shard shapes and with an unstructured A, the decode chain (cache- and
+HBM-resident states), the fp32 workloads, and Mamba-2's SSD layer at d_state 64 and 128
+(`ssd_scan`: call time, algorithmic GB/s and HBM fraction, MFMA TFLOP/s of the chunked form).
 """
 from __future__ import annotations
 
@@ -217,6 +222,70 @@ def general_a_leg(mss, torch, devc, Bt, Dn, N, L, calls=20, warmup=3, copies=2):
             "frac_hbm_peak": round(nb / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "carry_stage_avg_ms": round(carry / max(n, 1), 4), "main_avg_ms": round(main_ms, 4),
             "main_frac_hbm_peak": round(nb / (main_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+def ssd_bytes(Bt, L, H, P, G, N):
+    """Algorithmic bytes of one SSD layer call: x, z, out (bf16), dt (bf16), B, C (bf16), A, D,
+    dt_bias (fp32) and the final state (fp32), each once."""
+    return 3 * Bt * L * H * P * 2 + Bt * L * H * 2 + 2 * Bt * L * G * N * 2 + 3 * H * 4 + Bt * H * P * N * 4
+
+
+def ssd_flops(Bt, L, H, P, N, Q=64):
+    """Multiply-adds x 2 of the chunked form per (b, h, chunk of Q): C B^T and M X over the causal
+    triangle (Q (Q + 1) / 2 pairs), C H^T and the state update X^T (w B) in full."""
+    chunks = Bt * H * ((L + Q - 1) // Q)
+    tri = Q * (Q + 1) // 2
+    return chunks * 2 * (tri * N + tri * P + 2 * Q * N * P)
+
+
+def ssd_leg(mss, torch, devc, calls=20, warmup=3, copies=2):
+    """Mamba-2's SSD layer (mss_ssd_scan_fwd) at the 2.7B width (batch 4, L 2048, 80 heads of 64
+    channels, one group) for d_state 64 and 128: rotated input copies, HIP events on the stream.
+    The layer is HBM-bound in principle (about 60 flops per algorithmic byte against a bf16 ridge
+    of 2.5 PFLOP/s / 8 TB/s = 312); the MFMA rate is reported beside the HBM fraction."""
+    import numpy as np
+    from synth import SSD_CONFIGS, ssd_inputs
+    out_res = {}
+    for name in ("ssd_2p7b_n64", "ssd_2p7b_n128"):
+        c = SSD_CONFIGS[name]
+        Bt, L, H, P, G, N = c["batch"], c["L"], c["heads"], c["headdim"], c["groups"], c["d_state"]
+        s = ssd_inputs(Bt, L, H, P, G, N, seed=0)
+        up = lambda a, bf=False: (torch.from_numpy(np.ascontiguousarray(a)).to(devc).to(torch.bfloat16)
+                                  if bf else torch.from_numpy(np.ascontiguousarray(a)).to(devc))
+        A, D, bias = up(s.A), up(s.D), up(s.dt_bias)
+        sets = [dict(x=up(s.x, True), dt=up(s.dt, True), z=up(s.z, True), B=up(s.B, True), C=up(s.C, True))
+                for _ in range(copies)]
+        del s
+        out = torch.empty_like(sets[0]["x"])
+        last = torch.empty((Bt, H, P, N), dtype=torch.float32, device=devc)
+
+        def call(k):
+            p = sets[k % copies]
+            mss.ssd_scan_fwd(p["x"], p["dt"], A, p["B"], p["C"], D=D, z=p["z"], dt_bias=bias, out=out,
+                             last_state=last)
+
+        for k in range(warmup):
+            call(k)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        for k in range(calls):
+            ev[k][0].record(stream)
+            call(k)
+            ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in ev]
+        avg = sum(ms) / len(ms)
+        nb, fl = ssd_bytes(Bt, L, H, P, G, N), ssd_flops(Bt, L, H, P, N)
+        gbps = nb / (avg * 1e-3) / 1e9
+        out_res[name] = {"shape": {"batch": Bt, "seq_len": L, "heads": H, "headdim": P, "groups": G, "d_state": N},
+                         "avg_ms": round(avg, 4), "min_ms": round(min(ms), 4), "algorithmic_bytes": nb,
+                         "gbps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                         "algorithmic_flops": fl, "tflops": round(fl / (avg * 1e-3) / 1e12, 2),
+                         "frac_bf16_mfma_peak": round(fl / (avg * 1e-3) / 2.5e15, 4)}
+        del sets, out, last
+        torch.cuda.empty_cache()
+    return out_res
 
 
 def decode_chain(mss, torch, devc, steps=1024, pool=64):
@@ -475,6 +544,7 @@ def main():
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-shard", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the tiny / 130M / long-context fp32 forward")
+    ap.add_argument("--no-ssd", action="store_true", help="skip the Mamba-2 SSD layer leg")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library runs the scan on a single MI355X "
@@ -605,6 +675,8 @@ def main():
         res["decode_chain_hbm"] = decode_hbm_chain(mss, torch, devc)
     if not args.no_configs:
         res["other_configs"] = configs_leg(mss, torch, devc)
+    if not args.no_ssd:
+        res["ssd_scan"] = ssd_leg(mss, torch, devc)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(s, Bt, Dn, N, L)
     print(json.dumps(res), flush=True)

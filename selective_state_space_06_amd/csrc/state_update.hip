@@ -41,36 +41,56 @@ __device__ __forceinline__ float quad_sum(float v) {
 
 // Threads stride over the rows' quads (the grid is capped: a dispatch holds at most 2^32 - 1
 // work-items per dimension).  The stride is a multiple of four, so the four lanes of a row stay
-// together in every iteration and the quad's DPP sum sees only its own row.
+// together in every iteration and the quad's DPP sum sees only its own row.  Each thread takes
+// kItems quads per round, one stride apart, and issues all their loads before any arithmetic:
+// the step is bound by the latency of its state reads, and this doubles the reads in flight.
+// (An item past the end re-reads the round's first quad and stores nothing; a quad is valid or
+// invalid as a whole, so the DPP sums of valid rows see only valid lanes.)
+constexpr int kItems = 2;
+
 template <class E, bool HAS_Z>
 __global__ __launch_bounds__(256) void state_update_kernel(DArgs a) {
     const int64_t total = a.rows * 4;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gt < total; gt += stride) {
-        const int64_t row = gt >> 2;   // flat (b, d)
-        const int q = static_cast<int>(gt & 3);  // this lane holds states 4q .. 4q + 3
-        const int64_t d = row % a.Dn;
-        const int64_t b = row / a.Dn;
-        const float xv = E::load1(a.x, row);
-        const float dl = softplus(E::load1(a.dt, row) + (a.bias ? a.bias[d] : 0.0f));
-        float4* sp = reinterpret_cast<float4*>(a.state) + row * 4 + q;
-        const float4 s = *sp;
-        const float4 A4 = reinterpret_cast<const float4*>(a.A)[d * 4 + q];
-        const float4 B4 = reinterpret_cast<const float4*>(a.B)[b * 4 + q];
-        const float4 C4 = reinterpret_cast<const float4*>(a.C)[b * 4 + q];
-        const float dx = dl * xv;
-        float4 hn;
-        hn.x = fmaf(fast_exp2(dl * (A4.x * kLog2e)), s.x, dx * B4.x);
-        hn.y = fmaf(fast_exp2(dl * (A4.y * kLog2e)), s.y, dx * B4.y);
-        hn.z = fmaf(fast_exp2(dl * (A4.z * kLog2e)), s.z, dx * B4.z);
-        hn.w = fmaf(fast_exp2(dl * (A4.w * kLog2e)), s.w, dx * B4.w);
-        *sp = hn;
-        float y = fmaf(C4.w, hn.w, fmaf(C4.z, hn.z, fmaf(C4.y, hn.y, C4.x * hn.x)));
-        y = quad_sum(y);
-        if (q == 0) {
-            float o = fmaf(a.D ? a.D[d] : 0.0f, xv, y);
-            if (HAS_Z) o *= silu(E::load1(a.z, row));
-            E::store1(a.out, row, o);
+    const int q = static_cast<int>(threadIdx.x & 3);  // this lane holds states 4q .. 4q + 3 of its rows
+    for (int64_t g0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g0 < total; g0 += kItems * stride) {
+        int64_t row[kItems], d[kItems];
+        bool ok[kItems];
+        float xv[kItems], dtv[kItems], zv[kItems], bias[kItems];
+        float4 s[kItems], A4[kItems], B4[kItems], C4[kItems];
+#pragma unroll
+        for (int u = 0; u < kItems; ++u) {
+            const int64_t gt = g0 + u * stride;
+            ok[u] = gt < total;
+            row[u] = (ok[u] ? gt : g0) >> 2;  // flat (b, d)
+            d[u] = row[u] % a.Dn;
+            const int64_t b = row[u] / a.Dn;
+            xv[u] = E::load1(a.x, row[u]);
+            dtv[u] = E::load1(a.dt, row[u]);
+            zv[u] = HAS_Z ? E::load1(a.z, row[u]) : 0.0f;
+            bias[u] = a.bias ? a.bias[d[u]] : 0.0f;
+            s[u] = reinterpret_cast<const float4*>(a.state)[row[u] * 4 + q];
+            A4[u] = reinterpret_cast<const float4*>(a.A)[d[u] * 4 + q];
+            B4[u] = reinterpret_cast<const float4*>(a.B)[b * 4 + q];
+            C4[u] = reinterpret_cast<const float4*>(a.C)[b * 4 + q];
+        }
+#pragma unroll
+        for (int u = 0; u < kItems; ++u) {
+            const float dl = softplus(dtv[u] + bias[u]);
+            const float dx = dl * xv[u];
+            float4 hn;
+            hn.x = fmaf(fast_exp2(dl * (A4[u].x * kLog2e)), s[u].x, dx * B4[u].x);
+            hn.y = fmaf(fast_exp2(dl * (A4[u].y * kLog2e)), s[u].y, dx * B4[u].y);
+            hn.z = fmaf(fast_exp2(dl * (A4[u].z * kLog2e)), s[u].z, dx * B4[u].z);
+            hn.w = fmaf(fast_exp2(dl * (A4[u].w * kLog2e)), s[u].w, dx * B4[u].w);
+            if (ok[u]) reinterpret_cast<float4*>(a.state)[row[u] * 4 + q] = hn;
+            float y = fmaf(C4[u].w, hn.w, fmaf(C4[u].z, hn.z, fmaf(C4[u].y, hn.y, C4[u].x * hn.x)));
+            y = quad_sum(y);
+            if (q == 0 && ok[u]) {
+                float o = fmaf(a.D ? a.D[d[u]] : 0.0f, xv[u], y);
+                if (HAS_Z) o *= silu(zv[u]);
+                E::store1(a.out, row[u], o);
+            }
         }
     }
 }
@@ -78,7 +98,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(DArgs a) {
 template <class E, bool HAS_Z>
 hipError_t launch_t(const DArgs& k, hipStream_t stream) {
     const int64_t threads = k.rows * 4;
-    int64_t blocks = (threads + 255) / 256;
+    int64_t blocks = (threads + 256 * kItems - 1) / (256 * kItems);
     if (blocks > (1 << 22)) blocks = 1 << 22;
     state_update_kernel<E, HAS_Z><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(k);
     return hipGetLastError();
