@@ -48,12 +48,20 @@ WORKLOAD = "mamba2p8b_bf16"
 # v_exp_f32 ~8.4 cycles, v_log_f32 / v_rcp_f32 ~12.5 cycles per wave instruction.)
 VALU_WAVE_INSTR_PER_S = 256 * 4 * 2.4e9 / 4
 
-# HBM bytes per launch of the main scan kernel on this workload, from two rocprofv3 --pmc runs
-# of `python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline` (FETCH_SIZE, then WRITE_SIZE),
-# each scaled by what the counter reads for a plain 1 GiB device copy (FETCH_SIZE x2.0,
-# WRITE_SIZE x1.0), and its VALU instructions per (b, d, t) (SQ_INSTS_VALU x 64 / B D L).
+# Memory-side bytes per launch of the main scan kernel on this workload, from rocprofv3 --pmc
+# runs of the headline alone (`python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-bwd
+# --no-conv --no-shard --no-general-a --no-decode-chain --no-configs --no-ssd`): FETCH_SIZE, then
+# WRITE_SIZE, each scaled by what the counter reads for a plain 1 GiB device copy (FETCH_SIZE x2:
+# the L2 fills whole 128-byte lines, one TCC_EA0_RDREQ each, and the counter prices a request at 64
+# bytes; WRITE_SIZE x1), and the VALU instructions per (b, d, t) (SQ_INSTS_VALU x 64 / B D L).
 # Valid only for the kernel source with this SHA-256 prefix; otherwise reported as null.
-MAIN_COUNTERS = {"src_sha256": None, "fetch_bytes": None, "write_bytes": None, "valu_per_bdt": None}
+MAIN_COUNTERS = {"src_sha256": "1c16c1d099cf6a60", "fetch_bytes": 494850048, "write_bytes": 95760998,
+                 "valu_per_bdt": 92.12}
+
+
+def progress(what):
+    """One line per finished leg on stderr (stdout carries only the JSON line)."""
+    print(f"[bench] {what} done", file=sys.stderr, flush=True)
 
 
 def kernel_source_digest():
@@ -662,23 +670,32 @@ def main():
                      "call_achieved": round(scan_gbps, 1), "call_frac": round(scan_gbps / HBM_PEAK_GBPS, 4)},
         "valu": valu,
     }
+    progress("headline steps")
     if not args.no_bwd:
         res["scan_bwd"] = backward_leg(mss, torch, sets, A, D, bias, Bt, Dn, N, L, scan_avg_ms)
+        progress("backward")
     if not args.no_conv:
         res["conv1d"] = conv_leg(mss, torch, devc, Bt, Dn, L)
+        progress("conv1d")
     if not args.no_shard:
         res["shard_fwd"] = shard_leg(mss, torch, devc, s, Bt, Dn, N, L)
+        progress("shard shapes")
     if not args.no_general_a:
         res["scan_fwd_general_A"] = general_a_leg(mss, torch, devc, Bt, Dn, N, L)
+        progress("general A")
     if not args.no_decode_chain:
         res["decode_chain"] = decode_chain(mss, torch, devc)
         res["decode_chain_hbm"] = decode_hbm_chain(mss, torch, devc)
+        progress("decode chains")
     if not args.no_configs:
         res["other_configs"] = configs_leg(mss, torch, devc)
+        progress("fp32 workloads")
     if not args.no_ssd:
         res["ssd_scan"] = ssd_leg(mss, torch, devc)
+        progress("ssd")
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(s, Bt, Dn, N, L)
+        progress("cpu baseline")
     print(json.dumps(res), flush=True)
 
 
