@@ -9,7 +9,10 @@ namespace mss {
 
 constexpr int kN = 16;      // d_state handled by the kernels
 constexpr int kRows = 64;   // channels per wavefront (one lane per channel)
-constexpr int kFastTileBytes = 64;  // bytes of each row (per array) a fast-path tile covers
+// Bytes of each row (per array) a fast-path tile covers: 64 for bf16 rows (half a 128-byte line:
+// the LDS of two wavefronts per SIMD holds no more), a whole line for fp32 rows (one wavefront per
+// SIMD leaves the LDS for it, and each line is then fetched once).
+constexpr int fast_tile_bytes(bool bf16) { return bf16 ? 64 : 128; }
 
 struct ScanLaunch {
     const void* u;

@@ -44,13 +44,13 @@
 namespace mss {
 namespace {
 
-constexpr int kNV = kFastTileBytes / 16;  // 16-byte vectors per row and array in a tile
-
 template <class E>
 struct Geo {
-    static constexpr int V = E::kPerVec;           // elements per 16 bytes
-    static constexpr int TT = kNV * V;             // steps per tile
-    static constexpr int W = kFastTileBytes / 4;   // words per row and array
+    static constexpr int V = E::kPerVec;             // elements per 16 bytes
+    static constexpr int BYTES = fast_tile_bytes(V == 8);
+    static constexpr int NV = BYTES / 16;            // 16-byte vectors per row and array in a tile
+    static constexpr int TT = NV * V;                // steps per tile
+    static constexpr int W = BYTES / 4;              // words per row and array
     static constexpr int kBCChunks = TT / 8;       // 16-byte B|C chunks per lane
     static constexpr int kRowWords = 2 * W * 64;   // u and delta, [word][lane]
 };
@@ -99,8 +99,9 @@ __device__ __forceinline__ RowSetup row_setup(const float* __restrict__ A, const
 
 // One tile of this lane's row of u and delta as loaded from HBM (plain words: an array of vector
 // structs here ends up in scratch memory).
+template <class E>
 struct RawUD {
-    uint32_t u[4 * kNV], d[4 * kNV];
+    uint32_t u[4 * Geo<E>::NV], d[4 * Geo<E>::NV];
 };
 
 // The 16-byte vector of row rp at step t.  RAGGED (rows of any length, so only element-aligned):
@@ -125,12 +126,12 @@ __device__ __forceinline__ uint4 load_vec(const typename E::storage* __restrict_
 // Vectors at or past t_end re-read the last valid vector (their steps are never used), so every
 // load is unconditional and in bounds.  RAGGED: vectors past the row's end read as zeros.
 template <class E, bool RAGGED>
-__device__ __forceinline__ void load_ud(RawUD& r, const typename E::storage* __restrict__ up,
+__device__ __forceinline__ void load_ud(RawUD<E>& r, const typename E::storage* __restrict__ up,
                                         const typename E::storage* __restrict__ dp, int64_t t0,
                                         int64_t t_end, int64_t L) {
     constexpr int V = E::kPerVec;
 #pragma unroll
-    for (int v = 0; v < kNV; ++v) {
+    for (int v = 0; v < Geo<E>::NV; ++v) {
         int64_t t = t0 + v * V;
         if (!RAGGED) t = t < t_end ? t : t_end - V;
         const uint4 a = load_vec<E, RAGGED>(up, t, L);
@@ -142,7 +143,7 @@ __device__ __forceinline__ void load_ud(RawUD& r, const typename E::storage* __r
 
 // Word-major staging: word w of lane l at srow[w * 64 + l]; delta follows u after W words.
 template <class E>
-__device__ __forceinline__ void stage_ud(uint32_t* srow, const RawUD& r) {
+__device__ __forceinline__ void stage_ud(uint32_t* srow, const RawUD<E>& r) {
     constexpr int W = Geo<E>::W;
 #pragma unroll
     for (int w = 0; w < W; ++w) {
@@ -338,7 +339,8 @@ __device__ __forceinline__ void main_body(
     const uint32_t* su = srow;
     const uint32_t* sd = srow + W * 64;
     float* const srow_saved = SAVE ? saved + rs.row * 4 : nullptr;  // this lane's float4 in each plane
-    RawUD pre;
+    constexpr int kNV = G::NV;
+    RawUD<E> pre;
     RawBC<E> bpre;
     load_ud<E, RAGGED>(pre, up, dp, t_begin, t_end, L);
     load_bc<E, true, RAGGED>(bpre, Bb, Cb, L, t_begin, t_end);
@@ -596,7 +598,7 @@ __device__ __forceinline__ void agg_body(const RowSetup& rs, const typename E::s
     for (int n = 0; n < kN; ++n) acc[n] = 0.0f;
     dsum = 0.0f;
     float Rp = 1.0f;
-    RawUD pre;
+    RawUD<E> pre;
     RawBC<E> bpre;
     const int64_t ntiles = (t_end - t_begin + TT - 1) / TT;
     // tiles in visiting order (POW: from the last tile of the segment back to the first)
@@ -772,17 +774,22 @@ hipError_t launch_fast_e(const ScanLaunch& a, const ScanPlan& p, float* ws, hipS
 // 226 us at two per SIMD, 259 us at three, 239 / 250 us at 1.9 / 2.25 (uneven SIMD loads);
 // Mamba-130M fp32 layer 203 us at one per SIMD, 218 us at 1.5, 233 us at 2; long context 1341 us at
 // one, 1359 at 1.5 -- more streams in flight evict more of each other's lines.  At least two tiles
-// each (a shorter piece spends more on folding the aggregates before it than it saves).  `waves_override` > 0 replaces the count (tests use it to force many or few
+// each (a shorter piece spends more on folding the aggregates before it than it saves), except on
+// short rows.  fp32 tiles are whole 128-byte lines (long context 1.45 -> 1.29 ms against 64-byte
+// tiles, which fetched every line twice).  `waves_override` > 0 replaces the count (tests use it to force many or few
 // pieces per group, and ranges that cross groups).  `segments` reports whether some range ends
 // inside a group, i.e. whether the aggregate kernel has work.
 ScanPlan plan_fast(const ScanLaunch& a, int num_cus, int64_t waves_override) {
     ScanPlan p;
-    const int TT = kFastTileBytes / (a.bf16 ? 2 : 4);
+    const int TT = fast_tile_bytes(a.bf16) / (a.bf16 ? 2 : 4);
     const int64_t groups = a.Bt * ((a.Dn + 63) / 64);
     const int64_t tiles = (a.L + TT - 1) / TT;
     const int64_t GT = groups * tiles;
     int64_t W = (a.bf16 ? 8LL : 4LL) * (num_cus > 0 ? num_cus : 256);
-    if (W > GT / 2) W = GT / 2;
+    // pieces of at least two tiles, unless the rows are short (under 16 tiles): then parallelism
+    // matters more than the fold (2 x 64 x 256 fp32: 33 -> 22 us with one-tile pieces)
+    const int64_t min_piece = tiles >= 16 ? 2 : 1;
+    if (W > GT / min_piece) W = GT / min_piece;
     if (waves_override > 0) W = waves_override;
     if (W > GT) W = GT;
     if (W > 0x7fffffffLL) W = 0x7fffffffLL;
