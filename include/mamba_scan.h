@@ -344,7 +344,7 @@ int mss_profile_enable(int on);
 int mss_profile_fwd(int* calls, double* carry_ms, double* main_ms);
 
 /*
- * Mamba-2's SSD layer (the upstream README's Mamba-2 block, d_state "typically 64 or 128"): the
+ * Mamba-2's SSD layer (the upstream README's Mamba-2 block, whose state size is usually 64 or 128): the
  * selective recurrence above with Mamba-2's tied parameters, for every batch b, head h (P
  * channels p) and state n:
  *     delta_t   = softplus(dt[b, t, h] + dt_bias[h])               (or without softplus)

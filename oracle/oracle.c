@@ -354,8 +354,8 @@ int oracle_state_update(int64_t R, int64_t N, int64_t Bt, const int64_t* row_bat
 }
 
 /*
- * Mamba-2's SSD layer (the upstream README's Mamba-2 block: d_state "typically 64 or 128", and
- * its pointer to a minimal SSD module; the pages give no equations for it).  Reading: the same
+ * Mamba-2's SSD layer (the upstream README's Mamba-2 block, whose state size is usually 64 or 128,
+ * and its pointer to a minimal SSD module; the pages give no equations for it).  Reading: the same
  * selective recurrence as oracle_selective_scan with Mamba-2's tied parameters --
  *   - heads h of P channels each; the head's A is one scalar A[h], the same for every channel p
  *     and every state n;

@@ -167,8 +167,8 @@ def decode_inputs(batch: int, d_inner: int, d_state: int, steps: int, dtype: str
     return DecodeInputs(x=xs, dt=dts, z=zs, B=Bs, C=Cs, A=A, D=D, dt_bias=bias, dtype=dtype)
 
 
-# Mamba-2 SSD layer workloads (the upstream README's Mamba-2 block: d_state 64, "typically 64 or
-# 128"; d_model 2560 with expand 2 as for the 2.8B / 2.7B models gives d_inner 5120, here as 80 heads
+# Mamba-2 SSD layer workloads (the upstream README's Mamba-2 block: state size 64 by default, 64 or
+# 128 in use; d_model 2560 with expand 2 as for the 2.8B / 2.7B models gives d_inner 5120, here as 80 heads
 # of 64 channels; one group of B / C).  Layout (batch, L, heads, headdim).
 SSD_CONFIGS = {
     "ssd_tiny": dict(batch=2, L=256, heads=4, headdim=64, groups=1, d_state=64, dtype="bf16", with_z=True),
