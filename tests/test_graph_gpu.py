@@ -202,3 +202,50 @@ def test_concurrent_streams_have_separate_workspaces(mss):
         for k in range(2):
             for n, v in alone[k].items():
                 assert torch.equal(res[k][n], v), (rep, k, n)
+
+
+def test_ssd_graph_replays_match_eager(mss):
+    """Mamba-2's SSD layer (segment split: its segment states pass through the workspace) captured
+    after a warm-up on the capture stream: every replay, with new inputs copied in, equals the eager
+    call on those inputs bit for bit."""
+    import torch
+    from synth import ssd_inputs
+
+    def inputs(seed):
+        s = ssd_inputs(2, 700, 4, 64, 2, 64, dtype="bf16", with_z=True, seed=seed)
+        return dict(x=dev(s.x, "bf16"), dt=dev(s.dt, "bf16"), z=dev(s.z, "bf16"), B=dev(s.B, "bf16"),
+                    C=dev(s.C, "bf16")), dict(A=dev(s.A), D=dev(s.D), bias=dev(s.dt_bias))
+
+    x, p = inputs(80)
+    out = torch.empty_like(x["x"])
+    last = torch.empty((2, 4, 64, 64), dtype=torch.float32, device="cuda")
+
+    def body():
+        mss.ssd_scan_fwd(x["x"], x["dt"], p["A"], x["B"], x["C"], D=p["D"], z=x["z"], dt_bias=p["bias"],
+                         out=out, last_state=last)
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        body()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        body()
+    torch.cuda.synchronize()
+    prev = None
+    for rep in range(3):
+        nx, _ = inputs(81 + rep)
+        for k in x:
+            x[k].copy_(nx[k])
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            body()
+        torch.cuda.synchronize()
+        eager = (out.clone(), last.clone())
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(eager[0], out) and torch.equal(eager[1], last), rep
+        if prev is not None:
+            assert not torch.equal(prev, out)
+        prev = out.clone()
