@@ -55,7 +55,7 @@ VALU_WAVE_INSTR_PER_S = 256 * 4 * 2.4e9 / 4
 # the L2 fills whole 128-byte lines, one TCC_EA0_RDREQ each, and the counter prices a request at 64
 # bytes; WRITE_SIZE x1), and the VALU instructions per (b, d, t) (SQ_INSTS_VALU x 64 / B D L).
 # Valid only for the kernel source with this SHA-256 prefix; otherwise reported as null.
-MAIN_COUNTERS = {"src_sha256": "1c16c1d099cf6a60", "fetch_bytes": 494850048, "write_bytes": 95760998,
+MAIN_COUNTERS = {"src_sha256": "a57803b6a94eabc8", "fetch_bytes": 496183296, "write_bytes": 96316006,
                  "valu_per_bdt": 92.12}
 
 
