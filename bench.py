@@ -135,15 +135,17 @@ def single_thread_130m(rows=1536):
     return {"state_updates_per_s": n / wall, "rows": rows, "L": c["L"], "wall_s": round(wall, 3)}
 
 
-def decode_hbm_chain(mss, torch, devc, steps=1024, states=16, pool=64):
-    """Chained one-token updates of `states` distinct (64, 5120, 16) fp32 states in turn (one per
-    layer of a model, as generation steps a whole stack), 16 x 21 MB = 336 MB: more than the 256 MB
-    Infinity Cache, so every step reads and writes its state in HBM.  Timed as replays of a
-    captured HIP graph of `pool` steps (inputs cycle through `pool` resident sets)."""
+def decode_hbm_chain(mss, torch, devc, steps=1024, states=16, pool=64, N=None):
+    """Chained one-token updates of `states` distinct (64, 5120, N) fp32 states in turn (one per
+    layer of a model, as generation steps a whole stack); at N = 16, 16 x 21 MB = 336 MB, at
+    N = 128, 4 x 168 MB: more than the 256 MB Infinity Cache, so every step reads and writes its
+    state in HBM.  Timed as replays of a captured HIP graph of `pool` steps (inputs cycle through
+    `pool` resident sets)."""
     import numpy as np
     from synth import CONFIGS, decode_inputs
     c = CONFIGS["decode_bf16"]
-    Bt, Dn, N = c["batch"], c["d_inner"], c["d_state"]
+    Bt, Dn = c["batch"], c["d_inner"]
+    N = N or c["d_state"]
     d = decode_inputs(Bt, Dn, N, pool, dtype="bf16", with_z=True, seed=0)
     up = lambda a, bf=False: (torch.from_numpy(np.ascontiguousarray(a)).to(devc).to(torch.bfloat16)
                               if bf else torch.from_numpy(np.ascontiguousarray(a)).to(devc))
@@ -184,7 +186,8 @@ def decode_hbm_chain(mss, torch, devc, steps=1024, states=16, pool=64):
     return {"shape": [Bt, Dn, N], "distinct_states": states, "state_bytes_total": states * Bt * Dn * N * 4,
             "steps": reps * pool, "graph_us_per_step": round(us, 3), "graph_gbps": round(gbps, 1),
             "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
-            "note": "each step's state is one of 16 (336 MB in all, above the 256 MB Infinity Cache): HBM-resident"}
+            "note": f"each step's state is one of {states} ({states * Bt * Dn * N * 4 / 1e6:.0f} MB in all, above "
+                    "the 256 MB Infinity Cache): HBM-resident"}
 
 
 def general_a_leg(mss, torch, devc, Bt, Dn, N, L, calls=20, warmup=3, copies=2):
@@ -686,6 +689,7 @@ def main():
     if not args.no_decode_chain:
         res["decode_chain"] = decode_chain(mss, torch, devc)
         res["decode_chain_hbm"] = decode_hbm_chain(mss, torch, devc)
+        res["decode_chain_hbm_n128"] = decode_hbm_chain(mss, torch, devc, states=4, N=128)
         progress("decode chains")
     if not args.no_configs:
         res["other_configs"] = configs_leg(mss, torch, devc)

@@ -60,7 +60,7 @@ typedef enum {
     MSS_ERR_DTYPE = -3,       /* dtype not allowed for that argument                         */
     MSS_ERR_LAYOUT = -4,      /* not dense row-major, or misaligned data pointer             */
     MSS_ERR_ALIAS = -5,       /* an output overlaps an input or another output               */
-    MSS_ERR_UNSUPPORTED = -6, /* valid but not implemented (d_state not 16, sizes too large) */
+    MSS_ERR_UNSUPPORTED = -6, /* valid but not implemented (that d_state, sizes too large)    */
     MSS_ERR_HIP = -7          /* the HIP runtime reported an error while queuing the work    */
 } mss_status_t;
 
@@ -280,8 +280,8 @@ int mss_selective_scan_bwd_saved(const mss_tensor_t* u, const mss_tensor_t* delt
  *   z           (batch, d_inner)         dtype of x, nullable
  *   dt_bias     (d_inner,)               f32, nullable
  *   out         (batch, d_inner)         dtype of x, written
- * d_state must be 16.  out must not overlap any input or the state; the state must not
- * overlap any input.  state, A, B and C must be 16-byte aligned (MSS_ERR_LAYOUT otherwise).
+ * d_state must be 16, 32, 64 or 128.  out must not overlap any input or the state; the state
+ * must not overlap any input.  state, A, B and C must be 16-byte aligned (MSS_ERR_LAYOUT otherwise).
  */
 int mss_selective_state_update(const mss_tensor_t* state, const mss_tensor_t* x,
                                const mss_tensor_t* dt, const mss_tensor_t* A,

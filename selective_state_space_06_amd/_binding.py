@@ -560,8 +560,9 @@ def selective_scan_fwd_with_state(u, delta, A, B, C, initial_state, D=None, z=No
 
 
 def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None):
-    """One decode step on the current stream; `state` (batch, d_inner, 16) float32 is updated
-    in place.  x, dt, z: (batch, d_inner) float32 or bfloat16; B, C: (batch, 16) float32.
+    """One decode step on the current stream; `state` (batch, d_inner, d_state) float32 is updated
+    in place, d_state 16, 32, 64 or 128.  x, dt, z: (batch, d_inner) float32 or bfloat16; B, C:
+    (batch, d_state) float32.
     Returns out (batch, d_inner) in x's dtype."""
     import torch
     if out is None:

@@ -288,7 +288,7 @@ int validate_decode(const mss_tensor_t* state, const mss_tensor_t* x, const mss_
     }
     if (overlap(out, state)) return MSS_ERR_ALIAS;
 
-    if (N != kN) return MSS_ERR_UNSUPPORTED;
+    if (N != 16 && N != 32 && N != 64 && N != 128) return MSS_ERR_UNSUPPORTED;
     return MSS_OK;
 }
 
@@ -953,7 +953,7 @@ int mss_selective_state_update(const mss_tensor_t* state, const mss_tensor_t* x,
         a.D = D ? static_cast<const float*>(D->data) : nullptr;
         a.bias = dt_bias ? static_cast<const float*>(dt_bias->data) : nullptr;
         a.out = out->data;
-        a.Bt = state->shape[0]; a.Dn = state->shape[1];
+        a.Bt = state->shape[0]; a.Dn = state->shape[1]; a.N = static_cast<int>(state->shape[2]);
         a.bf16 = x->dtype == MSS_BF16;
         if (a.Bt * a.Dn == 0) return MSS_OK;
         return mss::launch_state_update(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MSS_OK

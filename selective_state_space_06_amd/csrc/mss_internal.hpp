@@ -54,6 +54,7 @@ struct DecodeLaunch {
     const float* bias;      // nullable
     void* out;
     int64_t Bt, Dn;
+    int N;                  // d_state: 16, 32, 64 or 128
     bool bf16;
 };
 

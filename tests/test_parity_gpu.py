@@ -172,6 +172,36 @@ def test_decode_row_counts(mss, orc, Bt, Dn, dtype, with_z, a_kind):
         assert_close(host64(state).reshape(Bt * Dn, 16), ref_state, what=f"decode state step {s}", **TOL_F32)
 
 
+@pytest.mark.parametrize("Bt,Dn,N,dtype,with_z,a_kind", [
+    (1, 1, 32, "f32", True, "s4d"), (3, 130, 32, "bf16", True, "random"), (1, 3, 64, "bf16", True, "s4d"),
+    (7, 333, 64, "f32", True, "random"), (5, 7, 128, "f32", False, "random"), (129, 64, 128, "bf16", True, "s4d"),
+    (2, 5120, 128, "bf16", False, "s4d")])
+def test_decode_state_sizes(mss, orc, Bt, Dn, N, dtype, with_z, a_kind):
+    """d_state 32, 64 and 128 (a lane holds N / 4 states of its row): every row of three chained
+    steps, state and out, against the oracle, with partial wavefronts and the 2.8B-wide d_inner."""
+    import torch
+    steps = 3
+    di = decode_inputs(Bt, Dn, N, steps, dtype=dtype, with_z=with_z, seed=Bt * 1000 + Dn + N, a_kind=a_kind)
+    state0 = (0.5 * np.random.default_rng(Bt + Dn + N).standard_normal((Bt, Dn, N))).astype(np.float32)
+    state = dev(state0)
+    A, D, bias = dev(di.A), dev(di.D), dev(di.dt_bias)
+    ref_state = state0.astype(np.float64).reshape(Bt * Dn, N).copy()
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    for s in range(steps):
+        z = dev(di.z[s], dtype) if with_z else None
+        out = mss.selective_state_update(state, dev(di.x[s], dtype), dev(di.dt[s], dtype), A,
+                                         dev(di.B[s]), dev(di.C[s]), D=D, z=z, dt_bias=bias)
+        torch.cuda.synchronize()
+        ref = orc.selective_state_update(ref_state, di.x[s], di.dt[s], di.A, di.B[s], di.C[s], D=di.D,
+                                         z=di.z[s] if with_z else None, dt_bias=di.dt_bias,
+                                         rows=np.arange(Bt * Dn))
+        record_margin(f"decode N={N} {Bt}x{Dn} out",
+                      assert_close(host64(out).reshape(-1), ref.reshape(-1), what=f"decode N={N} out step {s}", **tol))
+        record_margin(f"decode N={N} {Bt}x{Dn} state",
+                      assert_close(host64(state).reshape(Bt * Dn, N), ref_state, what=f"decode N={N} state step {s}",
+                                   **TOL_F32))
+
+
 # ------------------------------------------------------------------ shapes and flags
 
 @pytest.mark.parametrize("Bt,Dn,L,dtype", [
