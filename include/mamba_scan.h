@@ -84,8 +84,10 @@ typedef struct {
  *   softplus_flag  nonzero: delta = softplus(delta_raw + bias); zero: delta_raw + bias
  *   out         (batch, d_inner, L)      dtype of u, written
  *   last_state  (batch, d_inner, d_state) f32, nullable; written with h_L (zeros if L = 0)
- * d_state must be 16.  out must not overlap any input or last_state.  A and last_state must
- * be 16-byte aligned (MSS_ERR_LAYOUT otherwise).  When every row of u / delta / z / out spans
+ * d_state is 16, 32, 64 or 128 (MSS_ERR_UNSUPPORTED otherwise; 16 runs the fast kernels, the
+ * others the general ones, where d_state / 16 neighbouring lanes share a channel).  out must not
+ * overlap any input or last_state.  A and last_state must be 16-byte aligned
+ * (MSS_ERR_LAYOUT otherwise).  When every row of u / delta / z / out spans
  * a multiple of 16 bytes and those tensors and B / C start 16-byte aligned, the vectorised
  * kernels run with aligned 16-byte accesses; any other valid layout runs the same kernels with
  * element-aligned accesses (about 1.5x the time on the Mamba-2.8B layer shape).
@@ -153,6 +155,7 @@ int mss_selective_scan_fwd_varlen(const mss_tensor_t* u, const mss_tensor_t* del
  *     mss_set_plan_overrides beyond it returns MSS_ERR_UNSUPPORTED before any HIP call.  So do
  *     problems of 2^32 or more (64-channel group, time tile) pairs, which the other forward
  *     entry points hand to kernels that need row-sized scratch.
+ *   - d_state must be 16 (MSS_ERR_UNSUPPORTED otherwise).
  *   - Every call on one GPU shares that GPU's array (nothing in it needs to start at zero; a
  *     call leaves its own aggregates behind): calls that overlap in time on one GPU (on two
  *     streams, or two host threads) race and may give wrong results.  Order them on one stream.
@@ -233,7 +236,8 @@ int mss_selective_scan_bwd_varlen(const mss_tensor_t* u, const mss_tensor_t* del
  *                 16-byte aligned; may not overlap any input or output (MSS_ERR_ALIAS).
  *                 NULL: exactly mss_selective_scan_fwd_varlen.
  * Costs 64 / 8 = 8 bytes of extra writes per (batch, d_inner, step).  Every other argument as
- * for mss_selective_scan_fwd_varlen; out and last_state are bit-identical to it.
+ * for mss_selective_scan_fwd_varlen; out and last_state are bit-identical to it.  With
+ * saved_states given, d_state must be 16 (the backward's; MSS_ERR_UNSUPPORTED otherwise).
  */
 int mss_selective_scan_fwd_save(const mss_tensor_t* u, const mss_tensor_t* delta,
                                 const mss_tensor_t* A, const mss_tensor_t* B,

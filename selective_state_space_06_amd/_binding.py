@@ -308,9 +308,10 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
                        return_last_state=True, out=None, last_state=None):
     """Forward selective scan on the current stream of u's device.
 
-    u, delta, z: (batch, d_inner, L) float32 or bfloat16; A: (d_inner, 16) float32;
-    B, C: (batch, 16, L) float32; D, delta_bias: (d_inner,) float32.
-    Returns out (dtype of u), or (out, last_state) with last_state (batch, d_inner, 16) float32.
+    u, delta, z: (batch, d_inner, L) float32 or bfloat16; A: (d_inner, d_state) float32;
+    B, C: (batch, d_state, L) float32; D, delta_bias: (d_inner,) float32; d_state 16, 32, 64 or
+    128.  Returns out (dtype of u), or (out, last_state) with last_state (batch, d_inner, d_state)
+    float32.
     """
     import torch
     if out is None:
@@ -539,7 +540,7 @@ def saved_state_blocks(saved_states):
 
 def selective_scan_fwd_with_state(u, delta, A, B, C, initial_state, D=None, z=None,
                                   delta_bias=None, delta_softplus=True, out=None, last_state=None):
-    """Forward selective scan continued from `initial_state` (batch, d_inner, 16) float32
+    """Forward selective scan continued from `initial_state` (batch, d_inner, d_state) float32
     (None: from zeros).  Other arguments as selective_scan_fwd; returns (out, last_state).
     last_state must be a different buffer from initial_state."""
     import torch

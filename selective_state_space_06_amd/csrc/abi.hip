@@ -242,7 +242,7 @@ int validate_fwd(const mss_tensor_t* u, const mss_tensor_t* delta, const mss_ten
     }
     if (last && overlap(out, last)) return MSS_ERR_ALIAS;
 
-    if (N != kN) return MSS_ERR_UNSUPPORTED;
+    if (N != 16 && N != 32 && N != 64 && N != 128) return MSS_ERR_UNSUPPORTED;
     if (Bt > 65535) return MSS_ERR_UNSUPPORTED;
     return MSS_OK;
 }
@@ -480,6 +480,7 @@ int mss_selective_scan_fwd_save(const mss_tensor_t* u, const mss_tensor_t* delta
         int st = validate_fwd(u, delta, A, B, C, D, z, delta_bias, initial_state, out, last_state);
         if (st != MSS_OK) return st;
         if (saved_states) {
+            if (A->shape[1] != kN) return MSS_ERR_UNSUPPORTED;  // the backward that reads them is d_state 16
             st = check_saved(saved_states, u, A->shape[1]);
             if (st != MSS_OK) return st;
             for (const mss_tensor_t* t : {u, delta, A, B, C, D, z, delta_bias, initial_state, seq_lens, out,
@@ -506,7 +507,7 @@ int mss_selective_scan_fwd_save(const mss_tensor_t* u, const mss_tensor_t* delta
         a.h0 = initial_state ? static_cast<const float*>(initial_state->data) : nullptr;
         a.lens = (seq_lens && numel(*seq_lens) > 0) ? static_cast<const int32_t*>(seq_lens->data) : nullptr;
         a.saved = (saved_states && numel(*saved_states) > 0) ? static_cast<float*>(saved_states->data) : nullptr;
-        a.Bt = u->shape[0]; a.Dn = u->shape[1]; a.L = u->shape[2];
+        a.Bt = u->shape[0]; a.Dn = u->shape[1]; a.L = u->shape[2]; a.N = static_cast<int>(A->shape[1]);
         a.softplus = softplus_flag ? 1 : 0;
         a.bf16 = u->dtype == MSS_BF16;
         const size_t es = elem_size(u->dtype);
@@ -519,9 +520,10 @@ int mss_selective_scan_fwd_save(const mss_tensor_t* u, const mss_tensor_t* delta
         int dev = 0, cus = 0;
         if (hipGetDevice(&dev) != hipSuccess) return MSS_ERR_HIP;
         if (device_cus(dev, &cus) != hipSuccess) return MSS_ERR_HIP;
-        // the fast path takes every length (rows that are not whole 16-byte vectors run its
-        // element-aligned variant); the generic kernels run for L = 0 and when a test forces them
-        bool fast = a.L > 0 && (a.saved || g_force_generic.load() == 0);
+        // the fast path takes every length at d_state 16 (rows that are not whole 16-byte vectors
+        // run its element-aligned variant); the generic kernels run for L = 0, for d_state 32, 64
+        // and 128, and when a test forces them
+        bool fast = a.L > 0 && a.N == kN && (a.saved || g_force_generic.load() == 0);
         mss::ScanPlan plan;
         if (fast) {
             plan = mss::plan_fast(a, cus, g_fast_waves.load());
@@ -574,6 +576,7 @@ int mss_selective_scan_fwd_noalloc(const mss_tensor_t* u, const mss_tensor_t* de
     try {
         const int st = validate_fwd(u, delta, A, B, C, D, z, delta_bias, nullptr, out, last_state);
         if (st != MSS_OK) return st;
+        if (A->shape[1] != kN) return MSS_ERR_UNSUPPORTED;  // the fast kernels only: d_state 16
         // a forced wavefront count whose aggregates cannot fit: refused before any HIP call
         const int64_t forced = g_fast_waves.load();
         const size_t slot_bytes = (kN + 1) * 64 * sizeof(float);

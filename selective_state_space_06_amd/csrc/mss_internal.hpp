@@ -29,6 +29,7 @@ struct ScanLaunch {
     const int32_t* lens;    // nullable: per-batch sequence lengths (device), clamped to [0, L]
     float* saved;           // nullable: the state entering every 8-step tile, [ceil(L/8)][N][Bt*Dn]
     int64_t Bt, Dn, L;
+    int N = 16;             // d_state: 16 (fast and general kernels), 32, 64 or 128 (general kernels)
     int softplus;
     bool bf16;              // storage type of u / delta / z / out
     bool vec_ok;            // rows of u / delta / z / out are 16-byte aligned

@@ -165,9 +165,19 @@ def test_fwd_huge_or_negative_extents(lib):
     assert call_fwd(a) == SHAPE
 
 
-def test_fwd_unsupported_dstate(lib):
-    a = fwd_args(n=8)
+@pytest.mark.parametrize("n", [8, 24, 48, 96, 256])
+def test_fwd_unsupported_dstate(lib, n):
+    """d_state 16, 32, 64 and 128 are the forward's; any other is refused before any HIP call."""
+    a = fwd_args(n=n)
     assert call_fwd(a) == UNSUPPORTED
+
+
+def test_noalloc_and_saving_forward_refuse_other_dstate(lib):
+    """The fixed-scratch forward and the state-saving forward run the d_state 16 kernels only."""
+    a = fwd_args(n=64)
+    assert mss.scan_fwd_noalloc_raw(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["delta_bias"],
+                                    a["softplus_flag"], a["out"], a["last_state"], a["stream"]) == UNSUPPORTED
+    assert call_fwd_save(fwd_args(n=64), saved_desc(n=64)) == UNSUPPORTED
 
 
 def test_fwd_empty_batch_is_ok(lib):
