@@ -61,14 +61,17 @@ struct KArgs {
     int softplus;
 };
 
-// Shape of one wavefront's work for d_state N: Q lanes per channel, CH channels, TT-step tiles
-// (16 at N = 128, which keeps the B / C tile at 16.6 KB of LDS).
+// Shape of the work for d_state N: Q lanes per channel, CH channels per wavefront, TT-step tiles,
+// WPB wavefronts per workgroup.  At d_state 64 and 128 four wavefronts (consecutive channel
+// groups of one batch) share each tile's B | C in LDS: a quarter of the staging each, and a
+// quarter of the LDS, which leaves room for three wavefronts per SIMD.
 template <int N>
 struct Shape {
     static_assert(N == 16 || N == 32 || N == 64 || N == 128, "d_state");
     static constexpr int Q = N / 16;
     static constexpr int CH = kRows / Q;
-    static constexpr int TT = N == 128 ? 16 : 32;
+    static constexpr int TT = 32;
+    static constexpr int WPB = N >= 64 ? 4 : 1;
 };
 
 // Word of entry m of a step's B | C row in LDS (m = n for B_n, N + n for C_n): four pad words
@@ -82,11 +85,14 @@ struct Smem {
     static constexpr int TT = Shape<N>::TT;
     static constexpr int kRowStride = TT + 4;   // 16-byte pad: lane-row 16 B reads hit distinct banks
     static constexpr int kBCStride = bc_word(2 * N) + 4;
-    float dl[CH][kRowStride];  // delta (phase A) then y (phase B)
-    float x[CH][kRowStride];   // delta * u
-    float bc[TT][kBCStride];   // B[0..N-1] | C[0..N-1] per time step, at bc_word positions
-    float bias[CH];
-    float dsk[CH];
+    struct Wave {                  // one wavefront's channels
+        float dl[CH][kRowStride];  // delta (phase A) then y (phase B)
+        float x[CH][kRowStride];   // delta * u
+        float bias[CH];
+        float dsk[CH];
+    };
+    Wave w[Shape<N>::WPB];
+    float bc[TT][kBCStride];       // B[0..N-1] | C[0..N-1] per time step, at bc_word positions (shared)
 };
 
 // One time step of one lane: its 16 state updates and (main pass) their part of C.h.  A2 holds
@@ -150,14 +156,16 @@ struct Geo {
     static constexpr int BCHUNK = TT / 4;         // lanes per B / C row (four steps each)
     static constexpr int BROWS = kRows / BCHUNK;  // B / C rows per pass
     static constexpr int BPASS = (2 * N) / BROWS; // passes over the 2N rows of B | C
+    static constexpr int BPW = BPASS / Shape<N>::WPB;  // of them, each wavefront's
     static_assert(TT % V == 0 && kRows % CPR == 0 && (CH % RPI == 0 || ITERS == 1), "tile shape");
+    static_assert(BPASS % Shape<N>::WPB == 0, "B | C passes per wavefront");
 };
 
 // One tile's inputs in registers: u, delta, z in the coalesced layout and the B | C chunks.
 template <class E, int N>
 struct TileIn {
     uint4 u[Geo<E, N>::ITERS], d[Geo<E, N>::ITERS], z[Geo<E, N>::ITERS];
-    float4 bc[Geo<E, N>::BPASS];
+    float4 bc[Geo<E, N>::BPW];  // this wavefront's share of the B | C tile
 };
 
 // Issues every load of the tile starting at t0, at clamped addresses (row min(d, Dn - 1), step
@@ -165,8 +173,8 @@ struct TileIn {
 // outside the tile's valid part are masked by the consumers.  (A load behind a branch would be
 // waited for before the next one is issued.)
 template <class E, bool VEC, bool WANT_Z, int N>
-__device__ __forceinline__ void load_tile(const KArgs& a, TileIn<E, N>& in, const int lane, const int b,
-                                          const int64_t d0, const int64_t t0) {
+__device__ __forceinline__ void load_tile(const KArgs& a, TileIn<E, N>& in, const int lane, const int wave,
+                                          const int b, const int64_t d0, const int64_t t0) {
     using G = Geo<E, N>;
     constexpr int V = G::V;
     const int64_t L = a.L, Dn = a.Dn;
@@ -198,17 +206,17 @@ __device__ __forceinline__ void load_tile(const KArgs& a, TileIn<E, N>& in, cons
     }
     const int tlb = (lane % G::BCHUNK) * 4;
 #pragma unroll
-    for (int it = 0; it < G::BPASS; ++it) {
-        const int rr = it * G::BROWS + lane / G::BCHUNK;
+    for (int i = 0; i < G::BPW; ++i) {
+        const int rr = (wave * G::BPW + i) * G::BROWS + lane / G::BCHUNK;
         const float* src = (rr < N ? a.B : a.C) + ((int64_t)b * N + (rr % N)) * L;
         if (VEC) {
             const int64_t tv = t0 + tlb <= L - 4 ? t0 + tlb : L - 4;  // L is a multiple of 4 here
-            in.bc[it] = *reinterpret_cast<const float4*>(src + tv);
+            in.bc[i] = *reinterpret_cast<const float4*>(src + tv);
         } else {
             float v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = src[t0 + tlb + e < L ? t0 + tlb + e : L - 1];
-            in.bc[it] = make_float4(v[0], v[1], v[2], v[3]);
+            in.bc[i] = make_float4(v[0], v[1], v[2], v[3]);
         }
     }
 }
@@ -218,7 +226,9 @@ __device__ __forceinline__ void load_tile(const KArgs& a, TileIn<E, N>& in, cons
 // become identity updates (delta = 0, x = 0, B = C = 0, whatever the padding holds).
 template <class E, int N>
 __device__ __forceinline__ void stage_tile(const KArgs& a, Smem<N>& sm, const TileIn<E, N>& in, const int lane,
-                                           const int64_t d0, const int64_t t0, const int tvalid, const int64_t stop) {
+                                           const int wave, const int64_t d0, const int64_t t0, const int tvalid,
+                                           const int64_t stop) {
+    auto& w = sm.w[wave];
     using G = Geo<E, N>;
     constexpr int V = G::V;
 #pragma unroll
@@ -230,7 +240,7 @@ __device__ __forceinline__ void stage_tile(const KArgs& a, Smem<N>& sm, const Ti
         float uv[V], dv[V];
         E::unpack(in.u[it], uv);
         E::unpack(in.d[it], dv);
-        const float br = sm.bias[r];
+        const float br = w.bias[r];
         float dl[V], xv[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) {
@@ -242,17 +252,17 @@ __device__ __forceinline__ void stage_tile(const KArgs& a, Smem<N>& sm, const Ti
         }
 #pragma unroll
         for (int q = 0; q < V / 4; ++q) {
-            *reinterpret_cast<float4*>(&sm.dl[r][tl + 4 * q]) =
+            *reinterpret_cast<float4*>(&w.dl[r][tl + 4 * q]) =
                 make_float4(dl[4 * q], dl[4 * q + 1], dl[4 * q + 2], dl[4 * q + 3]);
-            *reinterpret_cast<float4*>(&sm.x[r][tl + 4 * q]) =
+            *reinterpret_cast<float4*>(&w.x[r][tl + 4 * q]) =
                 make_float4(xv[4 * q], xv[4 * q + 1], xv[4 * q + 2], xv[4 * q + 3]);
         }
     }
     const int tlb = (lane % G::BCHUNK) * 4;
 #pragma unroll
-    for (int it = 0; it < G::BPASS; ++it) {
-        const int rr = it * G::BROWS + lane / G::BCHUNK;
-        const float v[4] = {in.bc[it].x, in.bc[it].y, in.bc[it].z, in.bc[it].w};
+    for (int i = 0; i < G::BPW; ++i) {
+        const int rr = (wave * G::BPW + i) * G::BROWS + lane / G::BCHUNK;
+        const float v[4] = {in.bc[i].x, in.bc[i].y, in.bc[i].z, in.bc[i].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             sm.bc[tlb + e][bc_word(rr)] = (tlb + e < tvalid && t0 + tlb + e < stop) ? v[e] : 0.0f;
@@ -260,7 +270,7 @@ __device__ __forceinline__ void stage_tile(const KArgs& a, Smem<N>& sm, const Ti
 }
 
 template <class E, bool VEC, bool HAS_Z, int MODE, bool POW, int N>
-__device__ __forceinline__ void scan_body(const KArgs& a, Smem<N>& sm, const int lane, const int b,
+__device__ __forceinline__ void scan_body(const KArgs& a, Smem<N>& sm, const int lane, const int wave, const int b,
                                           const int64_t d0, const int64_t row, const bool active,
                                           const float (&A2)[16], const float A2b, float (&h)[16],
                                           const int64_t t_begin, const int64_t t_end, const int64_t stop) {
@@ -277,6 +287,7 @@ __device__ __forceinline__ void scan_body(const KArgs& a, Smem<N>& sm, const int
     const int rl = lane / G::CPR;        // row offset of this lane within a pass
     const int c = lane / Q;              // this lane's channel within the wave (phase B)
     const int k = lane % Q;              // its block of 16 states
+    auto& w = sm.w[wave];
     float dsum = 0.0f;
 
     // (Issuing the next tile's loads before the recurrence, to hide their latency, measured no
@@ -285,14 +296,14 @@ __device__ __forceinline__ void scan_body(const KArgs& a, Smem<N>& sm, const int
         const int tvalid = static_cast<int>(t_end - t0 < TT ? t_end - t0 : TT);
         __syncthreads();  // the previous tile's readers of sm are done
         TileIn<E, N> in;
-        load_tile<E, VEC, WANT_Z, N>(a, in, lane, b, d0, t0);
-        stage_tile<E, N>(a, sm, in, lane, d0, t0, tvalid, stop);
+        load_tile<E, VEC, WANT_Z, N>(a, in, lane, wave, b, d0, t0);
+        stage_tile<E, N>(a, sm, in, lane, wave, d0, t0, tvalid, stop);
         __syncthreads();
 
         // ---- phase B: the recurrence, lane = (channel, block of 16 states), sequential over the tile
         for (int tc = 0; tc < tvalid; tc += 4) {
-            const float4 dl4 = *reinterpret_cast<const float4*>(&sm.dl[c][tc]);
-            const float4 x4 = *reinterpret_cast<const float4*>(&sm.x[c][tc]);
+            const float4 dl4 = *reinterpret_cast<const float4*>(&w.dl[c][tc]);
+            const float4 x4 = *reinterpret_cast<const float4*>(&w.x[c][tc]);
             const float dlv[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
             const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
             float yv[4];
@@ -306,7 +317,7 @@ __device__ __forceinline__ void scan_body(const KArgs& a, Smem<N>& sm, const int
 #pragma unroll
                 for (int j = 0; j < 4; ++j) yv[j] = group_sum<Q>(yv[j]);
                 if (k == 0)
-                    *reinterpret_cast<float4*>(&sm.dl[c][tc]) = make_float4(yv[0], yv[1], yv[2], yv[3]);
+                    *reinterpret_cast<float4*>(&w.dl[c][tc]) = make_float4(yv[0], yv[1], yv[2], yv[3]);
             }
         }
 
@@ -325,10 +336,10 @@ __device__ __forceinline__ void scan_body(const KArgs& a, Smem<N>& sm, const int
                 E::unpack(in.u[it], uv);
                 float zv[V];
                 if (HAS_Z) E::unpack(in.z[it], zv);
-                const float dr = sm.dsk[r];
+                const float dr = w.dsk[r];
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
-                    const float yy = fmaf(dr, uv[e], sm.dl[r][tl + e]);
+                    const float yy = fmaf(dr, uv[e], w.dl[r][tl + e]);
                     ov[e] = HAS_Z ? yy * silu(zv[e]) : yy;
                     if (t0 + tl + e >= stop) ov[e] = 0.0f;  // past the batch's length
                 }
@@ -360,13 +371,14 @@ __device__ __forceinline__ void scan_body(const KArgs& a, Smem<N>& sm, const int
 }
 
 template <class E, bool VEC, bool HAS_Z, int MODE, int N>
-__global__ __launch_bounds__(kRows) void scan_kernel(KArgs a) {
+__global__ __launch_bounds__(kRows * Shape<N>::WPB) __attribute__((amdgpu_waves_per_eu(N >= 64 ? 3 : 1))) void scan_kernel(KArgs a) {
     constexpr int Q = Shape<N>::Q;
     constexpr int CH = Shape<N>::CH;
     __shared__ Smem<N> sm;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x % kRows;
+    const int wave = threadIdx.x / kRows;
     const int c = lane / Q, k = lane % Q;
-    const int64_t d0 = (int64_t)blockIdx.x * CH;
+    const int64_t d0 = ((int64_t)blockIdx.x * Shape<N>::WPB + wave) * CH;
     const int b = blockIdx.y;
     const int seg = blockIdx.z;
     const int64_t d = d0 + c;
@@ -396,8 +408,8 @@ __global__ __launch_bounds__(kRows) void scan_kernel(KArgs a) {
         for (int n = 0; n < 16; ++n) A2[n] = 0.0f;
     }
     if (k == 0) {
-        sm.bias[c] = (active && a.bias) ? a.bias[d] : 0.0f;
-        sm.dsk[c] = (active && a.D) ? a.D[d] : 0.0f;
+        sm.w[wave].bias[c] = (active && a.bias) ? a.bias[d] : 0.0f;
+        sm.w[wave].dsk[c] = (active && a.D) ? a.D[d] : 0.0f;
     }
 
     float h[16];
@@ -420,10 +432,13 @@ __global__ __launch_bounds__(kRows) void scan_kernel(KArgs a) {
         const int64_t l = a.lens[b];
         stop = l < 0 ? 0 : (l > a.L ? a.L : l);
     }
+    // (per wavefront; the wavefronts of a workgroup meet at the same barriers either way)
     if (__all(pow_ok))
-        scan_body<E, VEC, HAS_Z, MODE, true, N>(a, sm, lane, b, d0, row, active, A2, A2b, h, t_begin, t_end, stop);
+        scan_body<E, VEC, HAS_Z, MODE, true, N>(a, sm, lane, wave, b, d0, row, active, A2, A2b, h, t_begin, t_end,
+                                                stop);
     else
-        scan_body<E, VEC, HAS_Z, MODE, false, N>(a, sm, lane, b, d0, row, active, A2, A2b, h, t_begin, t_end, stop);
+        scan_body<E, VEC, HAS_Z, MODE, false, N>(a, sm, lane, wave, b, d0, row, active, A2, A2b, h, t_begin, t_end,
+                                                 stop);
 }
 
 // Folds the per-segment pairs (sum delta_s, local end state e_s) into inclusive end states:
@@ -467,9 +482,9 @@ constexpr int kTile = 32;  // segment lengths are multiples of this (and of ever
 template <class E, bool VEC, bool HAS_Z, int N>
 hipError_t launch_typed(const KArgs& k, const ScanLaunch& a, hipStream_t stream) {
     const int64_t Bt = a.Bt;
-    const dim3 block(kRows);
-    constexpr int CH = Shape<N>::CH;
-    const unsigned gx = static_cast<unsigned>((k.Dn + CH - 1) / CH);
+    const dim3 block(kRows * Shape<N>::WPB);
+    constexpr int CHB = Shape<N>::CH * Shape<N>::WPB;  // channels per workgroup
+    const unsigned gx = static_cast<unsigned>((k.Dn + CHB - 1) / CHB);
     mark(a, 0, stream);
     if (k.S > 1) {
         scan_kernel<E, VEC, HAS_Z, kAgg, N><<<dim3(gx, (unsigned)Bt, (unsigned)(k.S - 1)), block, 0, stream>>>(k);
@@ -498,7 +513,8 @@ hipError_t launch_n(const KArgs& k, const ScanLaunch& a, hipStream_t stream) {
 ScanPlan plan_scan(const ScanLaunch& a, int num_cus, int tile, int segments_override) {
     ScanPlan p;
     const int64_t ch = kRows / (a.N / 16);  // channels per wavefront
-    const int64_t groups = a.Bt * ((a.Dn + ch - 1) / ch);
+    const int64_t wpb = a.N >= 64 ? 4 : 1;  // wavefronts per workgroup
+    const int64_t groups = a.Bt * ((a.Dn + ch * wpb - 1) / (ch * wpb)) * wpb;
     const int64_t tiles = (a.L + tile - 1) / tile;
     // One wavefront per SIMD or more without a split: run unsplit (the aggregate pass a split adds
     // costs more than the fuller chip gains; at d_state 64, 4 x 5120 x 2048: 0.66 ms unsplit, 0.88
