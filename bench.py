@@ -50,7 +50,7 @@ VALU_WAVE_INSTR_PER_S = 256 * 4 * 2.4e9 / 4
 
 # Memory-side bytes per launch of the main scan kernel on this workload, from rocprofv3 --pmc
 # runs of the headline alone (`python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-bwd
-# --no-conv --no-shard --no-general-a --no-decode-chain --no-configs --no-ssd`): FETCH_SIZE, then
+# --no-conv --no-shard --no-general-a --no-decode-chain --no-configs --no-ssd --no-dstate`): FETCH_SIZE, then
 # WRITE_SIZE, each scaled by what the counter reads for a plain 1 GiB device copy (FETCH_SIZE x2:
 # the L2 fills whole 128-byte lines, one TCC_EA0_RDREQ each, and the counter prices a request at 64
 # bytes; WRITE_SIZE x1), and the VALU instructions per (b, d, t) (SQ_INSTS_VALU x 64 / B D L).
@@ -190,14 +190,13 @@ def decode_hbm_chain(mss, torch, devc, steps=1024, states=16, pool=64, N=None):
                     "the 256 MB Infinity Cache): HBM-resident"}
 
 
-def general_a_leg(mss, torch, devc, Bt, Dn, N, L, calls=20, warmup=3, copies=2):
-    """The forward on the same layer shape with an unstructured negative A (synth a_kind="random":
-    what a trained layer holds), so every state update takes its own exp: the path the
-    power-chain shortcut for A = -(n+1) does not cover.  Rotated input copies, events on the
-    stream, and the library's kernel split."""
+def fwd_leg(mss, torch, devc, Bt, Dn, N, L, a_kind, calls=20, warmup=3, copies=2):
+    """The forward on a layer shape with A of `a_kind` (synth: "s4d" is A = -(n+1), "random" an
+    unstructured negative A, what a trained layer holds, so every state update takes its own
+    exp).  Rotated input copies, events on the stream, and the library's kernel split."""
     import numpy as np
     from synth import scan_inputs
-    s = scan_inputs(Bt, Dn, N, L, dtype="bf16", with_z=True, seed=0, a_kind="random")
+    s = scan_inputs(Bt, Dn, N, L, dtype="bf16", with_z=True, seed=0, a_kind=a_kind)
     up = lambda a, bf=False: (torch.from_numpy(np.ascontiguousarray(a)).to(devc).to(torch.bfloat16)
                               if bf else torch.from_numpy(np.ascontiguousarray(a)).to(devc))
     A, D, bias = up(s.A), up(s.D), up(s.delta_bias)
@@ -228,11 +227,18 @@ def general_a_leg(mss, torch, devc, Bt, Dn, N, L, calls=20, warmup=3, copies=2):
     avg = sum(ms) / len(ms)
     nb = scan_bytes(Bt, Dn, N, L)
     main_ms = main / max(n, 1)
-    return {"shape": [Bt, Dn, N, L], "a": "random negative (synth a_kind=random)", "avg_ms": round(avg, 4),
-            "min_ms": round(min(ms), 4), "gbps": round(nb / (avg * 1e-3) / 1e9, 2),
+    return {"shape": [Bt, Dn, N, L],
+            "a": "A = -(n+1) (synth a_kind=s4d)" if a_kind == "s4d" else "random negative (synth a_kind=random)",
+            "avg_ms": round(avg, 4), "min_ms": round(min(ms), 4),
+            "state_updates_per_s": round(Bt * Dn * L * N / (avg * 1e-3), 1),
+            "gbps": round(nb / (avg * 1e-3) / 1e9, 2),
             "frac_hbm_peak": round(nb / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "carry_stage_avg_ms": round(carry / max(n, 1), 4), "main_avg_ms": round(main_ms, 4),
             "main_frac_hbm_peak": round(nb / (main_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+def general_a_leg(mss, torch, devc, Bt, Dn, N, L):
+    return fwd_leg(mss, torch, devc, Bt, Dn, N, L, "random")
 
 
 def ssd_bytes(Bt, L, H, P, G, N):
@@ -550,6 +556,7 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="input sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-chain", action="store_true")
+    ap.add_argument("--no-dstate", action="store_true", help="skip the d_state 64 / 128 forward legs")
     ap.add_argument("--no-general-a", action="store_true", help="skip the random-A forward leg")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
@@ -686,6 +693,11 @@ def main():
     if not args.no_general_a:
         res["scan_fwd_general_A"] = general_a_leg(mss, torch, devc, Bt, Dn, N, L)
         progress("general A")
+    if not args.no_dstate:
+        # the same layer at d_state 64 and 128 (the general kernels: d_state / 16 lanes per channel)
+        res["scan_fwd_dstate"] = {f"{n}_{k}": fwd_leg(mss, torch, devc, Bt, Dn, n, L, k, calls=10, copies=2)
+                                  for n in (64, 128) for k in ("s4d", "random")}
+        progress("d_state 64 / 128 forward")
     if not args.no_decode_chain:
         res["decode_chain"] = decode_chain(mss, torch, devc)
         res["decode_chain_hbm"] = decode_hbm_chain(mss, torch, devc)
