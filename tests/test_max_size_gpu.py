@@ -1,4 +1,4 @@
-"""Tensors past 2^31 elements: the forward scan, its backward and the causal conv1d on a
+"""Tensors past 2^31 elements: the forward scan (d_state 16 and 128), its backward and the causal conv1d on a
 (1, 65600, 32768) bf16 layer (2.15e9 elements per activation tensor, 4.3 GB), so element
 offsets beyond the 32-bit range occur in every kernel.  Rows at the start, middle and end of
 the tensors (the last rows lie past element 2^31) are checked against the fp64 oracle.
@@ -80,6 +80,32 @@ def test_forward_past_2_31_elements(mss, oracle_mod, layer):
     torch.cuda.empty_cache()
 
 
+def test_forward_dstate128_past_2_31_elements(mss, oracle_mod, layer):
+    """The general kernels (d_state 128, four-wavefront workgroups) on the same u / delta / z with
+    B, C of 128 states: the sampled rows' outputs and final states against the oracle."""
+    import torch
+    N2 = 128
+    g = torch.Generator(device="cuda").manual_seed(2029)
+    B = torch.randn((BT, N2, L), generator=g, device="cuda", dtype=torch.float32)
+    C = torch.randn((BT, N2, L), generator=g, device="cuda", dtype=torch.float32)
+    small = scan_inputs(1, DN, N2, 1, dtype="f32", seed=9)
+    A = torch.from_numpy(small.A).to("cuda")
+    out, last = mss.selective_scan_fwd(layer["u"], layer["delta"], A, B, C, D=layer["D"], z=layer["z"],
+                                       delta_bias=layer["delta_bias"])
+    torch.cuda.synchronize()
+    for r in ROWS:
+        b, d = divmod(r, DN)
+        ref_out, ref_last = oracle_mod.selective_scan(
+            _row(layer["u"], r)[None, None], _row(layer["delta"], r)[None, None], host64(A[d])[None],
+            host64(B[b])[None], host64(C[b])[None], D=host64(layer["D"][d : d + 1]), z=_row(layer["z"], r)[None, None],
+            delta_bias=host64(layer["delta_bias"][d : d + 1]))
+        assert_close(_row(out, r), ref_out[0, 0], what=f"d_state 128 out row {r}", **TOL_BF16)
+        assert_close(host64(last.reshape(-1, N2)[r]), ref_last[0, 0], what=f"d_state 128 last_state row {r}",
+                     **TOL_F32)
+    del out, last, B, C
+    torch.cuda.empty_cache()
+
+
 def test_backward_past_2_31_elements(mss, oracle_mod, layer):
     """du, ddelta, dz of the sampled rows (each depends only on its own row); the sums over rows
     (dA, dB, dC, dD, dbias) must be finite."""
@@ -153,12 +179,12 @@ def test_saved_states_past_2_31_elements(mss, oracle_mod, layer):
     torch.cuda.empty_cache()
 
 
-def test_decode_past_2_31_state_elements(mss, oracle_mod):
-    """One decode step on a (2100, 65600, 16) state (2.2e9 floats, 8.8 GB): sampled rows past
-    element 2^31 against the oracle."""
+@pytest.mark.parametrize("N,Bt", [(16, 2100), (128, 260)])
+def test_decode_past_2_31_state_elements(mss, oracle_mod, N, Bt):
+    """One decode step on a (2100, 65600, 16) or (260, 65600, 128) state (2.2e9 floats, 8.8 GB):
+    sampled rows past element 2^31 against the oracle."""
     import torch
-    Bt = 2100
-    rows = [0, 65599, 137_000_000, Bt * DN - 1]
+    rows = [0, 65599, int(0.99 * Bt * DN), Bt * DN - 1]   # the last two past element 2^31
     assert Bt * DN * N > 2**31
     g = torch.Generator(device="cuda").manual_seed(2028)
     state = torch.randn((Bt, DN, N), generator=g, device="cuda") * 0.5

@@ -1,7 +1,7 @@
 """Seeded random sweep of shapes and options through every GPU entry point, each case against the
 fp64 oracle: the hand-picked cases elsewhere cover the structure; this covers combinations of
 batch / channels / length / dtype / A kind / optional arguments / lengths / starting states /
-misaligned views / segment counts that nobody picked.
+misaligned views / segment counts / d_state that nobody picked.
 
 Each case prints its parameters before running, so a failure names the case.  Tolerances as in
 test_parity_gpu.py (forward, conv) and test_bwd_gpu.py (backward).
@@ -85,6 +85,39 @@ def test_forward_sweep(mss, oracle_mod, plan, i):
         delta_bias=s.delta_bias if c["use_bias"] else None, h0=h0, seq_lens=lens)
     assert_close(host64(out), ref_out, what=f"sweep fwd {i} out", **(TOL_BF16 if dt == "bf16" else TOL_F32))
     assert_close(host64(last), ref_last, what=f"sweep fwd {i} last_state", **TOL_F32)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_forward_dstate_sweep(mss, oracle_mod, plan, i):
+    """The same sweep at d_state 32, 64 and 128 (the general kernels), with forced segment counts."""
+    import torch
+    c = _case(100 + i)
+    N = int(np.random.default_rng(8000 + i).choice([32, 64, 128]))
+    print(f"[sweep fwd d_state {N} {i}] {c}", flush=True)
+    if c["segments"]:
+        plan(generic_segments=c["segments"])
+    s = scan_inputs(c["Bt"], c["Dn"], N, c["L"], dtype=c["dtype"], seed=c["seed"] % 100000,
+                    a_kind=c["a_kind"], with_z=c["use_z"])
+    rng = np.random.default_rng(c["seed"])
+    h0 = (0.5 * rng.standard_normal((c["Bt"], c["Dn"], N))).astype(np.float32) if c["with_h0"] else None
+    lens = rng.integers(0, c["L"] + 1, c["Bt"]).astype(np.int32) if c["with_lens"] else None
+    dt = c["dtype"]
+    args = [_to_dev(s.u, dt, c["offset"]), _to_dev(s.delta, dt, c["offset"]), dev(s.A), dev(s.B), dev(s.C)]
+    kw = dict(D=dev(s.D) if c["use_D"] else None,
+              z=_to_dev(s.z, dt, c["offset"]) if c["use_z"] else None,
+              delta_bias=dev(s.delta_bias) if c["use_bias"] else None)
+    if lens is not None:
+        out, last = mss.selective_scan_fwd_varlen(*args, torch.from_numpy(lens).to("cuda"),
+                                                  initial_state=None if h0 is None else dev(h0), **kw)
+    else:
+        out, last = mss.selective_scan_fwd_with_state(*args, None if h0 is None else dev(h0), **kw)
+    torch.cuda.synchronize()
+    ref_out, ref_last = oracle_mod.selective_scan(
+        s.u, s.delta, s.A, s.B, s.C, D=s.D if c["use_D"] else None, z=s.z if c["use_z"] else None,
+        delta_bias=s.delta_bias if c["use_bias"] else None, h0=h0, seq_lens=lens)
+    what = f"sweep fwd d_state {N} {i}"
+    assert_close(host64(out), ref_out, what=what + " out", **(TOL_BF16 if dt == "bf16" else TOL_F32))
+    assert_close(host64(last), ref_last, what=what + " last_state", **TOL_F32)
 
 
 @pytest.mark.parametrize("i", range(0, N_CASES, 2))
