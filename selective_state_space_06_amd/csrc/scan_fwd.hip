@@ -7,12 +7,14 @@
 //   h_t = Abar h_{t-1} + delta_t B_nt u_t (h_0 = 0, or a given state)
 //   out_t = (sum_n C_nt h_t + D_d u_t) silu(z_t)
 //
-// Work decomposition (one wavefront per workgroup), for d_state N = 16, 32, 64 or 128:
-//   * a lane owns 16 states of one channel (row b, d) in VGPRs, sequential in t: Q = N / 16
-//     neighbouring lanes share a channel, so a wave holds 64 / Q consecutive channels of one
-//     batch; each lane's part of C.h meets its neighbours' through DPP adds;
-//   * B_t and C_t are the same for every channel of the wave: they are staged once per time tile
-//     in LDS, transposed to [t][n], and read back as broadcast 16-byte LDS loads;
+// Work decomposition, for d_state N = 16, 32, 64 or 128:
+//   * a lane owns SPL states of one channel (row b, d) in VGPRs, sequential in t (SPL = 8 at
+//     d_state 32 and 64, 16 otherwise): Q = N / SPL neighbouring lanes share a channel, so a
+//     wave holds 64 / Q consecutive channels of one batch; each lane's part of C.h meets its
+//     neighbours' through DPP adds;
+//   * B_t and C_t are the same for every channel of a batch: they are staged once per time tile
+//     in LDS, transposed to [t][n], shared by the workgroup's wavefronts (one at d_state 16, four
+//     otherwise), and read back as broadcast 16-byte LDS loads;
 //   * u / delta / z / out move between HBM and LDS in 16-byte vectors along L (coalesced),
 //     and the per-element work (bias + softplus, delta * u, the D skip and the silu gate) is
 //     done in that coalesced layout, once per element;
@@ -29,8 +31,8 @@
 // exp(delta A) = exp2(delta * A log2e) with A log2e formed once per (d, n).  When a row
 // satisfies A[d, n] == (n + 1) A[d, 0] exactly (the S4D-real initialisation A = -(1..N) the
 // tutorial uses), Abar_n = Abar_0^(n+1) is formed by repeated multiplication: a lane holding
-// states 16k .. 16k + 15 takes exp(delta A[d, 16k]) and steps it by Abar_0, two exp2 per
-// (b, d, t) and lane (one when N = 16) instead of sixteen.  The choice is made per wavefront on
+// states SPL k .. SPL k + SPL - 1 takes exp(delta A[d, SPL k]) and steps it by Abar_0, two exp2
+// per (b, d, t) and lane (one when N = 16) instead of SPL.  The choice is made per wavefront on
 // the device from the A rows it loads; any other A takes the general path.
 #include "device_math.hpp"
 #include "mss_internal.hpp"
@@ -61,22 +63,26 @@ struct KArgs {
     int softplus;
 };
 
-// Shape of the work for d_state N: Q lanes per channel, CH channels per wavefront, TT-step tiles,
-// WPB wavefronts per workgroup.  At d_state 64 and 128 four wavefronts (consecutive channel
-// groups of one batch) share each tile's B | C in LDS: a quarter of the staging each, and a
-// quarter of the LDS, which leaves room for three wavefronts per SIMD.
+// Shape of the work for d_state N: SPL states per lane, Q lanes per channel, CH channels per
+// wavefront, TT-step tiles, WPB wavefronts per workgroup.  From d_state 32 on, four wavefronts
+// (consecutive channel groups of one batch) share each tile's B | C in LDS: a quarter of the
+// staging each, and a quarter of the LDS, which leaves room for three wavefronts per SIMD.  Eight
+// states per lane at d_state 32 and 64 give twice the wavefronts of sixteen (2560 on the 2.8B
+// layer shape at 64, which three per SIMD hold at once, against 1280 that leave a quarter of
+// the SIMDs with two and the rest with one).
 template <int N>
 struct Shape {
     static_assert(N == 16 || N == 32 || N == 64 || N == 128, "d_state");
-    static constexpr int Q = N / 16;
+    static constexpr int SPL = (N == 32 || N == 64) ? 8 : 16;  // states per lane
+    static constexpr int Q = N / SPL;
     static constexpr int CH = kRows / Q;
     static constexpr int TT = 32;
-    static constexpr int WPB = N >= 64 ? 4 : 1;
+    static constexpr int WPB = N >= 32 ? 4 : 1;
 };
 
 // Word of entry m of a step's B | C row in LDS (m = n for B_n, N + n for C_n): four pad words
-// after every 64, so that the Q blocks of 16 states a wavefront reads at one step (one per lane
-// group, 16-byte reads) start in distinct groups of four banks of the 64.
+// after every 64, so that the Q blocks of SPL states a wavefront reads at one step (one per lane
+// group, 16-byte reads) fall in distinct groups of four banks of the 64.
 __host__ __device__ constexpr int bc_word(int m) { return m + 4 * (m / 64); }
 
 template <int N>
@@ -95,15 +101,15 @@ struct Smem {
     float bc[TT][kBCStride];       // B[0..N-1] | C[0..N-1] per time step, at bc_word positions (shared)
 };
 
-// One time step of one lane: its 16 state updates and (main pass) their part of C.h.  A2 holds
+// One time step of one lane: its SPL state updates and (main pass) their part of C.h.  A2 holds
 // A log2e of the lane's states and A2b that of the channel's state 0; bc points at the step's B
 // entries for the lane's states, bc + cofs at its C entries.
-template <bool POW, bool WANT_Y, int Q>
-__device__ __forceinline__ float step16(float (&h)[16], const float (&A2)[16], float A2b, float dl, float x,
+template <bool POW, bool WANT_Y, int Q, int SPL>
+__device__ __forceinline__ float step_lane(float (&h)[SPL], const float (&A2)[SPL], float A2b, float dl, float x,
                                         const float* __restrict__ bc, int cofs) {
-    float Bv[16], Cv[16];
+    float Bv[SPL], Cv[SPL];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < SPL / 4; ++q) {
         const float4 b4 = reinterpret_cast<const float4*>(bc)[q];
         Bv[4 * q] = b4.x; Bv[4 * q + 1] = b4.y; Bv[4 * q + 2] = b4.z; Bv[4 * q + 3] = b4.w;
         if (WANT_Y) {
@@ -113,18 +119,18 @@ __device__ __forceinline__ float step16(float (&h)[16], const float (&A2)[16], f
     }
     float y = 0.0f;
     if (POW) {
-        // Abar_n = exp(dl A[d, 16k]) Abar_0^(n - 16k) across the lane's states 16k .. 16k + 15
+        // Abar_n = exp(dl A[d, SPL k]) Abar_0^(n - SPL k) across the lane's states from SPL k
         const float a = fast_exp2(dl * A2b);
         float p = Q == 1 ? a : fast_exp2(dl * A2[0]);
 #pragma unroll
-        for (int n = 0; n < 16; ++n) {
+        for (int n = 0; n < SPL; ++n) {
             if (n) p *= a;
             h[n] = fmaf(p, h[n], x * Bv[n]);
             if (WANT_Y) y = n ? fmaf(Cv[n], h[n], y) : Cv[0] * h[0];
         }
     } else {
 #pragma unroll
-        for (int n = 0; n < 16; ++n) {
+        for (int n = 0; n < SPL; ++n) {
             h[n] = fmaf(fast_exp2(dl * A2[n]), h[n], x * Bv[n]);
             if (WANT_Y) y = n ? fmaf(Cv[n], h[n], y) : Cv[0] * h[0];
         }
@@ -272,7 +278,8 @@ __device__ __forceinline__ void stage_tile(const KArgs& a, Smem<N>& sm, const Ti
 template <class E, bool VEC, bool HAS_Z, int MODE, bool POW, int N>
 __device__ __forceinline__ void scan_body(const KArgs& a, Smem<N>& sm, const int lane, const int wave, const int b,
                                           const int64_t d0, const int64_t row, const bool active,
-                                          const float (&A2)[16], const float A2b, float (&h)[16],
+                                          const float (&A2)[Shape<N>::SPL], const float A2b,
+                                          float (&h)[Shape<N>::SPL],
                                           const int64_t t_begin, const int64_t t_end, const int64_t stop) {
     using G = Geo<E, N>;
     constexpr int Q = G::Q;
@@ -280,18 +287,19 @@ __device__ __forceinline__ void scan_body(const KArgs& a, Smem<N>& sm, const int
     constexpr int TT = G::TT;
     constexpr int V = G::V;
     constexpr bool WANT_Z = MODE == kMain && HAS_Z;
+    constexpr int SPL = Shape<N>::SPL;
 
     const int64_t L = a.L;
     const int64_t Dn = a.Dn;
     const int cl = lane % G::CPR;        // vector column of this lane in the coalesced layout
     const int rl = lane / G::CPR;        // row offset of this lane within a pass
     const int c = lane / Q;              // this lane's channel within the wave (phase B)
-    const int k = lane % Q;              // its block of 16 states
+    const int k = lane % Q;              // its block of SPL states
     auto& w = sm.w[wave];
     float dsum = 0.0f;
 
     // (Issuing the next tile's loads before the recurrence, to hide their latency, measured no
-    // faster at d_state 64 and 128: two wavefronts per SIMD already hide it.)
+    // faster at d_state 64 and 128: the other wavefronts on the SIMD already hide it.)
     for (int64_t t0 = t_begin; t0 < t_end; t0 += TT) {
         const int tvalid = static_cast<int>(t_end - t0 < TT ? t_end - t0 : TT);
         __syncthreads();  // the previous tile's readers of sm are done
@@ -300,7 +308,7 @@ __device__ __forceinline__ void scan_body(const KArgs& a, Smem<N>& sm, const int
         stage_tile<E, N>(a, sm, in, lane, wave, d0, t0, tvalid, stop);
         __syncthreads();
 
-        // ---- phase B: the recurrence, lane = (channel, block of 16 states), sequential over the tile
+        // ---- phase B: the recurrence, lane = (channel, block of SPL states), sequential over the tile
         for (int tc = 0; tc < tvalid; tc += 4) {
             const float4 dl4 = *reinterpret_cast<const float4*>(&w.dl[c][tc]);
             const float4 x4 = *reinterpret_cast<const float4*>(&w.x[c][tc]);
@@ -309,8 +317,9 @@ __device__ __forceinline__ void scan_body(const KArgs& a, Smem<N>& sm, const int
             float yv[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                yv[j] = step16<POW, MODE == kMain, Q>(h, A2, A2b, dlv[j], xv[j], &sm.bc[tc + j][bc_word(16 * k)],
-                                                      bc_word(N + 16 * k) - bc_word(16 * k));
+                yv[j] = step_lane<POW, MODE == kMain, Q, SPL>(h, A2, A2b, dlv[j], xv[j],
+                                                              &sm.bc[tc + j][bc_word(SPL * k)],
+                                                              bc_word(N + SPL * k) - bc_word(SPL * k));
                 if (MODE == kAgg) dsum += dlv[j];
             }
             if (MODE == kMain) {
@@ -357,23 +366,24 @@ __device__ __forceinline__ void scan_body(const KArgs& a, Smem<N>& sm, const int
 
     if (MODE == kMain) {
         if (a.last_state && active && blockIdx.z == a.S - 1) {
-            float4* dst = reinterpret_cast<float4*>(a.last_state + row * N + 16 * k);
+            float4* dst = reinterpret_cast<float4*>(a.last_state + row * N + SPL * k);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < SPL / 4; ++q)
                 dst[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
         }
     } else if (active) {
         float* ws = a.ws + (int64_t)blockIdx.z * (N + 1) * a.rows_total + row;
 #pragma unroll
-        for (int n = 0; n < 16; ++n) ws[(int64_t)(16 * k + n) * a.rows_total] = h[n];
+        for (int n = 0; n < SPL; ++n) ws[(int64_t)(SPL * k + n) * a.rows_total] = h[n];
         if (k == 0) ws[(int64_t)N * a.rows_total] = dsum;
     }
 }
 
 template <class E, bool VEC, bool HAS_Z, int MODE, int N>
-__global__ __launch_bounds__(kRows * Shape<N>::WPB) __attribute__((amdgpu_waves_per_eu(N >= 64 ? 3 : 1))) void scan_kernel(KArgs a) {
+__global__ __launch_bounds__(kRows * Shape<N>::WPB) __attribute__((amdgpu_waves_per_eu(N >= 32 ? 3 : 1))) void scan_kernel(KArgs a) {
     constexpr int Q = Shape<N>::Q;
     constexpr int CH = Shape<N>::CH;
+    constexpr int SPL = Shape<N>::SPL;
     __shared__ Smem<N> sm;
     const int lane = threadIdx.x % kRows;
     const int wave = threadIdx.x / kRows;
@@ -385,44 +395,44 @@ __global__ __launch_bounds__(kRows * Shape<N>::WPB) __attribute__((amdgpu_waves_
     const bool active = d < a.Dn;
     const int64_t row = (int64_t)b * a.Dn + (active ? d : 0);
 
-    float A2[16];
+    float A2[SPL];
     float A2b = 0.0f;
     bool pow_ok = true;
     if (active) {
-        const float4* Ar = reinterpret_cast<const float4*>(a.A + d * N + 16 * k);
+        const float4* Ar = reinterpret_cast<const float4*>(a.A + d * N + SPL * k);
         const float A0 = a.A[d * N];
-        float Av[16];
+        float Av[SPL];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < SPL / 4; ++q) {
             const float4 v = Ar[q];
             Av[4 * q] = v.x; Av[4 * q + 1] = v.y; Av[4 * q + 2] = v.z; Av[4 * q + 3] = v.w;
         }
 #pragma unroll
-        for (int n = 0; n < 16; ++n) {
+        for (int n = 0; n < SPL; ++n) {
             A2[n] = Av[n] * kLog2e;
-            pow_ok = pow_ok && (Av[n] == static_cast<float>(16 * k + n + 1) * A0);
+            pow_ok = pow_ok && (Av[n] == static_cast<float>(SPL * k + n + 1) * A0);
         }
         A2b = A0 * kLog2e;
     } else {
 #pragma unroll
-        for (int n = 0; n < 16; ++n) A2[n] = 0.0f;
+        for (int n = 0; n < SPL; ++n) A2[n] = 0.0f;
     }
     if (k == 0) {
         sm.w[wave].bias[c] = (active && a.bias) ? a.bias[d] : 0.0f;
         sm.w[wave].dsk[c] = (active && a.D) ? a.D[d] : 0.0f;
     }
 
-    float h[16];
+    float h[SPL];
     if (MODE == kMain && seg > 0 && active) {
         const float* ws = a.ws + (int64_t)(seg - 1) * (N + 1) * a.rows_total + row;
 #pragma unroll
-        for (int n = 0; n < 16; ++n) h[n] = ws[(int64_t)(16 * k + n) * a.rows_total];
+        for (int n = 0; n < SPL; ++n) h[n] = ws[(int64_t)(SPL * k + n) * a.rows_total];
     } else if (MODE == kMain && a.h0 && active) {
 #pragma unroll
-        for (int n = 0; n < 16; ++n) h[n] = a.h0[row * N + 16 * k + n];
+        for (int n = 0; n < SPL; ++n) h[n] = a.h0[row * N + SPL * k + n];
     } else {
 #pragma unroll
-        for (int n = 0; n < 16; ++n) h[n] = 0.0f;
+        for (int n = 0; n < SPL; ++n) h[n] = 0.0f;
     }
 
     const int64_t t_begin = (int64_t)seg * a.seg_len;
@@ -512,8 +522,9 @@ hipError_t launch_n(const KArgs& k, const ScanLaunch& a, hipStream_t stream) {
 
 ScanPlan plan_scan(const ScanLaunch& a, int num_cus, int tile, int segments_override) {
     ScanPlan p;
-    const int64_t ch = kRows / (a.N / 16);  // channels per wavefront
-    const int64_t wpb = a.N >= 64 ? 4 : 1;  // wavefronts per workgroup
+    const int64_t spl = (a.N == 32 || a.N == 64) ? 8 : 16;   // states per lane (Shape<N>::SPL)
+    const int64_t ch = kRows / (a.N / spl);   // channels per wavefront
+    const int64_t wpb = a.N >= 32 ? 4 : 1;  // wavefronts per workgroup
     const int64_t groups = a.Bt * ((a.Dn + ch * wpb - 1) / (ch * wpb)) * wpb;
     const int64_t tiles = (a.L + tile - 1) / tile;
     // One wavefront per SIMD or more without a split: run unsplit (the aggregate pass a split adds
