@@ -1,4 +1,5 @@
-"""The scan forward, the forward that saves states and both backwards captured in a HIP graph
+"""The scan forward (d_state 16, 64 and 128), the forward that saves states, both backwards and the
+decode step captured in a HIP graph
 (torch.cuda.graph) and replayed: every replay, with new inputs copied in between and eager
 library calls interleaved, must give exactly the eager results for those inputs.  The library's
 workspace belongs to a (device, stream) pair, so one warm-up call on the capture stream comes
@@ -246,6 +247,69 @@ def test_ssd_graph_replays_match_eager(mss):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(eager[0], out) and torch.equal(eager[1], last), rep
+        if prev is not None:
+            assert not torch.equal(prev, out)
+        prev = out.clone()
+
+
+@pytest.mark.parametrize("N", [64, 128])
+def test_dstate_graph_replays_match_eager(mss, N):
+    """The general forward at d_state 64 / 128 with a segment split (its aggregates and the
+    combine kernel go through the workspace) and a decode step at the same d_state, captured after
+    a warm-up on the capture stream: every replay, with new inputs copied in and the decode state
+    reset, equals the eager calls on those inputs bit for bit."""
+    import torch
+    from synth import decode_inputs
+
+    Bt, Dn, L = 1, 96, 600
+
+    def inputs(seed):
+        s = scan_inputs(Bt, Dn, N, L, dtype="bf16", seed=seed, a_kind="random" if N == 64 else "s4d")
+        d = decode_inputs(Bt, Dn, N, 1, dtype="bf16", seed=seed)
+        return dict(u=dev(s.u, "bf16"), delta=dev(s.delta, "bf16"), z=dev(s.z, "bf16"), B=dev(s.B), C=dev(s.C),
+                    x1=dev(d.x[0], "bf16"), dt1=dev(d.dt[0], "bf16"), B1=dev(d.B[0]), C1=dev(d.C[0])), \
+            dict(A=dev(s.A), D=dev(s.D), bias=dev(s.delta_bias))
+
+    x, p = inputs(90)
+    out = torch.empty_like(x["u"])
+    last = torch.empty((Bt, Dn, N), dtype=torch.float32, device="cuda")
+    state0 = torch.randn((Bt, Dn, N), device="cuda") * 0.5
+    state = state0.clone()
+    out1 = torch.empty((Bt, Dn), dtype=torch.bfloat16, device="cuda")
+
+    def body():
+        mss.selective_scan_fwd(x["u"], x["delta"], p["A"], x["B"], x["C"], D=p["D"], z=x["z"],
+                               delta_bias=p["bias"], out=out, last_state=last)
+        mss.selective_state_update(state, x["x1"], x["dt1"], p["A"], x["B1"], x["C1"], D=p["D"],
+                                   dt_bias=p["bias"], out=out1)
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        body()  # allocates the workspace outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        body()
+    torch.cuda.synchronize()
+    prev = None
+    for rep in range(3):
+        nx, _ = inputs(91 + rep)
+        for k in x:
+            x[k].copy_(nx[k])
+        state.copy_(state0)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            body()
+        torch.cuda.synchronize()
+        eager = (out.clone(), last.clone(), state.clone(), out1.clone())
+        state.copy_(state0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (out, last, state, out1)
+        for k in range(4):
+            assert torch.equal(eager[k], got[k]), (N, rep, k)
         if prev is not None:
             assert not torch.equal(prev, out)
         prev = out.clone()
