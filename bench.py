@@ -81,8 +81,10 @@ def ramp_clocks(torch, fn, seconds=RAMP_S, batch=8):
 # WRITE_SIZE, each scaled by what the counter reads for a plain 1 GiB device copy (FETCH_SIZE x2:
 # the L2 fills whole 128-byte lines, one TCC_EA0_RDREQ each, and the counter prices a request at 64
 # bytes; WRITE_SIZE x1), and the VALU instructions per (b, d, t) (SQ_INSTS_VALU x 64 / B D L).
-# Valid only for the kernel source with this SHA-256 prefix; otherwise reported as null.
-MAIN_COUNTERS = {"src_sha256": "a57803b6a94eabc8", "fetch_bytes": 496183296, "write_bytes": 96316006,
+# Valid only for the kernel source with this SHA-256 prefix; otherwise reported as null.  (Taken
+# on the source before the whole-tile loads of element-aligned rows; this layer's kernels compile
+# to the same machine code from both.)
+MAIN_COUNTERS = {"src_sha256": "ab71073fb2cc8aed", "fetch_bytes": 496183296, "write_bytes": 96316006,
                  "valu_per_bdt": 92.12}
 
 

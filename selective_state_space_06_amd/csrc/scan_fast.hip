@@ -123,13 +123,32 @@ __device__ __forceinline__ uint4 load_vec(const typename E::storage* __restrict_
     return E::pack(f);  // exact: the values came from this storage type
 }
 
+// An element-aligned 16-byte access (RAGGED rows; gfx950 serves it whole).
+__device__ __forceinline__ uint4 load16u(const void* p) {
+    uint4 w;
+    __builtin_memcpy(&w, p, 16);
+    return w;
+}
+
 // Vectors at or past t_end re-read the last valid vector (their steps are never used), so every
-// load is unconditional and in bounds.  RAGGED: vectors past the row's end read as zeros.
+// load is unconditional and in bounds.  RAGGED: vectors past the row's end read as zeros; a tile
+// that lies wholly inside the row (all but a row's last) takes plain element-aligned loads with
+// no per-vector test, so they issue together (the tested form waits on each load in turn).
 template <class E, bool RAGGED>
 __device__ __forceinline__ void load_ud(RawUD<E>& r, const typename E::storage* __restrict__ up,
                                         const typename E::storage* __restrict__ dp, int64_t t0,
                                         int64_t t_end, int64_t L) {
     constexpr int V = E::kPerVec;
+    if (RAGGED && t0 + Geo<E>::TT <= L) {
+#pragma unroll
+        for (int v = 0; v < Geo<E>::NV; ++v) {
+            const uint4 a = load16u(up + t0 + v * V);
+            const uint4 b = load16u(dp + t0 + v * V);
+            r.u[4 * v] = a.x; r.u[4 * v + 1] = a.y; r.u[4 * v + 2] = a.z; r.u[4 * v + 3] = a.w;
+            r.d[4 * v] = b.x; r.d[4 * v + 1] = b.y; r.d[4 * v + 2] = b.z; r.d[4 * v + 3] = b.w;
+        }
+        return;
+    }
 #pragma unroll
     for (int v = 0; v < Geo<E>::NV; ++v) {
         int64_t t = t0 + v * V;
@@ -166,13 +185,14 @@ __device__ __forceinline__ void load_bc(RawBC<E>& r, const float* __restrict__ B
                                         int64_t t_end) {
     constexpr int K = Geo<E>::kBCChunks;
     const int n = threadIdx.x & 15;
+    const bool whole = RAGGED && t0 + Geo<E>::TT <= L;  // the tile lies inside the rows (uniform)
 #pragma unroll
     for (int k = 0; k < (WITH_C ? K : K / 2); ++k) {
         const float* src = k < K / 2 ? Bb : Cb;
         const int kk = k % (K / 2);
         int64_t t = t0 + 4 * (4 * kk + (threadIdx.x >> 4));
         if (!RAGGED) t = t < t_end ? t : t_end - 4;
-        const uint4 v = load_vec<F32, RAGGED>(src + n * L, t, L);
+        const uint4 v = whole ? load16u(src + n * L + t) : load_vec<F32, RAGGED>(src + n * L, t, L);
         r.w[4 * k] = v.x; r.w[4 * k + 1] = v.y; r.w[4 * k + 2] = v.z; r.w[4 * k + 3] = v.w;
     }
 }
@@ -350,12 +370,13 @@ __device__ __forceinline__ void main_body(
         stage_bc<E, true, VARLEN>(sbc, bpre, t0, rs.stop);
         __syncthreads();
         uint32_t zw[4 * kNV];  // z of this tile, consumed by the epilogue
+        const bool whole = RAGGED && t0 + TT <= L;  // the tile lies inside the row (uniform)
         if (HAS_Z) {
 #pragma unroll
             for (int v = 0; v < kNV; ++v) {
                 int64_t t = t0 + v * V;
                 if (!RAGGED) t = t < t_end ? t : t_end - V;
-                const uint4 a = load_vec<E, RAGGED>(zp, t, L);
+                const uint4 a = whole ? load16u(zp + t) : load_vec<E, RAGGED>(zp, t, L);
                 zw[4 * v] = a.x; zw[4 * v + 1] = a.y; zw[4 * v + 2] = a.z; zw[4 * v + 3] = a.w;
             }
         }
@@ -400,7 +421,10 @@ __device__ __forceinline__ void main_body(
             }
             packed[v] = E::pack(o);
         }
-        if (rs.active) {
+        if (rs.active && RAGGED && t0 + TT <= t_end) {  // every vector of the tile is the row's
+#pragma unroll
+            for (int v = 0; v < kNV; ++v) __builtin_memcpy(op + t0 + v * V, &packed[v], 16);
+        } else if (rs.active) {
 #pragma unroll
             for (int v = 0; v < kNV; ++v) {
                 const int64_t t = t0 + v * V;
