@@ -19,7 +19,8 @@ forward average 0.27 ms per call against 0.235 ms at steady clocks).
 Prints ONE JSON line.  `value` is algorithmic GB/s of the whole step (every input read once,
 every output written once) over the K timed steps; the scan alone is also timed with HIP
 events on the stream it runs on, and the library's launch-timing hook (mss_profile_enable /
-mss_profile_fwd) times its two kernels separately over the same timed steps.
+mss_profile_fwd) times its two kernels separately over a second pass of the same steps (the
+hook's events between the kernels cost ~11 us per call, so the timed steps run without it).
 
 `roofline` prices the scan's dominant kernel, the main scan kernel, against HBM: achieved =
 the call's algorithmic bytes (every input read once, every output written once: 338,272,256
@@ -81,11 +82,9 @@ def ramp_clocks(torch, fn, seconds=RAMP_S, batch=8):
 # WRITE_SIZE, each scaled by what the counter reads for a plain 1 GiB device copy (FETCH_SIZE x2:
 # the L2 fills whole 128-byte lines, one TCC_EA0_RDREQ each, and the counter prices a request at 64
 # bytes; WRITE_SIZE x1), and the VALU instructions per (b, d, t) (SQ_INSTS_VALU x 64 / B D L).
-# Valid only for the kernel source with this SHA-256 prefix; otherwise reported as null.  (Taken
-# on the source before the whole-tile loads of element-aligned rows; this layer's kernels compile
-# to the same machine code from both.)
-MAIN_COUNTERS = {"src_sha256": "ab71073fb2cc8aed", "fetch_bytes": 496183296, "write_bytes": 96316006,
-                 "valu_per_bdt": 92.12}
+# Valid only for the kernel source with this SHA-256 prefix; otherwise reported as null.
+MAIN_COUNTERS = {"src_sha256": "ae5b8104b96d2c5c", "fetch_bytes": 503828685, "write_bytes": 93198234,
+                 "valu_per_bdt": 86.69}
 
 
 def progress(what):
@@ -246,11 +245,14 @@ def fwd_leg(mss, torch, devc, Bt, Dn, N, L, a_kind, calls=20, warmup=3, copies=2
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
-    mss.profile_enable(True)
     for k in range(calls):
         ev[k][0].record(stream)
         call(k)
         ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    mss.profile_enable(True)  # the kernel split: a second pass with the timing hook on
+    for k in range(calls):
+        call(k)
     torch.cuda.synchronize()
     mss.profile_enable(False)
     n, carry, main = mss.profile_fwd()
@@ -657,12 +659,18 @@ def main():
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    mss.profile_enable(True)
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(k, evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # The kernel split comes from a second pass of the same steps with the library's timing hook
+    # on: its events between the two kernels cost ~11 us per call (239 against 227 us for the
+    # forward on this layer), so the timed steps above run without it.
+    mss.profile_enable(True)
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
     mss.profile_enable(False)
     n_calls, carry_ms_tot, main_ms_tot = mss.profile_fwd()
 
@@ -714,7 +722,9 @@ def main():
         "decode_token": {"avg_us": round(float(np.mean(dec_ms)) * 1e3, 2)},
         "kernels": {"calls_timed": n_calls, "carry_stage_avg_ms": round(carry_ms, 4),
                     "main_avg_ms": round(main_ms, 4),
-                    "carry_share_of_call": round(carry_ms / scan_avg_ms, 4)},
+                    "carry_share_of_call": round(carry_ms / scan_avg_ms, 4),
+                    "note": "a separate pass of the same steps with the library's timing hook on "
+                            "(its events between the kernels are left out of the timed steps)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "scan_main_kernel (the main kernel of mss_selective_scan_fwd), "
