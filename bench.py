@@ -83,8 +83,8 @@ def ramp_clocks(torch, fn, seconds=RAMP_S, batch=8):
 # the L2 fills whole 128-byte lines, one TCC_EA0_RDREQ each, and the counter prices a request at 64
 # bytes; WRITE_SIZE x1), and the VALU instructions per (b, d, t) (SQ_INSTS_VALU x 64 / B D L).
 # Valid only for the kernel source with this SHA-256 prefix; otherwise reported as null.
-MAIN_COUNTERS = {"src_sha256": "ae5b8104b96d2c5c", "fetch_bytes": 503828685, "write_bytes": 93198234,
-                 "valu_per_bdt": 86.69}
+MAIN_COUNTERS = {"src_sha256": "948bfebd2efa8503", "fetch_bytes": 507106918, "write_bytes": 91376230,
+                 "valu_per_bdt": 84.73}
 
 
 def progress(what):
