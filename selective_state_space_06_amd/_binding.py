@@ -69,6 +69,14 @@ def load_library(path: str = LIB_PATH):
                 raise RuntimeError(
                     f"{path} is missing: build it with `python -m selective_state_space_06_amd.build` "
                     "or __graft_entry__.build(); there is no fallback implementation")
+            # torch's ROCm wheel carries its own libamdhip64.so: load it first, so that this
+            # library binds to the HIP runtime torch's streams and allocations belong to (loaded
+            # first itself, it would pull in /opt/rocm's copy, and a second runtime in the process
+            # rejects torch's stream handles at launch)
+            try:
+                import torch  # noqa: F401
+            except ImportError:
+                pass
             lib = ctypes.CDLL(path)
             lib.mss_selective_scan_fwd.restype = ctypes.c_int
             lib.mss_selective_scan_fwd.argtypes = [_TP, _TP, _TP, _TP, _TP, _TP, _TP, _TP,
