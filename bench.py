@@ -51,8 +51,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, AMD published peak
 WORKLOAD = "mamba2p8b_bf16"
 # VALU issue ceiling: 256 CUs x 4 SIMDs, one wave64 fp32 instruction per 4 cycles each (16 lanes),
-# 2.4 GHz: 614.4e9 wave-instructions per second.  (Transcendentals take 2-3 such slots: measured
-# v_exp_f32 ~8.4 cycles, v_log_f32 / v_rcp_f32 ~12.5 cycles per wave instruction.)
+# 2.4 GHz: 614.4e9 wave-instructions per second.  (Transcendentals take longer than one such slot;
+# timing probes that are not shipped put v_exp_f32 near 8 and v_log_f32 / v_rcp_f32 near 12 cycles
+# per wave instruction -- unverified here, and nothing below depends on it.)
 VALU_WAVE_INSTR_PER_S = 256 * 4 * 2.4e9 / 4
 
 # The GPU's clocks ramp up over the first few hundred milliseconds of work after an idle spell
