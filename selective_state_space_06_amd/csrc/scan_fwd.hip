@@ -138,6 +138,42 @@ __device__ __forceinline__ float step_lane(float (&h)[SPL], const float (&A2)[SP
     return y;
 }
 
+// The power path at 16 states per lane keeps each lane's states scaled, g = h / sc with sc the
+// scale of the step last taken: step t takes s_t = x_t + copysign(2^-40, x_t) (never zero) and
+// computes g = (sc / s_t) abar^(n+1) g + B_t, so B enters the state update without a
+// multiplication by x (16 fewer per lane and step, against a reciprocal and three more
+// multiplications), and the caller scales the channel's C.g by s_t.  Adding s_t B_t for x_t B_t
+// moves each state by at most 2^-40 |B_t| per step (B is staged as 0 past a sequence's end).
+__device__ __forceinline__ float scale_of(float x) {
+#pragma clang fp contract(off)
+    return x + copysignf(0x1p-40f, x);
+}
+
+template <bool WANT_Y, int Q, int SPL>
+__device__ __forceinline__ float step_lane_scaled(float (&g)[SPL], const float (&A2)[SPL], float A2b, float dl,
+                                                  float r, const float* __restrict__ bc, int cofs) {
+    float Bv[SPL], Cv[SPL];
+#pragma unroll
+    for (int q = 0; q < SPL / 4; ++q) {
+        const float4 b4 = reinterpret_cast<const float4*>(bc)[q];
+        Bv[4 * q] = b4.x; Bv[4 * q + 1] = b4.y; Bv[4 * q + 2] = b4.z; Bv[4 * q + 3] = b4.w;
+        if (WANT_Y) {
+            const float4 c4 = reinterpret_cast<const float4*>(bc + cofs)[q];
+            Cv[4 * q] = c4.x; Cv[4 * q + 1] = c4.y; Cv[4 * q + 2] = c4.z; Cv[4 * q + 3] = c4.w;
+        }
+    }
+    const float a = fast_exp2(dl * A2b);
+    float p = r * (Q == 1 ? a : fast_exp2(dl * A2[0]));
+    float y = 0.0f;
+#pragma unroll
+    for (int n = 0; n < SPL; ++n) {
+        if (n) p *= a;
+        g[n] = fmaf(p, g[n], Bv[n]);
+        if (WANT_Y) y = n ? fmaf(Cv[n], g[n], y) : Cv[0] * g[0];
+    }
+    return y;
+}
+
 // Sum over the Q neighbouring lanes of a channel (Q = 1, 2, 4 or 8): quad_perm [1,0,3,2], then
 // [2,3,0,1], then row_half_mirror (lane i of each eight takes lane 7 - i, the other quad); every
 // lane of the group ends with the group's sum.
@@ -297,6 +333,8 @@ __device__ __forceinline__ void scan_body(const KArgs& a, Smem<N>& sm, const int
     const int k = lane % Q;              // its block of SPL states
     auto& w = sm.w[wave];
     float dsum = 0.0f;
+    constexpr bool SCALED = POW && SPL == 16;
+    float sc = 1.0f;  // SCALED: h = sc * g, the array h holding g
 
     // (Issuing the next tile's loads before the recurrence, to hide their latency, measured no
     // faster at d_state 64 and 128: the other wavefronts on the SIMD already hide it.)
@@ -314,17 +352,25 @@ __device__ __forceinline__ void scan_body(const KArgs& a, Smem<N>& sm, const int
             const float4 x4 = *reinterpret_cast<const float4*>(&w.x[c][tc]);
             const float dlv[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
             const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
-            float yv[4];
+            float yv[4], sv[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                yv[j] = step_lane<POW, MODE == kMain, Q, SPL>(h, A2, A2b, dlv[j], xv[j],
-                                                              &sm.bc[tc + j][bc_word(SPL * k)],
-                                                              bc_word(N + SPL * k) - bc_word(SPL * k));
+                if (SCALED) {
+                    sv[j] = scale_of(xv[j]);
+                    yv[j] = step_lane_scaled<MODE == kMain, Q, SPL>(h, A2, A2b, dlv[j], sc * fast_rcp(sv[j]),
+                                                                    &sm.bc[tc + j][bc_word(SPL * k)],
+                                                                    bc_word(N + SPL * k) - bc_word(SPL * k));
+                    sc = sv[j];
+                } else {
+                    yv[j] = step_lane<POW, MODE == kMain, Q, SPL>(h, A2, A2b, dlv[j], xv[j],
+                                                                  &sm.bc[tc + j][bc_word(SPL * k)],
+                                                                  bc_word(N + SPL * k) - bc_word(SPL * k));
+                }
                 if (MODE == kAgg) dsum += dlv[j];
             }
             if (MODE == kMain) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) yv[j] = group_sum<Q>(yv[j]);
+                for (int j = 0; j < 4; ++j) yv[j] = SCALED ? sv[j] * group_sum<Q>(yv[j]) : group_sum<Q>(yv[j]);
                 if (k == 0)
                     *reinterpret_cast<float4*>(&w.dl[c][tc]) = make_float4(yv[0], yv[1], yv[2], yv[3]);
             }
@@ -364,6 +410,10 @@ __device__ __forceinline__ void scan_body(const KArgs& a, Smem<N>& sm, const int
         }
     }
 
+    if (SCALED) {
+#pragma unroll
+        for (int n = 0; n < SPL; ++n) h[n] *= sc;  // back to the state itself
+    }
     if (MODE == kMain) {
         if (a.last_state && active && blockIdx.z == a.S - 1) {
             float4* dst = reinterpret_cast<float4*>(a.last_state + row * N + SPL * k);
