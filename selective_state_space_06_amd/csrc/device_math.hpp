@@ -39,6 +39,17 @@ __device__ __forceinline__ float silu(float v) {
     return v * fast_rcp(1.0f + fast_exp2(-v * kLog2e));
 }
 
+// The scale of one step in the forward kernels' scaled state form (S4D power path): the lane
+// keeps g = h / sc and step t takes s_t = x_t + copysign(2^-40, x_t), never zero, so B enters
+// the state update without a multiplication by x.  The addition is kept apart from the
+// multiplication that formed x (no fused multiply-add), so every kernel variant forms the same
+// s from the same x.
+constexpr float kScaleEps = 0x1p-40f;
+__device__ __forceinline__ float step_scale(float x) {
+#pragma clang fp contract(off)
+    return x + copysignf(kScaleEps, x);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {

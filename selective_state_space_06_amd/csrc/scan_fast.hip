@@ -247,22 +247,15 @@ struct Pair {
 };
 
 // The main kernel's power path keeps the state scaled: the lane holds g = h / sc, sc the scale
-// of the step last taken (1 where the state was set).  Step t takes the scale
-// s_t = x_t + copysign(kEps, x_t), never zero, and computes g_t = (sc / s_t) a^(n+1) g_(t-1) + B_t
+// of the step last taken (1 where the state was set).  Step t takes the scale s_t = step_scale(x_t)
+// = x_t + copysign(2^-40, x_t), never zero, and computes g_t = (sc / s_t) a^(n+1) g_(t-1) + B_t
 // and y_t = s_t (C_t . g_t) + D u_t: B enters the state update without a multiplication by x (16
-// fewer per step).  This adds s_t B_t instead of x_t B_t, kEps |B_t| per state and step away
-// from the recurrence: an absolute 2^-40 |B| per step, far below what the fp32 state resolves
-// at the magnitudes the tolerances allow (identity steps past a sequence's end stage B as 0 and
-// add nothing).  |g| <= |h| / kEps keeps g far from overflow.
-constexpr float kEps = 0x1p-40f;
-
-// s_t from x_t.  The addition is kept apart from the multiplication that formed x (no fused
-// multiply-add): every kernel variant then forms the same s from the same x, so a scan with
-// per-batch lengths equal to L gives the plain scan's results bit for bit.
-__device__ __forceinline__ float scale_of(float x) {
-#pragma clang fp contract(off)
-    return x + copysignf(kEps, x);
-}
+// fewer per step).  This adds s_t B_t instead of x_t B_t, 2^-40 |B_t| per state and step away
+// from the recurrence: an absolute deviation far below what the fp32 state resolves at the
+// magnitudes the tolerances allow (identity steps past a sequence's end stage B as 0 and add
+// nothing).  |g| <= |h| 2^40 keeps g far from overflow.  Every kernel variant forms the same s
+// from the same x, so a scan with per-batch lengths equal to L gives the plain scan's results
+// bit for bit.
 
 template <class E, bool SOFTPLUS, bool POW, bool WITH_DU, bool VARLEN = false>
 __device__ __forceinline__ Pair pair_of(const uint32_t* su, const uint32_t* sd, int j, const RowSetup& rs,
@@ -464,8 +457,8 @@ __device__ __forceinline__ void main_body(
                 pair_of<E, SOFTPLUS, POW, true, VARLEN>(su, sd, j + 2 < nsteps ? j + 2 : j, rs, t0);
             float y0, y1;
             if (SCALED) {
-                const float s0 = scale_of(cur.x[0]);
-                const float s1 = scale_of(cur.x[1]);
+                const float s0 = step_scale(cur.x[0]);
+                const float s1 = step_scale(cur.x[1]);
                 y0 = step_scaled(h, sc * fast_rcp(s0), cur.a[0], s0, sbc + j * 36, cur.du[0]);
                 y1 = step_scaled(h, s0 * fast_rcp(s1), cur.a[1], s1, sbc + (j + 1) * 36, cur.du[1]);
                 sc = s1;

@@ -139,15 +139,11 @@ __device__ __forceinline__ float step_lane(float (&h)[SPL], const float (&A2)[SP
 }
 
 // The power path at 16 states per lane keeps each lane's states scaled, g = h / sc with sc the
-// scale of the step last taken: step t takes s_t = x_t + copysign(2^-40, x_t) (never zero) and
+// scale of the step last taken: step t takes s_t = step_scale(x_t) = x_t + copysign(2^-40, x_t) and
 // computes g = (sc / s_t) abar^(n+1) g + B_t, so B enters the state update without a
 // multiplication by x (16 fewer per lane and step, against a reciprocal and three more
 // multiplications), and the caller scales the channel's C.g by s_t.  Adding s_t B_t for x_t B_t
 // moves each state by at most 2^-40 |B_t| per step (B is staged as 0 past a sequence's end).
-__device__ __forceinline__ float scale_of(float x) {
-#pragma clang fp contract(off)
-    return x + copysignf(0x1p-40f, x);
-}
 
 template <bool WANT_Y, int Q, int SPL>
 __device__ __forceinline__ float step_lane_scaled(float (&g)[SPL], const float (&A2)[SPL], float A2b, float dl,
@@ -356,7 +352,7 @@ __device__ __forceinline__ void scan_body(const KArgs& a, Smem<N>& sm, const int
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 if (SCALED) {
-                    sv[j] = scale_of(xv[j]);
+                    sv[j] = step_scale(xv[j]);
                     yv[j] = step_lane_scaled<MODE == kMain, Q, SPL>(h, A2, A2b, dlv[j], sc * fast_rcp(sv[j]),
                                                                     &sm.bc[tc + j][bc_word(SPL * k)],
                                                                     bc_word(N + SPL * k) - bc_word(SPL * k));
