@@ -91,6 +91,10 @@ typedef struct {
  * a multiple of 16 bytes and those tensors and B / C start 16-byte aligned, the vectorised
  * kernels run with aligned 16-byte accesses; any other valid layout runs the same kernels with
  * element-aligned accesses (about 1.5x the time on the Mamba-2.8B layer shape).
+ * Accuracy: fp32 arithmetic with an fp32 state.  Where every row of A is (n + 1) A[d, 0] exactly
+ * (bf16 rows at d_state 16, any rows at d_state 128) the kernels keep the state scaled by
+ * delta u and add (delta u + copysign(2^-40, delta u)) B in place of delta u B: at most
+ * 2^-40 |B| per state and step away from the recurrence.
  */
 int mss_selective_scan_fwd(const mss_tensor_t* u, const mss_tensor_t* delta,
                            const mss_tensor_t* A, const mss_tensor_t* B, const mss_tensor_t* C,
