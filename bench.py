@@ -84,9 +84,9 @@ def ramp_clocks(torch, fn, seconds=RAMP_S, batch=8):
 # the L2 fills whole 128-byte lines, one TCC_EA0_RDREQ each, and the counter prices a request at 64
 # bytes; WRITE_SIZE x1), and the VALU instructions per (b, d, t) (SQ_INSTS_VALU x 64 / B D L).
 # Valid only for the kernel source with this SHA-256 prefix; otherwise reported as null.  (Taken
-# on the source before the step scale's helper moved into device_math.hpp; every kernel compiles
-# to the same machine code from both.)
-MAIN_COUNTERS = {"src_sha256": "7cda057fb5ebb201", "fetch_bytes": 507106918, "write_bytes": 91376230,
+# on an earlier revision of this source that differs in comments and in where the step scale's
+# helper is defined; every kernel compiles to the same machine code from both.)
+MAIN_COUNTERS = {"src_sha256": "2339725ab3a89351", "fetch_bytes": 507106918, "write_bytes": 91376230,
                  "valu_per_bdt": 84.73}
 
 

@@ -447,8 +447,8 @@ __device__ __forceinline__ void main_body(
                 // streamed past the caches (read back only by the backward)
                 f32x4* sp = reinterpret_cast<f32x4*>(srow_saved + ((t0 + j) >> 3) * kN * R);
 #pragma unroll
-                for (int q = 0; q < kN / 4; ++q) {
-                    const f32x4 v = {sc * h[4 * q], sc * h[4 * q + 1], sc * h[4 * q + 2], sc * h[4 * q + 3]};  // sc = 1 unless SCALED
+                for (int q = 0; q < kN / 4; ++q) {  // h = sc g (sc stays 1 off the scaled path)
+                    const f32x4 v = {sc * h[4 * q], sc * h[4 * q + 1], sc * h[4 * q + 2], sc * h[4 * q + 3]};
                     __builtin_nontemporal_store(v, sp + q * R);
                 }
             }
