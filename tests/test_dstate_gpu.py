@@ -13,7 +13,7 @@ final state keeps the fp32 bound.
 import numpy as np
 import pytest
 
-from synth import sample_rows, scan_inputs
+from synth import scan_inputs
 from tests.gpu_helpers import (TOL_BF16, TOL_F32, assert_close, dev, host64, oracle_scan, record_margin,
                                run_scan)
 
@@ -126,13 +126,13 @@ def test_dstate_varlen(mss, oracle_mod, N):
     assert not np.any(go[t >= lens[np.arange(Bt * Dn) // Dn][:, None]])
 
 
-@pytest.mark.parametrize("N", [64, 128])
-def test_dstate_mamba2p8b_width_sampled(mss, oracle_mod, N):
+@pytest.mark.parametrize("N,a_kind", [(64, "s4d"), (128, "s4d"), (128, "random")])
+def test_dstate_mamba2p8b_width_all_rows(mss, oracle_mod, N, a_kind):
     """The Mamba-2.8B layer shape (4 x 5120 x 2048, bf16 activations) at d_state 64 and 128: every
-    output of 48 sampled rows, the first and last included, and their final states."""
-    s = scan_inputs(4, 5120, N, 2048, dtype="bf16", seed=760 + N)
-    rows = sample_rows(4 * 5120, 48, seed=N)
-    _check(mss, oracle_mod, s, f"d_state {N} mamba2p8b width", rows=rows)
+    output and final state of all 20480 rows against the oracle (S4D A: at d_state 128 the scaled
+    state step; random A: an exponential per update)."""
+    s = scan_inputs(4, 5120, N, 2048, dtype="bf16", seed=760 + N, a_kind=a_kind)
+    _check(mss, oracle_mod, s, f"d_state {N} mamba2p8b width" + ("" if a_kind == "s4d" else " random A"))
 
 
 def test_dstate_deterministic(mss):
