@@ -7,7 +7,7 @@ Tolerances as in test_parity_gpu.py: fp32 rtol 1e-4 / atol 1e-5; bf16 out rtol 2
 import numpy as np
 import pytest
 
-from synth import CONFIGS, sample_rows, scan_inputs
+from synth import CONFIGS, scan_inputs
 from tests.gpu_helpers import TOL_BF16, TOL_F32, assert_close, dev, host64, run_scan, waves_for
 
 pytestmark = pytest.mark.gpu
@@ -77,12 +77,12 @@ def test_with_state_generic_path(mss, oracle_mod, dtype, plan):
     _check(mss, oracle_mod, s, _h0(2, 96, 42), what=f"h0 generic {dtype}")
 
 
-def test_with_state_mamba2p8b_sampled(mss, oracle_mod):
+def test_with_state_mamba2p8b_all_rows(mss, oracle_mod):
+    """The 2.8B layer continued from a given state: all 20480 rows against the oracle."""
     c = CONFIGS["mamba2p8b_bf16"]
     s = scan_inputs(c["batch"], c["d_inner"], 16, c["L"], dtype="bf16", seed=43)
     h0 = _h0(c["batch"], c["d_inner"], 43)
-    rows = sample_rows(c["batch"] * c["d_inner"], 64, seed=43)
-    _check(mss, oracle_mod, s, h0, rows=rows, what="h0 mamba2p8b")
+    _check(mss, oracle_mod, s, h0, what="h0 mamba2p8b")
 
 
 def test_zero_or_absent_state_is_the_plain_scan(mss):
