@@ -590,6 +590,38 @@ def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, 
     return out
 
 
+class StateUpdateStep:
+    """mss_selective_state_update bound to fixed device buffers, for decode loops that refill the
+    same input buffers every token: the argument descriptors and the stream are taken once, here,
+    so each call costs one foreign-function call (the library still validates every call).
+    Arguments as for selective_state_update; `stream` defaults to the current stream of x's
+    device at construction.  The object keeps its tensors alive; calling it updates `state` in
+    place and writes `out` (returned)."""
+
+    def __init__(self, state, x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None, stream=None):
+        import torch
+        if not x.is_cuda:
+            raise ValueError("libmamba_scan takes device tensors")
+        if out is None:
+            out = torch.empty_like(x, memory_format=torch.contiguous_format)
+        if stream is None:
+            with torch.cuda.device(x.device):
+                stream = torch.cuda.current_stream(x.device).cuda_stream
+        elif not isinstance(stream, int):
+            stream = stream.cuda_stream
+        self.out = out
+        self._keep = (state, x, dt, A, B, C, D, z, dt_bias, out)
+        self._descs = [_desc(t) for t in self._keep]
+        self._args = tuple(_ref(d) for d in self._descs) + (stream,)
+        self._fn = load_library().mss_selective_state_update
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            raise MssError(st, "mss_selective_state_update")
+        return self.out
+
+
 def ssd_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True, return_last_state=True,
                  out=None, last_state=None):
     """Mamba-2 SSD layer (mss_ssd_scan_fwd) on the current stream of x's device.

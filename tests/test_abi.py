@@ -700,3 +700,13 @@ def test_ssd_empty_batch_is_ok(lib):
         t = a[k]
         a[k] = Tensor.make(t.data, t.dtype, [0] + [t.shape[i] for i in range(1, t.ndim)])
     assert call_ssd(a) == OK
+
+
+def test_bound_decode_step_refuses_host_tensors():
+    """StateUpdateStep takes device tensors only (it binds their device addresses once)."""
+    import torch
+    import selective_state_space_06_amd as m
+    t = torch.zeros((2, 8))
+    with pytest.raises(ValueError):
+        m.StateUpdateStep(torch.zeros((2, 8, 16)), t, t, torch.zeros((8, 16)), torch.zeros((2, 16)),
+                          torch.zeros((2, 16)))

@@ -1,0 +1,72 @@
+"""GPU tests of StateUpdateStep: mss_selective_state_update bound once to fixed device buffers,
+then called per token with its input buffers refilled in place (a decode loop).  Every row of
+every step against the fp64 oracle (tolerances as in the other decode tests), and bit for bit
+against the unbound call on a second state."""
+import numpy as np
+import pytest
+
+from synth import decode_inputs
+from tests.gpu_helpers import TOL_BF16, TOL_F32, assert_close, dev, host64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mss():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_06_amd as m
+    m.load_library()
+    return m
+
+
+@pytest.mark.parametrize("Bt,Dn,N,dtype,with_z,side_stream", [
+    (3, 333, 16, "bf16", True, False), (2, 130, 64, "f32", False, False), (4, 5120, 16, "bf16", True, True),
+])
+def test_bound_step_chain(mss, oracle_mod, Bt, Dn, N, dtype, with_z, side_stream):
+    import torch
+    steps = 5
+    di = decode_inputs(Bt, Dn, N, steps, dtype=dtype, with_z=with_z, seed=7 * Bt + Dn + N)
+    state0 = (0.5 * np.random.default_rng(Bt * Dn + N).standard_normal((Bt, Dn, N))).astype(np.float32)
+    state, state_ref = dev(state0), dev(state0)
+    A, D, bias = dev(di.A), dev(di.D), dev(di.dt_bias)
+    # the buffers the step is bound to, refilled every token
+    x, dt = dev(di.x[0], dtype), dev(di.dt[0], dtype)
+    z = dev(di.z[0], dtype) if with_z else None
+    Bb, Cb = dev(di.B[0]), dev(di.C[0])
+    stream = torch.cuda.Stream() if side_stream else None
+    step = mss.StateUpdateStep(state, x, dt, A, Bb, Cb, D=D, z=z, dt_bias=bias, stream=stream)
+    ref_state = state0.astype(np.float64).reshape(Bt * Dn, N).copy()
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    for s in range(steps):
+        x.copy_(dev(di.x[s], dtype)); dt.copy_(dev(di.dt[s], dtype))
+        Bb.copy_(dev(di.B[s])); Cb.copy_(dev(di.C[s]))
+        if with_z:
+            z.copy_(dev(di.z[s], dtype))
+        torch.cuda.synchronize()
+        out = step()
+        torch.cuda.synchronize()
+        out_ref = mss.selective_state_update(state_ref, x, dt, A, Bb, Cb, D=D, z=z, dt_bias=bias)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out_ref) and torch.equal(state, state_ref), f"step {s}: bound != unbound"
+        ref = oracle_mod.selective_state_update(ref_state, di.x[s], di.dt[s], di.A, di.B[s], di.C[s], D=di.D,
+                                                z=di.z[s] if with_z else None, dt_bias=di.dt_bias,
+                                                rows=np.arange(Bt * Dn))
+        assert_close(host64(out).reshape(-1), ref.reshape(-1), what=f"bound step out {s}", **tol)
+        assert_close(host64(state).reshape(Bt * Dn, N), ref_state, what=f"bound step state {s}", **TOL_F32)
+
+
+def test_bound_step_rejects_bad_shapes_per_call(mss):
+    """Validation runs on every call: a buffer bound with the wrong shape is refused (before any
+    GPU work) each time the step is called."""
+    import torch
+    state = torch.zeros((2, 64, 16), device="cuda")
+    x = torch.zeros((2, 65), device="cuda")  # d_inner does not match the state
+    dt = torch.zeros((2, 64), device="cuda")
+    A, Bv, Cv = -torch.ones((64, 16), device="cuda"), torch.zeros((2, 16), device="cuda"), torch.zeros((2, 16), device="cuda")
+    step = mss.StateUpdateStep(state, x, dt, A, Bv, Cv, out=torch.empty((2, 64), device="cuda"))
+    for _ in range(2):
+        with pytest.raises(mss.MssError):
+            step()
+    assert torch.count_nonzero(state) == 0
