@@ -215,9 +215,32 @@ def decode_hbm_chain(mss, torch, devc, steps=1024, states=16, pool=64, N=None):
     us = e0.elapsed_time(e1) * 1e3 / (reps * pool)
     nbytes = decode_bytes(Bt, Dn, N)
     gbps = nbytes / (us * 1e-6) / 1e9
+    # for comparison: torch's own in-place elementwise kernel (state *= 0.5) over the same states in
+    # the same graph-chain shape, which reads and writes each step's state once and nothing else
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        for k in range(pool):
+            st[k % states].mul_(0.5)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(gr):
+        for k in range(pool):
+            st[k % states].mul_(0.5)
+    gr.replay()
+    torch.cuda.synchronize()
+    ramp_clocks(torch, lambda k: gr.replay(), batch=1)
+    e0.record()
+    for _ in range(reps):
+        gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    rmw_us = e0.elapsed_time(e1) * 1e3 / (reps * pool)
+    rmw_bytes = 2 * Bt * Dn * N * 4
     return {"shape": [Bt, Dn, N], "distinct_states": states, "state_bytes_total": states * Bt * Dn * N * 4,
             "steps": reps * pool, "graph_us_per_step": round(us, 3), "graph_gbps": round(gbps, 1),
             "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "torch_inplace_scale_same_states": {"us_per_step": round(rmw_us, 3),
+                                                "gbps": round(rmw_bytes / (rmw_us * 1e-6) / 1e9, 1)},
             "note": f"each step's state is one of {states} ({states * Bt * Dn * N * 4 / 1e6:.0f} MB in all, above "
                     "the 256 MB Infinity Cache): HBM-resident"}
 

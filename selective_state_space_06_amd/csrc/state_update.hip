@@ -10,9 +10,10 @@
 // (generation benchmarks) run the model this way, one token at a time.
 //
 // The step reads and writes the (batch, d_inner, N) fp32 state once (N = 16, 32, 64 or 128) and is
-// bound by memory traffic.  Four lanes share a row (N / 4 states each, 16 B per access, a row's
-// four lanes covering 64 contiguous bytes); the partial C.h sums meet through two DPP quad-permute
-// adds.
+// bound by memory traffic.  N / 4 lanes share a row, one 16-byte vector of states each, so the 64
+// lanes of a wave cover 64 / (N / 4) whole consecutive rows: every load and store of the state is
+// one contiguous KiB.  The partial C.h sums meet through DPP quad-permute adds and, for N > 16,
+// lane-exchange adds across the quads of the row.
 #include "device_math.hpp"
 #include "mss_internal.hpp"
 
@@ -40,24 +41,34 @@ __device__ __forceinline__ float quad_sum(float v) {
     return v;
 }
 
-// Threads stride over the rows' quads (the grid is capped: a dispatch holds at most 2^32 - 1
-// work-items per dimension).  The stride is a multiple of four, so the four lanes of a row stay
-// together in every iteration and the quad's DPP sum sees only its own row.  Lane q of a row holds
-// the states 4 (4 v + q) .. + 3 for v < N / 16 (each 16-byte load of the row's four lanes covers 64
-// contiguous bytes).  For N = 16 each thread takes kItems quads per round, one stride apart, and
-// issues all their loads before any arithmetic: the step is bound by the latency of its state
-// reads, and this doubles the reads in flight.  (An item past the end re-reads the round's first
-// quad and stores nothing; a quad is valid or invalid as a whole, so the DPP sums of valid rows
-// see only valid lanes.)
+// Sum over the LR lanes of a row (LR = 4, 8, 16 or 32 consecutive lanes, aligned): every lane of
+// the row ends with the row's sum.
+template <int LR>
+__device__ __forceinline__ float row_sum(float v) {
+    v = quad_sum(v);
+    if (LR >= 8) v += __shfl_xor(v, 4);
+    if (LR >= 16) v += __shfl_xor(v, 8);
+    if (LR >= 32) v += __shfl_xor(v, 16);
+    return v;
+}
+
+// Threads stride over the rows' lanes (the grid is capped: a dispatch holds at most 2^32 - 1
+// work-items per dimension).  The stride is a multiple of LR, so the lanes of a row stay together
+// in every iteration and the row sum sees only its own row; lane k of a row holds states
+// 4 k .. 4 k + 3.  Each thread takes kItems rows per round, one stride apart, and issues all their
+// loads before any arithmetic: the step is bound by the latency of its state reads, and this
+// doubles the reads in flight (64 x 5120 states in HBM: 12.4 -> 12.0 us at N = 16; four items
+// were slower at every N).  An item past the end re-reads the round's first row and stores
+// nothing; a row is valid or invalid as a whole, so the sums of valid rows see only valid lanes.
 constexpr int kItems = 2;
 
 template <class E, bool HAS_Z, int N>
 __global__ __launch_bounds__(256) void state_update_kernel(DArgs a) {
-    constexpr int VQ = N / 16;                  // 16-byte vectors of a row per lane
-    constexpr int IT = N == 16 ? kItems : 1;    // quads per thread and round
-    const int64_t total = a.rows * 4;
+    constexpr int LR = N / 4;  // lanes per row
+    constexpr int IT = kItems;
+    const int64_t total = a.rows * LR;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    const int q = static_cast<int>(threadIdx.x & 3);
+    const int k = static_cast<int>(threadIdx.x & (LR - 1));
     const float4* st4 = reinterpret_cast<const float4*>(a.state);
     const float4* A4p = reinterpret_cast<const float4*>(a.A);
     const float4* B4p = reinterpret_cast<const float4*>(a.B);
@@ -66,44 +77,36 @@ __global__ __launch_bounds__(256) void state_update_kernel(DArgs a) {
         int64_t row[IT], d[IT];
         bool ok[IT];
         float xv[IT], dtv[IT], zv[IT], bias[IT];
-        float4 s[IT][VQ], A4[IT][VQ], B4[IT][VQ], C4[IT][VQ];
+        float4 s[IT], A4[IT], B4[IT], C4[IT];
 #pragma unroll
         for (int u = 0; u < IT; ++u) {
             const int64_t gt = g0 + u * stride;
             ok[u] = gt < total;
-            row[u] = (ok[u] ? gt : g0) >> 2;  // flat (b, d)
+            row[u] = (ok[u] ? gt : g0) / LR;  // flat (b, d)
             d[u] = row[u] % a.Dn;
             const int64_t b = row[u] / a.Dn;
             xv[u] = E::load1(a.x, row[u]);
             dtv[u] = E::load1(a.dt, row[u]);
             zv[u] = HAS_Z ? E::load1(a.z, row[u]) : 0.0f;
             bias[u] = a.bias ? a.bias[d[u]] : 0.0f;
-#pragma unroll
-            for (int v = 0; v < VQ; ++v) {
-                const int k = 4 * v + q;
-                s[u][v] = st4[row[u] * (N / 4) + k];
-                A4[u][v] = A4p[d[u] * (N / 4) + k];
-                B4[u][v] = B4p[b * (N / 4) + k];
-                C4[u][v] = C4p[b * (N / 4) + k];
-            }
+            s[u] = st4[row[u] * LR + k];
+            A4[u] = A4p[d[u] * LR + k];
+            B4[u] = B4p[b * LR + k];
+            C4[u] = C4p[b * LR + k];
         }
 #pragma unroll
         for (int u = 0; u < IT; ++u) {
             const float dl = softplus(dtv[u] + bias[u]);
             const float dx = dl * xv[u];
-            float y = 0.0f;
-#pragma unroll
-            for (int v = 0; v < VQ; ++v) {
-                float4 hn;
-                hn.x = fmaf(fast_exp2(dl * (A4[u][v].x * kLog2e)), s[u][v].x, dx * B4[u][v].x);
-                hn.y = fmaf(fast_exp2(dl * (A4[u][v].y * kLog2e)), s[u][v].y, dx * B4[u][v].y);
-                hn.z = fmaf(fast_exp2(dl * (A4[u][v].z * kLog2e)), s[u][v].z, dx * B4[u][v].z);
-                hn.w = fmaf(fast_exp2(dl * (A4[u][v].w * kLog2e)), s[u][v].w, dx * B4[u][v].w);
-                if (ok[u]) reinterpret_cast<float4*>(a.state)[row[u] * (N / 4) + 4 * v + q] = hn;
-                y = fmaf(C4[u][v].w, hn.w, fmaf(C4[u][v].z, hn.z, fmaf(C4[u][v].y, hn.y, fmaf(C4[u][v].x, hn.x, y))));
-            }
-            y = quad_sum(y);
-            if (q == 0 && ok[u]) {
+            float4 hn;
+            hn.x = fmaf(fast_exp2(dl * (A4[u].x * kLog2e)), s[u].x, dx * B4[u].x);
+            hn.y = fmaf(fast_exp2(dl * (A4[u].y * kLog2e)), s[u].y, dx * B4[u].y);
+            hn.z = fmaf(fast_exp2(dl * (A4[u].z * kLog2e)), s[u].z, dx * B4[u].z);
+            hn.w = fmaf(fast_exp2(dl * (A4[u].w * kLog2e)), s[u].w, dx * B4[u].w);
+            if (ok[u]) reinterpret_cast<float4*>(a.state)[row[u] * LR + k] = hn;
+            float y = fmaf(C4[u].w, hn.w, fmaf(C4[u].z, hn.z, fmaf(C4[u].y, hn.y, C4[u].x * hn.x)));
+            y = row_sum<LR>(y);
+            if (k == 0 && ok[u]) {
                 float o = fmaf(a.D ? a.D[d[u]] : 0.0f, xv[u], y);
                 if (HAS_Z) o *= silu(zv[u]);
                 E::store1(a.out, row[u], o);
@@ -114,9 +117,8 @@ __global__ __launch_bounds__(256) void state_update_kernel(DArgs a) {
 
 template <class E, bool HAS_Z, int N>
 hipError_t launch_t(const DArgs& k, hipStream_t stream) {
-    constexpr int IT = N == 16 ? kItems : 1;
-    const int64_t threads = k.rows * 4;
-    int64_t blocks = (threads + 256 * IT - 1) / (256 * IT);
+    const int64_t threads = k.rows * (N / 4);
+    int64_t blocks = (threads + 256 * kItems - 1) / (256 * kItems);
     if (blocks > (1 << 22)) blocks = 1 << 22;
     state_update_kernel<E, HAS_Z, N><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(k);
     return hipGetLastError();

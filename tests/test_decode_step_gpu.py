@@ -23,6 +23,7 @@ def mss():
 
 @pytest.mark.parametrize("Bt,Dn,N,dtype,with_z,side_stream", [
     (3, 333, 16, "bf16", True, False), (2, 130, 64, "f32", False, False), (4, 5120, 16, "bf16", True, True),
+    (2, 96, 128, "bf16", True, False), (1, 70, 32, "f32", True, True),
 ])
 def test_bound_step_chain(mss, oracle_mod, Bt, Dn, N, dtype, with_z, side_stream):
     import torch
