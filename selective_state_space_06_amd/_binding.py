@@ -590,6 +590,16 @@ def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, 
     return out
 
 
+def _bound_stream(x, stream):
+    import torch
+    if not x.is_cuda:
+        raise ValueError("libmamba_scan takes device tensors")
+    if stream is None:
+        with torch.cuda.device(x.device):
+            return torch.cuda.current_stream(x.device).cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
 class StateUpdateStep:
     """mss_selective_state_update bound to fixed device buffers, for decode loops that refill the
     same input buffers every token: the argument descriptors and the stream are taken once, here,
@@ -600,15 +610,9 @@ class StateUpdateStep:
 
     def __init__(self, state, x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None, stream=None):
         import torch
-        if not x.is_cuda:
-            raise ValueError("libmamba_scan takes device tensors")
+        stream = _bound_stream(x, stream)
         if out is None:
             out = torch.empty_like(x, memory_format=torch.contiguous_format)
-        if stream is None:
-            with torch.cuda.device(x.device):
-                stream = torch.cuda.current_stream(x.device).cuda_stream
-        elif not isinstance(stream, int):
-            stream = stream.cuda_stream
         self.out = out
         self._keep = (state, x, dt, A, B, C, D, z, dt_bias, out)
         self._descs = [_desc(t) for t in self._keep]
@@ -619,6 +623,30 @@ class StateUpdateStep:
         st = self._fn(*self._args)
         if st != 0:
             raise MssError(st, "mss_selective_state_update")
+        return self.out
+
+
+class Conv1dUpdateStep:
+    """mss_causal_conv1d_update bound to fixed device buffers (the one-token conv of a decode loop,
+    in front of StateUpdateStep): descriptors and stream taken once, here.  Arguments as for
+    causal_conv1d_update; calling it shifts `state` in place and writes `out` (returned)."""
+
+    def __init__(self, state, x, weight, bias=None, silu=True, out=None, stream=None):
+        import torch
+        stream = _bound_stream(x, stream)
+        if out is None:
+            out = torch.empty_like(x, memory_format=torch.contiguous_format)
+        self.out = out
+        self._keep = (state, x, weight, bias, out)
+        d = [_desc(t) for t in self._keep]
+        self._descs = d
+        self._args = (_ref(d[0]), _ref(d[1]), _ref(d[2]), _ref(d[3]), 1 if silu else 0, _ref(d[4]), stream)
+        self._fn = load_library().mss_causal_conv1d_update
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            raise MssError(st, "mss_causal_conv1d_update")
         return self.out
 
 

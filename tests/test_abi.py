@@ -710,3 +710,5 @@ def test_bound_decode_step_refuses_host_tensors():
     with pytest.raises(ValueError):
         m.StateUpdateStep(torch.zeros((2, 8, 16)), t, t, torch.zeros((8, 16)), torch.zeros((2, 16)),
                           torch.zeros((2, 16)))
+    with pytest.raises(ValueError):
+        m.Conv1dUpdateStep(torch.zeros((2, 8, 3)), t, torch.zeros((8, 4)))

@@ -1,7 +1,7 @@
-"""GPU tests of StateUpdateStep: mss_selective_state_update bound once to fixed device buffers,
-then called per token with its input buffers refilled in place (a decode loop).  Every row of
-every step against the fp64 oracle (tolerances as in the other decode tests), and bit for bit
-against the unbound call on a second state."""
+"""GPU tests of StateUpdateStep and Conv1dUpdateStep: the one-token entry points bound once to
+fixed device buffers, then called per token with their input buffers refilled in place (a decode
+loop).  Every row of every step against the fp64 oracle (tolerances as in the other decode tests),
+and bit for bit against the unbound call on a second state."""
 import numpy as np
 import pytest
 
@@ -71,3 +71,38 @@ def test_bound_step_rejects_bad_shapes_per_call(mss):
         with pytest.raises(mss.MssError):
             step()
     assert torch.count_nonzero(state) == 0
+
+
+@pytest.mark.parametrize("dtype,K,silu", [("bf16", 4, True), ("f32", 3, False), ("bf16", 2, True)])
+def test_bound_conv_update_chain(mss, oracle_mod, dtype, K, silu):
+    """Conv1dUpdateStep over a chain of tokens (its x buffer refilled per token): bit for bit the
+    unbound call, and the whole chain equal to the oracle's conv over the sequence."""
+    import torch
+    rng = np.random.default_rng(K)
+    Bt, Dn, L = 3, 200, 6
+    x = rng.standard_normal((Bt, Dn, L)).astype(np.float32)
+    w = (0.5 * rng.standard_normal((Dn, K))).astype(np.float32)
+    b = (0.1 * rng.standard_normal(Dn)).astype(np.float32)
+    st0 = rng.standard_normal((Bt, Dn, K - 1)).astype(np.float32)
+    if dtype == "bf16":
+        from synth import round_to_bf16
+        x, st0 = round_to_bf16(x), round_to_bf16(st0)
+    wd, bd = dev(w), dev(b)
+    state, state_ref = dev(st0, dtype), dev(st0, dtype)
+    xb = dev(x[..., 0], dtype)
+    step = mss.Conv1dUpdateStep(state, xb, wd, bd, silu=silu, stream=torch.cuda.Stream())
+    outs = []
+    for t in range(L):
+        xb.copy_(dev(np.ascontiguousarray(x[..., t]), dtype))
+        torch.cuda.synchronize()
+        step()  # on its own stream: wait for it before reading out on this one
+        torch.cuda.synchronize()
+        out = step.out.clone()
+        ref_out = mss.causal_conv1d_update(state_ref, xb, wd, bd, silu=silu)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(state, state_ref), f"token {t}: bound != unbound"
+        outs.append(host64(out))
+    ref, rfin = oracle_mod.causal_conv1d(x, w, b, state=st0, silu=silu)
+    assert_close(np.stack(outs, -1), ref, what="bound conv update chain",
+                 **(TOL_BF16 if dtype == "bf16" else TOL_F32))
+    np.testing.assert_array_equal(host64(state), rfin)
