@@ -106,3 +106,38 @@ def test_bound_conv_update_chain(mss, oracle_mod, dtype, K, silu):
     assert_close(np.stack(outs, -1), ref, what="bound conv update chain",
                  **(TOL_BF16 if dtype == "bf16" else TOL_F32))
     np.testing.assert_array_equal(host64(state), rfin)
+
+
+def test_bound_steps_replayed_from_a_graph(mss):
+    """A chain of bound steps captured in a HIP graph on their own stream: every replay (with eager
+    work and synchronisations between them) matches the unbound eager chain from the same state,
+    bit for bit."""
+    import torch
+    Bt, Dn, N, steps = 4, 640, 16, 8
+    di = decode_inputs(Bt, Dn, N, steps, dtype="bf16", with_z=True, seed=99)
+    A, D, bias = dev(di.A), dev(di.D), dev(di.dt_bias)
+    X, DT, Z = dev(di.x, "bf16"), dev(di.dt, "bf16"), dev(di.z, "bf16")
+    Bs, Cs = dev(di.B), dev(di.C)
+    state_g = dev((0.5 * np.random.default_rng(5).standard_normal((Bt, Dn, N))).astype(np.float32))
+    state_e = torch.empty_like(state_g)
+    outs_g = torch.zeros((steps, Bt, Dn), dtype=torch.bfloat16, device="cuda")
+    outs_e = torch.empty_like(outs_g)
+    s = torch.cuda.Stream()
+    bound = [mss.StateUpdateStep(state_g, X[j], DT[j], A, Bs[j], Cs[j], D=D, z=Z[j], dt_bias=bias, out=outs_g[j],
+                                 stream=s) for j in range(steps)]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for step in bound:
+            step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        state_e.copy_(state_g)
+        for j in range(steps):
+            mss.selective_state_update(state_e, X[j], DT[j], A, Bs[j], Cs[j], D=D, z=Z[j], dt_bias=bias,
+                                       out=outs_e[j])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs_g, outs_e), f"replay {rep}: out"
+        assert torch.equal(state_g, state_e), f"replay {rep}: state"
