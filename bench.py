@@ -34,7 +34,9 @@ wave64 fp32 VALU instruction on a 16-lane SIMD (1024 SIMDs at 2.4 GHz).
 
 Beside the headline the line carries legs for the rest of the path: the backward, the causal
 conv, the forward at shard shapes and with an unstructured A, the decode chain (cache- and
-HBM-resident states), the fp32 workloads, and Mamba-2's SSD layer at d_state 64 and 128
+HBM-resident states; launches through the per-call wrapper, through bound steps and from a HIP
+graph; beside the HBM-resident chains, torch's own in-place elementwise kernel over the same
+states as a reference for what one launch over those bytes reaches), the fp32 workloads, and Mamba-2's SSD layer at d_state 64 and 128
 (`ssd_scan`: call time, algorithmic GB/s and HBM fraction, MFMA TFLOP/s of the chunked form).
 """
 from __future__ import annotations
