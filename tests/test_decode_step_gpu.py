@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 from synth import decode_inputs
-from tests.gpu_helpers import TOL_BF16, TOL_F32, assert_close, dev, host64
+from tests.gpu_helpers import TOL_BF16, TOL_F32, assert_close, dev, host64, record_margin
 
 pytestmark = pytest.mark.gpu
 
@@ -54,8 +54,11 @@ def test_bound_step_chain(mss, oracle_mod, Bt, Dn, N, dtype, with_z, side_stream
         ref = oracle_mod.selective_state_update(ref_state, di.x[s], di.dt[s], di.A, di.B[s], di.C[s], D=di.D,
                                                 z=di.z[s] if with_z else None, dt_bias=di.dt_bias,
                                                 rows=np.arange(Bt * Dn))
-        assert_close(host64(out).reshape(-1), ref.reshape(-1), what=f"bound step out {s}", **tol)
-        assert_close(host64(state).reshape(Bt * Dn, N), ref_state, what=f"bound step state {s}", **TOL_F32)
+        record_margin(f"bound decode step {Bt}x{Dn}x{N} {dtype} out",
+                      assert_close(host64(out).reshape(-1), ref.reshape(-1), what=f"bound step out {s}", **tol))
+        record_margin(f"bound decode step {Bt}x{Dn}x{N} {dtype} state",
+                      assert_close(host64(state).reshape(Bt * Dn, N), ref_state, what=f"bound step state {s}",
+                                   **TOL_F32))
 
 
 def test_bound_step_rejects_bad_shapes_per_call(mss):
@@ -103,8 +106,9 @@ def test_bound_conv_update_chain(mss, oracle_mod, dtype, K, silu):
         assert torch.equal(out, ref_out) and torch.equal(state, state_ref), f"token {t}: bound != unbound"
         outs.append(host64(out))
     ref, rfin = oracle_mod.causal_conv1d(x, w, b, state=st0, silu=silu)
-    assert_close(np.stack(outs, -1), ref, what="bound conv update chain",
-                 **(TOL_BF16 if dtype == "bf16" else TOL_F32))
+    record_margin(f"bound conv update K={K} {dtype}",
+                  assert_close(np.stack(outs, -1), ref, what="bound conv update chain",
+                               **(TOL_BF16 if dtype == "bf16" else TOL_F32)))
     np.testing.assert_array_equal(host64(state), rfin)
 
 
